@@ -1,0 +1,57 @@
+"""fp64 CPU oracle for the Infini-attention block forward.
+
+This package is TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call it. The product
+path (the HIP library and its Python binding) never imports it, and it imports
+nothing from the product path: the two share no code. Its inputs are plain
+numpy arrays; its arithmetic is numpy float64.
+
+Sources (page title, then section):
+
+* "Infini-Attention" (AI Wiki), section "What happens inside the
+  Infini-attention block?": the local causal softmax attention A_dot, the
+  memory retrieval A_mem = sigma(Q) M / (sigma(Q) z) with sigma = ELU + 1, and
+  the per-head sigmoid gate A = sigmoid(beta) A_mem + (1 - sigmoid(beta)) A_dot.
+* same page, section "How does the compressive memory work?": the delta-rule
+  update of M, the update of z, and the additive (linear) variant.
+* same page, section "Why is the memory footprint bounded?": segments of fixed
+  length N, with the state (M, z) carried and nothing else.
+* "Hugging Face Infini-Attention Reproduction Analysis", section
+  "Infini-Attention Mechanism", steps 1-6: the per-segment order (segment,
+  local attention, retrieval from M_{s-1}, gate, update, carry only the
+  memory).
+
+Pins (each function is checked against something other than itself in
+``tests/test_oracle_pins.py``):
+
+* ``feature_map``       -- torch ``elu`` + 1, special values.
+* ``gate_weight``       -- ``scipy.special.expit``.
+* ``local_causal_attention`` -- torch ``scaled_dot_product_attention``
+  (fp64, is_causal) and a per-token scalar softmax loop.
+* ``memory_retrieval``  -- the block-strictly-causal quadratic form (closed
+  form of the linear recurrence), causal linear attention at seg_len 1,
+  constant-value invariant, a hand-worked example in exact dyadic rationals.
+* ``memory_update`` (linear) -- segmentation independence and the one-shot
+  sums over all keys, the hand-worked example.
+* ``memory_update`` (delta)  -- the hand-worked two-segment d = 2 example,
+  zero-residual invariance, the d = 1 scalar closed form, equality with the
+  linear rule from a zero memory, joint linearity in (V, M0), the affine
+  transition form.
+* ``forward``           -- single-segment reduction to causal attention,
+  gate extremes, chunked calls with a carried state, GQA equal to MHA on
+  repeated K/V, batch/head permutation.
+
+No function here is "parity unpinned".
+"""
+
+from .infini_attention import (  # noqa: F401
+    RULES,
+    feature_map,
+    gate_weight,
+    local_causal_attention,
+    memory_retrieval,
+    memory_update,
+    num_segments,
+    forward,
+)
+from .compare import max_rel_err, slice_errors  # noqa: F401

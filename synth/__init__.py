@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the Infini-attention block forward.
+
+This module holds the workload table and the input generators, and nothing of
+the method's arithmetic. Both sides of every parity check (the HIP library and
+the fp64 oracle) receive the same tensors made here; the oracle reads them back
+as float64 on the host.
+
+Every (tensor, batch, head) slice is drawn from its own torch generator, seeded
+from ``numpy.random.SeedSequence([config_seed, tensor_id, b, h])``, so any slice
+can be regenerated alone. Draws are N(0, 1) in float32, scaled in float32 where
+a workload asks for it, then rounded to the workload's dtype (round to nearest
+even for bfloat16). The same seed gives different numbers on a CPU and on a GPU
+generator; a parity check always gives both sides one set of tensors.
+
+The pages evaluate on PG19, Arxiv-math, BookSum and passkey data; none of that
+is used. These Gaussian inputs take the shapes the pages describe instead:
+2048-token segments and a 1M-token stream ("Infini-Attention" (AI Wiki),
+"Why is the memory footprint bounded?" and "Can Infini-attention retrieve a
+passkey at one million tokens?"), and 16 rollouts of 64-token segments
+("Hugging Face Infini-Attention Reproduction Analysis", "Weight Decay and
+Rollouts").
+"""
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "outlier": 4}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    d: int
+    seg_len: int
+    dtype: str  # "f32" or "bf16"
+    rules: tuple
+    seed: int
+    key_std: float = 1.0
+    key_outlier_p: float = 0.0
+    key_outlier_scale: float = 1.0
+    z0: float = 1e-6
+    note: str = field(default="", compare=False)
+
+    @property
+    def segments(self):
+        return -(-self.L // self.seg_len)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", B=1, Hq=2, Hkv=2, L=64, d=32, seg_len=16, dtype="f32",
+        rules=("linear",), seed=0,
+        note="B1 H2 d32, 4 segments of 16, fp32, linear rule"),
+    "hf_repro": Workload(
+        "hf_repro", B=8, Hq=16, Hkv=16, L=1024, d=64, seg_len=64, dtype="bf16",
+        rules=("linear", "delta"), seed=1,
+        note="B8 H16 d64, 16 rollouts of 64-token segments, bf16"),
+    "llama3_8b": Workload(
+        "llama3_8b", B=4, Hq=32, Hkv=8, L=32768, d=128, seg_len=2048,
+        dtype="bf16", rules=("delta",), seed=2,
+        note="B4, 32 query / 8 KV heads, d128, 16 segments of 2048, bf16"),
+    "long_stream": Workload(
+        "long_stream", B=1, Hq=16, Hkv=16, L=1048576, d=128, seg_len=2048,
+        dtype="bf16", rules=("linear",), seed=3, key_std=1.0 / math.sqrt(128),
+        note="B1 H16 d128, 512 segments of 2048 (1M tokens), keys std 1/sqrt(d)"),
+    "small_segment": Workload(
+        "small_segment", B=16, Hq=32, Hkv=32, L=32768, d=128, seg_len=128,
+        dtype="bf16", rules=("delta",), seed=4, key_outlier_p=0.05,
+        key_outlier_scale=8.0,
+        note="B16 H32 d128, 256 segments of 128, 5% of key rows scaled by 8"),
+}
+
+
+def slice_seed(config_seed, tensor, b, h):
+    """64-bit seed of one (tensor, batch, head) slice."""
+    ss = np.random.SeedSequence([config_seed, TENSOR_IDS[tensor], b, h])
+    return int(ss.generate_state(1, dtype=np.uint64)[0])
+
+
+def _normal(shape, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def _uniform(shape, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def make_inputs(w, device="cpu"):
+    """Inputs of workload ``w`` on ``device``.
+
+    Returns a dict with q [B,Hq,L,d], k and v [B,Hkv,L,d] in the workload's
+    dtype, beta [Hq] float32, M0 [B,Hkv,d,d] float32 (zeros) and z0 [B,Hkv,d]
+    float32 (all ``w.z0``).
+    """
+    dt = w.torch_dtype
+    q = torch.empty((w.B, w.Hq, w.L, w.d), dtype=dt, device=device)
+    k = torch.empty((w.B, w.Hkv, w.L, w.d), dtype=dt, device=device)
+    v = torch.empty((w.B, w.Hkv, w.L, w.d), dtype=dt, device=device)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            q[b, h] = _normal((w.L, w.d), slice_seed(w.seed, "q", b, h), device).to(dt)
+        for h in range(w.Hkv):
+            kk = _normal((w.L, w.d), slice_seed(w.seed, "k", b, h), device)
+            if w.key_std != 1.0:
+                kk = kk * w.key_std
+            if w.key_outlier_p > 0.0:
+                pick = _uniform((w.L,), slice_seed(w.seed, "outlier", b, h), device)
+                kk = torch.where((pick < w.key_outlier_p)[:, None],
+                                 kk * w.key_outlier_scale, kk)
+            k[b, h] = kk.to(dt)
+            v[b, h] = _normal((w.L, w.d), slice_seed(w.seed, "v", b, h), device).to(dt)
+    beta = _normal((w.Hq,), slice_seed(w.seed, "beta", 0, 0), device)
+    M0 = torch.zeros((w.B, w.Hkv, w.d, w.d), dtype=torch.float32, device=device)
+    z0 = torch.full((w.B, w.Hkv, w.d), w.z0, dtype=torch.float32, device=device)
+    return dict(q=q, k=k, v=v, beta=beta, M0=M0, z0=z0)
+
+
+def to_f64(t):
+    """A tensor (any dtype, any device) as a float64 numpy array on the host."""
+    return t.detach().to("cpu", torch.float32).double().numpy()
+
+
+def flops(w, rule):
+    """Algorithmic matrix-product FLOPs of one forward call.
+
+    Per (query head, token): 2d(N+1) for the causal QK^T and PV with the
+    diagonal counted (the mean of 2d per visible key over a segment of N is
+    2d(N+1)/2 each for QK^T and PV), 2d^2 for sigma(Q) M, and per (KV head,
+    token) 2d^2 (linear) or 4d^2 (delta) for the update. Summed exactly over
+    segments so a short final segment is counted as it is.
+    """
+    d = w.d
+    per_seg = []
+    for s in range(w.segments):
+        n = min(w.seg_len, w.L - s * w.seg_len)
+        local = 2 * d * n * (n + 1)  # both products over the causal triangle
+        retrieval = 2 * n * d * d
+        update = (2 if rule == "linear" else 4) * n * d * d
+        per_seg.append(w.Hq * (local + retrieval) + w.Hkv * update)
+    return w.B * sum(per_seg)
+
+
+def hbm_bytes(w):
+    """Compulsory HBM bytes of one call: Q, K, V read once, out written once,
+    the fp32 state read and written once, beta read once."""
+    e = 4 if w.dtype == "f32" else 2
+    return (e * w.d * w.L * w.B * (2 * w.Hq + 2 * w.Hkv)
+            + 8 * w.B * w.Hkv * (w.d * w.d + w.d) + 4 * w.Hq)
