@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the Infini-attention block forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+One step is one infini_attn_forward call over the whole workload (every
+segment, every head): the memory scan and the fused local-attention /
+retrieval / gate kernel, on synthetic Gaussian inputs already resident in HBM.
+W untimed steps, then K timed steps between two device synchronisations.
+Prints one JSON line: tokens/s (B*L / step time), TFLOP/s and its fraction of
+the bf16 MFMA peak, the roofline record of the dominant kernel (timed with HIP
+events on the stream it runs on) and the fp64 CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "Infini-attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 1×MI355X"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc", "attn.hip")
+
+
+def attn_kernel_flops(w):
+    """Algorithmic matrix-product FLOPs of the attention kernel in one call:
+    per (query head, token) 2d(N+1) for the causal QK^T and PV (diagonal
+    counted) and 2d^2 for sigma(Q) M, summed exactly over segments."""
+    total = 0
+    for s in range(w.segments):
+        n = min(w.seg_len, w.L - s * w.seg_len)
+        total += 2 * w.d * n * (n + 1) + 2 * n * w.d * w.d
+    return w.B * w.Hq * total
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from committed rocprofv3 counters, or
+    None when there are none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, rule, inp, target_s):
+    """The fp64 oracle, as it is, on whole (batch, KV head) units of the same
+    workload until about target_s seconds have run."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from tests.parity import unit_inputs
+
+    G = w.Hq // w.Hkv
+    order = [(b, j) for b in range(w.B) for j in range(w.Hkv)]
+    done, elapsed = 0, 0.0
+    for b, j in order:
+        u = unit_inputs(inp, b, j, G)
+        t0 = time.perf_counter()
+        oracle.forward(u["q"], u["k"], u["v"], u["beta"], u["M0"], u["z0"], w.seg_len, rule)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= target_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    tokens = w.B * w.L * done / len(order)
+    return {
+        "value": tokens / elapsed,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {len(order)} (batch, KV head) units, each {G} query heads x "
+                   f"{w.segments} segments of {w.seg_len}; fp64 numpy, {elapsed:.1f} s; "
+                   f"value = B*L*{done}/{len(order)} tokens / time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--rule", default=None, choices=["linear", "delta"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import compressive_memory_transformers_amd as lib
+
+    w = synth.WORKLOADS[args.workload]
+    rule = args.rule or w.rules[-1]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_inputs(w, dev)
+    out = torch.empty_like(inp["q"])
+    M = torch.empty_like(inp["M0"])
+    z = torch.empty_like(inp["z0"])
+    full, _ = lib.workspace_size(w.B, w.Hq, w.Hkv, w.L, w.d, w.seg_len, rule, inp["q"].dtype)
+    ws = torch.empty(full, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                    w.seg_len, rule, out=out, M_final=M, z_final=z, workspace=ws,
+                    stream=stream, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-phase events for every timed step; recorded once first so each
+    # underlying HIP event exists before the library records it
+    phase = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for evs in phase:
+        for e in evs:
+            e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(phase[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+
+    ms = start.elapsed_time(end) / args.steps
+    scan_ms = sum(e[0].elapsed_time(e[1]) for e in phase) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in phase) / args.steps
+
+    tokens = w.B * w.L
+    flops = synth.flops(w, rule)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    a_flops = attn_kernel_flops(w)
+    a_tflops = a_flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V in HBM; random beta; M0 = 0, z0 = 1e-6)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "d": w.d,
+                   "seg_len": w.seg_len, "segments": w.segments, "rule": rule},
+        "tflops": tflops,
+        "frac_of_peak": tflops / peak,
+        "peak_tflops": peak,
+        "head_tokens_per_s": w.B * w.Hq * w.L / (ms * 1e-3),
+        "hbm_gbs_compulsory": synth.hbm_bytes(w) / (ms * 1e-3) / 1e9,
+        "phase_ms": {"scan": scan_ms, "attn": attn_ms},
+        "roofline": {
+            "kernel": "attn_kernel (local causal attention + retrieval + gate)",
+            "bound": "mfma",
+            "achieved": a_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": a_tflops / peak,
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": a_flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, rule, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""ctypes binding of libinfini_attn.so (include/infini_attn.h).
+
+Argument marshalling only: shapes are read off torch tensors, data pointers and
+the current HIP stream are passed to the C entry points, and a non-OK status
+becomes an exception. Every step of the computation runs in the library's HIP
+kernels; nothing here computes a result, and there is no fallback: if the
+library is missing or a call fails, an error is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+RULES = {"linear": 0, "delta": 1}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+# (name, restype, argtypes) of every entry point the header declares
+SIGNATURES = {
+    "infini_attn_workspace_size": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
+    "infini_attn_forward": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_forward_timed": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
+        + [ctypes.POINTER(_c_p), _c_i32]),
+    "infini_attn_status_string": (ctypes.c_char_p, [_c_i32]),
+    "infini_attn_version": (_c_i32, []),
+}
+
+_lib = None
+
+
+class InfiniAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path():
+    return os.environ.get("INFINI_ATTN_LIB", LIB_PATH)
+
+
+def load_library():
+    """Load libinfini_attn.so once; raise ImportError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python compressive_memory_transformers_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().infini_attn_status_string(int(status)).decode()
+
+
+def version():
+    return int(load_library().infini_attn_version())
+
+
+def workspace_size(B, Hq, Hkv, L, d, seg_len, rule, dtype):
+    """(full_bytes, min_bytes) of the workspace for these sizes."""
+    lib = load_library()
+    full, least = _c_size(0), _c_size(0)
+    st = lib.infini_attn_workspace_size(B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[dtype],
+                                        ctypes.byref(full), ctypes.byref(least))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_workspace_size")
+    return int(full.value), int(least.value)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_final=None,
+            workspace=None, stream=None, events=None):
+    """Infini-attention block forward on the GPU.
+
+    q [B,Hq,L,d], k and v [B,Hkv,L,d] (float32 or bfloat16, contiguous, on one
+    GPU), beta [Hq] float32, M0 [B,Hkv,d,d] float32, z0 [B,Hkv,d] float32.
+    Returns (out, M_final, z_final). Output buffers and a workspace (a uint8
+    tensor) may be passed in; M_final may be M0 and z_final may be z0. Runs on
+    ``stream`` (a torch.cuda.Stream) or torch's current stream, asynchronously.
+    ``events``: optional list of torch.cuda.Event to record around each phase
+    (see infini_attn_forward_timed); each must have been recorded once so that
+    its HIP event exists.
+    """
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if not (k.shape == v.shape == (B, Hkv, L, d)):
+        raise ValueError(f"k and v must be [B,Hkv,L,d]; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+        raise ValueError("beta, M0 or z0 has the wrong shape")
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
+    if beta.dtype != torch.float32 or M0.dtype != torch.float32 or z0.dtype != torch.float32:
+        raise TypeError("beta, M0 and z0 must be float32")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
+    tensors = [q, k, v, beta, M0, z0]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    for t in tensors:
+        if t.device != dev:
+            raise ValueError("all tensors must be on one GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    if M_final is None:
+        M_final = torch.empty_like(M0)
+    if z_final is None:
+        z_final = torch.empty_like(z0)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if M_final.shape != M0.shape or z_final.shape != z0.shape:
+        raise ValueError("M_final / z_final must have the shapes of M0 / z0")
+    if workspace is None:
+        full, _ = workspace_size(B, Hq, Hkv, L, d, seg_len, rule, q.dtype)
+        workspace = torch.empty(full, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    args = [B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[q.dtype],
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+            _ptr(out), _ptr(M_final), _ptr(z_final),
+            _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream.cuda_stream)]
+    if events:
+        handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib.infini_attn_forward_timed(*args, handles, len(events))
+        name = "infini_attn_forward_timed"
+    else:
+        st = lib.infini_attn_forward(*args)
+        name = "infini_attn_forward"
+    if st != 0:
+        raise InfiniAttnError(st, name)
+    return out, M_final, z_final

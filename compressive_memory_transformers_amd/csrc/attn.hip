@@ -1,0 +1,264 @@
+// Local causal attention with the memory retrieval and the gate fused in.
+//
+// "Infini-Attention" (AI Wiki), "What happens inside the Infini-attention
+// block?": A_dot = causal softmax(Q K^T / sqrt(d)) V inside the segment,
+// A_mem = sigma(Q) M_{s-1} / (sigma(Q) z_{s-1}), and
+// out = sigmoid(beta) A_mem + (1 - sigmoid(beta)) A_dot.
+//
+// One workgroup computes 32*NW query rows of one (batch, query head, segment);
+// every segment of a window runs in parallel, because the only thing a segment
+// needs from its predecessors is the state snapshot the scan wrote.
+//
+// Each wave owns 32 query rows and forms S^T = K Q^T rather than Q K^T: in the
+// 32x32 accumulator a lane then holds one query (its column) and 16 keys, so a
+// query's running max and sum need only one exchange between the two
+// half-waves, and the probabilities sit in registers exactly where the B
+// operand of O^T += V^T P^T wants them (keys in the accumulator's row order).
+// Q stays in registers for the whole key loop; K tiles are staged in LDS row
+// major, V tiles transposed, so every MFMA operand is a 16- or 8-byte LDS read.
+//
+// The retrieval reuses the output accumulator: after the key loop the
+// accumulator is scaled by (1 - g)/l per query, and one more product
+// O^T += M^T (g sigma(Q) / den)^T adds the gated memory read, with the
+// per-query factor g/den folded into the B operand.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infini {
+
+namespace {
+
+template <typename T, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = 32 * NW;
+  constexpr int NC = D / 16;    // 16-wide chunks of the head dimension
+  constexpr int NDB = D / 32;   // 32-row blocks of the value dimension
+  constexpr int NKB = BN / 32;  // 32-key blocks of a key tile
+  constexpr int NPC = BN / 16;  // 16-key chunks of a key tile
+  constexpr int KS = D + pad16<T>();
+  constexpr int VS = BN + pad16<T>();
+
+  __shared__ __align__(16) T Ks[BN * KS];  // K tile, [key][dim]
+  __shared__ __align__(16) T Vt[D * VS];   // V tile transposed, [dim][key]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+
+  // Tile order. Hardware hands consecutive workgroups to the 8 XCDs in turn;
+  // remapping makes each XCD take a contiguous range of logical tiles, so the
+  // query tiles and grouped heads that read one segment's K/V share an L2.
+  // Within a (batch, KV head, segment) group the heaviest query tiles (the
+  // longest causal rows) come first.
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int G = a.Hq / a.Hkv;
+  const int in_grp = a.n_qt * G;
+  const int grp = t / in_grp, rr = t % in_grp;
+  const int qt = a.n_qt - 1 - rr / G;
+  const int hg = rr % G;
+  const int sl = grp % a.s_count;
+  const int unit = grp / a.s_count;  // b * Hkv + kv head
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int hq = kvh * G + hg;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int q0 = qt * BM;
+  if (q0 >= n_s) return;  // the tail of a short last segment; uniform per workgroup
+
+  const int64_t qh = (int64_t)b * a.Hq + hq;
+  const T* Q = static_cast<const T*>(a.q) + (qh * a.L + seg_start) * D;
+  const T* K = static_cast<const T*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const T* V = static_cast<const T*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  T* O = static_cast<T*>(a.out) + (qh * a.L + seg_start) * D;
+
+  const int row = q0 + 32 * w + i;  // this lane's query, relative to the segment
+  const bool wave_on = q0 + 32 * w < n_s;
+  const int wave_last = min(q0 + 32 * w + 31, n_s - 1);
+
+  // B operand of S^T = K Q^T: column i is query `row`, k = 16c + 8h + e.
+  frag_t<T> qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = zero_frag<T>();
+    if (row < n_s) qf[c] = load8<T>(Q + (int64_t)row * D + 16 * c + 8 * h);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
+  float m_run = -INFINITY;  // running max of this query's scaled scores (log2 units)
+  float l_run = 0.f;        // this half-wave's share of the running softmax sum
+
+  const int n_kv = min(q0 + BM, n_s);  // keys any row of the workgroup can see
+  const int n_kt = (n_kv + BN - 1) / BN;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BN;
+    __syncthreads();  // the previous tile has been read by every wave
+    for (int c = tid; c < BN * (D / 8); c += NT) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      frag_t<T> val = zero_frag<T>();
+      if (k0 + r < n_s) val = load8<T>(K + (int64_t)(k0 + r) * D + col);
+      store8<T>(Ks + r * KS + col, val);
+    }
+    for (int c = tid; c < (BN / 4) * (D / 4); c += NT) {
+      const int d4 = c % (D / 4), k4 = c / (D / 4);
+      vec4_t<T> x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = zero4<T>();
+        if (k0 + 4 * k4 + j < n_s) x[j] = load4<T>(V + (int64_t)(k0 + 4 * k4 + j) * D + 4 * d4);
+      }
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        vec4_t<T> y;
+        y[0] = x[0][dd]; y[1] = x[1][dd]; y[2] = x[2][dd]; y[3] = x[3][dd];
+        store4<T>(Vt + (4 * d4 + dd) * VS + 4 * k4, y);
+      }
+    }
+    __syncthreads();
+    if (!wave_on || k0 > wave_last) continue;  // every key of the tile is after every row of the wave
+
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = zero16();
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        mma32(sacc[kb], load8<T>(Ks + (32 * kb + i) * KS + 16 * c + 8 * h), qf[c]);
+    }
+
+    const bool need_mask = k0 + BN - 1 > q0 + 32 * w;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[kb][r] * a.scale_log2;
+        if (need_mask && k0 + 32 * kb + acc_row(r, h) > row) x = -INFINITY;
+        sacc[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Key 0 of the segment is visible to every row, so after the first tile
+    // m_new is finite and alpha is well defined.
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+    frag_t<T> pf[NPC];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+        l_run += p;
+        pf[2 * kb + (r >> 3)][r & 7] = from_f32<T>(p);
+      }
+    // O^T += V^T P^T. Element e of pf[pc] is key 16pc + 8(e/4) + 4h + e%4 of
+    // the tile, so the A operand reads two runs of four keys from Vt.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int pc = 0; pc < NPC; ++pc) {
+        const T* vrow = Vt + (32 * db + i) * VS + 16 * pc + 4 * h;
+        mma32(oacc[db], load4x2<T>(vrow, vrow + 8), pf[pc]);
+      }
+    m_run = m_new;
+  }
+  if (!wave_on) return;  // no barrier follows
+
+  const float l = l_run + __shfl_xor(l_run, 32);
+  const int64_t snap = (int64_t)unit * a.s_count + sl;
+  const float* zs = a.snapZ + snap * D;
+  const T* Mts = static_cast<const T*>(a.snapM) + snap * D * D;
+
+  float sq[NC][8];
+  float dp = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = feature_map(to_f32<T>(qf[c][e]));
+      sq[c][e] = s;
+      dp += s * zs[16 * c + 8 * h + e];
+    }
+  const float den = dp + __shfl_xor(dp, 32);
+  const float g = 1.f / (1.f + __expf(-a.beta[hq]));
+  const float ca = (1.f - g) / l, cm = g / den;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] *= ca;
+  frag_t<T> sf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sf[c][e] = from_f32<T>(sq[c][e] * cm);
+  // O^T += M^T (g sigma(Q)/den)^T; the snapshot is M^T, [value][key].
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      mma32(oacc[db], load8<T>(Mts + (int64_t)(32 * db + i) * D + 16 * c + 8 * h), sf[c]);
+
+  if (row < n_s) {
+    T* orow = O + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        vec4_t<T> y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = from_f32<T>(oacc[db][4 * rq + j]);
+        store4<T>(orow + 32 * db + 8 * rq + 4 * h, y);
+      }
+  }
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_attn_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
+  constexpr int BN = 64;
+  const int64_t G = a.Hq / a.Hkv;
+  const int64_t total = units * a.s_count * a.n_qt * G;
+  hipLaunchKernelGGL((attn_kernel<T, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attn_w(const AttnArgs& a, int64_t units, hipStream_t stream) {
+  switch (attn_waves(a.seg_len < a.L ? a.seg_len : a.L)) {
+    case 1: return launch_attn_t<T, D, 1>(a, units, stream);
+    case 2: return launch_attn_t<T, D, 2>(a, units, stream);
+    default: return launch_attn_t<T, D, 4>(a, units, stream);
+  }
+}
+
+template <typename T>
+hipError_t launch_attn_d(int d, const AttnArgs& a, int64_t units, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_attn_w<T, 32>(a, units, stream);
+    case 64: return launch_attn_w<T, 64>(a, units, stream);
+    case 128: return launch_attn_w<T, 128>(a, units, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int attn_waves(int64_t seg_len) { return seg_len <= 32 ? 1 : (seg_len <= 64 ? 2 : 4); }
+
+hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream) {
+  return dtype == kBF16 ? launch_attn_d<bf16>(d, a, units, stream)
+                        : launch_attn_d<float>(d, a, units, stream);
+}
+
+}  // namespace infini

@@ -1,0 +1,143 @@
+/*
+ * infini_attn.h -- C ABI of the Infini-attention block forward on gfx950.
+ *
+ * The operation ("Infini-Attention" (AI Wiki), sections "What happens inside
+ * the Infini-attention block?" and "How does the compressive memory work?";
+ * "Hugging Face Infini-Attention Reproduction Analysis", section
+ * "Infini-Attention Mechanism", steps 1-6):
+ *
+ *   the length-L stream is cut into segments of seg_len tokens (the last one
+ *   may be shorter); for segment s, with Q_s, K_s, V_s its rows and (M, z) the
+ *   state left by segment s-1,
+ *     A_dot = causal softmax(Q_s K_s^T / sqrt(d)) V_s        (inside the segment)
+ *     A_mem = sigma(Q_s) M / (sigma(Q_s) z)                   (one scalar per row)
+ *     out_s = sigmoid(beta_h) A_mem + (1 - sigmoid(beta_h)) A_dot
+ *   then the state absorbs the segment:
+ *     linear: M += sigma(K_s)^T V_s
+ *     delta:  M += sigma(K_s)^T (V_s - sigma(K_s) M / (sigma(K_s) z))
+ *     both:   z += sum_t sigma(K_s,t)
+ *   with sigma(x) = ELU(x) + 1 = (x > 0 ? x + 1 : exp(x)). Retrieval and the
+ *   delta prediction both read the state from before the segment. Only (M, z)
+ *   crosses a segment boundary.
+ *
+ * Readings of what the pages leave open: the softmax scale is 1/sqrt(d) with d
+ * the head width; there is one (M, z) per (batch element, KV head) with M of
+ * shape (d, d), and grouped query heads h read the memory of KV head
+ * h / (Hq / Hkv); the causal mask keeps the diagonal; sigma applies to the
+ * unscaled Q and K; no epsilon is added to any denominator (z0 > 0 makes them
+ * positive).
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   q, out      [B][Hq][L][d]      element type `dtype`
+ *   k, v        [B][Hkv][L][d]     element type `dtype`
+ *   beta        [Hq]               float (raw beta; the sigmoid is applied inside)
+ *   M0, M_final [B][Hkv][d][d]     float, M[key dim][value dim]
+ *   z0, z_final [B][Hkv][d]        float, every entry > 0 (not checked)
+ *
+ * Ownership: the caller owns every buffer, including the workspace; the
+ * library allocates no device memory and keeps no mutable global state, so
+ * calls on different streams with different workspaces may run concurrently.
+ * `out` must not overlap any input. M_final may be M0 and z_final may be z0
+ * (an in-place carry); any other overlap is rejected.
+ *
+ * Errors: every check runs on the host before anything is enqueued; on an
+ * error nothing is written and nothing launches. Execution is asynchronous on
+ * `stream`: a fault inside a kernel surfaces at the caller's next
+ * synchronisation. NaN or Inf inputs are not checked; they stay inside the
+ * (batch, head) slices they touch.
+ */
+#ifndef INFINI_ATTN_H
+#define INFINI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Memory update rule ("How does the compressive memory work?"). */
+typedef enum {
+  INFINI_RULE_LINEAR = 0, /* M += sigma(K)^T V (the additive variant) */
+  INFINI_RULE_DELTA = 1   /* M += sigma(K)^T (V - sigma(K) M / (sigma(K) z)) */
+} infini_rule_t;
+
+/* Element type of q, k, v and out. The state is always float. */
+typedef enum {
+  INFINI_F32 = 0,  /* float in and out; every product in float */
+  INFINI_BF16 = 1  /* bfloat16 in and out; bf16 MFMA operands, float accumulation */
+} infini_dtype_t;
+
+typedef enum {
+  INFINI_OK = 0,
+  INFINI_ERR_INVALID_ARG = 1, /* a size < 1, Hq % Hkv != 0, a null pointer, a bad enum, a forbidden overlap */
+  INFINI_ERR_UNSUPPORTED = 2, /* d not in {32, 64, 128} */
+  INFINI_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned */
+  INFINI_ERR_WORKSPACE = 4,   /* workspace smaller than infini_attn_workspace_size's minimum */
+  INFINI_ERR_HIP = 5          /* the HIP runtime refused a launch or a copy */
+} infini_status_t;
+
+/*
+ * Workspace sizes of a forward call with these sizes, in bytes.
+ *   *full_bytes: enough to process every segment in one pass (fastest);
+ *   *min_bytes:  the least the call accepts; it then walks the segments in
+ *                windows that fit, which adds launches but gives the same
+ *                result bit for bit.
+ * Pure host function; touches no device. Either output pointer may be NULL.
+ * Returns INFINI_ERR_INVALID_ARG / INFINI_ERR_UNSUPPORTED for sizes that
+ * infini_attn_forward would reject.
+ */
+infini_status_t infini_attn_workspace_size(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype, size_t* full_bytes, size_t* min_bytes);
+
+/*
+ * The block forward: out, M_final, z_final from q, k, v, beta, M0, z0.
+ *   B, Hq, Hkv, L, d, seg_len: sizes (all >= 1, Hq % Hkv == 0, d in {32, 64, 128});
+ *   rule: an infini_rule_t; dtype: an infini_dtype_t;
+ *   q, k, v, beta, M0, z0: inputs (device pointers, layouts above);
+ *   out, M_final, z_final: outputs (device pointers, layouts above);
+ *   workspace, workspace_bytes: caller-owned device scratch (256-byte aligned
+ *     recommended, 16 required), at least the minimum size above;
+ *   stream: a hipStream_t, or NULL for the null stream.
+ * Returns INFINI_OK once every kernel is enqueued.
+ */
+infini_status_t infini_attn_forward(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * infini_attn_forward, plus HIP events recorded on `stream` around its
+ * kernels, for timing each phase. The segments run in windows (one window
+ * when the workspace has the full size); for window w the call records
+ *   events[3w + 0] before the memory scan of the window,
+ *   events[3w + 1] after the scan, before the attention kernel,
+ *   events[3w + 2] after the attention kernel,
+ * for every index below n_events; later windows record nothing. `events`
+ * holds hipEvent_t handles the caller created (as void*); none may be NULL.
+ * Everything else is as in infini_attn_forward.
+ */
+infini_status_t infini_attn_forward_timed(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
+/* A static, human-readable name of a status code. Never NULL. */
+const char* infini_attn_status_string(int32_t status);
+
+/* The ABI version: major * 10000 + minor * 100 + patch. */
+int32_t infini_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFINI_ATTN_H */

@@ -1,0 +1,66 @@
+"""Helpers shared by the GPU parity tests: run the library and the oracle on
+the same inputs and measure the worst slice error (normwise for out and M,
+per element for z)."""
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+def tolerance(dtype):
+    return F32_TOL if dtype == torch.float32 else BF16_TOL
+
+
+def unit_inputs(inp, b, j, G):
+    """float64 host copies of one (batch, KV head) unit's inputs, with
+    leading dimensions of size 1 so the oracle sees B = Hkv = 1."""
+    sl = slice(j * G, (j + 1) * G)
+    return dict(
+        q=synth.to_f64(inp["q"][b:b + 1, sl]),
+        k=synth.to_f64(inp["k"][b:b + 1, j:j + 1]),
+        v=synth.to_f64(inp["v"][b:b + 1, j:j + 1]),
+        beta=synth.to_f64(inp["beta"][sl]),
+        M0=synth.to_f64(inp["M0"][b:b + 1, j:j + 1]),
+        z0=synth.to_f64(inp["z0"][b:b + 1, j:j + 1]),
+    )
+
+
+def compare_units(inp, result, seg_len, rule, units, out_segments=None):
+    """Run the oracle on each (b, j) of ``units`` and return the worst errors
+    (out, M_final, z_final) of the GPU result over those units."""
+    out, M, z = result
+    Hq, Hkv = inp["q"].shape[1], inp["k"].shape[1]
+    G = Hq // Hkv
+    worst = [0.0, 0.0, 0.0]
+    for b, j in units:
+        u = unit_inputs(inp, b, j, G)
+        ro, rM, rz = oracle.forward(u["q"], u["k"], u["v"], u["beta"], u["M0"], u["z0"],
+                                    seg_len, rule, out_segments=out_segments)
+        go = synth.to_f64(out[b:b + 1, j * G:(j + 1) * G])
+        gM = synth.to_f64(M[b:b + 1, j:j + 1])
+        gz = synth.to_f64(z[b:b + 1, j:j + 1])
+        worst[0] = max(worst[0], oracle.slice_errors(go, ro))
+        worst[1] = max(worst[1], oracle.slice_errors(gM, rM))
+        worst[2] = max(worst[2], oracle.slice_errors(gz, rz, elementwise=True))
+    return tuple(worst)
+
+
+def all_units(B, Hkv):
+    return [(b, j) for b in range(B) for j in range(Hkv)]
+
+
+def random_inputs(B, Hq, Hkv, L, d, dtype, device, seed=0, m0_scale=0.0, z0=1e-6):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    mk = lambda *s: torch.randn(*s, generator=g, dtype=torch.float32)
+    inp = dict(
+        q=mk(B, Hq, L, d).to(dtype), k=mk(B, Hkv, L, d).to(dtype), v=mk(B, Hkv, L, d).to(dtype),
+        beta=mk(Hq), M0=m0_scale * mk(B, Hkv, d, d),
+        z0=(torch.full((B, Hkv, d), z0) if m0_scale == 0.0
+            else 0.5 + torch.rand(B, Hkv, d, generator=g)),
+    )
+    return {k: v.to(device).contiguous() for k, v in inp.items()}

@@ -1,0 +1,192 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects bad arguments before touching a device. No kernel runs here: every
+forward call below carries an argument the host checks refuse."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infini_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from compressive_memory_transformers_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from compressive_memory_transformers_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(infini_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_status_string",
+        "infini_attn_version", "infini_attn_workspace_size"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from compressive_memory_transformers_amd import binding
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SIGNATURES
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", nm, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950(lib):
+    from compressive_memory_transformers_amd import binding
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_version_and_status_strings(lib):
+    assert lib.infini_attn_version() == 100
+    names = {s: lib.infini_attn_status_string(s).decode() for s in range(7)}
+    assert names[0] == "ok" and names[4] == "workspace too small"
+    assert names[6] == "unknown status"
+    assert lib.infini_attn_status_string(-3).decode() == "unknown status"
+
+
+def ws(lib, *args):
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib.infini_attn_workspace_size(*args, ctypes.byref(full), ctypes.byref(least))
+    return st, full.value, least.value
+
+
+def test_workspace_sizes(lib):
+    # Llama-3-8B-shaped, bf16: 32 units, 16 segments of d*d bf16 + d floats
+    st, full, least = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 1)
+    assert st == 0
+    per_seg = 32 * (128 * 128 * 2 + 128 * 4)
+    assert full - least == 15 * per_seg
+    assert least >= per_seg + 2 * 32 * (128 * 128 + 128) * 4
+    st, full32, _ = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 0)
+    assert st == 0 and full32 > full
+    # a ragged final segment counts as a segment
+    st, a, _ = ws(lib, 1, 1, 1, 100, 32, 30, 0, 0)
+    st, b, _ = ws(lib, 1, 1, 1, 120, 32, 30, 0, 0)
+    assert a == b
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 1, 8, 32, 4, 0, 0), 1),     # B < 1
+    ((1, 3, 2, 8, 32, 4, 0, 0), 1),     # Hq % Hkv
+    ((1, 1, 1, 0, 32, 4, 0, 0), 1),     # L < 1
+    ((1, 1, 1, 8, 32, 0, 0, 0), 1),     # seg_len < 1
+    ((1, 1, 1, 8, 32, 4, 2, 0), 1),     # bad rule
+    ((1, 1, 1, 8, 32, 4, 0, 5), 1),     # bad dtype
+    ((1, 1, 1, 8, 48, 4, 0, 0), 2),     # d unsupported
+    ((1, 1, 1, 8, 256, 4, 0, 0), 2),
+    ((1 << 20, 1 << 20, 1, 1 << 20, 128, 4, 0, 1), 1),  # element count overflow
+])
+def test_workspace_size_rejects(lib, args, status):
+    assert ws(lib, *args)[0] == status
+
+
+class FakeBuffers:
+    """Distinct, aligned, never-dereferenced addresses sized like real buffers."""
+
+    def __init__(self, B, Hq, Hkv, L, d, e):
+        sizes = dict(q=B * Hq * L * d * e, k=B * Hkv * L * d * e, v=B * Hkv * L * d * e,
+                     beta=Hq * 4, M0=B * Hkv * d * d * 4, z0=B * Hkv * d * 4,
+                     out=B * Hq * L * d * e, M_final=B * Hkv * d * d * 4, z_final=B * Hkv * d * 4,
+                     workspace=1 << 40)
+        base = 1 << 44
+        self.addr, self.size = {}, sizes
+        for name, n in sizes.items():
+            self.addr[name] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+
+
+def call(lib, shape, bufs, **over):
+    B, Hq, Hkv, L, d, N, rule, dt = shape
+    a = {**bufs.addr, **over}
+    wsb = over.get("workspace_bytes", bufs.size["workspace"])
+    return lib.infini_attn_forward(
+        B, Hq, Hkv, L, d, N, rule, dt,
+        *[ctypes.c_void_p(a[n]) for n in ("q", "k", "v", "beta", "M0", "z0", "out", "M_final",
+                                           "z_final", "workspace")],
+        wsb, None)
+
+
+SHAPE = (2, 4, 2, 64, 32, 16, 1, 1)
+
+
+def test_forward_rejects_bad_sizes(lib):
+    bufs = FakeBuffers(2, 4, 2, 64, 32, 2)
+    assert call(lib, (2, 3, 2, 64, 32, 16, 1, 1), bufs) == 1
+    assert call(lib, (2, 4, 2, 64, 40, 16, 1, 1), bufs) == 2
+    assert call(lib, (2, 4, 2, 64, 32, 16, 7, 1), bufs) == 1
+    assert call(lib, (2, 4, 2, 64, 32, 16, 1, 9), bufs) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "beta", "M0", "z0", "out", "M_final", "z_final",
+                                  "workspace"])
+def test_forward_rejects_null_and_misaligned(lib, name):
+    bufs = FakeBuffers(2, 4, 2, 64, 32, 2)
+    assert call(lib, SHAPE, bufs, **{name: None}) == 1
+    assert call(lib, SHAPE, bufs, **{name: bufs.addr[name] + 8}) == 3
+
+
+def test_forward_rejects_overlaps(lib):
+    bufs = FakeBuffers(2, 4, 2, 64, 32, 2)
+    a = bufs.addr
+    assert call(lib, SHAPE, bufs, out=a["q"]) == 1
+    assert call(lib, SHAPE, bufs, out=a["k"] + 256) == 1
+    assert call(lib, SHAPE, bufs, M_final=a["z0"]) == 1
+    assert call(lib, SHAPE, bufs, z_final=a["M0"] + 16) == 1
+    assert call(lib, SHAPE, bufs, M_final=a["M0"] + 16) == 1    # partial overlap
+    assert call(lib, SHAPE, bufs, workspace=a["v"]) == 1
+    assert call(lib, SHAPE, bufs, M_final=a["out"]) == 1
+
+
+def test_forward_rejects_small_workspace(lib):
+    bufs = FakeBuffers(2, 4, 2, 64, 32, 2)
+    _, full, least = ws(lib, 2, 4, 2, 64, 32, 16, 1, 1)
+    assert call(lib, SHAPE, bufs, workspace_bytes=least - 1) == 4
+    assert call(lib, SHAPE, bufs, workspace_bytes=0) == 4
+
+
+def test_binding_validates_before_the_library():
+    import compressive_memory_transformers_amd as m
+    x = torch.zeros(1, 2, 8, 32)
+    with pytest.raises(ValueError):
+        m.forward(x, x[:, :1], x, torch.zeros(2), torch.zeros(1, 1, 32, 32),
+                  torch.ones(1, 1, 32), 4, "linear")
+    with pytest.raises(ValueError):
+        m.forward(x, x, x, torch.zeros(2), torch.zeros(1, 2, 32, 32), torch.ones(1, 2, 32),
+                  4, "hebbian")
+    with pytest.raises(ValueError):  # host tensors are refused: no CPU path exists
+        m.forward(x, x, x, torch.zeros(2), torch.zeros(1, 2, 32, 32), torch.ones(1, 2, 32),
+                  4, "linear")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    env = dict(os.environ, INFINI_ATTN_LIB=str(tmp_path / "absent.so"))
+    res = subprocess.run([sys.executable, "-c", "import compressive_memory_transformers_amd"],
+                         cwd=ROOT, env=env, capture_output=True, text=True)
+    assert res.returncode != 0
+    assert "is not built" in res.stderr
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "compressive_memory_transformers_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f

@@ -1,0 +1,200 @@
+"""Parity of the HIP library with the fp64 oracle, on the GPU.
+
+Each case prints what it runs before touching the GPU, so a failure names it.
+Large workloads are checked at their full sizes, in the launch configuration
+the benchmark times, on sampled (batch, KV head) units (and, for the 1M-token
+stream, on sampled segments of the output; the state chain is always checked
+whole). The oracle is exact for every slice it computes.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.parity import (all_units, compare_units, random_inputs, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import compressive_memory_transformers_amd as m
+    return m
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run(lib, inp, seg_len, rule, **kw):
+    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                      seg_len, rule, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def check(inp, res, seg_len, rule, units, tol, out_segments=None):
+    eo, eM, ez = compare_units(inp, res, seg_len, rule, units, out_segments)
+    _say(f"errors out={eo:.3e} M={eM:.3e} z={ez:.3e} (tol {tol:g})")
+    assert eo <= tol and eM <= tol and ez <= tol, (eo, eM, ez)
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_tiny_fp32(lib):
+    w = synth.WORKLOADS["tiny"]
+    _say(f"tiny {w}")
+    inp = synth.make_inputs(w, DEV)
+    for rule in ("linear", "delta"):
+        res = run(lib, inp, w.seg_len, rule)
+        check(inp, res, w.seg_len, rule, all_units(w.B, w.Hkv), 1e-4)
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_hf_repro_bf16(lib, rule):
+    w = synth.WORKLOADS["hf_repro"]
+    _say(f"hf_repro {rule}")
+    inp = synth.make_inputs(w, DEV)
+    res = run(lib, inp, w.seg_len, rule)
+    check(inp, res, w.seg_len, rule, all_units(w.B, w.Hkv), 2e-2)
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_hf_repro_shape_fp32(lib, rule):
+    w = synth.WORKLOADS["hf_repro"].with_(dtype="f32")
+    _say(f"hf_repro shape in fp32, {rule}")
+    inp = synth.make_inputs(w, DEV)
+    res = run(lib, inp, w.seg_len, rule)
+    check(inp, res, w.seg_len, rule, [(0, 0), (3, 7), (7, 15)], 1e-4)
+
+
+def test_llama3_8b_shape(lib):
+    w = synth.WORKLOADS["llama3_8b"]
+    _say("llama3_8b (delta, GQA 32/8), units (0,0) and (3,7)")
+    inp = synth.make_inputs(w, DEV)
+    res = run(lib, inp, w.seg_len, "delta")
+    check(inp, res, w.seg_len, "delta", [(0, 0), (3, 7)], 2e-2)
+
+
+def test_long_stream(lib):
+    w = synth.WORKLOADS["long_stream"]
+    segs = {0, 1, 2, 127, 255, 383, 510, 511}
+    _say(f"long_stream (linear, 512 segments), units (0,0) (0,11), out segments {sorted(segs)}")
+    inp = synth.make_inputs(w, DEV)
+    res = run(lib, inp, w.seg_len, "linear")
+    check(inp, res, w.seg_len, "linear", [(0, 0), (0, 11)], 2e-2, out_segments=segs)
+
+
+def test_small_segment_outliers(lib):
+    w = synth.WORKLOADS["small_segment"]
+    units = [(0, 0), (1, 5), (4, 31), (7, 12), (9, 3), (12, 20), (15, 31), (15, 0)]
+    _say(f"small_segment (delta, 256 segments of 128, outlier keys), units {units}")
+    inp = synth.make_inputs(w, DEV)
+    res = run(lib, inp, w.seg_len, "delta")
+    check(inp, res, w.seg_len, "delta", units, 2e-2)
+
+
+# --- shapes, edge cases, and the ABI's promises -------------------------------
+
+EDGE = [
+    # B, Hq, Hkv, L, d, seg_len, dtype
+    (1, 1, 1, 1, 32, 16, torch.float32),      # one token
+    (1, 2, 1, 37, 32, 16, torch.float32),     # ragged last segment, GQA 2
+    (2, 4, 2, 70, 64, 1, torch.float32),      # one-token segments
+    (1, 3, 3, 50, 64, 200, torch.float32),    # seg_len > L
+    (2, 4, 1, 300, 128, 96, torch.float32),   # GQA 4, 3 waves' worth of rows, ragged
+    (1, 2, 2, 257, 128, 130, torch.bfloat16), # ragged key tiles and query tiles
+    (2, 8, 2, 500, 64, 128, torch.bfloat16),
+    (1, 4, 4, 64, 32, 33, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}L{c[3]}d{c[4]}N{c[5]}{str(c[6])[6:]}" for c in EDGE])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_edge_shapes(lib, case, rule):
+    B, Hq, Hkv, L, d, N, dt = case
+    _say(f"edge {case} {rule}")
+    inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=L + d)
+    res = run(lib, inp, N, rule)
+    check(inp, res, N, rule, all_units(B, Hkv), tolerance(dt))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_nonzero_initial_state(lib, dt, rule):
+    _say(f"nonzero M0, z0 {dt} {rule}")
+    inp = random_inputs(2, 4, 2, 200, 64, dt, DEV, seed=7, m0_scale=0.5)
+    res = run(lib, inp, 64, rule)
+    check(inp, res, 64, rule, all_units(2, 2), tolerance(dt))
+
+
+def test_windows_match_one_pass(lib):
+    """A workspace of the minimum size walks the segments in windows; the
+    result equals the one-pass result bit for bit."""
+    _say("windowed vs one pass")
+    inp = random_inputs(2, 4, 2, 1000, 64, torch.bfloat16, DEV, seed=3)
+    B, Hq, L, d = inp["q"].shape
+    full, least = lib.workspace_size(B, Hq, 2, L, d, 100, "delta", torch.bfloat16)
+    a = run(lib, inp, 100, "delta")
+    for size in (least, least + (full - least) // 3):
+        ws = torch.empty(size, dtype=torch.uint8, device=DEV)
+        b = run(lib, inp, 100, "delta", workspace=ws)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_in_place_state_carry(lib):
+    """M_final may be M0 and z_final may be z0."""
+    _say("in-place carry")
+    inp = random_inputs(1, 4, 2, 256, 64, torch.bfloat16, DEV, seed=5, m0_scale=0.3)
+    ref = run(lib, inp, 64, "delta")
+    M = inp["M0"].clone()
+    z = inp["z0"].clone()
+    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], M, z, 64, "delta",
+                      M_final=M, z_final=z)
+    torch.cuda.synchronize()
+    assert torch.equal(res[0], ref[0]) and torch.equal(M, ref[1]) and torch.equal(z, ref[2])
+
+
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_chunked_calls_equal_one_call(lib, rule):
+    _say(f"chunked calls {rule}")
+    inp = random_inputs(1, 2, 2, 384, 64, torch.float32, DEV, seed=11)
+    out, M, z = run(lib, inp, 64, rule)
+    cut = 192
+    first = {k: (v[:, :, :cut].contiguous() if k in "qkv" else v) for k, v in inp.items()}
+    second = {k: (v[:, :, cut:].contiguous() if k in "qkv" else v) for k, v in inp.items()}
+    o1, M1, z1 = run(lib, first, 64, rule)
+    second["M0"], second["z0"] = M1, z1
+    o2, M2, z2 = run(lib, second, 64, rule)
+    torch.testing.assert_close(torch.cat([o1, o2], dim=2), out, rtol=1e-5, atol=1e-6)
+    torch.testing.assert_close(M2, M, rtol=1e-5, atol=1e-5)
+    torch.testing.assert_close(z2, z, rtol=1e-6, atol=0)
+
+
+def test_deterministic(lib):
+    _say("determinism")
+    inp = random_inputs(2, 8, 2, 2048, 128, torch.bfloat16, DEV, seed=9)
+    a = run(lib, inp, 512, "delta")
+    b = run(lib, inp, 512, "delta")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_streams_and_null_stream(lib):
+    _say("side stream")
+    inp = random_inputs(1, 2, 2, 128, 32, torch.float32, DEV, seed=2)
+    ref = run(lib, inp, 32, "linear")
+    s = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s):
+        res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                          32, "linear", stream=s)
+    s.synchronize()
+    for x, y in zip(ref, res):
+        assert torch.equal(x, y)
