@@ -1,0 +1,319 @@
+// The memory recurrence in affine form, parallel over segments.
+//
+// "Infini-Attention" (AI Wiki), "How does the compressive memory work?": per
+// segment, with Phi = sigma(K_s) and den_t = Phi_t . z_{s-1},
+//   delta:  M_s = M_{s-1} + Phi^T (V_s - Phi M_{s-1} / den)
+//              = M_{s-1} + Phi^T V_s - (Phi^T diag(1/den) Phi) M_{s-1}
+//   linear: M_s = M_{s-1} + Phi^T V_s
+//   both:   z_s = z_{s-1} + sum_t Phi_t.
+// Written this way, every product over the segment's N tokens depends on K, V
+// and z only, not on M. So the O(N d^2) work runs for all segments at once, and
+// only a d x d by d x d product per segment stays sequential:
+//   1. colsum:  c_s = sum_t sigma(K_s,t)                 (parallel over segments)
+//   2. prefix:  z_{s-1} = z_0 + sum_{s'<s} c_s'           (a short loop over s)
+//   3. affine:  A_s = -Phi^T diag(1/den) Phi, B_s = Phi^T V_s   (parallel)
+//   4. chain:   M_s = M_{s-1} + B_s + A_s M_{s-1}        (sequential, per slab of M)
+// The chain writes the state before each segment (M^T in the element type, as
+// the attention kernel's retrieval reads it); step 2 writes z before each
+// segment. This pays off when N is large next to d: the sequential part costs
+// 2 d^3 per segment instead of the direct scan's 6 N d^2.
+//
+// Precision: A_s is stored in the element type (its product with M is a small
+// correction); B_s and M stay in float. V never passes through a rounding of
+// V - prediction, which would lose the prediction.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace infini {
+
+namespace {
+
+// ---- 1. column sums of sigma(K) per (unit, segment) ------------------------
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void colsum_kernel(AffineArgs a) {
+  constexpr int CG = D / 8;      // 8-column groups of a row
+  constexpr int TL = 256 / CG;   // token lanes
+  __shared__ float red[TL * D];
+  const int tid = threadIdx.x, cg = tid % CG, tl = tid / CG;
+  const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const T* K = static_cast<const T*>(a.k) + ((int64_t)unit * a.L + seg_start) * D + 8 * cg;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int t = tl; t < n_s; t += TL) {
+    const frag_t<T> kv = load8<T>(K + (int64_t)t * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += feature_map(to_f32<T>(kv[e]));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tl * D + 8 * cg + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int j = 0; j < TL; ++j) s += red[j * D + tid];
+    a.colsum[((int64_t)unit * a.s_count + sl) * D + tid] = s;
+  }
+}
+
+// ---- 2. z before each segment, and after the window ------------------------
+
+template <int D>
+__global__ __launch_bounds__(D) void prefix_kernel(AffineArgs a) {
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  float z = a.z_in[(int64_t)unit * D + tid];
+  for (int sl = 0; sl < a.s_count; ++sl) {
+    const int64_t idx = ((int64_t)unit * a.s_count + sl) * D + tid;
+    a.snapZ[idx] = z;
+    z += a.colsum[idx];
+  }
+  a.z_out[(int64_t)unit * D + tid] = z;
+}
+
+// ---- 3. A_s = -Phi^T diag(1/den) Phi and B_s = Phi^T V_s --------------------
+
+template <int D, int RULE>
+struct AffineShape {
+  static constexpr int RT = D / 32;                                // row tiles (key dim)
+  static constexpr int CT = (RULE == kRuleDelta ? 2 : 1) * (D / 32);  // column tiles
+  static constexpr int NTILE = RT * CT;
+  static constexpr int NW = NTILE < 4 ? NTILE : 4;
+  static constexpr int TPW = NTILE / NW;  // tiles per wave
+  static_assert(NTILE % NW == 0, "tile split");
+};
+
+template <typename T, int D, int RULE>
+__global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel(AffineArgs a) {
+  using S = AffineShape<D, RULE>;
+  constexpr int NW = S::NW, NT = NW * 64, RT = S::RT, TPW = S::TPW;
+  constexpr bool DELTA = RULE == kRuleDelta;
+  constexpr int TC = 64;                  // tokens per chunk
+  constexpr int TS = TC + pad16<T>();     // row stride of the transposed tiles
+  constexpr int CG = D / 8;               // 8-column groups
+  constexpr int ITEMS = (TC / 4) * CG;    // (4 tokens x 8 columns) staging items
+  constexpr int IPT = (ITEMS + NT - 1) / NT;
+
+  __shared__ __align__(16) T PhiT[D * TS];                 // sigma(K)^T  [key dim][token]
+  __shared__ __align__(16) T DPhiT[DELTA ? D * TS : 1];    // (Phi / den)^T
+  __shared__ __align__(16) T VT[D * TS];                   // V^T         [value dim][token]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const T* K = static_cast<const T*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const T* V = static_cast<const T*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  const float* z = a.snapZ + ((int64_t)unit * a.s_count + sl) * D;
+
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) acc[j] = zero16();
+
+  // registers of the next chunk's staging items
+  frag_t<T> kr[IPT][4], vr[IPT][4];
+  auto load_chunk = [&](int t0) {
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int cg = item % CG, tq = item / CG;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 4 * tq + q;
+        kr[it][q] = zero_frag<T>();
+        vr[it][q] = zero_frag<T>();
+        if (item < ITEMS && t < n_s) {
+          kr[it][q] = load8<T>(K + (int64_t)t * D + 8 * cg);
+          vr[it][q] = load8<T>(V + (int64_t)t * D + 8 * cg);
+        }
+      }
+    }
+  };
+  float zc[IPT][8];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int cg = (tid + it * NT) % CG;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zc[it][e] = z[8 * cg + e];
+  }
+
+  load_chunk(0);
+  for (int t0 = 0; t0 < n_s; t0 += TC) {
+    // stage the chunk: sigma, den, transposed stores
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int item = tid + it * NT;
+      const int cg = item % CG, tq = item / CG;
+      float ph[4][8], dp[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = t0 + 4 * tq + q < n_s;
+        dp[q] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ph[q][e] = ok ? feature_map(to_f32<T>(kr[it][q][e])) : 0.f;
+          dp[q] += ph[q][e] * zc[it][e];
+        }
+      }
+      if constexpr (DELTA) {
+        // den_t: sum over the CG lanes that hold token t's columns
+#pragma unroll
+        for (int m = 1; m < CG; m <<= 1)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dp[q] += __shfl_xor(dp[q], m);
+      }
+      if (item < ITEMS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          vec4_t<T> p4, v4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            p4[q] = from_f32<T>(ph[q][e]);
+            v4[q] = vr[it][q][e];
+          }
+          store4<T>(PhiT + (8 * cg + e) * TS + 4 * tq, p4);
+          store4<T>(VT + (8 * cg + e) * TS + 4 * tq, v4);
+          if constexpr (DELTA) {
+            vec4_t<T> d4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool ok = t0 + 4 * tq + q < n_s;
+              d4[q] = from_f32<T>(ok ? ph[q][e] / dp[q] : 0.f);
+            }
+            store4<T>(DPhiT + (8 * cg + e) * TS + 4 * tq, d4);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (t0 + TC < n_s) load_chunk(t0 + TC);  // in flight during the products
+
+#pragma unroll
+    for (int kc = 0; kc < TC / 16; ++kc) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int tile = w * TPW + j;
+        const int rt = tile % RT, ct = tile / RT;
+        const frag_t<T> af = load8<T>(PhiT + (32 * rt + i) * TS + 16 * kc + 8 * h);
+        const T* bsrc;
+        if (DELTA && ct < RT) bsrc = DPhiT + (32 * ct + i) * TS;
+        else bsrc = VT + (32 * (ct - (DELTA ? RT : 0)) + i) * TS;
+        mma32(acc[j], af, load8<T>(bsrc + 16 * kc + 8 * h));
+      }
+    }
+    __syncthreads();
+  }
+
+  const int64_t base = ((int64_t)unit * a.s_count + sl) * D * D;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tile = w * TPW + j;
+    const int rt = tile % RT, ct = tile / RT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * rt + acc_row(r, h);
+      if (DELTA && ct < RT)
+        static_cast<T*>(a.Amat)[base + (int64_t)row * D + 32 * ct + i] = from_f32<T>(-acc[j][r]);
+      else
+        a.Bmat[base + (int64_t)row * D + 32 * (ct - (DELTA ? RT : 0)) + i] = acc[j][r];
+    }
+  }
+}
+
+// ---- 4. M_s = M_{s-1} + B_s + A_s M_{s-1}, per 32-column slab ---------------
+
+template <typename T, int D, int RULE>
+__global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
+  constexpr int NC = D / 16;
+  constexpr int MTS = D + pad16<T>();
+  constexpr bool DELTA = RULE == kRuleDelta;
+  __shared__ __align__(16) T Mt[DELTA ? 32 * MTS : 1];  // M_{s-1}^T of the slab
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int slab = blockIdx.x % (D / 32), unit = blockIdx.x / (D / 32);
+  const int col0 = 32 * slab;
+
+  // this lane's 16 entries of the slab: rows 32w + acc_row(r, h), column col0 + i
+  f32x16 acc;
+  const float* Min = a.M_in + (int64_t)unit * D * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = Min[(32 * w + acc_row(r, h)) * D + col0 + i];
+
+  for (int sl = 0; sl < a.s_count; ++sl) {
+    const int64_t seg = (int64_t)unit * a.s_count + sl;
+    // issue this segment's loads first; they are independent of M
+    float bv[16];
+    const float* Bs = a.Bmat + seg * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bv[r] = Bs[(32 * w + acc_row(r, h)) * D + col0 + i];
+    frag_t<T> af[NC];
+    if constexpr (DELTA) {
+      const T* As = static_cast<const T*>(a.Amat) + seg * D * D + (int64_t)(32 * w + i) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) af[c] = load8<T>(As + 16 * c + 8 * h);
+    }
+
+    // the state before segment s: snapshot (M^T, element type)
+    T* sM = static_cast<T*>(a.snapM) + seg * D * D + (int64_t)(col0 + i) * D + 32 * w + 4 * h;
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      vec4_t<T> y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = from_f32<T>(acc[4 * rq + j]);
+      store4<T>(sM + 8 * rq, y);
+      if constexpr (DELTA) store4<T>(Mt + i * MTS + 32 * w + 8 * rq + 4 * h, y);
+    }
+    if constexpr (DELTA) {
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) mma32(acc, af[c], load8<T>(Mt + i * MTS + 16 * c + 8 * h));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += bv[r];
+    if constexpr (DELTA) __syncthreads();
+  }
+
+  float* Mout = a.M_out + (int64_t)unit * D * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Mout[(32 * w + acc_row(r, h)) * D + col0 + i] = acc[r];
+}
+
+template <typename T, int D, int RULE>
+hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
+  const unsigned segs = (unsigned)(a.units * a.s_count);
+  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((affine_kernel<T, D, RULE>), dim3(segs), dim3(AffineShape<D, RULE>::NW * 64),
+                     0, stream, a);
+  hipLaunchKernelGGL((chain_kernel<T, D, RULE>), dim3((unsigned)(a.units * (D / 32))),
+                     dim3(D / 32 * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_affine_rule(int rule, const AffineArgs& a, hipStream_t stream) {
+  return rule == kRuleDelta ? launch_affine_t<T, D, kRuleDelta>(a, stream)
+                            : launch_affine_t<T, D, kRuleLinear>(a, stream);
+}
+
+template <typename T>
+hipError_t launch_affine_d(int d, int rule, const AffineArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 32: return launch_affine_rule<T, 32>(rule, a, stream);
+    case 64: return launch_affine_rule<T, 64>(rule, a, stream);
+    case 128: return launch_affine_rule<T, 128>(rule, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {
+  return dtype == kBF16 ? launch_affine_d<bf16>(d, rule, a, stream)
+                        : launch_affine_d<float>(d, rule, a, stream);
+}
+
+}  // namespace infini

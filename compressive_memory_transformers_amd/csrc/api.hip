@@ -14,6 +14,13 @@
 //      in parallel, reading its segment's snapshot for the retrieval.
 // W is as large as the workspace allows; with the full size the whole call is
 // one window.
+//
+// The scan has two forms. The direct scan walks each segment's tokens in
+// order (cost 6 N d^2 per segment on the sequential path, no extra memory).
+// The affine form (affine.hip) computes each segment's d x d transition in
+// parallel and leaves 2 d^3 per segment on the sequential path, at the price
+// of two d x d matrices per segment in the workspace. It is used when
+// seg_len >= 4 d, where its sequential part is at least 12x shorter.
 #include <stdint.h>
 #include <string.h>
 
@@ -25,6 +32,7 @@
 namespace {
 
 using infini::AttnArgs;
+using infini::AffineArgs;
 using infini::ScanArgs;
 
 constexpr int32_t kVersion = 100;  // 0.1.0
@@ -34,10 +42,16 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t units, S, d, e;
+  bool affine;         // scan in affine form
   size_t state_bytes;  // one (M, z) buffer, aligned
-  size_t per_seg;      // snapshot bytes per segment
-  size_t fixed;        // bytes before the snapshots, plus alignment slack
+  size_t per_seg;      // workspace bytes per segment of a window
+  size_t fixed;        // bytes before the per-segment regions, plus alignment slack
 };
+
+bool use_affine(int64_t L, int64_t d, int64_t seg_len) {
+  const int64_t eff = seg_len < L ? seg_len : L;
+  return eff >= 4 * d;
+}
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -70,9 +84,15 @@ infini_status_t check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64
     plan->S = S;
     plan->d = d;
     plan->e = dtype == INFINI_BF16 ? 2 : 4;
+    plan->affine = use_affine(L, d, seg_len);
     plan->state_bytes = align_up((size_t)units * (size_t)(d * d + d) * 4);
-    plan->per_seg = (size_t)units * (size_t)(d * d * plan->e + d * 4);
-    plan->fixed = 2 * plan->state_bytes + 2 * kAlign;
+    // snapshots: M^T in the element type, z in float
+    size_t per = (size_t)(d * d * plan->e + d * 4);
+    // affine form: column sums, B_s in float, A_s in the element type (delta)
+    if (plan->affine)
+      per += (size_t)(d * 4 + d * d * 4 + (rule == INFINI_RULE_DELTA ? d * d * plan->e : 0));
+    plan->per_seg = (size_t)units * per;
+    plan->fixed = 2 * plan->state_bytes + 6 * kAlign;
   }
   return INFINI_OK;
 }
@@ -160,10 +180,23 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   float* stM[2] = {reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + p.state_bytes)};
   float* stz[2] = {reinterpret_cast<float*>(ws + mbytes),
                    reinterpret_cast<float*>(ws + p.state_bytes + mbytes)};
-  char* snap_base = ws + 2 * p.state_bytes;
-  const size_t snapM_bytes = align_up((size_t)p.units * (size_t)W * (size_t)(d * d * p.e));
-  void* snapM = snap_base;
-  float* snapZ = reinterpret_cast<float*>(snap_base + snapM_bytes);
+  char* cur = ws + 2 * p.state_bytes;
+  auto carve = [&](size_t bytes) {
+    char* r = cur;
+    cur += align_up(bytes);
+    return r;
+  };
+  const size_t uW = (size_t)p.units * (size_t)W;
+  void* snapM = carve(uW * (size_t)(d * d * p.e));
+  float* snapZ = reinterpret_cast<float*>(carve(uW * (size_t)d * 4));
+  float* colsum = nullptr;
+  float* Bmat = nullptr;
+  void* Amat = nullptr;
+  if (p.affine) {
+    colsum = reinterpret_cast<float*>(carve(uW * (size_t)d * 4));
+    Bmat = reinterpret_cast<float*>(carve(uW * (size_t)(d * d) * 4));
+    if (rule == INFINI_RULE_DELTA) Amat = carve(uW * (size_t)(d * d * p.e));
+  }
 
   if (n_events < 0 || (n_events > 0 && events == nullptr)) return INFINI_ERR_INVALID_ARG;
   for (int32_t e = 0; e < n_events; ++e)
@@ -177,9 +210,10 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   };
   const float* Min = M0;
   const float* zin = z0;
-  if (z_final == z0) {
-    // Several slab workgroups read z0 while one of them writes z_final; read a
-    // copy instead.
+  if (z_final == z0 && !p.affine) {
+    // In the direct scan several slab workgroups read z0 while one of them
+    // writes z_final; read a copy instead. (The affine form reads and writes
+    // each z entry in the same thread.)
     if (infini::launch_copy_f32(stz[1], z0, B * Hkv * d, s) != hipSuccess) return INFINI_ERR_HIP;
     zin = stz[1];
   }
@@ -192,6 +226,27 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     float* Mout = last ? M_final : stM[wi & 1];
     float* zout = last ? z_final : stz[wi & 1];
 
+    if (!mark(wi, 0)) return INFINI_ERR_HIP;
+    if (p.affine) {
+      AffineArgs fa;
+      fa.k = k;
+      fa.v = v;
+      fa.M_in = Min;
+      fa.z_in = zin;
+      fa.M_out = Mout;
+      fa.z_out = zout;
+      fa.snapM = snapM;
+      fa.snapZ = snapZ;
+      fa.colsum = colsum;
+      fa.Amat = Amat;
+      fa.Bmat = Bmat;
+      fa.L = L;
+      fa.seg_len = seg_len;
+      fa.units = (int32_t)p.units;
+      fa.s_begin = (int32_t)s_begin;
+      fa.s_count = (int32_t)s_count;
+      if (infini::launch_affine(dtype, (int)d, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
+    } else {
     ScanArgs sa;
     sa.k = k;
     sa.v = v;
@@ -206,8 +261,8 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     sa.units = (int32_t)p.units;
     sa.s_begin = (int32_t)s_begin;
     sa.s_count = (int32_t)s_count;
-    if (!mark(wi, 0)) return INFINI_ERR_HIP;
     if (infini::launch_scan(dtype, (int)d, rule, sa, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
     if (!mark(wi, 1)) return INFINI_ERR_HIP;
 
     AttnArgs aa;

@@ -28,19 +28,83 @@ namespace infini {
 
 namespace {
 
+// Threshold of the lazy softmax rescale, in log2 units: the running max a
+// query's exponents are taken against is only raised when a new score exceeds
+// it by more than this, so exp2 arguments stay <= kRescaleTau and the
+// accumulator is rescaled rarely. The result is exact either way: numerator
+// and denominator use the same reference.
+constexpr float kRescaleTau = 8.f;
+
 template <typename T, int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
+struct AttnTile {
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D + pad16<T>();   // Ks row stride (elements)
+  static constexpr int VS = BN + pad16<T>();  // Vt row stride (elements)
+  static constexpr int K_TOTAL = BN * (D / 8);         // 8-element K chunks per tile
+  static constexpr int V_TOTAL = (BN / 4) * (D / 4);   // 4x4 V blocks per tile
+  static constexpr int K_CHUNKS = (K_TOTAL + NT - 1) / NT;  // per thread
+  static constexpr int V_BLOCKS = (V_TOTAL + NT - 1) / NT;
+  frag_t<T> k[K_CHUNKS];
+  vec4_t<T> v[V_BLOCKS][4];
+
+  // Global -> registers for key tile k0 (keys >= n_s read as zero).
+  __device__ __forceinline__ void load(const T* K, const T* V, int k0, int n_s, int tid) {
+#pragma unroll
+    for (int j = 0; j < K_CHUNKS; ++j) {
+      const int c = tid + j * NT;
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      k[j] = zero_frag<T>();
+      if (c < K_TOTAL && k0 + r < n_s) k[j] = load8<T>(K + (int64_t)(k0 + r) * D + col);
+    }
+#pragma unroll
+    for (int j = 0; j < V_BLOCKS; ++j) {
+      const int c = tid + j * NT;
+      const int d4 = c % (D / 4), k4 = c / (D / 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[j][q] = zero4<T>();
+        if (c < V_TOTAL && k0 + 4 * k4 + q < n_s) v[j][q] = load4<T>(V + (int64_t)(k0 + 4 * k4 + q) * D + 4 * d4);
+      }
+    }
+  }
+
+  // Registers -> LDS: K row major, V transposed.
+  __device__ __forceinline__ void store(T* Ks, T* Vt, int tid) const {
+#pragma unroll
+    for (int j = 0; j < K_CHUNKS; ++j) {
+      const int c = tid + j * NT;
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      if (c < K_TOTAL) store8<T>(Ks + r * KS + col, k[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < V_BLOCKS; ++j) {
+      const int c = tid + j * NT;
+      const int d4 = c % (D / 4), k4 = c / (D / 4);
+      if (c >= V_TOTAL) continue;
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        vec4_t<T> y;
+        y[0] = v[j][0][dd]; y[1] = v[j][1][dd]; y[2] = v[j][2][dd]; y[3] = v[j][3][dd];
+        store4<T>(Vt + (4 * d4 + dd) * VS + 4 * k4, y);
+      }
+    }
+  }
+};
+
+template <typename T, int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
+  using Tile = AttnTile<T, D, NW, BN>;
   constexpr int BM = 32 * NW;
   constexpr int NC = D / 16;    // 16-wide chunks of the head dimension
   constexpr int NDB = D / 32;   // 32-row blocks of the value dimension
   constexpr int NKB = BN / 32;  // 32-key blocks of a key tile
   constexpr int NPC = BN / 16;  // 16-key chunks of a key tile
-  constexpr int KS = D + pad16<T>();
-  constexpr int VS = BN + pad16<T>();
+  constexpr int KS = Tile::KS;
+  constexpr int VS = Tile::VS;
 
-  __shared__ __align__(16) T Ks[BN * KS];  // K tile, [key][dim]
-  __shared__ __align__(16) T Vt[D * VS];   // V tile transposed, [dim][key]
+  // Two buffers: tile kt+1 is written while tile kt is read.
+  __shared__ __align__(16) T Ks[2][BN * KS];  // K tiles, [key][dim]
+  __shared__ __align__(16) T Vt[2][D * VS];   // V tiles transposed, [dim][key]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 31, h = lane >> 5;
@@ -78,100 +142,99 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int row = q0 + 32 * w + i;  // this lane's query, relative to the segment
   const bool wave_on = q0 + 32 * w < n_s;
   const int wave_last = min(q0 + 32 * w + 31, n_s - 1);
+  const float c = a.scale_log2;
+
+  const int n_kv = min(q0 + BM, n_s);  // keys any row of the workgroup can see
+  const int n_kt = (n_kv + BN - 1) / BN;
+
+  Tile tile;
+  tile.load(K, V, 0, n_s, tid);
 
   // B operand of S^T = K Q^T: column i is query `row`, k = 16c + 8h + e.
   frag_t<T> qf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qf[c] = zero_frag<T>();
-    if (row < n_s) qf[c] = load8<T>(Q + (int64_t)row * D + 16 * c + 8 * h);
+  for (int cc = 0; cc < NC; ++cc) {
+    qf[cc] = zero_frag<T>();
+    if (row < n_s) qf[cc] = load8<T>(Q + (int64_t)row * D + 16 * cc + 8 * h);
   }
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
-  float m_run = -INFINITY;  // running max of this query's scaled scores (log2 units)
-  float l_run = 0.f;        // this half-wave's share of the running softmax sum
+  float m_run = -INFINITY;  // reference max of this query's raw scores
+  float l_run = 0.f;        // this half-wave's share of the softmax sum
 
-  const int n_kv = min(q0 + BM, n_s);  // keys any row of the workgroup can see
-  const int n_kt = (n_kv + BN - 1) / BN;
+  tile.store(Ks[0], Vt[0], tid);
+  __syncthreads();
+
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * BN;
-    __syncthreads();  // the previous tile has been read by every wave
-    for (int c = tid; c < BN * (D / 8); c += NT) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      frag_t<T> val = zero_frag<T>();
-      if (k0 + r < n_s) val = load8<T>(K + (int64_t)(k0 + r) * D + col);
-      store8<T>(Ks + r * KS + col, val);
-    }
-    for (int c = tid; c < (BN / 4) * (D / 4); c += NT) {
-      const int d4 = c % (D / 4), k4 = c / (D / 4);
-      vec4_t<T> x[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = zero4<T>();
-        if (k0 + 4 * k4 + j < n_s) x[j] = load4<T>(V + (int64_t)(k0 + 4 * k4 + j) * D + 4 * d4);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        vec4_t<T> y;
-        y[0] = x[0][dd]; y[1] = x[1][dd]; y[2] = x[2][dd]; y[3] = x[3][dd];
-        store4<T>(Vt + (4 * d4 + dd) * VS + 4 * k4, y);
-      }
-    }
-    __syncthreads();
-    if (!wave_on || k0 > wave_last) continue;  // every key of the tile is after every row of the wave
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) tile.load(K, V, k0 + BN, n_s, tid);  // in flight during this tile
 
-    f32x16 sacc[NKB];
+    if (wave_on && k0 <= wave_last) {
+      const T* Kb = Ks[buf];
+      const T* Vb = Vt[buf];
+      f32x16 sacc[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = zero16();
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = zero16();
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        mma32(sacc[kb], load8<T>(Ks + (32 * kb + i) * KS + 16 * c + 8 * h), qf[c]);
+        for (int cc = 0; cc < NC; ++cc)
+          mma32(sacc[kb], load8<T>(Kb + (32 * kb + i) * KS + 16 * cc + 8 * h), qf[cc]);
+      }
+
+      if (k0 + BN - 1 > q0 + 32 * w) {  // the tile reaches past the wave's first row
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + 32 * kb + acc_row(r, h) > row) sacc[kb][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Key 0 of the segment is visible to every row, so the first tile sets
+      // a finite reference for every lane.
+      if (__any((mx - m_run) * c > kRescaleTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c;
+      frag_t<T> pf[NPC];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+          l_run += p;
+          pf[2 * kb + (r >> 3)][r & 7] = from_f32<T>(p);
+        }
+      // O^T += V^T P^T. Element e of pf[pc] is key 16pc + 8(e/4) + 4h + e%4 of
+      // the tile, so the A operand reads two runs of four keys from Vt.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int pc = 0; pc < NPC; ++pc) {
+          const T* vrow = Vb + (32 * db + i) * VS + 16 * pc + 4 * h;
+          mma32(oacc[db], load4x2<T>(vrow, vrow + 8), pf[pc]);
+        }
     }
-
-    const bool need_mask = k0 + BN - 1 > q0 + 32 * w;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * a.scale_log2;
-        if (need_mask && k0 + 32 * kb + acc_row(r, h) > row) x = -INFINITY;
-        sacc[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Key 0 of the segment is visible to every row, so after the first tile
-    // m_new is finite and alpha is well defined.
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-    frag_t<T> pf[NPC];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
-        l_run += p;
-        pf[2 * kb + (r >> 3)][r & 7] = from_f32<T>(p);
-      }
-    // O^T += V^T P^T. Element e of pf[pc] is key 16pc + 8(e/4) + 4h + e%4 of
-    // the tile, so the A operand reads two runs of four keys from Vt.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int pc = 0; pc < NPC; ++pc) {
-        const T* vrow = Vt + (32 * db + i) * VS + 16 * pc + 4 * h;
-        mma32(oacc[db], load4x2<T>(vrow, vrow + 8), pf[pc]);
-      }
-    m_run = m_new;
+    if (kt + 1 < n_kt) {
+      // buffer buf^1 was last read in iteration kt-1, before that iteration's
+      // barrier
+      tile.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+      __syncthreads();
+    }
   }
   if (!wave_on) return;  // no barrier follows
 
@@ -183,12 +246,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   float sq[NC][8];
   float dp = 0.f;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float s = feature_map(to_f32<T>(qf[c][e]));
-      sq[c][e] = s;
-      dp += s * zs[16 * c + 8 * h + e];
+      const float s = feature_map(to_f32<T>(qf[cc][e]));
+      sq[cc][e] = s;
+      dp += s * zs[16 * cc + 8 * h + e];
     }
   const float den = dp + __shfl_xor(dp, 32);
   const float g = 1.f / (1.f + __expf(-a.beta[hq]));
@@ -199,15 +262,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] *= ca;
   frag_t<T> sf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sf[c][e] = from_f32<T>(sq[c][e] * cm);
+    for (int e = 0; e < 8; ++e) sf[cc][e] = from_f32<T>(sq[cc][e] * cm);
   // O^T += M^T (g sigma(Q)/den)^T; the snapshot is M^T, [value][key].
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      mma32(oacc[db], load8<T>(Mts + (int64_t)(32 * db + i) * D + 16 * c + 8 * h), sf[c]);
+    for (int cc = 0; cc < NC; ++cc)
+      mma32(oacc[db], load8<T>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
 
   if (row < n_s) {
     T* orow = O + (int64_t)row * D;

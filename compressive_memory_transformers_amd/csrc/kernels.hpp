@@ -29,6 +29,26 @@ struct ScanArgs {
   int32_t s_begin, s_count;
 };
 
+// The affine form of the recurrence (affine.hip): column sums, z prefix,
+// per-segment A_s = -Phi^T diag(1/den) Phi and B_s = Phi^T V in parallel, then
+// a short sequential chain over the window's segments.
+struct AffineArgs {
+  const void* k;       // [B][Hkv][L][d]
+  const void* v;       // [B][Hkv][L][d]
+  const float* M_in;   // [B][Hkv][d][d]
+  const float* z_in;   // [B][Hkv][d]
+  float* M_out;        // [B][Hkv][d][d]
+  float* z_out;        // [B][Hkv][d]
+  void* snapM;         // as ScanArgs::snapM
+  float* snapZ;        // as ScanArgs::snapZ
+  float* colsum;       // [B*Hkv][s_count][d]
+  void* Amat;          // [B*Hkv][s_count][d][d], element type (delta rule only)
+  float* Bmat;         // [B*Hkv][s_count][d][d]
+  int64_t L, seg_len;
+  int32_t units;
+  int32_t s_begin, s_count;
+};
+
 // Local causal attention of every (batch, query head, segment, query tile)
 // of a window, with the memory retrieval and the gate fused into its epilogue.
 struct AttnArgs {
@@ -51,6 +71,7 @@ struct AttnArgs {
 int attn_waves(int64_t seg_len);
 
 hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
 

@@ -23,8 +23,7 @@
 //   Phi = sigma(K rows)            -> registers (A operand) and Phi^T in LDS
 //   den_t = Phi_t . z_{s-1}        -> float, from the unrounded Phi
 //   P = Phi M_{s-1}                -> one 32x32 accumulator (delta only)
-//   R = V - P / den  (or R = V)    -> accumulator layout = B operand layout
-//   dM += Phi^T R                  -> d/32 accumulators
+//   dM += Phi^T V - Phi^T (P/den)  -> d/32 accumulators, two products
 // z's column sums are kept per lane in float and reduced across lanes once per
 // segment with a reduce-scatter of fixed order.
 #include "common.hpp"
@@ -106,7 +105,7 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
     }
 
     frag_t<T> mfr[NC];  // B operand of P = Phi M_{s-1}: column i of M is row i of Mt
-    if (RULE == kRuleDelta) {
+    if constexpr (RULE == kRuleDelta) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) mfr[c] = load8<T>(Mt + i * MTS + 16 * c + 8 * h);
     }
@@ -142,31 +141,39 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
       __syncthreads();
 
       f32x16 accp;
-      if (RULE == kRuleDelta) {
+      if constexpr (RULE == kRuleDelta) {
         accp = zero16();
 #pragma unroll
         for (int c = 0; c < NC; ++c) mma32(accp, phf[c], mfr[c]);
       }
-      // R in the accumulator layout: register r of lane (i, h) is token
-      // acc_row(r, h) of the wave's 32 and value column i of the slab.
-      frag_t<T> rf[2];
+      // V and, for the delta rule, the negated prediction -P/den, in the
+      // accumulator layout: register r of lane (i, h) is token acc_row(r, h)
+      // of the wave's 32 and value column i of the slab. The two stay separate
+      // B operands: V is exact in the element type, while V - P/den rounded
+      // as one value would lose most of the (small) prediction to rounding,
+      // and that loss adds up coherently over the segment's tokens.
+      frag_t<T> vf[2], pf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tr = acc_row(r, h);
         const int tk = t0 + 32 * w + tr;
-        float rv = 0.f;
-        if (tk < n_s) rv = to_f32<T>(V[(seg_start + tk) * D + col0 + i]);
-        if (RULE == kRuleDelta) rv -= accp[r] / den_s[32 * w + tr];
-        rf[r >> 3][r & 7] = from_f32<T>(rv);
+        T vv = from_f32<T>(0.f);
+        if (tk < n_s) vv = V[(seg_start + tk) * D + col0 + i];
+        vf[r >> 3][r & 7] = vv;
+        if constexpr (RULE == kRuleDelta)
+          pf[r >> 3][r & 7] = from_f32<T>(-accp[r] / den_s[32 * w + tr]);
       }
-      // dM += Phi^T R: the A operand needs, for key row 32db + i, the tokens
-      // that R's register order gives (two runs of four).
+      // dM += Phi^T V (- Phi^T P/den): the A operand needs, for key row
+      // 32db + i, the tokens that the B operands' register order gives (two
+      // runs of four).
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const T* prow = PhiT + (32 * db + i) * PTS + 32 * w + 16 * c + 4 * h;
-          mma32(dM[db], load4x2<T>(prow, prow + 8), rf[c]);
+          const frag_t<T> af = load4x2<T>(prow, prow + 8);
+          mma32(dM[db], af, vf[c]);
+          if constexpr (RULE == kRuleDelta) mma32(dM[db], af, pf[c]);
         }
       }
       __syncthreads();

@@ -68,12 +68,21 @@ def ws(lib, *args):
 
 
 def test_workspace_sizes(lib):
-    # Llama-3-8B-shaped, bf16: 32 units, 16 segments of d*d bf16 + d floats
+    # Llama-3-8B-shaped, bf16, delta rule: seg_len >= 4 d, so the scan runs in
+    # affine form. Per segment and unit: snapshots (d*d bf16 + d floats),
+    # column sums (d floats), B_s (d*d floats) and A_s (d*d bf16).
     st, full, least = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 1)
     assert st == 0
-    per_seg = 32 * (128 * 128 * 2 + 128 * 4)
+    d = 128
+    per_seg = 32 * (d * d * 2 + d * 4 + d * 4 + d * d * 4 + d * d * 2)
     assert full - least == 15 * per_seg
-    assert least >= per_seg + 2 * 32 * (128 * 128 + 128) * 4
+    assert least >= per_seg + 2 * 32 * (d * d + d) * 4
+    # the linear rule needs no A_s
+    st, full_lin, least_lin = ws(lib, 4, 32, 8, 32768, 128, 2048, 0, 1)
+    assert full - full_lin == 16 * 32 * d * d * 2
+    # direct scan (seg_len < 4 d): snapshots only
+    st, full_dir, least_dir = ws(lib, 16, 32, 32, 32768, 128, 128, 1, 1)
+    assert full_dir - least_dir == 255 * 512 * (d * d * 2 + d * 4)
     st, full32, _ = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 0)
     assert st == 0 and full32 > full
     # a ragged final segment counts as a segment

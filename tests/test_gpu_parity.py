@@ -112,6 +112,11 @@ EDGE = [
     (1, 2, 2, 257, 128, 130, torch.bfloat16), # ragged key tiles and query tiles
     (2, 8, 2, 500, 64, 128, torch.bfloat16),
     (1, 4, 4, 64, 32, 33, torch.bfloat16),
+    # seg_len >= 4 d: the scan runs in affine form
+    (1, 2, 2, 600, 32, 130, torch.float32),
+    (2, 4, 2, 1100, 64, 300, torch.bfloat16),
+    (1, 4, 1, 1500, 128, 520, torch.bfloat16),
+    (1, 2, 2, 1200, 128, 600, torch.float32),
 ]
 
 
@@ -134,45 +139,48 @@ def test_nonzero_initial_state(lib, dt, rule):
     check(inp, res, 64, rule, all_units(2, 2), tolerance(dt))
 
 
-def test_windows_match_one_pass(lib):
+@pytest.mark.parametrize("seg_len", [100, 260])  # direct scan, affine form
+def test_windows_match_one_pass(lib, seg_len):
     """A workspace of the minimum size walks the segments in windows; the
     result equals the one-pass result bit for bit."""
-    _say("windowed vs one pass")
+    _say(f"windowed vs one pass, seg_len {seg_len}")
     inp = random_inputs(2, 4, 2, 1000, 64, torch.bfloat16, DEV, seed=3)
     B, Hq, L, d = inp["q"].shape
-    full, least = lib.workspace_size(B, Hq, 2, L, d, 100, "delta", torch.bfloat16)
-    a = run(lib, inp, 100, "delta")
+    full, least = lib.workspace_size(B, Hq, 2, L, d, seg_len, "delta", torch.bfloat16)
+    a = run(lib, inp, seg_len, "delta")
     for size in (least, least + (full - least) // 3):
         ws = torch.empty(size, dtype=torch.uint8, device=DEV)
-        b = run(lib, inp, 100, "delta", workspace=ws)
+        b = run(lib, inp, seg_len, "delta", workspace=ws)
         for x, y in zip(a, b):
             assert torch.equal(x, y)
 
 
-def test_in_place_state_carry(lib):
+@pytest.mark.parametrize("seg_len", [64, 256])  # direct scan, affine form
+def test_in_place_state_carry(lib, seg_len):
     """M_final may be M0 and z_final may be z0."""
-    _say("in-place carry")
-    inp = random_inputs(1, 4, 2, 256, 64, torch.bfloat16, DEV, seed=5, m0_scale=0.3)
-    ref = run(lib, inp, 64, "delta")
+    _say(f"in-place carry, seg_len {seg_len}")
+    inp = random_inputs(1, 4, 2, 1024, 64, torch.bfloat16, DEV, seed=5, m0_scale=0.3)
+    ref = run(lib, inp, seg_len, "delta")
     M = inp["M0"].clone()
     z = inp["z0"].clone()
-    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], M, z, 64, "delta",
+    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], M, z, seg_len, "delta",
                       M_final=M, z_final=z)
     torch.cuda.synchronize()
     assert torch.equal(res[0], ref[0]) and torch.equal(M, ref[1]) and torch.equal(z, ref[2])
 
 
+@pytest.mark.parametrize("seg_len", [64, 256])  # direct scan, affine form
 @pytest.mark.parametrize("rule", ["linear", "delta"])
-def test_chunked_calls_equal_one_call(lib, rule):
-    _say(f"chunked calls {rule}")
-    inp = random_inputs(1, 2, 2, 384, 64, torch.float32, DEV, seed=11)
-    out, M, z = run(lib, inp, 64, rule)
-    cut = 192
+def test_chunked_calls_equal_one_call(lib, rule, seg_len):
+    _say(f"chunked calls {rule} seg_len {seg_len}")
+    inp = random_inputs(1, 2, 2, 6 * seg_len, 64, torch.float32, DEV, seed=11)
+    out, M, z = run(lib, inp, seg_len, rule)
+    cut = 3 * seg_len
     first = {k: (v[:, :, :cut].contiguous() if k in "qkv" else v) for k, v in inp.items()}
     second = {k: (v[:, :, cut:].contiguous() if k in "qkv" else v) for k, v in inp.items()}
-    o1, M1, z1 = run(lib, first, 64, rule)
+    o1, M1, z1 = run(lib, first, seg_len, rule)
     second["M0"], second["z0"] = M1, z1
-    o2, M2, z2 = run(lib, second, 64, rule)
+    o2, M2, z2 = run(lib, second, seg_len, rule)
     torch.testing.assert_close(torch.cat([o1, o2], dim=2), out, rtol=1e-5, atol=1e-6)
     torch.testing.assert_close(M2, M, rtol=1e-5, atol=1e-5)
     torch.testing.assert_close(z2, z, rtol=1e-6, atol=0)
