@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before the steps, copy MIB MiB device to device once (a kernel "
+                         "of known traffic that calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,6 +136,15 @@ def main():
         lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
                     w.seg_len, rule, out=out, M_final=M, z_final=z, workspace=ws,
                     stream=stream, events=events)
+
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -38,32 +38,53 @@ constexpr float kRescaleTau = 8.f;
 template <typename T, int D, int NW, int BN>
 struct AttnTile {
   static constexpr int NT = NW * 64;
-  static constexpr int KS = D + pad16<T>();   // Ks row stride (elements)
-  static constexpr int VS = BN + pad16<T>();  // Vt row stride (elements)
-  static constexpr int K_TOTAL = BN * (D / 8);         // 8-element K chunks per tile
-  static constexpr int V_TOTAL = (BN / 4) * (D / 4);   // 4x4 V blocks per tile
+  // Row strides (elements). K rows: 16 bytes of padding, so the 16 lanes of a
+  // quarter-wave reading 16-byte chunks of 16 consecutive rows hit 16
+  // different 4-bank groups. V^T rows: 4 elements of padding, so 32 lanes
+  // reading 4-element runs of 32 consecutive rows, and the transposed stores
+  // below, each cover the 64 banks once.
+  static constexpr int KS = D + pad16<T>();
+  static constexpr int VS = BN + 4;
+  static constexpr int K_TOTAL = BN * (D / 8);   // 8-element K chunks per tile
   static constexpr int K_CHUNKS = (K_TOTAL + NT - 1) / NT;  // per thread
-  static constexpr int V_BLOCKS = (V_TOTAL + NT - 1) / NT;
+  // V is staged in 4 keys x 4 dims blocks; a group of 32 lanes takes 8
+  // consecutive dim-quads x 4 consecutive key-quads.
+  static constexpr int DQ = D / 4, KQ = BN / 4;
+  static constexpr int V_GROUPS = (DQ / 8) * (KQ / 4);
+  static constexpr int V_PER_THREAD = (V_GROUPS * 32 + NT - 1) / NT;
+  static_assert(DQ % 8 == 0 && KQ % 4 == 0, "V staging layout");
   frag_t<T> k[K_CHUNKS];
-  vec4_t<T> v[V_BLOCKS][4];
+  vec4_t<T> v[V_PER_THREAD][4];
 
-  // Global -> registers for key tile k0 (keys >= n_s read as zero).
+  __device__ __forceinline__ static bool k_item(int j, int tid, int& r, int& col) {
+    const int c = tid + j * NT;
+    r = c / (D / 8);
+    col = (c % (D / 8)) * 8;
+    return K_TOTAL % NT == 0 || c < K_TOTAL;
+  }
+  __device__ __forceinline__ static bool v_item(int j, int tid, int& d4, int& k4) {
+    const int g = (tid >> 5) + j * (NT / 32), l = tid & 31;
+    d4 = (g % (DQ / 8)) * 8 + (l & 7);
+    k4 = (g / (DQ / 8)) * 4 + (l >> 3);
+    return (V_GROUPS * 32) % NT == 0 || g < V_GROUPS;
+  }
+
+  // Global -> registers for key tile k0. Rows past the segment's end repeat
+  // its last row: finite values whose scores the causal mask removes.
   __device__ __forceinline__ void load(const T* K, const T* V, int k0, int n_s, int tid) {
+    const int last = n_s - 1;
 #pragma unroll
     for (int j = 0; j < K_CHUNKS; ++j) {
-      const int c = tid + j * NT;
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      k[j] = zero_frag<T>();
-      if (c < K_TOTAL && k0 + r < n_s) k[j] = load8<T>(K + (int64_t)(k0 + r) * D + col);
+      int r, col;
+      if (k_item(j, tid, r, col)) k[j] = load8<T>(K + (int64_t)min(k0 + r, last) * D + col);
     }
 #pragma unroll
-    for (int j = 0; j < V_BLOCKS; ++j) {
-      const int c = tid + j * NT;
-      const int d4 = c % (D / 4), k4 = c / (D / 4);
+    for (int j = 0; j < V_PER_THREAD; ++j) {
+      int d4, k4;
+      if (v_item(j, tid, d4, k4)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[j][q] = zero4<T>();
-        if (c < V_TOTAL && k0 + 4 * k4 + q < n_s) v[j][q] = load4<T>(V + (int64_t)(k0 + 4 * k4 + q) * D + 4 * d4);
+        for (int q = 0; q < 4; ++q)
+          v[j][q] = load4<T>(V + (int64_t)min(k0 + 4 * k4 + q, last) * D + 4 * d4);
       }
     }
   }
@@ -72,24 +93,87 @@ struct AttnTile {
   __device__ __forceinline__ void store(T* Ks, T* Vt, int tid) const {
 #pragma unroll
     for (int j = 0; j < K_CHUNKS; ++j) {
-      const int c = tid + j * NT;
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      if (c < K_TOTAL) store8<T>(Ks + r * KS + col, k[j]);
+      int r, col;
+      if (k_item(j, tid, r, col)) store8<T>(Ks + r * KS + col, k[j]);
     }
 #pragma unroll
-    for (int j = 0; j < V_BLOCKS; ++j) {
-      const int c = tid + j * NT;
-      const int d4 = c % (D / 4), k4 = c / (D / 4);
-      if (c >= V_TOTAL) continue;
+    for (int j = 0; j < V_PER_THREAD; ++j) {
+      int d4, k4;
+      if (v_item(j, tid, d4, k4)) {
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        vec4_t<T> y;
-        y[0] = v[j][0][dd]; y[1] = v[j][1][dd]; y[2] = v[j][2][dd]; y[3] = v[j][3][dd];
-        store4<T>(Vt + (4 * d4 + dd) * VS + 4 * k4, y);
+        for (int dd = 0; dd < 4; ++dd) {
+          vec4_t<T> y;
+          y[0] = v[j][0][dd]; y[1] = v[j][1][dd]; y[2] = v[j][2][dd]; y[3] = v[j][3][dd];
+          store4<T>(Vt + (4 * d4 + dd) * VS + 4 * k4, y);
+        }
       }
     }
   }
 };
+
+// One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// MASK: the tile reaches past the wave's first query row, so the causal mask
+// applies (only the tiles on the diagonal).
+template <typename T, int D, int BN, bool MASK>
+__device__ __forceinline__ void attn_tile(const T* Kb, const T* Vb, const frag_t<T>* qf,
+                                          f32x16* oacc, float& m_run, float& l_run, float c,
+                                          int k0, int row, int i, int h) {
+  constexpr int NC = D / 16, NDB = D / 32, NKB = BN / 32, NPC = BN / 16;
+  constexpr int KS = D + pad16<T>();
+  constexpr int VS = BN + 4;
+  f32x16 sacc[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    sacc[kb] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      mma32(sacc[kb], load8<T>(Kb + (32 * kb + i) * KS + 16 * cc + 8 * h), qf[cc]);
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + 32 * kb + acc_row(r, h) > row) sacc[kb][r] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Key 0 of the segment is visible to every row, so the first tile sets a
+  // finite reference for every lane.
+  if (__any((mx - m_run) * c > kRescaleTau)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  const float mc = m_run * c;
+  frag_t<T> pf[NPC];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+      l_run += p;
+      pf[2 * kb + (r >> 3)][r & 7] = from_f32<T>(p);
+    }
+  // O^T += V^T P^T. Element e of pf[pc] is key 16pc + 8(e/4) + 4h + e%4 of the
+  // tile, so the A operand reads two runs of four keys from Vt.
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc) {
+      const T* vrow = Vb + (32 * db + i) * VS + 16 * pc + 4 * h;
+      mma32(oacc[db], load4x2<T>(vrow, vrow + 8), pf[pc]);
+    }
+}
 
 template <typename T, int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
@@ -173,61 +257,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
     if (kt + 1 < n_kt) tile.load(K, V, k0 + BN, n_s, tid);  // in flight during this tile
 
     if (wave_on && k0 <= wave_last) {
-      const T* Kb = Ks[buf];
-      const T* Vb = Vt[buf];
-      f32x16 sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = zero16();
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-          mma32(sacc[kb], load8<T>(Kb + (32 * kb + i) * KS + 16 * cc + 8 * h), qf[cc]);
-      }
-
-      if (k0 + BN - 1 > q0 + 32 * w) {  // the tile reaches past the wave's first row
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (k0 + 32 * kb + acc_row(r, h) > row) sacc[kb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Key 0 of the segment is visible to every row, so the first tile sets
-      // a finite reference for every lane.
-      if (__any((mx - m_run) * c > kRescaleTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-      }
-      const float mc = m_run * c;
-      frag_t<T> pf[NPC];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
-          l_run += p;
-          pf[2 * kb + (r >> 3)][r & 7] = from_f32<T>(p);
-        }
-      // O^T += V^T P^T. Element e of pf[pc] is key 16pc + 8(e/4) + 4h + e%4 of
-      // the tile, so the A operand reads two runs of four keys from Vt.
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int pc = 0; pc < NPC; ++pc) {
-          const T* vrow = Vb + (32 * db + i) * VS + 16 * pc + 4 * h;
-          mma32(oacc[db], load4x2<T>(vrow, vrow + 8), pf[pc]);
-        }
+      if (k0 + BN - 1 > q0 + 32 * w)
+        attn_tile<T, D, BN, true>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i, h);
+      else
+        attn_tile<T, D, BN, false>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i, h);
     }
     if (kt + 1 < n_kt) {
       // buffer buf^1 was last read in iteration kt-1, before that iteration's
@@ -286,13 +319,277 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ---- bf16, d in {64, 128}: tiles streamed straight into LDS ------------------
+//
+// K and V tiles go from global memory into LDS with gfx950's LDS-DMA loads
+// (global_load_lds, 16 bytes per lane: lane l of one instruction fills bytes
+// [16l, 16l + 16) of a 1 KB block), so no registers or VALU are spent staging
+// them. Both tiles stay row major, [key][dim], with 16-byte chunks XOR-swizzled
+// within a row instead of padded:
+//   K: chunk c of row r sits at c ^ swk(r), so the 16 rows that a quarter-wave
+//      reads for one MFMA A operand (same logical chunk) hit 16 bank groups;
+//   V: chunk c of row r sits at c ^ swv(r); the A operand of O^T += V^T P^T
+//      (rows of V^T = columns of V) is read with ds_read_b64_tr_b16, which
+//      hands lane j of a 16-lane group element (j % 4) of the 8-byte loads of
+//      lanes 4e + j/4, e = 0..3. If lane 4a + b of the group loads columns
+//      [4b, 4b + 4) of row key0 + a, lane j receives V[key0 + e][j], e = 0..3:
+//      four consecutive keys of one value column, as the fragment needs. The
+//      swizzle spreads the 4 rows x 4 chunks a half-wave reads over the banks.
+
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int D, int NW, int BN>
+struct DmaTile {
+  static constexpr int NT = NW * 64;
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int CHUNKS = BN * CPR;            // per tile, per tensor
+  static constexpr int PER_WAVE = CHUNKS / 64 / NW;  // DMA instructions per wave and tensor
+  static_assert(CHUNKS % (64 * NW) == 0, "tile split");
+  // per lane and instruction: the row and the logical chunk it fetches
+  int k_row[PER_WAVE], k_col[PER_WAVE], v_row[PER_WAVE], v_col[PER_WAVE];
+
+  __device__ __forceinline__ void init(int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int p = (w * PER_WAVE + j) * 64 + lane;  // physical chunk of the tile
+      const int r = p / CPR, phys = p % CPR;
+      k_row[j] = r;
+      k_col[j] = 8 * (phys ^ swz_k<D>(r));
+      v_row[j] = r;
+      v_col[j] = 8 * (phys ^ swz_v<D>(r));
+    }
+  }
+  // Issue the loads of key tile k0 into Ks / Vs (each [BN][D]). Rows past the
+  // segment's end repeat its last row (finite; the causal mask removes them).
+  __device__ __forceinline__ void issue(const bf16* K, const bf16* V, bf16* Ks, bf16* Vs, int k0,
+                                        int n_s, int w) const {
+    const bool tail = k0 + BN > n_s;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int r = tail ? min(k0 + k_row[j], n_s - 1) : k0 + k_row[j];
+      const int blk = (w * PER_WAVE + j) * 64 * 8;  // element offset of this wave's 1 KB block
+      __builtin_amdgcn_global_load_lds(K + (int64_t)r * D + k_col[j], (lds_void*)(Ks + blk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(V + (int64_t)r * D + v_col[j], (lds_void*)(Vs + blk), 16, 0, 0);
+    }
+  }
+};
+
+template <int D, int BN, bool MASK>
+__device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, const bf16x8* qf,
+                                              f32x16* oacc, float& m_run, float& l_run, float c,
+                                              int k0, int row, int lane) {
+  constexpr int NC = D / 16, NDB = D / 32, NKB = BN / 32, NPC = BN / 16;
+  const int i = lane & 31, h = lane >> 5;
+  f32x16 sacc[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    sacc[kb] = zero16();
+    const int r = 32 * kb + i;
+    const bf16* krow = Kb + r * D;
+    const int sw = swz_k<D>(r);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      mma32(sacc[kb], load8<bf16>(krow + 8 * ((2 * cc + h) ^ sw)), qf[cc]);
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + 32 * kb + acc_row(r, h) > row) sacc[kb][r] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__any((mx - m_run) * c > kRescaleTau)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  const float mc = m_run * c;
+  bf16x8 pf[NPC];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+      l_run += p;
+      pf[2 * kb + (r >> 3)][r & 7] = (bf16)p;
+    }
+  // A operand of O^T += V^T P^T by transposing reads: lane 16G + 4a + b
+  // (G = lane / 16, half-wave h = G / 2) points at row 16pc + 8s + 4h + a,
+  // columns 32db + 16(G % 2) + 4b .. + 3, for s = 0 (elements 0..3) and
+  // s = 1 (elements 4..7).
+  const int G = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = 32 * db + 16 * (G & 1) + 4 * b;
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc) {
+      const int r0 = 16 * pc + 4 * h + a, r1 = r0 + 8;
+      const bf16x4 lo = lds_read_tr(Vb + r0 * D + 8 * ((col >> 3) ^ swz_v<D>(r0)) + (col & 7));
+      const bf16x4 hi = lds_read_tr(Vb + r1 * D + 8 * ((col >> 3) ^ swz_v<D>(r1)) + (col & 7));
+      mma32(oacc[db], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[pc]);
+    }
+  }
+}
+
+template <int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
+  constexpr int BM = 32 * NW;
+  constexpr int NC = D / 16, NDB = D / 32;
+  __shared__ __align__(1024) bf16 Ks[2][BN * D];
+  __shared__ __align__(1024) bf16 Vs[2][BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int G = a.Hq / a.Hkv;
+  const int in_grp = a.n_qt * G;
+  const int grp = t / in_grp, rr = t % in_grp;
+  const int qt = a.n_qt - 1 - rr / G;
+  const int hg = rr % G;
+  const int sl = grp % a.s_count;
+  const int unit = grp / a.s_count;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int hq = kvh * G + hg;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int q0 = qt * BM;
+  if (q0 >= n_s) return;
+
+  const int64_t qh = (int64_t)b * a.Hq + hq;
+  const bf16* Q = static_cast<const bf16*>(a.q) + (qh * a.L + seg_start) * D;
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * D;
+
+  const int row = q0 + 32 * w + i;
+  const bool wave_on = q0 + 32 * w < n_s;
+  const int wave_last = min(q0 + 32 * w + 31, n_s - 1);
+  const float c = a.scale_log2;
+  const int n_kv = min(q0 + BM, n_s);
+  const int n_kt = (n_kv + BN - 1) / BN;
+
+  DmaTile<D, NW, BN> tile;
+  tile.init(w, lane);
+  tile.issue(K, V, Ks[0], Vs[0], 0, n_s, w);
+
+  bf16x8 qf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    qf[cc] = zero_frag<bf16>();
+    if (row < n_s) qf[cc] = load8<bf16>(Q + (int64_t)row * D + 16 * cc + 8 * h);
+  }
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * BN;
+    const int buf = kt & 1;
+    // buffer buf^1 was last read in iteration kt-1, before that iteration's barrier
+    if (kt + 1 < n_kt) tile.issue(K, V, Ks[buf ^ 1], Vs[buf ^ 1], k0 + BN, n_s, w);
+    if (wave_on && k0 <= wave_last) {
+      if (k0 + BN - 1 > q0 + 32 * w)
+        attn_tile_dma<D, BN, true>(Ks[buf], Vs[buf], qf, oacc, m_run, l_run, c, k0, row, lane);
+      else
+        attn_tile_dma<D, BN, false>(Ks[buf], Vs[buf], qf, oacc, m_run, l_run, c, k0, row, lane);
+    }
+    if (kt + 1 < n_kt) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA loads of tile kt+1 have landed
+      __syncthreads();
+    }
+  }
+  if (!wave_on) return;
+
+  const float l = l_run + __shfl_xor(l_run, 32);
+  const int64_t snap = (int64_t)unit * a.s_count + sl;
+  const float* zs = a.snapZ + snap * D;
+  const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * D * D;
+  float sq[NC][8];
+  float dp = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = feature_map((float)qf[cc][e]);
+      sq[cc][e] = s;
+      dp += s * zs[16 * cc + 8 * h + e];
+    }
+  const float den = dp + __shfl_xor(dp, 32);
+  const float g = 1.f / (1.f + __expf(-a.beta[hq]));
+  const float ca = (1.f - g) / l, cm = g / den;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] *= ca;
+  bf16x8 sf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sf[cc][e] = (bf16)(sq[cc][e] * cm);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      mma32(oacc[db], load8<bf16>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
+  if (row < n_s) {
+    bf16* orow = O + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = (bf16)oacc[db][4 * rq + j];
+        store4<bf16>(orow + 32 * db + 8 * rq + 4 * h, y);
+      }
+  }
+}
+
 template <typename T, int D, int NW>
 hipError_t launch_attn_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
   constexpr int BN = 64;
   const int64_t G = a.Hq / a.Hkv;
   const int64_t total = units * a.s_count * a.n_qt * G;
-  hipLaunchKernelGGL((attn_kernel<T, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
-                     stream, a);
+  if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
+    hipLaunchKernelGGL((attn_kernel_dma<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<T, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 
