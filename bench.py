@@ -33,6 +33,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc", "attn.hip")
 
 
+def attn_kernel_bytes(w):
+    """Algorithmic HBM bytes of the attention kernel in one call: Q and out
+    once, K and V once, and the per-segment state it reads (M^T in the element
+    type and z in float, per KV head and segment), beta once."""
+    e = 4 if w.dtype == "f32" else 2
+    return (e * w.d * w.L * w.B * (2 * w.Hq + 2 * w.Hkv)
+            + w.B * w.Hkv * w.segments * (w.d * w.d * e + 4 * w.d) + 4 * w.Hq)
+
+
 def attn_kernel_flops(w):
     """Algorithmic matrix-product FLOPs of the attention kernel in one call:
     per (query head, token) 2d(N+1) for the causal QK^T and PV (diagonal
@@ -205,6 +214,7 @@ def main():
             "frac": a_tflops / peak,
             "traffic": traffic,
             "algorithmic_flop_per_launch": a_flops,
+            "algorithmic_bytes_per_launch": attn_kernel_bytes(w),
         },
         "cpu_baseline": None,
     }
