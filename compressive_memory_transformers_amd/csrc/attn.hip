@@ -352,6 +352,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ const bf16* lds_at(const bf16* base, uint32_t byte_off) {
+  return reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw, no stride; dword 3 as
+// gfx9 wants it for untyped loads). Loads through it take the base from
+// scalar registers and a 32-bit per-lane offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)bytes, 0x00020000);
+}
+
 template <int D, int NW, int BN>
 struct DmaTile {
   static constexpr int NT = NW * 64;
@@ -359,53 +372,109 @@ struct DmaTile {
   static constexpr int CHUNKS = BN * CPR;            // per tile, per tensor
   static constexpr int PER_WAVE = CHUNKS / 64 / NW;  // DMA instructions per wave and tensor
   static_assert(CHUNKS % (64 * NW) == 0, "tile split");
-  // per lane and instruction: the row and the logical chunk it fetches
-  int k_row[PER_WAVE], k_col[PER_WAVE], v_row[PER_WAVE], v_col[PER_WAVE];
+  // Instruction j of wave w fills tile rows from (j NW + w) 64 / CPR on. When
+  // the swizzles of those rows do not depend on j (NW a multiple of 4 for
+  // d = 128, even for d = 64), instruction j's lane offsets are instruction
+  // 0's plus J_STEP j bytes, which the load takes as a scalar offset.
+  static constexpr bool J_INV = D == 128 ? NW % 4 == 0 : NW % 2 == 0;
+  static constexpr uint32_t J_STEP = NW * (64 / CPR) * 2 * D;
+  static constexpr int NOFF = J_INV ? 1 : PER_WAVE;
+  // per lane: byte offset, from the tile's first row, of the 16-byte chunk
+  // it fetches (the same tile row for K and V)
+  uint32_t k_off[NOFF], v_off[NOFF];
 
   __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int p = (w * PER_WAVE + j) * 64 + lane;  // physical chunk of the tile
+    for (int j = 0; j < NOFF; ++j) {
+      const int p = (j * NW + w) * 64 + lane;  // physical chunk of the tile
       const int r = p / CPR, phys = p % CPR;
-      k_row[j] = r;
-      k_col[j] = 8 * (phys ^ swz_k<D>(r));
-      v_row[j] = r;
-      v_col[j] = 8 * (phys ^ swz_v<D>(r));
+      k_off[j] = 2 * (r * D + 8 * (phys ^ swz_k<D>(r)));
+      v_off[j] = 2 * (r * D + 8 * (phys ^ swz_v<D>(r)));
     }
   }
-  // Issue the loads of key tile k0 into Ks / Vs (each [BN][D]). Rows past the
-  // segment's end repeat its last row (finite; the causal mask removes them).
+  __device__ __forceinline__ uint32_t koff(int j) const {
+    return J_INV ? k_off[0] + j * J_STEP : k_off[j];
+  }
+  __device__ __forceinline__ uint32_t voff(int j) const {
+    return J_INV ? v_off[0] + j * J_STEP : v_off[j];
+  }
+  // Issue the loads of key tile k0 into Ks / Vs (each [BN][D]); w is the
+  // (wave-uniform) wave index. Each load is a buffer_load ... lds of 16 bytes
+  // per lane from a resource over the tile's rows. In a tail tile, rows past
+  // the segment's end repeat its last row (finite; the causal mask removes
+  // them).
   __device__ __forceinline__ void issue(const bf16* K, const bf16* V, bf16* Ks, bf16* Vs, int k0,
                                         int n_s, int w) const {
-    const bool tail = k0 + BN > n_s;
+    const int rows = min(BN, n_s - k0);
+    const __amdgpu_buffer_rsrc_t rk = raw_rsrc(K + (int64_t)k0 * D, (uint32_t)rows * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = raw_rsrc(V + (int64_t)k0 * D, (uint32_t)rows * D * 2);
+    if (rows == BN) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int r = tail ? min(k0 + k_row[j], n_s - 1) : k0 + k_row[j];
-      const int blk = (w * PER_WAVE + j) * 64 * 8;  // element offset of this wave's 1 KB block
-      __builtin_amdgcn_global_load_lds(K + (int64_t)r * D + k_col[j], (lds_void*)(Ks + blk), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(V + (int64_t)r * D + v_col[j], (lds_void*)(Vs + blk), 16, 0, 0);
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int blk = (j * NW + w) * 64 * 8;  // element offset of this wave's 1 KB block
+        const uint32_t sj = J_INV ? j * J_STEP : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Ks + blk), 16, k_off[J_INV ? 0 : j], sj, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vs + blk), 16, v_off[J_INV ? 0 : j], sj, 0, 0);
+      }
+    } else {
+      const uint32_t lim = (uint32_t)rows * (2 * D);  // bytes of the valid rows
+      const uint32_t last = lim - 2 * D;              // start of the last valid row
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int blk = (j * NW + w) * 64 * 8;
+        const uint32_t kj = koff(j), vj = voff(j);
+        const bool in = kj < lim;  // same row for K and V
+        const uint32_t ko = in ? kj : last + (kj & (2 * D - 1));
+        const uint32_t vo = in ? vj : last + (vj & (2 * D - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Ks + blk), 16, ko, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vs + blk), 16, vo, 0, 0, 0);
+      }
     }
   }
 };
 
-template <int D, int BN, bool MASK>
-__device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, const bf16x8* qf,
-                                              f32x16* oacc, float& m_run, float& l_run, float c,
-                                              int k0, int row, int lane) {
+// Per-lane state of the key loop, with the lane's LDS read offsets computed
+// once: with the swizzles above, a lane's K and V read addresses differ
+// between key blocks, probability chunks and the two LDS buffers only by
+// constants, which the reads take as immediate offsets.
+template <int D>
+struct DmaLane {
+  static constexpr int NC = D / 16, NDB = D / 32;
+  bf16x8 qf[NC];
+  f32x16 oacc[NDB];
+  float m_run, l0, l1;  // running max (log2 units before scaling) and two partial sums
+  uint32_t ko;          // K: byte offset of chunk h of tile row i; chunk 2cc + h is at ko ^ 32cc
+  uint32_t vo[NDB];     // V: byte offset of this lane's transposing read for value block db
+
+  __device__ __forceinline__ void init_offsets(int lane) {
+    const int i = lane & 31, h = lane >> 5;
+    ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+    // lane 16G + 4a + b reads rows 16pc + 8s + 4h + a, columns
+    // 32db + 16(G % 2) + 4b .. + 3 (see the V swizzle); the row's swizzle
+    // depends on a only, so pc and s are constant offsets
+    const int G = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+    const int r0 = 4 * h + a;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * b;
+      vo[db] = 2 * (r0 * D + 8 * ((col >> 3) ^ swz_v<D>(r0)) + (col & 7));
+    }
+  }
+};
+
+template <int D, int BN>
+__device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, DmaLane<D>& st,
+                                              float c, int k0, int row, int h, bool diag) {
   constexpr int NC = D / 16, NDB = D / 32, NKB = BN / 32, NPC = BN / 16;
-  const int i = lane & 31, h = lane >> 5;
   f32x16 sacc[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     sacc[kb] = zero16();
-    const int r = 32 * kb + i;
-    const bf16* krow = Kb + r * D;
-    const int sw = swz_k<D>(r);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      mma32(sacc[kb], load8<bf16>(krow + 8 * ((2 * cc + h) ^ sw)), qf[cc]);
+      mma32(sacc[kb], load8<bf16>(lds_at(Kb, (st.ko ^ (32u * cc)) + 2 * 32 * kb * D)), st.qf[cc]);
   }
-  if constexpr (MASK) {
+  if (diag) {  // wave-uniform: the tile crosses this wave's diagonal
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -418,41 +487,64 @@ __device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, co
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (__any((mx - m_run) * c > kRescaleTau)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    l_run *= alpha;
+  if (__any((mx - st.m_run) * c > kRescaleTau)) {
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);
+    st.l0 *= alpha;
+    st.l1 *= alpha;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    m_run = m_new;
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+    st.m_run = m_new;
   }
-  const float mc = m_run * c;
+  const float mc = st.m_run * c;
   bf16x8 pf[NPC];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
-      l_run += p;
-      pf[2 * kb + (r >> 3)][r & 7] = (bf16)p;
-    }
-  // A operand of O^T += V^T P^T by transposing reads: lane 16G + 4a + b
-  // (G = lane / 16, half-wave h = G / 2) points at row 16pc + 8s + 4h + a,
-  // columns 32db + 16(G % 2) + 4b .. + 3, for s = 0 (elements 0..3) and
-  // s = 1 (elements 4..7).
-  const int G = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+    for (int r = 0; r < 16; ++r)
+      pf[2 * kb + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
+  // the row sum adds the probabilities as rounded for the product with V,
+  // two at a time (v_dot2 with (1, 1))
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int col = 32 * db + 16 * (G & 1) + 4 * b;
+  for (int pc = 0; pc < NPC; ++pc)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x2 pr = {pf[pc][2 * q], pf[pc][2 * q + 1]};
+      if (q & 1)
+        st.l1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l1, false);
+      else
+        st.l0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l0, false);
+    }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int pc = 0; pc < NPC; ++pc) {
-      const int r0 = 16 * pc + 4 * h + a, r1 = r0 + 8;
-      const bf16x4 lo = lds_read_tr(Vb + r0 * D + 8 * ((col >> 3) ^ swz_v<D>(r0)) + (col & 7));
-      const bf16x4 hi = lds_read_tr(Vb + r1 * D + 8 * ((col >> 3) ^ swz_v<D>(r1)) + (col & 7));
-      mma32(oacc[db], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[pc]);
+      const bf16x4 lo = lds_read_tr(lds_at(Vb, st.vo[db] + 2 * 16 * pc * D));
+      const bf16x4 hi = lds_read_tr(lds_at(Vb, st.vo[db] + 2 * (16 * pc + 8) * D));
+      mma32(st.oacc[db], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[pc]);
     }
+}
+
+// One key tile of the loop on LDS buffer BUF (a constant, so every LDS
+// address in the tile is a lane offset plus an immediate): issue the next
+// tile into the other buffer, compute this one, wait for the next.
+template <int D, int NW, int BN, int BUF>
+__device__ __forceinline__ void attn_step(int kt, int n_kt, const DmaTile<D, NW, BN>& tile,
+                                          const bf16* K, const bf16* V, bf16 (*Ks)[BN * D],
+                                          bf16 (*Vs)[BN * D], int n_s, int w, bool wave_on,
+                                          int wave_last, int q0, DmaLane<D>& st, float c, int row,
+                                          int h) {
+  const int k0 = kt * BN;
+  // buffer BUF^1 was last read in tile kt-1, before that tile's barrier
+  if (kt + 1 < n_kt) tile.issue(K, V, Ks[BUF ^ 1], Vs[BUF ^ 1], k0 + BN, n_s, w);
+  if (wave_on && k0 <= wave_last)
+    attn_tile_dma<D, BN>(Ks[BUF], Vs[BUF], st, c, k0, row, h, k0 + BN - 1 > q0 + 32 * w);
+  if (kt + 1 < n_kt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA loads of tile kt+1 have landed
+    __syncthreads();
   }
 }
 
@@ -463,7 +555,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   __shared__ __align__(1024) bf16 Ks[2][BN * D];
   __shared__ __align__(1024) bf16 Vs[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 31, h = lane >> 5;
 
   int t = blockIdx.x;
@@ -502,38 +595,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   tile.init(w, lane);
   tile.issue(K, V, Ks[0], Vs[0], 0, n_s, w);
 
-  bf16x8 qf[NC];
+  DmaLane<D> st;
+  st.init_offsets(lane);
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
-    qf[cc] = zero_frag<bf16>();
-    if (row < n_s) qf[cc] = load8<bf16>(Q + (int64_t)row * D + 16 * cc + 8 * h);
+    st.qf[cc] = zero_frag<bf16>();
+    if (row < n_s) st.qf[cc] = load8<bf16>(Q + (int64_t)row * D + 16 * cc + 8 * h);
   }
-  f32x16 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = zero16();
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int db = 0; db < NDB; ++db) st.oacc[db] = zero16();
+  st.m_run = -INFINITY;
+  st.l0 = st.l1 = 0.f;
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * BN;
-    const int buf = kt & 1;
-    // buffer buf^1 was last read in iteration kt-1, before that iteration's barrier
-    if (kt + 1 < n_kt) tile.issue(K, V, Ks[buf ^ 1], Vs[buf ^ 1], k0 + BN, n_s, w);
-    if (wave_on && k0 <= wave_last) {
-      if (k0 + BN - 1 > q0 + 32 * w)
-        attn_tile_dma<D, BN, true>(Ks[buf], Vs[buf], qf, oacc, m_run, l_run, c, k0, row, lane);
-      else
-        attn_tile_dma<D, BN, false>(Ks[buf], Vs[buf], qf, oacc, m_run, l_run, c, k0, row, lane);
-    }
-    if (kt + 1 < n_kt) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA loads of tile kt+1 have landed
-      __syncthreads();
-    }
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    attn_step<D, NW, BN, 0>(kt, n_kt, tile, K, V, Ks, Vs, n_s, w, wave_on, wave_last, q0, st, c,
+                            row, h);
+    if (kt + 1 < n_kt)
+      attn_step<D, NW, BN, 1>(kt + 1, n_kt, tile, K, V, Ks, Vs, n_s, w, wave_on, wave_last, q0,
+                              st, c, row, h);
   }
   if (!wave_on) return;
 
-  const float l = l_run + __shfl_xor(l_run, 32);
+  float l = st.l0 + st.l1;
+  l += __shfl_xor(l, 32);
   const int64_t snap = (int64_t)unit * a.s_count + sl;
   const float* zs = a.snapZ + snap * D;
   const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * D * D;
@@ -543,7 +629,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float s = feature_map((float)qf[cc][e]);
+      const float s = feature_map((float)st.qf[cc][e]);
       sq[cc][e] = s;
       dp += s * zs[16 * cc + 8 * h + e];
     }
@@ -553,7 +639,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] *= ca;
+    for (int r = 0; r < 16; ++r) st.oacc[db][r] *= ca;
   bf16x8 sf[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc)
@@ -563,7 +649,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      mma32(oacc[db], load8<bf16>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
+      mma32(st.oacc[db], load8<bf16>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
   if (row < n_s) {
     bf16* orow = O + (int64_t)row * D;
 #pragma unroll
@@ -572,7 +658,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
       for (int rq = 0; rq < 4; ++rq) {
         bf16x4 y;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = (bf16)oacc[db][4 * rq + j];
+        for (int j = 0; j < 4; ++j) y[j] = (bf16)st.oacc[db][4 * rq + j];
         store4<bf16>(orow + 32 * db + 8 * rq + 4 * h, y);
       }
   }
