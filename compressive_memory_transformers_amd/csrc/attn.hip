@@ -392,29 +392,22 @@ struct DmaTile {
       v_off[j] = 2 * (r * D + 8 * (phys ^ swz_v<D>(r)));
     }
   }
-  __device__ __forceinline__ uint32_t koff(int j) const {
-    return J_INV ? k_off[0] + j * J_STEP : k_off[j];
-  }
-  __device__ __forceinline__ uint32_t voff(int j) const {
-    return J_INV ? v_off[0] + j * J_STEP : v_off[j];
-  }
-  // Issue the loads of key tile k0 into Ks / Vs (each [BN][D]); w is the
-  // (wave-uniform) wave index. Each load is a buffer_load ... lds of 16 bytes
-  // per lane from a resource over the tile's rows. In a tail tile, rows past
-  // the segment's end repeat its last row (finite; the causal mask removes
-  // them).
-  __device__ __forceinline__ void issue(const bf16* K, const bf16* V, bf16* Ks, bf16* Vs, int k0,
-                                        int n_s, int w) const {
+  // Issue the loads of key tile k0 of one tensor (K if IS_K, else V) into
+  // Xs ([BN][D]); w is the (wave-uniform) wave index. Each load is a
+  // buffer_load ... lds of 16 bytes per lane from a resource over the tile's
+  // rows. In a tail tile, rows past the segment's end repeat its last row
+  // (finite; the causal mask removes them).
+  template <bool IS_K>
+  __device__ __forceinline__ void issue(const bf16* X, bf16* Xs, int k0, int n_s, int w) const {
+    const uint32_t* off = IS_K ? k_off : v_off;
     const int rows = min(BN, n_s - k0);
-    const __amdgpu_buffer_rsrc_t rk = raw_rsrc(K + (int64_t)k0 * D, (uint32_t)rows * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = raw_rsrc(V + (int64_t)k0 * D, (uint32_t)rows * D * 2);
+    const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + (int64_t)k0 * D, (uint32_t)rows * D * 2);
     if (rows == BN) {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
         const int blk = (j * NW + w) * 64 * 8;  // element offset of this wave's 1 KB block
         const uint32_t sj = J_INV ? j * J_STEP : 0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Ks + blk), 16, k_off[J_INV ? 0 : j], sj, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vs + blk), 16, v_off[J_INV ? 0 : j], sj, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, off[J_INV ? 0 : j], sj, 0, 0);
       }
     } else {
       const uint32_t lim = (uint32_t)rows * (2 * D);  // bytes of the valid rows
@@ -422,12 +415,9 @@ struct DmaTile {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j) {
         const int blk = (j * NW + w) * 64 * 8;
-        const uint32_t kj = koff(j), vj = voff(j);
-        const bool in = kj < lim;  // same row for K and V
-        const uint32_t ko = in ? kj : last + (kj & (2 * D - 1));
-        const uint32_t vo = in ? vj : last + (vj & (2 * D - 1));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Ks + blk), 16, ko, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vs + blk), 16, vo, 0, 0, 0);
+        const uint32_t xj = J_INV ? off[0] + j * J_STEP : off[j];
+        const uint32_t xo = xj < lim ? xj : last + (xj & (2 * D - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, xo, 0, 0, 0);
       }
     }
   }
@@ -462,11 +452,17 @@ struct DmaLane {
   }
 };
 
+// The key loop is software-pipelined by one tile, so that each wave has
+// matrix work to issue beside its softmax arithmetic: iteration j turns the
+// exp2 arguments of tile j into probabilities while S(j+1) = K(j+1) Q^T runs
+// on the matrix cores, then issues O += V(j) P(j) while it takes the row
+// maxima of S(j+1), decides the lazy rescale and forms the next exp2
+// arguments.
+
+// S^T = K Q^T for one key tile (K in LDS).
 template <int D, int BN>
-__device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, DmaLane<D>& st,
-                                              float c, int k0, int row, int h, bool diag) {
-  constexpr int NC = D / 16, NDB = D / 32, NKB = BN / 32, NPC = BN / 16;
-  f32x16 sacc[NKB];
+__device__ __forceinline__ void dma_scores(const bf16* Kb, const DmaLane<D>& st, f32x16* sacc) {
+  constexpr int NC = D / 16, NKB = BN / 32;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     sacc[kb] = zero16();
@@ -474,7 +470,15 @@ __device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, Dm
     for (int cc = 0; cc < NC; ++cc)
       mma32(sacc[kb], load8<bf16>(lds_at(Kb, (st.ko ^ (32u * cc)) + 2 * 32 * kb * D)), st.qf[cc]);
   }
-  if (diag) {  // wave-uniform: the tile crosses this wave's diagonal
+}
+
+// Causal mask (on a tile that crosses the wave's diagonal), then the running
+// maximum with the lazy rescale of O and l.
+template <int D, int BN>
+__device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<D>& st, float c, int k0, int row,
+                                        int h, bool diag) {
+  constexpr int NDB = D / 32, NKB = BN / 32;
+  if (diag) {  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -498,15 +502,22 @@ __device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, Dm
       for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
     st.m_run = m_new;
   }
+}
+
+// Probabilities exp2(c s - c m) of one tile as the bf16 B operand of
+// O^T += V^T P^T, and the row sums of the probabilities as rounded for that
+// product (pairwise, with v_dot2_f32_bf16 against (1, 1)).
+template <int D, int BN>
+__device__ __forceinline__ void dma_probs(const f32x16* sacc, DmaLane<D>& st, float c,
+                                          bf16x8* pf) {
+  constexpr int NKB = BN / 32, NPC = BN / 16;
   const float mc = st.m_run * c;
-  bf16x8 pf[NPC];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      pf[2 * kb + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
-  // the row sum adds the probabilities as rounded for the product with V,
-  // two at a time (v_dot2 with (1, 1))
+      pf[2 * kb + (r >> 3)][r & 7] =
+          (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
   for (int pc = 0; pc < NPC; ++pc)
@@ -518,6 +529,12 @@ __device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, Dm
       else
         st.l0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l0, false);
     }
+}
+
+// O^T += V^T P^T for one key tile (V in LDS, read transposed).
+template <int D, int BN>
+__device__ __forceinline__ void dma_values(const bf16* Vb, DmaLane<D>& st, const bf16x8* pf) {
+  constexpr int NDB = D / 32, NPC = BN / 16;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -528,22 +545,60 @@ __device__ __forceinline__ void attn_tile_dma(const bf16* Kb, const bf16* Vb, Dm
     }
 }
 
-// One key tile of the loop on LDS buffer BUF (a constant, so every LDS
-// address in the tile is a lane offset plus an immediate): issue the next
-// tile into the other buffer, compute this one, wait for the next.
-template <int D, int NW, int BN, int BUF>
-__device__ __forceinline__ void attn_step(int kt, int n_kt, const DmaTile<D, NW, BN>& tile,
-                                          const bf16* K, const bf16* V, bf16 (*Ks)[BN * D],
-                                          bf16 (*Vs)[BN * D], int n_s, int w, bool wave_on,
-                                          int wave_last, int q0, DmaLane<D>& st, float c, int row,
-                                          int h) {
-  const int k0 = kt * BN;
-  // buffer BUF^1 was last read in tile kt-1, before that tile's barrier
-  if (kt + 1 < n_kt) tile.issue(K, V, Ks[BUF ^ 1], Vs[BUF ^ 1], k0 + BN, n_s, w);
-  if (wave_on && k0 <= wave_last)
-    attn_tile_dma<D, BN>(Ks[BUF], Vs[BUF], st, c, k0, row, h, k0 + BN - 1 > q0 + 32 * w);
-  if (kt + 1 < n_kt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA loads of tile kt+1 have landed
+// The retrieval's operands, loaded during the workgroup's last key tile into
+// the two LDS buffers that tile no longer needs: M^T (d x d, element type)
+// rows 0..63 into Ma and rows 64..127 (d = 128) into Mb, with the K tile
+// layout, so the epilogue reads its A operand as it reads K; z (d floats)
+// into Zs by one 16-byte load per lane of wave 0 (lanes past d/4 read
+// outside the resource, which returns zeros).
+template <int D, int NW, int BN>
+__device__ __forceinline__ void dma_snapshot(const DmaTile<D, NW, BN>& tile, const bf16* Mts,
+                                             const float* zs, bf16* Ma, bf16* Mb, float* Zs,
+                                             int w) {
+  static_assert(BN == 64 && D % 64 == 0, "M^T is loaded as d / 64 key tiles");
+  tile.template issue<true>(Mts, Ma, 0, 64, w);
+  if constexpr (D == 128) tile.template issue<true>(Mts + 64 * D, Mb, 0, 64, w);
+  if (w == 0) {
+    const __amdgpu_buffer_rsrc_t rz = raw_rsrc(reinterpret_cast<const bf16*>(zs), D * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)Zs, 16, (threadIdx.x & 63) * 16, 0, 0, 0);
+  }
+}
+
+// Iteration j of the key loop on LDS buffer parity P = j % 2 (a constant, so
+// every LDS address is a lane offset plus an immediate). On entry K(j + 1) is
+// in Ks[P ^ 1] and V(j) in Vs[P]; sacc holds the exp2 arguments of tile j.
+// The iteration loads K(j + 2) over K(j) and V(j + 1) over V(j - 1), both
+// last read before the previous barrier, and waits for them at its end.
+// FULL: the caller knows that tile j + 1 is this wave's too and below its
+// diagonal (every iteration but a workgroup's last few), so the iteration is
+// one straight-line block apart from the rare rescale.
+template <int D, int NW, int BN, int P, bool FULL>
+__device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile<D, NW, BN>& tile,
+                                         const bf16* K, const bf16* V, bf16 (*Ks)[BN * D],
+                                         bf16 (*Vs)[BN * D], int n_s, int w, int q0,
+                                         DmaLane<D>& st, f32x16* sacc, float c, int row, int h,
+                                         const bf16* Mts, const float* zs, float* Zs) {
+  constexpr int NKB = BN / 32, NPC = BN / 16;
+  if (j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
+  if (j + 1 < n_kt) tile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+  if (!FULL && j + 1 == n_kt) dma_snapshot<D, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
+  if (FULL || j + 1 < n_w) {
+    bf16x8 pf[NPC];
+    dma_probs<D, BN>(sacc, st, c, pf);
+    f32x16 snext[NKB];
+    dma_scores<D, BN>(Ks[P ^ 1], st, snext);
+    dma_values<D, BN>(Vs[P], st, pf);
+    const int k1 = (j + 1) * BN;
+    dma_max<D, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + 32 * w);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = snext[kb];
+  } else if (!FULL && j < n_w) {  // this wave's last tile
+    bf16x8 pf[NPC];
+    dma_probs<D, BN>(sacc, st, c, pf);
+    dma_values<D, BN>(Vs[P], st, pf);
+  }
+  if (j + 1 < n_kt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j + 2), V(j + 1) have landed
     __syncthreads();
   }
 }
@@ -554,6 +609,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   constexpr int NC = D / 16, NDB = D / 32;
   __shared__ __align__(1024) bf16 Ks[2][BN * D];
   __shared__ __align__(1024) bf16 Vs[2][BN * D];
+  __shared__ __align__(16) float Zs[256];  // z of the segment (one 16-byte DMA per lane of wave 0)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -593,7 +649,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
 
   DmaTile<D, NW, BN> tile;
   tile.init(w, lane);
-  tile.issue(K, V, Ks[0], Vs[0], 0, n_s, w);
+  tile.template issue<true>(K, Ks[0], 0, n_s, w);
+  tile.template issue<false>(V, Vs[0], 0, n_s, w);
+  if (n_kt > 1) tile.template issue<true>(K, Ks[1], BN, n_s, w);
 
   DmaLane<D> st;
   st.init_offsets(lane);
@@ -607,22 +665,49 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   st.m_run = -INFINITY;
   st.l0 = st.l1 = 0.f;
 
+  // key tiles this wave computes (its last is the one holding its last row)
+  const int n_w = wave_on ? wave_last / BN + 1 : 0;
+  constexpr int NKB = BN / 32;
+  f32x16 sacc[NKB];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    attn_step<D, NW, BN, 0>(kt, n_kt, tile, K, V, Ks, Vs, n_s, w, wave_on, wave_last, q0, st, c,
-                            row, h);
-    if (kt + 1 < n_kt)
-      attn_step<D, NW, BN, 1>(kt + 1, n_kt, tile, K, V, Ks, Vs, n_s, w, wave_on, wave_last, q0,
-                              st, c, row, h);
+  if (n_w > 0) {
+    dma_scores<D, BN>(Ks[0], st, sacc);
+    dma_max<D, BN>(sacc, st, c, 0, row, h, BN - 1 > q0 + 32 * w);
   }
-  if (!wave_on) return;
-
-  float l = st.l0 + st.l1;
-  l += __shfl_xor(l, 32);
+  __syncthreads();  // K(0) read by every wave before iteration 0 loads K(2) over it
+  // Wave 0 has the fewest tiles and the first diagonal one; when every wave
+  // has rows, iterations j with tile j + 1 before wave 0's last tile are full
+  // for all of them.
+  const int n_full = q0 + BM <= n_s ? q0 / BN - 1 : 0;
   const int64_t snap = (int64_t)unit * a.s_count + sl;
   const float* zs = a.snapZ + snap * D;
   const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * D * D;
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    dma_iter<D, NW, BN, 0, true>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row, h,
+                                 Mts, zs, Zs);
+    dma_iter<D, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+                                 h, Mts, zs, Zs);
+  }
+  for (; j < n_kt; ++j) {
+    if ((j & 1) == 0)
+      dma_iter<D, NW, BN, 0, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+                                    h, Mts, zs, Zs);
+    else
+      dma_iter<D, NW, BN, 1, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+                                    h, Mts, zs, Zs);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's part of M^T and z has landed
+  __syncthreads();
+  if (!wave_on) return;
+
+  // M^T sits in the buffers the last tile (parity (n_kt - 1) % 2) freed
+  const bool pl = ((n_kt - 1) & 1) != 0;
+  const bf16* Ma = pl ? Ks[1] : Ks[0];
+  const bf16* Mb = pl ? Vs[0] : Vs[1];
+  float l = st.l0 + st.l1;
+  l += __shfl_xor(l, 32);
   float sq[NC][8];
   float dp = 0.f;
 #pragma unroll
@@ -631,7 +716,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
     for (int e = 0; e < 8; ++e) {
       const float s = feature_map((float)st.qf[cc][e]);
       sq[cc][e] = s;
-      dp += s * zs[16 * cc + 8 * h + e];
+      dp += s * Zs[16 * cc + 8 * h + e];
     }
   const float den = dp + __shfl_xor(dp, 32);
   const float g = 1.f / (1.f + __expf(-a.beta[hq]));
@@ -649,7 +734,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      mma32(st.oacc[db], load8<bf16>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
+      mma32(st.oacc[db],
+            load8<bf16>(lds_at(db >= 2 ? Mb : Ma, (st.ko ^ (32u * cc)) + 2 * 32 * (db & 1) * D)),
+            sf[cc]);
   if (row < n_s) {
     bf16* orow = O + (int64_t)row * D;
 #pragma unroll
