@@ -23,6 +23,7 @@
 // V - prediction, which would lose the prediction.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace infini {
 
@@ -43,7 +44,18 @@ __global__ __launch_bounds__(256) void colsum_kernel(AffineArgs a) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int t = tl; t < n_s; t += TL) {
+  // four rows per step, loaded before any is used, so four loads are in flight
+  int t = tl;
+  for (; t + 3 * TL < n_s; t += 4 * TL) {
+    frag_t<T> kv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kv[u] = load8<T>(K + (int64_t)(t + u * TL) * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += feature_map(to_f32<T>(kv[u][e]));
+  }
+  for (; t < n_s; t += TL) {
     const frag_t<T> kv = load8<T>(K + (int64_t)t * D);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += feature_map(to_f32<T>(kv[e]));
@@ -79,7 +91,7 @@ struct AffineShape {
   static constexpr int RT = D / 32;                                // row tiles (key dim)
   static constexpr int CT = (RULE == kRuleDelta ? 2 : 1) * (D / 32);  // column tiles
   static constexpr int NTILE = RT * CT;
-  static constexpr int NW = NTILE < 4 ? NTILE : 4;
+  static constexpr int NW = NTILE < 8 ? NTILE : 8;
   static constexpr int TPW = NTILE / NW;  // tiles per wave
   static_assert(NTILE % NW == 0, "tile split");
 };
@@ -112,9 +124,12 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 #pragma unroll
   for (int j = 0; j < TPW; ++j) acc[j] = zero16();
 
-  // registers of the next chunk's staging items
-  frag_t<T> kr[IPT][4], vr[IPT][4];
-  auto load_chunk = [&](int t0) {
+  // registers of the staging items of the current chunk (kr, vr) and of the
+  // next ones (kr1/vr1, kr2/vr2): with 2-byte elements two chunks of loads are
+  // in flight while one is staged and multiplied (float elements: one)
+  constexpr bool DEEP = sizeof(T) == 2;
+  frag_t<T> kr[IPT][4], vr[IPT][4], kr1[IPT][4], vr1[IPT][4], kr2[IPT][4], vr2[IPT][4];
+  auto load_chunk = [&](int t0, frag_t<T> (&kx)[IPT][4], frag_t<T> (&vx)[IPT][4]) {
 #pragma unroll
     for (int it = 0; it < IPT; ++it) {
       const int item = tid + it * NT;
@@ -122,11 +137,11 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = t0 + 4 * tq + q;
-        kr[it][q] = zero_frag<T>();
-        vr[it][q] = zero_frag<T>();
+        kx[it][q] = zero_frag<T>();
+        vx[it][q] = zero_frag<T>();
         if (item < ITEMS && t < n_s) {
-          kr[it][q] = load8<T>(K + (int64_t)t * D + 8 * cg);
-          vr[it][q] = load8<T>(V + (int64_t)t * D + 8 * cg);
+          kx[it][q] = load8<T>(K + (int64_t)t * D + 8 * cg);
+          vx[it][q] = load8<T>(V + (int64_t)t * D + 8 * cg);
         }
       }
     }
@@ -139,7 +154,8 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
     for (int e = 0; e < 8; ++e) zc[it][e] = z[8 * cg + e];
   }
 
-  load_chunk(0);
+  load_chunk(0, kr, vr);
+  if (DEEP) load_chunk(TC, kr1, vr1);  // rows past n_s are not loaded (zeros)
   for (int t0 = 0; t0 < n_s; t0 += TC) {
     // stage the chunk: sigma, den, transposed stores
 #pragma unroll
@@ -157,12 +173,14 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
           dp[q] += ph[q][e] * zc[it][e];
         }
       }
+      float rd[4];  // 1 / den_t
       if constexpr (DELTA) {
         // den_t: sum over the CG lanes that hold token t's columns
 #pragma unroll
-        for (int m = 1; m < CG; m <<= 1)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dp[q] += __shfl_xor(dp[q], m);
+        for (int q = 0; q < 4; ++q) {
+          dp[q] = row_sum<CG>(dp[q]);
+          rd[q] = 1.f / dp[q];
+        }
       }
       if (item < ITEMS) {
 #pragma unroll
@@ -180,7 +198,7 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const bool ok = t0 + 4 * tq + q < n_s;
-              d4[q] = from_f32<T>(ok ? ph[q][e] / dp[q] : 0.f);
+              d4[q] = from_f32<T>(ok ? ph[q][e] * rd[q] : 0.f);
             }
             store4<T>(DPhiT + (8 * cg + e) * TS + 4 * tq, d4);
           }
@@ -188,7 +206,11 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
       }
     }
     __syncthreads();
-    if (t0 + TC < n_s) load_chunk(t0 + TC);  // in flight during the products
+    if (DEEP) {
+      if (t0 + 2 * TC < n_s) load_chunk(t0 + 2 * TC, kr2, vr2);  // in flight for two chunks
+    } else {
+      if (t0 + TC < n_s) load_chunk(t0 + TC, kr1, vr1);  // in flight during the products
+    }
 
 #pragma unroll
     for (int kc = 0; kc < TC / 16; ++kc) {
@@ -204,6 +226,17 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IPT; ++it)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kr[it][q] = kr1[it][q];
+        vr[it][q] = vr1[it][q];
+        if (DEEP) {
+          kr1[it][q] = kr2[it][q];
+          vr1[it][q] = vr2[it][q];
+        }
+      }
   }
 
   const int64_t base = ((int64_t)unit * a.s_count + sl) * D * D;
@@ -220,6 +253,157 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
         a.Bmat[base + (int64_t)row * D + 32 * (ct - (DELTA ? RT : 0)) + i] = acc[j][r];
     }
   }
+}
+
+// ---- 3'. the same products for bf16, d = 128, from DMA-fed LDS tiles ---------
+//
+// Chunks of 64 tokens of K and V stream into a 3-deep LDS ring (K in the "K"
+// layout, V in the "V" layout, lds_tile.hpp). All 512 threads then stage the
+// chunk in place, row major: 8 threads per token, 16 columns each, form
+// sigma(K) and its dot with z (the 8 partial dots summed by DPP), and write
+// Phi and Phi / den in the "V" layout. The products read every operand with
+// transposing LDS reads (the token index is the k index): wave w owns the
+// 2 x 2 (delta) or 2 x 1 (linear) block of 32 x 32 output tiles at row tiles
+// 2 (w / 4), + 1 and column tiles 2 (w % 4), + 1 of [Phi/den | V] (delta), or
+// column tile w % 4 of V (linear).
+template <int RULE>
+__global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
+  constexpr int D = 128, NW = 8, TC = 64, NBUF = 3;
+  constexpr bool DELTA = RULE == kRuleDelta;
+  constexpr int BC = DELTA ? 2 : 1;  // column tiles per wave (row tiles: 2)
+  using Tile = DmaTile<D, NW, TC>;
+  __shared__ __align__(1024) bf16 Kr[NBUF][TC * D];
+  __shared__ __align__(1024) bf16 Vr[NBUF][TC * D];
+  __shared__ __align__(1024) bf16 Ph[TC * D];
+  __shared__ __align__(1024) bf16 DPh[DELTA ? TC * D : 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  const int n_c = (n_s + TC - 1) / TC;
+
+  // staging role (z loaded before the DMA, so the vmcnt waits below count
+  // DMA loads only): token st_t of the chunk, columns 16 st_g .. + 15
+  const int st_t = tid >> 3, st_g = tid & 7;
+  float zc[16];
+  {
+    const float* z = a.snapZ + ((int64_t)unit * a.s_count + sl) * D + 16 * st_g;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) zc[e] = z[e];
+  }
+  Tile tile;
+  tile.init(w, lane);
+  tile.template issue<true>(K, Kr[0], 0, n_s, w);
+  tile.template issue<false>(V, Vr[0], 0, n_s, w);
+  if (n_c > 1) {
+    tile.template issue<true>(K, Kr[1], TC, n_s, w);
+    tile.template issue<false>(V, Vr[1], TC, n_s, w);
+  }
+
+  // product role: row tiles rt0, rt0 + 1; column tiles BC cq + c
+  const int rt0 = 2 * (w >> 2), cq = w & 3;
+  uint32_t ao[2], bo[BC];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ao[r] = tr_offset<D>(lane, rt0 + r);
+#pragma unroll
+  for (int c = 0; c < BC; ++c) bo[c] = tr_offset<D>(lane, (BC * cq + c) & 3);
+  f32x16 acc[2][BC];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < BC; ++c) acc[r][c] = zero16();
+
+  for (int ch = 0; ch < n_c; ++ch) {
+    const int buf = ch % NBUF;
+    // this wave's loads of chunk ch have landed (the 2 PER_WAVE of chunk
+    // ch + 1, issued later, may still be in flight)
+    if (ch + 1 < n_c)
+      wait_vmcnt<2 * Tile::PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // chunk ch complete everywhere; chunk ch - 1's products done
+    if (ch + 2 < n_c) {  // into the buffer chunk ch - 1 used
+      tile.template issue<true>(K, Kr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+      tile.template issue<false>(V, Vr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+    }
+    // stage Phi and Phi / den of token st_t (zero past the segment's end)
+    {
+      const bool ok = ch * TC + st_t < n_s;
+      const bf16* krow = Kr[buf] + st_t * D;
+      float ph[16];
+      float dp = 0.f;
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const bf16x8 kv = load8<bf16>(krow + 8 * ((2 * st_g + hc) ^ swz_k<D>(st_t)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = ok ? feature_map((float)kv[e]) : 0.f;
+          ph[8 * hc + e] = f;
+          dp += f * zc[8 * hc + e];
+        }
+      }
+      bf16* prow = Ph + st_t * D;
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        bf16x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)ph[8 * hc + e];
+        store8<bf16>(prow + 8 * ((2 * st_g + hc) ^ swz_v<D>(st_t)), y);
+      }
+      if constexpr (DELTA) {
+        const float den = row_sum<8>(dp);
+        const float rd = ok ? 1.f / den : 0.f;
+        bf16* drow = DPh + st_t * D;
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+          bf16x8 y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (bf16)(ph[8 * hc + e] * rd);
+          store8<bf16>(drow + 8 * ((2 * st_g + hc) ^ swz_v<D>(st_t)), y);
+        }
+      }
+    }
+    __syncthreads();
+    // products over the chunk's 4 k chunks of 16 tokens
+#pragma unroll
+    for (int p = 0; p < TC / 16; ++p) {
+      bf16x8 af[2], bf[BC];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) af[r] = tr_frag<D>(Ph, ao[r], p);
+#pragma unroll
+      for (int c = 0; c < BC; ++c) {
+        const bool of_v = !DELTA || BC * cq + c >= 4;
+        bf[c] = tr_frag<D>(of_v ? Vr[buf] : DPh, bo[c], p);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < BC; ++c) mma32(acc[r][c], af[r], bf[c]);
+    }
+  }
+
+  const int i = lane & 31, h = lane >> 5;
+  const int64_t base = ((int64_t)unit * a.s_count + sl) * D * D;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < BC; ++c) {
+      const int ct = BC * cq + c;  // of [Phi/den | V] (delta) or of V (linear)
+      const bool is_a = DELTA && ct < 4;
+      const int col = 32 * (ct & 3) + i;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = 32 * (rt0 + r) + acc_row(q, h);
+        if (is_a)
+          static_cast<bf16*>(a.Amat)[base + (int64_t)row * D + col] = (bf16)(-acc[r][c][q]);
+        else
+          a.Bmat[base + (int64_t)row * D + col] = acc[r][c][q];
+      }
+    }
 }
 
 // ---- 4. M_s = M_{s-1} + B_s + A_s M_{s-1}, per 32-column slab ---------------
@@ -286,8 +470,11 @@ hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
   const unsigned segs = (unsigned)(a.units * a.s_count);
   hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
   hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
-  hipLaunchKernelGGL((affine_kernel<T, D, RULE>), dim3(segs), dim3(AffineShape<D, RULE>::NW * 64),
-                     0, stream, a);
+  if constexpr (sizeof(T) == 2 && D == 128)
+    hipLaunchKernelGGL((affine_dma_kernel<RULE>), dim3(segs), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((affine_kernel<T, D, RULE>), dim3(segs),
+                       dim3(AffineShape<D, RULE>::NW * 64), 0, stream, a);
   hipLaunchKernelGGL((chain_kernel<T, D, RULE>), dim3((unsigned)(a.units * (D / 32))),
                      dim3(D / 32 * 64), 0, stream, a);
   return hipGetLastError();

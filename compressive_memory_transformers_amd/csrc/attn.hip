@@ -23,6 +23,7 @@
 // per-query factor g/den folded into the B operand.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace infini {
 
@@ -321,107 +322,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
 
 // ---- bf16, d in {64, 128}: tiles streamed straight into LDS ------------------
 //
-// K and V tiles go from global memory into LDS with gfx950's LDS-DMA loads
-// (global_load_lds, 16 bytes per lane: lane l of one instruction fills bytes
-// [16l, 16l + 16) of a 1 KB block), so no registers or VALU are spent staging
-// them. Both tiles stay row major, [key][dim], with 16-byte chunks XOR-swizzled
-// within a row instead of padded:
-//   K: chunk c of row r sits at c ^ swk(r), so the 16 rows that a quarter-wave
-//      reads for one MFMA A operand (same logical chunk) hit 16 bank groups;
-//   V: chunk c of row r sits at c ^ swv(r); the A operand of O^T += V^T P^T
-//      (rows of V^T = columns of V) is read with ds_read_b64_tr_b16, which
-//      hands lane j of a 16-lane group element (j % 4) of the 8-byte loads of
-//      lanes 4e + j/4, e = 0..3. If lane 4a + b of the group loads columns
-//      [4b, 4b + 4) of row key0 + a, lane j receives V[key0 + e][j], e = 0..3:
-//      four consecutive keys of one value column, as the fragment needs. The
-//      swizzle spreads the 4 rows x 4 chunks a half-wave reads over the banks.
-
-template <int D> __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D> __device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ const bf16* lds_at(const bf16* base, uint32_t byte_off) {
-  return reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(base) + byte_off);
-}
-
-// Buffer resource over `bytes` bytes from `base` (raw, no stride; dword 3 as
-// gfx9 wants it for untyped loads). Loads through it take the base from
-// scalar registers and a 32-bit per-lane offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)bytes, 0x00020000);
-}
-
-template <int D, int NW, int BN>
-struct DmaTile {
-  static constexpr int NT = NW * 64;
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int CHUNKS = BN * CPR;            // per tile, per tensor
-  static constexpr int PER_WAVE = CHUNKS / 64 / NW;  // DMA instructions per wave and tensor
-  static_assert(CHUNKS % (64 * NW) == 0, "tile split");
-  // Instruction j of wave w fills tile rows from (j NW + w) 64 / CPR on. When
-  // the swizzles of those rows do not depend on j (NW a multiple of 4 for
-  // d = 128, even for d = 64), instruction j's lane offsets are instruction
-  // 0's plus J_STEP j bytes, which the load takes as a scalar offset.
-  static constexpr bool J_INV = D == 128 ? NW % 4 == 0 : NW % 2 == 0;
-  static constexpr uint32_t J_STEP = NW * (64 / CPR) * 2 * D;
-  static constexpr int NOFF = J_INV ? 1 : PER_WAVE;
-  // per lane: byte offset, from the tile's first row, of the 16-byte chunk
-  // it fetches (the same tile row for K and V)
-  uint32_t k_off[NOFF], v_off[NOFF];
-
-  __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int j = 0; j < NOFF; ++j) {
-      const int p = (j * NW + w) * 64 + lane;  // physical chunk of the tile
-      const int r = p / CPR, phys = p % CPR;
-      k_off[j] = 2 * (r * D + 8 * (phys ^ swz_k<D>(r)));
-      v_off[j] = 2 * (r * D + 8 * (phys ^ swz_v<D>(r)));
-    }
-  }
-  // Issue the loads of key tile k0 of one tensor (K if IS_K, else V) into
-  // Xs ([BN][D]); w is the (wave-uniform) wave index. Each load is a
-  // buffer_load ... lds of 16 bytes per lane from a resource over the tile's
-  // rows. In a tail tile, rows past the segment's end repeat its last row
-  // (finite; the causal mask removes them).
-  template <bool IS_K>
-  __device__ __forceinline__ void issue(const bf16* X, bf16* Xs, int k0, int n_s, int w) const {
-    const uint32_t* off = IS_K ? k_off : v_off;
-    const int rows = min(BN, n_s - k0);
-    const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + (int64_t)k0 * D, (uint32_t)rows * D * 2);
-    if (rows == BN) {
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int blk = (j * NW + w) * 64 * 8;  // element offset of this wave's 1 KB block
-        const uint32_t sj = J_INV ? j * J_STEP : 0;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, off[J_INV ? 0 : j], sj, 0, 0);
-      }
-    } else {
-      const uint32_t lim = (uint32_t)rows * (2 * D);  // bytes of the valid rows
-      const uint32_t last = lim - 2 * D;              // start of the last valid row
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int blk = (j * NW + w) * 64 * 8;
-        const uint32_t xj = J_INV ? off[0] + j * J_STEP : off[j];
-        const uint32_t xo = xj < lim ? xj : last + (xj & (2 * D - 1));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, xo, 0, 0, 0);
-      }
-    }
-  }
-};
+// K and V tiles go from global memory into LDS by DMA (DmaTile, lds_tile.hpp),
+// row major with XOR-swizzled 16-byte chunks; K is read as the A operand of
+// S^T = K Q^T with 16-byte reads, V as the A operand of O^T += V^T P^T with
+// transposing reads.
 
 // Per-lane state of the key loop, with the lane's LDS read offsets computed
 // once: with the swizzles above, a lane's K and V read addresses differ
@@ -439,16 +343,8 @@ struct DmaLane {
   __device__ __forceinline__ void init_offsets(int lane) {
     const int i = lane & 31, h = lane >> 5;
     ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
-    // lane 16G + 4a + b reads rows 16pc + 8s + 4h + a, columns
-    // 32db + 16(G % 2) + 4b .. + 3 (see the V swizzle); the row's swizzle
-    // depends on a only, so pc and s are constant offsets
-    const int G = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
-    const int r0 = 4 * h + a;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int col = 32 * db + 16 * (G & 1) + 4 * b;
-      vo[db] = 2 * (r0 * D + 8 * ((col >> 3) ^ swz_v<D>(r0)) + (col & 7));
-    }
+    for (int db = 0; db < NDB; ++db) vo[db] = tr_offset<D>(lane, db);
   }
 };
 
@@ -538,11 +434,7 @@ __device__ __forceinline__ void dma_values(const bf16* Vb, DmaLane<D>& st, const
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int pc = 0; pc < NPC; ++pc) {
-      const bf16x4 lo = lds_read_tr(lds_at(Vb, st.vo[db] + 2 * 16 * pc * D));
-      const bf16x4 hi = lds_read_tr(lds_at(Vb, st.vo[db] + 2 * (16 * pc + 8) * D));
-      mma32(st.oacc[db], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[pc]);
-    }
+    for (int pc = 0; pc < NPC; ++pc) mma32(st.oacc[db], tr_frag<D>(Vb, st.vo[db], pc), pf[pc]);
 }
 
 // The retrieval's operands, loaded during the workgroup's last key tile into
