@@ -481,7 +481,7 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile
     dma_scores<D, BN>(Ks[P ^ 1], st, snext);
     dma_values<D, BN>(Vs[P], st, pf);
     const int k1 = (j + 1) * BN;
-    dma_max<D, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + 32 * w);
+    dma_max<D, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + w);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = snext[kb];
   } else if (!FULL && j < n_w) {  // this wave's last tile
@@ -532,9 +532,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
   bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * D;
 
-  const int row = q0 + 32 * w + i;
-  const bool wave_on = q0 + 32 * w < n_s;
-  const int wave_last = min(q0 + 32 * w + 31, n_s - 1);
+  // Rows are dealt to the waves round robin (row q0 + w + NW i for lane i),
+  // so every wave spans the whole block and meets the causal diagonal in the
+  // same key tiles: the waves run the same number of iterations and none
+  // idles at the barriers of the block's last tiles.
+  const int row = q0 + w + NW * i;  // this lane's query, relative to the segment
+  const int wave_first = q0 + w;
+  const bool wave_on = wave_first < n_s;
+  const int wave_last = wave_on ? wave_first + NW * min(31, (n_s - 1 - wave_first) / NW) : -1;
   const float c = a.scale_log2;
   const int n_kv = min(q0 + BM, n_s);
   const int n_kt = (n_kv + BN - 1) / BN;
@@ -565,12 +570,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   __syncthreads();
   if (n_w > 0) {
     dma_scores<D, BN>(Ks[0], st, sacc);
-    dma_max<D, BN>(sacc, st, c, 0, row, h, BN - 1 > q0 + 32 * w);
+    dma_max<D, BN>(sacc, st, c, 0, row, h, BN - 1 > wave_first);
   }
   __syncthreads();  // K(0) read by every wave before iteration 0 loads K(2) over it
-  // Wave 0 has the fewest tiles and the first diagonal one; when every wave
-  // has rows, iterations j with tile j + 1 before wave 0's last tile are full
-  // for all of them.
+  // When every row of the block is in the segment, iterations j whose next
+  // tile j + 1 lies wholly below the block's first row are full for every
+  // wave.
   const int n_full = q0 + BM <= n_s ? q0 / BN - 1 : 0;
   const int64_t snap = (int64_t)unit * a.s_count + sl;
   const float* zs = a.snapZ + snap * D;
