@@ -30,7 +30,9 @@ METRIC = "Infini-attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc", "attn.hip")
+# the sources that decide the attention kernel's memory traffic
+ATTN_SOURCES = [os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc", f)
+                for f in ("attn.hip", "lds_tile.hpp")]
 
 
 def attn_kernel_bytes(w):
@@ -53,9 +55,12 @@ def attn_kernel_flops(w):
     return w.B * w.Hq * total
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
@@ -66,7 +71,7 @@ def measured_traffic(workload):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCE):
+    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 

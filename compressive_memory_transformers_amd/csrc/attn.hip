@@ -527,6 +527,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   if (q0 >= n_s) return;
 
   const int64_t qh = (int64_t)b * a.Hq + hq;
+  const float g = 1.f / (1.f + __expf(-a.beta[hq]));  // the gate, read early
   const bf16* Q = static_cast<const bf16*>(a.q) + (qh * a.L + seg_start) * D;
   const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
   const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
@@ -587,13 +588,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
     dma_iter<D, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
                                  h, Mts, zs, Zs);
   }
-  for (; j < n_kt; ++j) {
-    if ((j & 1) == 0)
-      dma_iter<D, NW, BN, 0, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
-                                    h, Mts, zs, Zs);
-    else
-      dma_iter<D, NW, BN, 1, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
-                                    h, Mts, zs, Zs);
+  for (; j < n_kt; j += 2) {  // j is even here
+    dma_iter<D, NW, BN, 0, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+                                  h, Mts, zs, Zs);
+    if (j + 1 < n_kt)
+      dma_iter<D, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c,
+                                    row, h, Mts, zs, Zs);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's part of M^T and z has landed
   __syncthreads();
@@ -616,7 +616,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
       dp += s * Zs[16 * cc + 8 * h + e];
     }
   const float den = dp + __shfl_xor(dp, 32);
-  const float g = 1.f / (1.f + __expf(-a.beta[hq]));
   const float ca = (1.f - g) / l, cm = g / den;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
