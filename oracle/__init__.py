@@ -40,6 +40,10 @@ Pins (each function is checked against something other than itself in
 * ``forward``           -- single-segment reduction to causal attention,
   gate extremes, chunked calls with a carried state, GQA equal to MHA on
   repeated K/V, batch/head permutation.
+* ``decode_step``       -- token-by-token decoding of a stream equals
+  ``forward`` on it (every output row, and the state at every segment end);
+  the first token of a segment attends to itself alone (closed form); the
+  state is unchanged inside a segment.
 
 No function here is "parity unpinned".
 """
@@ -53,5 +57,6 @@ from .infini_attention import (  # noqa: F401
     memory_update,
     num_segments,
     forward,
+    decode_step,
 )
 from .compare import max_rel_err, slice_errors  # noqa: F401

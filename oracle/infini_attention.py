@@ -176,3 +176,58 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, units=None, out_segments=None)
         M_final[b, j] = M
         z_final[b, j] = z
     return out, M_final, z_final
+
+
+def decode_step(q, k, v, beta, M, z, k_cache, v_cache, pos, seg_len, rule):
+    """One streaming step: the token at position ``pos`` (0-based) of its segment.
+
+    q: [B, Hq, d_key]; k: [B, Hkv, d_key]; v: [B, Hkv, d_value] for the new
+    token. M: [B, Hkv, d_key, d_value], z: [B, Hkv, d_key]: the state before
+    the token's segment. k_cache / v_cache: [B, Hkv, seg_len, d]: rows
+    0 .. pos-1 hold the segment's earlier tokens. Returns
+    (out [B, Hq, d_value], M', z', k_cache', v_cache'), all float64 copies.
+
+    The token's key and value join the cache at row ``pos``; its query attends
+    causally to rows 0 .. pos of the segment, reads the memory of the previous
+    segments, and the two are gated, exactly as row ``pos`` of the segment in
+    ``forward``. When the segment is full (pos == seg_len - 1) it is folded
+    into (M, z) with ``memory_update`` and M', z' are the state after it;
+    otherwise M', z' equal M, z.
+
+    "Infini-Attention" (AI Wiki), "Why is the memory footprint bounded?": a
+    stream is processed segment by segment with only (M, z) carried, so the
+    work per token does not grow with the stream; "What happens inside the
+    Infini-attention block?" for the per-token arithmetic.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    M = np.array(M, dtype=np.float64)
+    z = np.array(z, dtype=np.float64)
+    k_cache = np.array(k_cache, dtype=np.float64)
+    v_cache = np.array(v_cache, dtype=np.float64)
+    B, Hq, d_key = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if not 0 <= pos < seg_len or k_cache.shape[2] != seg_len:
+        raise ValueError("pos must lie in [0, seg_len) and the cache hold seg_len rows")
+    group = Hq // Hkv
+    out = np.empty((B, Hq, v.shape[2]))
+    for b in range(B):
+        for j in range(Hkv):
+            k_cache[b, j, pos] = k[b, j]
+            v_cache[b, j, pos] = v[b, j]
+            keys, values = k_cache[b, j, :pos + 1], v_cache[b, j, :pos + 1]
+            for h in range(j * group, (j + 1) * group):
+                scores = keys @ q[b, h] / math.sqrt(d_key)
+                weights = np.exp(scores - scores.max())
+                a_dot = weights @ values / weights.sum()
+                a_mem = memory_retrieval(q[b, h][None, :], M[b, j], z[b, j])[0]
+                g = gate_weight(beta[h])
+                out[b, h] = g * a_mem + (1.0 - g) * a_dot
+            if pos == seg_len - 1:
+                M[b, j], z[b, j] = memory_update(k_cache[b, j], v_cache[b, j], M[b, j], z[b, j],
+                                                 rule)
+    return out, M, z, k_cache, v_cache
