@@ -9,6 +9,8 @@ from .binding import (  # noqa: F401
     DTYPES,
     RULES,
     InfiniAttnError,
+    decode_step,
+    decode_workspace_size,
     forward,
     load_library,
     status_string,

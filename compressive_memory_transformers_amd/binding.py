@@ -31,6 +31,10 @@ SIGNATURES = {
     "infini_attn_forward_timed": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
+    "infini_attn_decode_workspace_size": (
+        _c_i32, [_c_i64] * 5 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_decode_step": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
     "infini_attn_status_string": (ctypes.c_char_p, [_c_i32]),
     "infini_attn_version": (_c_i32, []),
 }
@@ -154,3 +158,67 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     if st != 0:
         raise InfiniAttnError(st, name)
     return out, M_final, z_final
+
+
+def decode_workspace_size(B, Hq, Hkv, d, seg_len, rule, dtype):
+    """Workspace bytes of a decode step with these sizes."""
+    lib = load_library()
+    n = _c_size(0)
+    st = lib.infini_attn_decode_workspace_size(B, Hq, Hkv, d, seg_len, RULES[rule], DTYPES[dtype],
+                                               ctypes.byref(n))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_decode_workspace_size")
+    return int(n.value)
+
+
+def decode_step(q, k, v, beta, k_cache, v_cache, M, z, pos, rule, *, out=None, workspace=None,
+                stream=None):
+    """One streaming decode step on the GPU (infini_attn_decode_step).
+
+    q [B,Hq,d], k and v [B,Hkv,d] (float32 or bfloat16) for the token at
+    position ``pos`` of its segment; k_cache, v_cache [B,Hkv,seg_len,d] of the
+    same dtype; M [B,Hkv,d,d] and z [B,Hkv,d] float32, the state before the
+    segment. Writes the token into the caches and, when pos == seg_len - 1,
+    folds the segment into M and z in place. Returns out [B,Hq,d].
+    Asynchronous on ``stream`` (or torch's current stream).
+    """
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    seg_len = k_cache.shape[2]
+    if k.shape != (B, Hkv, d) or v.shape != (B, Hkv, d):
+        raise ValueError("k and v must be [B,Hkv,d]")
+    if k_cache.shape != (B, Hkv, seg_len, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [B,Hkv,seg_len,d]")
+    if beta.shape != (Hq,) or M.shape != (B, Hkv, d, d) or z.shape != (B, Hkv, d):
+        raise ValueError("beta, M or z has the wrong shape")
+    if q.dtype not in DTYPES or any(t.dtype != q.dtype for t in (k, v, k_cache, v_cache)):
+        raise TypeError("q, k, v and the caches must share one dtype, float32 or bfloat16")
+    if beta.dtype != torch.float32 or M.dtype != torch.float32 or z.dtype != torch.float32:
+        raise TypeError("beta, M and z must be float32")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    for t in (q, k, v, beta, k_cache, v_cache, M, z):
+        if t.device != dev:
+            raise ValueError("all tensors must be on one GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(B, Hq, Hkv, d, seg_len, rule, q.dtype),
+                                dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = load_library().infini_attn_decode_step(
+        B, Hq, Hkv, d, seg_len, int(pos), RULES[rule], DTYPES[q.dtype],
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_cache), _ptr(v_cache), _ptr(M), _ptr(z),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_decode_step")
+    return out

@@ -105,6 +105,89 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace regions of a window of W segments: state A, state B (each (M, z)),
+// then the window's snapshots and, for the affine form, its column sums and
+// per-segment matrices.
+struct Carved {
+  float* stM[2];
+  float* stz[2];
+  void* snapM;
+  float* snapZ;
+  float* colsum;
+  float* Bmat;
+  void* Amat;
+};
+
+Carved carve(const Plan& p, int64_t W, int32_t rule, void* workspace) {
+  Carved c{};
+  char* ws = static_cast<char*>(workspace);
+  const int64_t d = p.d;
+  const size_t mbytes = (size_t)p.units * (size_t)(d * d) * 4;
+  c.stM[0] = reinterpret_cast<float*>(ws);
+  c.stM[1] = reinterpret_cast<float*>(ws + p.state_bytes);
+  c.stz[0] = reinterpret_cast<float*>(ws + mbytes);
+  c.stz[1] = reinterpret_cast<float*>(ws + p.state_bytes + mbytes);
+  char* cur = ws + 2 * p.state_bytes;
+  auto take = [&](size_t bytes) {
+    char* r = cur;
+    cur += align_up(bytes);
+    return r;
+  };
+  const size_t uW = (size_t)p.units * (size_t)W;
+  c.snapM = take(uW * (size_t)(d * d * p.e));
+  c.snapZ = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
+  if (p.affine) {
+    c.colsum = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
+    c.Bmat = reinterpret_cast<float*>(take(uW * (size_t)(d * d) * 4));
+    if (rule == INFINI_RULE_DELTA) c.Amat = take(uW * (size_t)(d * d * p.e));
+  }
+  return c;
+}
+
+// The memory recurrence over segments [s_begin, s_begin + s_count) of k / v
+// ([B*Hkv][L][d]), from (Min, zin) to (Mout, zout), writing the snapshots into
+// the carved regions: the direct scan or the affine form, as the plan says.
+hipError_t launch_recurrence(const Plan& p, const Carved& cw, int32_t rule, int32_t dtype,
+                             const void* k, const void* v, const float* Min, const float* zin,
+                             float* Mout, float* zout, int64_t L, int64_t seg_len,
+                             int64_t s_begin, int64_t s_count, hipStream_t s) {
+  if (p.affine) {
+    AffineArgs fa;
+    fa.k = k;
+    fa.v = v;
+    fa.M_in = Min;
+    fa.z_in = zin;
+    fa.M_out = Mout;
+    fa.z_out = zout;
+    fa.snapM = cw.snapM;
+    fa.snapZ = cw.snapZ;
+    fa.colsum = cw.colsum;
+    fa.Amat = cw.Amat;
+    fa.Bmat = cw.Bmat;
+    fa.L = L;
+    fa.seg_len = seg_len;
+    fa.units = (int32_t)p.units;
+    fa.s_begin = (int32_t)s_begin;
+    fa.s_count = (int32_t)s_count;
+    return infini::launch_affine(dtype, (int)p.d, rule, fa, s);
+  }
+  ScanArgs sa;
+  sa.k = k;
+  sa.v = v;
+  sa.M_in = Min;
+  sa.z_in = zin;
+  sa.M_out = Mout;
+  sa.z_out = zout;
+  sa.snapM = cw.snapM;
+  sa.snapZ = cw.snapZ;
+  sa.L = L;
+  sa.seg_len = seg_len;
+  sa.units = (int32_t)p.units;
+  sa.s_begin = (int32_t)s_begin;
+  sa.s_count = (int32_t)s_count;
+  return infini::launch_scan(dtype, (int)p.d, rule, sa, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,29 +257,14 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   const int64_t tiles_per_seg = B * Hq * n_qt;  // <= INT32_MAX, checked above
   if (W > INT32_MAX / tiles_per_seg) W = INT32_MAX / tiles_per_seg;
 
-  // Workspace: state A, state B, then the snapshots of one window.
-  char* ws = static_cast<char*>(workspace);
-  const size_t mbytes = (size_t)p.units * (size_t)(d * d) * 4;
-  float* stM[2] = {reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + p.state_bytes)};
-  float* stz[2] = {reinterpret_cast<float*>(ws + mbytes),
-                   reinterpret_cast<float*>(ws + p.state_bytes + mbytes)};
-  char* cur = ws + 2 * p.state_bytes;
-  auto carve = [&](size_t bytes) {
-    char* r = cur;
-    cur += align_up(bytes);
-    return r;
-  };
-  const size_t uW = (size_t)p.units * (size_t)W;
-  void* snapM = carve(uW * (size_t)(d * d * p.e));
-  float* snapZ = reinterpret_cast<float*>(carve(uW * (size_t)d * 4));
-  float* colsum = nullptr;
-  float* Bmat = nullptr;
-  void* Amat = nullptr;
-  if (p.affine) {
-    colsum = reinterpret_cast<float*>(carve(uW * (size_t)d * 4));
-    Bmat = reinterpret_cast<float*>(carve(uW * (size_t)(d * d) * 4));
-    if (rule == INFINI_RULE_DELTA) Amat = carve(uW * (size_t)(d * d * p.e));
-  }
+  const Carved cw = carve(p, W, rule, workspace);
+  float* const* stM = cw.stM;
+  float* const* stz = cw.stz;
+  void* snapM = cw.snapM;
+  float* snapZ = cw.snapZ;
+  float* colsum = cw.colsum;
+  float* Bmat = cw.Bmat;
+  void* Amat = cw.Amat;
 
   if (n_events < 0 || (n_events > 0 && events == nullptr)) return INFINI_ERR_INVALID_ARG;
   for (int32_t e = 0; e < n_events; ++e)
@@ -227,42 +295,9 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     float* zout = last ? z_final : stz[wi & 1];
 
     if (!mark(wi, 0)) return INFINI_ERR_HIP;
-    if (p.affine) {
-      AffineArgs fa;
-      fa.k = k;
-      fa.v = v;
-      fa.M_in = Min;
-      fa.z_in = zin;
-      fa.M_out = Mout;
-      fa.z_out = zout;
-      fa.snapM = snapM;
-      fa.snapZ = snapZ;
-      fa.colsum = colsum;
-      fa.Amat = Amat;
-      fa.Bmat = Bmat;
-      fa.L = L;
-      fa.seg_len = seg_len;
-      fa.units = (int32_t)p.units;
-      fa.s_begin = (int32_t)s_begin;
-      fa.s_count = (int32_t)s_count;
-      if (infini::launch_affine(dtype, (int)d, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
-    } else {
-    ScanArgs sa;
-    sa.k = k;
-    sa.v = v;
-    sa.M_in = Min;
-    sa.z_in = zin;
-    sa.M_out = Mout;
-    sa.z_out = zout;
-    sa.snapM = snapM;
-    sa.snapZ = snapZ;
-    sa.L = L;
-    sa.seg_len = seg_len;
-    sa.units = (int32_t)p.units;
-    sa.s_begin = (int32_t)s_begin;
-    sa.s_count = (int32_t)s_count;
-    if (infini::launch_scan(dtype, (int)d, rule, sa, s) != hipSuccess) return INFINI_ERR_HIP;
-    }
+    if (launch_recurrence(p, cw, rule, dtype, k, v, Min, zin, Mout, zout, L, seg_len, s_begin,
+                          s_count, s) != hipSuccess)
+      return INFINI_ERR_HIP;
     if (!mark(wi, 1)) return INFINI_ERR_HIP;
 
     AttnArgs aa;
@@ -316,11 +351,131 @@ infini_status_t infini_attn_forward_timed(int64_t B, int64_t Hq, int64_t Hkv, in
                       M_final, z_final, workspace, workspace_bytes, stream, events, n_events);
 }
 
+// ---- streaming decode --------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+struct DecodePlan {
+  Plan fold;           // the recurrence over one segment of the cache
+  int64_t G, n_chunks_max;
+  size_t part_bytes;   // chunk partials, aligned
+};
+
+infini_status_t check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t seg_len,
+                             int32_t rule, int32_t dtype, DecodePlan* dp) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || seg_len < 1) return INFINI_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return INFINI_ERR_INVALID_ARG;
+  if (Hq / Hkv > infini::kDecodeMaxGroup) return INFINI_ERR_UNSUPPORTED;
+  if (seg_len > 256 * (int64_t)infini::kDecodeMaxChunks) return INFINI_ERR_UNSUPPORTED;
+  Plan fold;
+  const infini_status_t st = check_sizes(B, Hq, Hkv, seg_len, d, seg_len, rule, dtype, &fold);
+  if (st != INFINI_OK) return st;
+  if (fold.units * ((seg_len + 255) / 256) > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  if (dp) {
+    dp->fold = fold;
+    dp->G = Hq / Hkv;
+    dp->n_chunks_max = (seg_len + 255) / 256;
+    dp->part_bytes = align_up((size_t)fold.units * (size_t)dp->n_chunks_max * (size_t)dp->G *
+                              (size_t)(d + 2) * 4);
+  }
+  return INFINI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                                  int64_t seg_len, int32_t rule, int32_t dtype,
+                                                  size_t* bytes) {
+  DecodePlan dp;
+  const infini_status_t st = check_decode(B, Hq, Hkv, d, seg_len, rule, dtype, &dp);
+  if (st != INFINI_OK) return st;
+  if (bytes) *bytes = dp.part_bytes + dp.fold.fixed + dp.fold.per_seg;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                        int64_t seg_len, int64_t pos, int32_t rule,
+                                        int32_t dtype, const void* q, const void* k,
+                                        const void* v, const float* beta, void* k_cache,
+                                        void* v_cache, float* M, float* z, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan dp;
+  const infini_status_t st = check_decode(B, Hq, Hkv, d, seg_len, rule, dtype, &dp);
+  if (st != INFINI_OK) return st;
+  if (pos < 0 || pos >= seg_len) return INFINI_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, beta, k_cache, v_cache, M, z, out, workspace};
+  for (const void* ptr : ptrs) {
+    if (ptr == nullptr) return INFINI_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : ptrs) {
+    if (!aligned16(ptr)) return INFINI_ERR_MISALIGNED;
+  }
+  const Plan& p = dp.fold;
+  const size_t e = (size_t)p.e;
+  const size_t nq = (size_t)(B * Hq * d) * e, nkv = (size_t)(B * Hkv * d) * e;
+  const size_t ncache = (size_t)(B * Hkv) * (size_t)seg_len * (size_t)d * e;
+  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  struct Range { const void* p; size_t n; };
+  const Range all[] = {{q, nq},           {k, nkv},           {v, nkv},
+                       {beta, (size_t)Hq * 4}, {k_cache, ncache}, {v_cache, ncache},
+                       {M, nM},           {z, nz},            {out, nq},
+                       {workspace, workspace_bytes}};
+  // the caches, the state, the output and the workspace are written: none of
+  // them may overlap any other argument
+  const int n_all = (int)(sizeof(all) / sizeof(all[0]));
+  for (int x = 4; x < n_all; ++x)
+    for (int y = 0; y < n_all; ++y)
+      if (x != y && overlap(all[x].p, all[x].n, all[y].p, all[y].n)) return INFINI_ERR_INVALID_ARG;
+  if (workspace_bytes < dp.part_bytes + p.fixed + p.per_seg) return INFINI_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  infini::DecodeArgs da;
+  da.q = q;
+  da.k = k;
+  da.v = v;
+  da.beta = beta;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.M = M;
+  da.z = z;
+  da.out = out;
+  da.part = reinterpret_cast<float*>(ws);
+  da.seg_len = seg_len;
+  da.B = (int32_t)B;
+  da.Hq = (int32_t)Hq;
+  da.Hkv = (int32_t)Hkv;
+  da.G = (int32_t)dp.G;
+  da.pos = (int32_t)pos;
+  da.n_chunks = (int32_t)((pos + 1 + 255) / 256);
+  da.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+  if (infini::launch_decode(dtype, (int)d, da, s) != hipSuccess) return INFINI_ERR_HIP;
+
+  if (pos == seg_len - 1) {
+    // the segment is complete: fold the cache into (M, z), in place
+    const Carved cw = carve(p, 1, rule, ws + dp.part_bytes);
+    const float* zin = z;
+    if (!p.affine) {
+      // the direct scan's slab workgroups read z while one of them writes it
+      if (infini::launch_copy_f32(cw.stz[1], z, B * Hkv * d, s) != hipSuccess) return INFINI_ERR_HIP;
+      zin = cw.stz[1];
+    }
+    if (launch_recurrence(p, cw, rule, dtype, k_cache, v_cache, M, zin, M, z, seg_len, seg_len, 0,
+                          1, s) != hipSuccess)
+      return INFINI_ERR_HIP;
+  }
+  return INFINI_OK;
+}
+
 const char* infini_attn_status_string(int32_t status) {
   switch (status) {
     case INFINI_OK: return "ok";
     case INFINI_ERR_INVALID_ARG: return "invalid argument";
-    case INFINI_ERR_UNSUPPORTED: return "unsupported head dimension";
+    case INFINI_ERR_UNSUPPORTED: return "unsupported size (head dimension, group or segment length)";
     case INFINI_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case INFINI_ERR_WORKSPACE: return "workspace too small";
     case INFINI_ERR_HIP: return "HIP runtime error";

@@ -66,6 +66,27 @@ struct AttnArgs {
   float scale_log2;    // log2(e) / sqrt(d)
 };
 
+// One streaming decode step (decode.hip): the token at row pos of its
+// segment, for every (batch, head).
+constexpr int kDecodeMaxGroup = 16;   // query heads per KV head
+constexpr int kDecodeMaxChunks = 64;  // 256-row cache chunks (seg_len <= 16384)
+struct DecodeArgs {
+  const void* q;       // [B][Hq][d]
+  const void* k;       // [B][Hkv][d]
+  const void* v;       // [B][Hkv][d]
+  const float* beta;   // [Hq]
+  void* k_cache;       // [B][Hkv][seg_len][d]; row pos is written
+  void* v_cache;       // [B][Hkv][seg_len][d]
+  const float* M;      // [B][Hkv][d][d]: the state before the segment
+  const float* z;      // [B][Hkv][d]
+  void* out;           // [B][Hq][d]
+  float* part;         // [B*Hkv][n_chunks][G][2 + d]: chunk max, weight sum, value sums
+  int64_t seg_len;
+  int32_t B, Hq, Hkv, G;
+  int32_t pos, n_chunks;  // n_chunks = ceil((pos + 1) / 256)
+  float scale_log2;       // log2(e) / sqrt(d)
+};
+
 // Wave count of the attention workgroup for a segment length: one wave per 32
 // query rows, at most four.
 int attn_waves(int64_t seg_len);
@@ -73,6 +94,7 @@ int attn_waves(int64_t seg_len);
 hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
+hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
 
 }  // namespace infini

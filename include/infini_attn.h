@@ -71,7 +71,7 @@ typedef enum {
 typedef enum {
   INFINI_OK = 0,
   INFINI_ERR_INVALID_ARG = 1, /* a size < 1, Hq % Hkv != 0, a null pointer, a bad enum, a forbidden overlap */
-  INFINI_ERR_UNSUPPORTED = 2, /* d not in {32, 64, 128} */
+  INFINI_ERR_UNSUPPORTED = 2, /* d not in {32, 64, 128}; decode: Hq / Hkv > 16 or seg_len > 16384 */
   INFINI_ERR_MISALIGNED = 3,  /* a pointer not 16-byte aligned */
   INFINI_ERR_WORKSPACE = 4,   /* workspace smaller than infini_attn_workspace_size's minimum */
   INFINI_ERR_HIP = 5          /* the HIP runtime refused a launch or a copy */
@@ -129,6 +129,51 @@ infini_status_t infini_attn_forward_timed(
     void* out, float* M_final, float* z_final,
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);
+
+/*
+ * Streaming decode ("Infini-Attention" (AI Wiki), "Why is the memory
+ * footprint bounded?": a stream runs segment by segment with only (M, z)
+ * carried, so the work per token is bounded by seg_len; the per-token
+ * arithmetic is the forward's, "What happens inside the Infini-attention
+ * block?").
+ *
+ * One call takes one new token for every (batch element, head): the token at
+ * position `pos` (0 <= pos < seg_len) of its segment. It
+ *   1. writes the token's key and value into row `pos` of the caches;
+ *   2. computes, for every query head h, the forward's output for this token:
+ *      causal softmax over cache rows 0..pos (this segment's tokens so far,
+ *      the new one included), retrieval sigma(q) M / (sigma(q) z) from (M, z)
+ *      as passed (the state before the segment), and the sigmoid(beta_h) gate;
+ *   3. when pos == seg_len - 1 (the segment is complete), folds cache rows
+ *      0..seg_len-1 into (M, z) in place with the update rule.
+ * Decoding a stream token by token, with pos = t mod seg_len and the same
+ * caches and state passed each time, gives the outputs of infini_attn_forward
+ * on the stream and, after each full segment, its state (up to rounding: the
+ * retrieval here reads the float state, the forward a snapshot in the element
+ * type). The caller keeps `pos`; cache rows pos+1.. are neither read nor
+ * written.
+ *
+ * Layouts (row-major, contiguous, device memory):
+ *   q, out            [B][Hq][d]            element type `dtype`
+ *   k, v              [B][Hkv][d]           element type `dtype`
+ *   beta              [Hq]                  float
+ *   k_cache, v_cache  [B][Hkv][seg_len][d]  element type `dtype`; read and written
+ *   M, z              [B][Hkv][d][d], [B][Hkv][d]  float; read, and written at a segment end
+ * Sizes as for the forward, plus Hq / Hkv <= 16 and seg_len <= 16384
+ * (INFINI_ERR_UNSUPPORTED beyond). The caches, M, z, out and the workspace
+ * may not overlap each other or the inputs. Checks, ownership and
+ * asynchrony as for the forward.
+ */
+infini_status_t infini_attn_decode_workspace_size(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype, size_t* bytes);
+
+infini_status_t infini_attn_decode_step(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t seg_len, int64_t pos,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    void* k_cache, void* v_cache, float* M, float* z, void* out,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /* A static, human-readable name of a status code. Never NULL. */
 const char* infini_attn_status_string(int32_t status);

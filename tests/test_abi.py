@@ -32,6 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
+        "infini_attn_decode_step", "infini_attn_decode_workspace_size",
         "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_status_string",
         "infini_attn_version", "infini_attn_workspace_size"])
 
@@ -199,3 +200,87 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f
+
+
+# ---- streaming decode ----------------------------------------------------------
+
+def dws(lib, *args):
+    n = ctypes.c_size_t(0)
+    st = lib.infini_attn_decode_workspace_size(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_decode_workspace_size(lib):
+    # Llama-3-8B-shaped: 32 units, 8 chunks of 256 rows, 4 query heads a unit,
+    # plus the one-segment recurrence workspace of the forward
+    st, n = dws(lib, 4, 32, 8, 128, 2048, 1, 1)
+    assert st == 0
+    _, _, fold = ws(lib, 4, 32, 8, 2048, 128, 2048, 1, 1)
+    part = 32 * 8 * 4 * (128 + 2) * 4
+    assert n == (part + 255) // 256 * 256 + fold
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 1, 32, 16, 0, 0), 1),        # B < 1
+    ((1, 3, 2, 32, 16, 0, 0), 1),        # Hq % Hkv
+    ((1, 1, 1, 32, 0, 0, 0), 1),         # seg_len < 1
+    ((1, 1, 1, 48, 16, 0, 0), 2),        # d unsupported
+    ((1, 17, 1, 32, 16, 0, 0), 2),       # more than 16 query heads per KV head
+    ((1, 1, 1, 32, 16385, 0, 0), 2),     # segment longer than 64 chunks of 256
+    ((1, 1, 1, 32, 16, 2, 0), 1),        # bad rule
+])
+def test_decode_workspace_size_rejects(lib, args, status):
+    assert dws(lib, *args)[0] == status
+
+
+class FakeDecodeBuffers:
+    def __init__(self, B, Hq, Hkv, d, N, e):
+        sizes = dict(q=B * Hq * d * e, k=B * Hkv * d * e, v=B * Hkv * d * e, beta=Hq * 4,
+                     k_cache=B * Hkv * N * d * e, v_cache=B * Hkv * N * d * e,
+                     M=B * Hkv * d * d * 4, z=B * Hkv * d * 4, out=B * Hq * d * e,
+                     workspace=1 << 40)
+        base = 1 << 44
+        self.addr, self.size = {}, sizes
+        for name, n in sizes.items():
+            self.addr[name] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+
+
+def dcall(lib, shape, pos, bufs, **over):
+    B, Hq, Hkv, d, N, rule, dt = shape
+    a = {**bufs.addr, **over}
+    wsb = over.get("workspace_bytes", bufs.size["workspace"])
+    return lib.infini_attn_decode_step(
+        B, Hq, Hkv, d, N, pos, rule, dt,
+        *[ctypes.c_void_p(a[n]) for n in ("q", "k", "v", "beta", "k_cache", "v_cache", "M", "z",
+                                           "out", "workspace")],
+        wsb, None)
+
+
+DSHAPE = (2, 4, 2, 64, 40, 1, 1)
+
+
+@pytest.mark.parametrize("pos", [-1, 40, 1000])
+def test_decode_rejects_positions_outside_the_segment(lib, pos):
+    assert dcall(lib, DSHAPE, pos, FakeDecodeBuffers(2, 4, 2, 64, 40, 2)) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "beta", "k_cache", "v_cache", "M", "z", "out",
+                                  "workspace"])
+def test_decode_rejects_null_and_misaligned_pointers(lib, name):
+    bufs = FakeDecodeBuffers(2, 4, 2, 64, 40, 2)
+    assert dcall(lib, DSHAPE, 3, bufs, **{name: 0}) == 1
+    assert dcall(lib, DSHAPE, 3, bufs, **{name: bufs.addr[name] + 8}) == 3
+
+
+@pytest.mark.parametrize("a,b", [("out", "q"), ("k_cache", "v_cache"), ("k_cache", "k"),
+                                 ("M", "z"), ("workspace", "M"), ("v_cache", "out")])
+def test_decode_rejects_overlaps(lib, a, b):
+    bufs = FakeDecodeBuffers(2, 4, 2, 64, 40, 2)
+    assert dcall(lib, DSHAPE, 3, bufs, **{a: bufs.addr[b]}) == 1
+
+
+def test_decode_rejects_small_workspace(lib):
+    bufs = FakeDecodeBuffers(2, 4, 2, 64, 40, 2)
+    _, need = dws(lib, 2, 4, 2, 64, 40, 1, 1)
+    assert dcall(lib, DSHAPE, 3, bufs, workspace_bytes=need - 1) == 4
