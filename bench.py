@@ -109,6 +109,87 @@ def cpu_baseline(w, rule, inp, target_s):
     }
 
 
+def decode_bytes(w, pos):
+    """Algorithmic HBM bytes of one decode step at position pos: the cached
+    keys and values of rows 0..pos once, the float state once, q and out of
+    the token, its key and value written into the caches."""
+    e = 4 if w.dtype == "f32" else 2
+    units = w.B * w.Hkv
+    return (units * (2 * (pos + 1) * w.d * e + 4 * (w.d * w.d + w.d))
+            + 2 * w.B * w.Hq * w.d * e + 2 * units * w.d * e)
+
+
+def bench_decode(lib, w, rule, dev, args):
+    """The streaming decode step over one full segment of the workload's
+    shape: seg_len steps, positions 0 .. seg_len-1, the last one folding the
+    segment into the state. Every step takes one token per (batch, head)."""
+    import torch
+
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    N, d = w.seg_len, w.d
+    mk = lambda *s: torch.randn(*s, generator=g, dtype=torch.float32).to(dt).to(dev)
+    q = [mk(w.B, w.Hq, d) for _ in range(8)]
+    k = [mk(w.B, w.Hkv, d) for _ in range(8)]
+    v = [mk(w.B, w.Hkv, d) for _ in range(8)]
+    beta = torch.randn(w.Hq, generator=g).to(dev)
+    kc = torch.zeros(w.B, w.Hkv, N, d, dtype=dt, device=dev)
+    vc = torch.zeros_like(kc)
+    M = torch.zeros(w.B, w.Hkv, d, d, device=dev)
+    z = torch.full((w.B, w.Hkv, d), 1e-6, device=dev)
+    out = torch.empty_like(q[0])
+    ws = torch.empty(lib.decode_workspace_size(w.B, w.Hq, w.Hkv, d, N, rule, dt),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(pos):
+        lib.decode_step(q[pos % 8], k[pos % 8], v[pos % 8], beta, kc, vc, M, z, pos, rule,
+                        out=out, workspace=ws, stream=stream)
+
+    for pos in range(min(args.warmup, N)):
+        step(pos)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for pos in range(N):
+        step(pos)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    seg_ms = e0.elapsed_time(e1)
+    # one step at a full cache without the fold (pos = N - 2), repeated
+    reps = 50
+    e0.record(stream)
+    for _ in range(reps):
+        step(N - 2)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    full_us = e0.elapsed_time(e1) / reps * 1e3
+    gbs = decode_bytes(w, N - 2) / (full_us * 1e-6) / 1e9
+    return {
+        "metric": "Infini-attn streaming decode tokens/s, 1xMI355X",
+        "value": w.B * N / (seg_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": N,
+        "warmup": min(args.warmup, N),
+        "ms_per_step": seg_ms / N,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian q/k/v; zero initial state)",
+        "config": {"workload": w.name + "/decode", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": d,
+                   "seg_len": N, "rule": rule, "tokens_per_step": w.B},
+        "segment_ms": seg_ms,
+        "full_cache_step_us": full_us,
+        "roofline": {"kernel": "decode step at a full cache (partial + combine)", "bound": "hbm",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": decode_bytes(w, N - 2)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +200,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
+                    help="forward: the block forward over the workload (default); decode: "
+                         "the streaming decode step over one full segment of it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the steps, copy MIB MiB device to device once (a kernel "
                          "of known traffic that calibrates the HBM byte counters)")
@@ -138,6 +222,9 @@ def main():
     rule = args.rule or w.rules[-1]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "decode":
+        print(json.dumps(bench_decode(lib, w, rule, dev, args)), flush=True)
+        return
     inp = synth.make_inputs(w, dev)
     out = torch.empty_like(inp["q"])
     M = torch.empty_like(inp["M0"])

@@ -368,15 +368,15 @@ infini_status_t check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int6
   if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || seg_len < 1) return INFINI_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return INFINI_ERR_INVALID_ARG;
   if (Hq / Hkv > infini::kDecodeMaxGroup) return INFINI_ERR_UNSUPPORTED;
-  if (seg_len > 256 * (int64_t)infini::kDecodeMaxChunks) return INFINI_ERR_UNSUPPORTED;
+  if (seg_len > 64 * (int64_t)infini::kDecodeMaxChunks) return INFINI_ERR_UNSUPPORTED;
   Plan fold;
   const infini_status_t st = check_sizes(B, Hq, Hkv, seg_len, d, seg_len, rule, dtype, &fold);
   if (st != INFINI_OK) return st;
-  if (fold.units * ((seg_len + 255) / 256) > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  if (fold.units * ((seg_len + 63) / 64) > INT32_MAX) return INFINI_ERR_INVALID_ARG;
   if (dp) {
     dp->fold = fold;
     dp->G = Hq / Hkv;
-    dp->n_chunks_max = (seg_len + 255) / 256;
+    dp->n_chunks_max = (seg_len + 63) / 64;
     dp->part_bytes = align_up((size_t)fold.units * (size_t)dp->n_chunks_max * (size_t)dp->G *
                               (size_t)(d + 2) * 4);
   }
@@ -451,7 +451,7 @@ infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int6
   da.Hkv = (int32_t)Hkv;
   da.G = (int32_t)dp.G;
   da.pos = (int32_t)pos;
-  da.n_chunks = (int32_t)((pos + 1 + 255) / 256);
+  da.n_chunks = (int32_t)((pos + 1 + 63) / 64);
   da.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   if (infini::launch_decode(dtype, (int)d, da, s) != hipSuccess) return INFINI_ERR_HIP;
 

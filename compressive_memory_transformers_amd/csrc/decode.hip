@@ -9,35 +9,50 @@
 // sigmoid(beta) gate ("What happens inside the Infini-attention block?").
 //
 // Two kernels, memory-bound (the cache is read once per step):
-//   partial: per (batch, KV head, chunk of 256 cache rows), the grouped query
-//            heads' scores, chunk maximum, exp2 weights, their sum and the
-//            weighted value sum (split over key groups, then reduced in LDS);
-//            the workgroup whose chunk holds row pos also appends the token's
-//            key and value to the cache (no workgroup reads that row from the
-//            cache in this step: it takes the new key/value directly);
-//   combine: per (batch, KV head), the chunks merged by their maxima, the
-//            retrieval from the float state, the gate, the output row.
+//   partial: per (batch, KV head, chunk of 64 cache rows), the grouped query
+//            heads' scores, the chunk maximum and exp2 weight sum, and the
+//            weighted value sums; the workgroup whose chunk holds row pos also
+//            appends the token's key and value to the cache (no workgroup
+//            reads that row from the cache in this step: it takes the new
+//            key/value directly);
+//   combine: per (batch, KV head, 32 output columns), the chunks merged by
+//            their maxima, the retrieval from the float state, the gate.
 // The fold of a full segment into (M, z) reuses the recurrence kernels
 // (api.hip).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace infini {
 
 namespace {
 
-constexpr int kDecodeKC = 256;  // cache rows per partial workgroup
-constexpr int kDecodeNT = 256;  // threads per workgroup
+constexpr int kDecodeKC = 64;   // cache rows per partial workgroup (one wave)
+constexpr int kDecodeNT = 256;  // threads per combine workgroup
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDecodeNT) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int KC = kDecodeKC, NT = kDecodeNT, GM = kDecodeMaxGroup, C8 = D / 8;
+__device__ __forceinline__ const T* cache_row(const DecodeArgs& a, const T* cache, const T* fresh,
+                                              int t) {
+  return t == a.pos ? fresh : cache + (int64_t)t * D;
+}
+
+// One 256-thread workgroup per (batch, KV head, chunk of 64 cache rows).
+// Thread (row r = tid / 4, quarter u = tid % 4) loads columns [u d/4,
+// (u+1) d/4) of row r of K and of V at once (one memory latency for the whole chunk); the
+// four quarters' partial scores are summed by DPP; one wave per head takes the
+// chunk maximum and weight sum; the value sums run over (head, 8-column group,
+// quarter of the rows) triples and are added in LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int KC = kDecodeKC, GM = kDecodeMaxGroup, C8 = D / 8;
+  constexpr int QW = D / 4, QC = QW / 8;  // columns, 8-column chunks of a row quarter
   __shared__ float qs[GM * D];  // the group's queries, scaled by log2(e) / sqrt(d)
   __shared__ float ps[GM * KC]; // scores, then exp2 weights
-  __shared__ float ov[NT * 8];  // per key-group partial value sums
-  __shared__ float hm[GM], hl[GM];
+  __shared__ __align__(16) T vs[KC * D];
+  __shared__ float ov[4 * GM * D];  // value sums of the four row quarters
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int G = a.G;
   const int unit = blockIdx.x / a.n_chunks, ch = blockIdx.x % a.n_chunks;
   const int b = unit / a.Hkv, j = unit % a.Hkv;
@@ -49,153 +64,180 @@ __global__ __launch_bounds__(kDecodeNT) void decode_partial_kernel(DecodeArgs a)
   const T* kc = static_cast<const T*>(a.k_cache) + (int64_t)unit * a.seg_len * D;
   const T* vc = static_cast<const T*>(a.v_cache) + (int64_t)unit * a.seg_len * D;
 
-  for (int x = tid; x < G * D; x += NT) qs[x] = to_f32<T>(q[x]) * a.scale_log2;
+  // this thread's quarter row (a row past the chunk repeats row t0: finite, weight 0)
+  const int r = tid >> 2, u = tid & 3;
+  const int t = t0 + (r < n ? r : 0);
+  const T* krow = cache_row<T, D>(a, kc, knew, t) + QW * u;
+  const T* vrow = cache_row<T, D>(a, vc, vnew, t) + QW * u;
+  frag_t<T> kv[QC], vv[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) kv[c] = load8<T>(krow + 8 * c);
+#pragma unroll
+  for (int c = 0; c < QC; ++c) vv[c] = load8<T>(vrow + 8 * c);
+  for (int x = tid; x < G * D; x += 256) qs[x] = to_f32<T>(q[x]) * a.scale_log2;
+#pragma unroll
+  for (int c = 0; c < QC; ++c) store8<T>(vs + r * D + QW * u + 8 * c, vv[c]);
   __syncthreads();
 
-  // scores: one cache row per thread
-  {
-    float s[GM];
+  // scores: the quarter's partial dot for every head, summed over the quad
 #pragma unroll
-    for (int g = 0; g < GM; ++g) s[g] = 0.f;
-    if (tid < n) {
-      const int t = t0 + tid;
-      const T* row = t == a.pos ? knew : kc + (int64_t)t * D;
-#pragma unroll
-      for (int c = 0; c < C8; ++c) {
-        const frag_t<T> kv = load8<T>(row + 8 * c);
-#pragma unroll
-        for (int g = 0; g < GM; ++g)
-          if (g < G) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[g] += to_f32<T>(kv[e]) * qs[g * D + 8 * c + e];
-          }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-      if (g < G) ps[g * KC + tid] = tid < n ? s[g] : -INFINITY;
-  }
-  __syncthreads();
-
-  // per head: chunk maximum, then exp2 weights and their sum (32 threads a head)
-  for (int g0 = 0; g0 < G; g0 += NT / 32) {
-    const int g = g0 + tid / 32, l32 = tid & 31;
+  for (int g = 0; g < GM; ++g)
     if (g < G) {
-      float m = -INFINITY;
+      float sp = 0.f;
 #pragma unroll
-      for (int i = 0; i < KC / 32; ++i) m = fmaxf(m, ps[g * KC + l32 * (KC / 32) + i]);
+      for (int c = 0; c < QC; ++c)
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-      float l = 0.f;
-#pragma unroll
-      for (int i = 0; i < KC / 32; ++i) {
-        const int x = g * KC + l32 * (KC / 32) + i;
-        const float p = exp2f(ps[x] - m);  // -inf rows give 0
-        ps[x] = p;
-        l += p;
-      }
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 32);
-      if (l32 == 0) {
-        hm[g] = m;
-        hl[g] = l;
-      }
+        for (int e = 0; e < 8; ++e) sp += to_f32<T>(kv[c][e]) * qs[g * D + QW * u + 8 * c + e];
+      sp = row_sum<4>(sp);
+      if (u == 0) ps[g * KC + r] = r < n ? sp : -INFINITY;
+    }
+  __syncthreads();
+
+  // per head (one wave a head): chunk maximum and weight sum, lane = row
+  float* part = a.part + ((int64_t)unit * a.n_chunks + ch) * G * (D + 2);
+  for (int g = w; g < G; g += 4) {
+    const float sc = ps[g * KC + lane];
+    const float m = wave_max(sc);
+    const float p = exp2f(sc - m);  // 0 past the chunk's rows
+    const float l = wave_sum(p);
+    ps[g * KC + lane] = p;
+    if (lane == 0) {
+      part[g * (D + 2)] = m;
+      part[g * (D + 2) + 1] = l;
     }
   }
   __syncthreads();
 
-  // weighted value sums: (head, 8-column group) pairs, split over key groups
-  const int npairs = G * C8;
-  const int ks = max(1, NT / npairs);
-  for (int p = tid; p < npairs * ks; p += NT) {
-    const int pair = p % npairs, kg = p / npairs;
-    const int g = pair / C8, c = pair % C8;
+  // value sums: (head, 8-column group, row quarter) triples
+  for (int x = tid; x < G * C8 * 4; x += 256) {
+    const int kq = x / (G * C8), pr = x % (G * C8);
+    const int g = pr / C8, c = pr % C8;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int tt = kg; tt < n; tt += ks) {
-      const int t = t0 + tt;
-      const T* row = t == a.pos ? vnew : vc + (int64_t)t * D;
-      const frag_t<T> vv = load8<T>(row + 8 * c);
-      const float w = ps[g * KC + tt];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += w * to_f32<T>(vv[e]);
-    }
-    if (p < NT) {  // one slot per thread: npairs * ks <= NT when npairs <= NT
+    for (int i = 0; i < KC / 4; ++i) {
+      const int tt = kq * (KC / 4) + i;  // rows past n carry weight 0
+      const frag_t<T> vx = load8<T>(vs + tt * D + 8 * c);
+      const float wgt = ps[g * KC + tt];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ov[p * 8 + e] = acc[e];
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * to_f32<T>(vx[e]);
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[(kq * G + g) * D + 8 * c + e] = acc[e];
   }
   __syncthreads();
-
-  float* part = a.part + ((int64_t)unit * a.n_chunks + ch) * G * (D + 2);
-  for (int x = tid; x < G * D; x += NT) {
-    const int g = x / D, col = x % D, c = col / 8, e = col % 8;
-    float o = 0.f;
-    for (int kg = 0; kg < ks; ++kg) o += ov[(kg * npairs + g * C8 + c) * 8 + e];
-    part[g * (D + 2) + 2 + col] = o;
-  }
-  if (tid < G) {
-    part[tid * (D + 2)] = hm[tid];
-    part[tid * (D + 2) + 1] = hl[tid];
+  for (int x = tid; x < G * D; x += 256) {
+    const int g = x / D, col = x % D;
+    part[g * (D + 2) + 2 + col] = (ov[(0 * G + g) * D + col] + ov[(1 * G + g) * D + col]) +
+                                  (ov[(2 * G + g) * D + col] + ov[(3 * G + g) * D + col]);
   }
 
-  // append the token to the cache
+  // append the token to the cache (no workgroup reads row pos from the cache)
   if (t0 <= a.pos && a.pos < t0 + KC) {
     T* kw = static_cast<T*>(a.k_cache) + ((int64_t)unit * a.seg_len + a.pos) * D;
     T* vw = static_cast<T*>(a.v_cache) + ((int64_t)unit * a.seg_len + a.pos) * D;
-    for (int x = tid; x < D; x += NT) {
+    for (int x = tid; x < D; x += 256) {
       kw[x] = knew[x];
       vw[x] = vnew[x];
     }
   }
 }
 
+// Per (batch, KV head, 32-column slab of the output): merge the chunks,
+// retrieve from the float state, gate. The slab of M, z and the queries are
+// loaded at once into LDS; the small reductions run across the workgroup.
 template <typename T, int D>
 __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a) {
   constexpr int NT = kDecodeNT, GM = kDecodeMaxGroup, NCM = kDecodeMaxChunks;
   __shared__ float sq[GM * D];    // sigma(q)
-  __shared__ float wch[GM * NCM]; // chunk weights exp2(m_c - m) / l
-  __shared__ float den[GM], gate[GM];
+  __shared__ float ms[D * 32];    // M[:, slab]
+  __shared__ float zs[D];
+  __shared__ float wch[GM * NCM]; // chunk maxima, then weights exp2(m_c - m)
+  __shared__ float den[GM], gate[GM], mx[GM], lsum[GM];
+  constexpr int OC = 4096;           // staged value sums: chunks x heads x 32 columns
+  __shared__ float os[OC];
 
   const int tid = threadIdx.x;
   const int G = a.G, NC = a.n_chunks;
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x / (D / 32), slab = blockIdx.x % (D / 32);
   const int b = unit / a.Hkv, j = unit % a.Hkv;
   const int hq0 = j * G;
   const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + hq0) * D;
-  const float* M = a.M + (int64_t)unit * D * D;
+  const float* M = a.M + (int64_t)unit * D * D + 32 * slab;
   const float* z = a.z + (int64_t)unit * D;
   const float* part = a.part + (int64_t)unit * NC * G * (D + 2);
 
+  for (int x = tid; x < D * 8; x += NT) {  // 8 float4 per row of the slab
+    const int k = x / 8, c4 = x % 8;
+    *reinterpret_cast<f32x4*>(ms + k * 32 + 4 * c4) =
+        *reinterpret_cast<const f32x4*>(M + (int64_t)k * D + 4 * c4);
+  }
   for (int x = tid; x < G * D; x += NT) sq[x] = feature_map(to_f32<T>(q[x]));
-  __syncthreads();
-  if (tid < G) {
-    const int g = tid;
-    float dp = 0.f;
-    for (int k = 0; k < D; ++k) dp += sq[g * D + k] * z[k];
-    den[g] = dp;
-    gate[g] = 1.f / (1.f + expf(-a.beta[hq0 + g]));
-    float m = -INFINITY;
-    for (int c = 0; c < NC; ++c) m = fmaxf(m, part[(c * G + g) * (D + 2)]);
-    float l = 0.f;
-    for (int c = 0; c < NC; ++c) {
-      const float w = exp2f(part[(c * G + g) * (D + 2)] - m);
-      wch[g * NCM + c] = w;
-      l += w * part[(c * G + g) * (D + 2) + 1];
+  for (int x = tid; x < D; x += NT) zs[x] = z[x];
+  for (int x = tid; x < G * NC; x += NT) wch[(x / NC) * NCM + x % NC] = part[((x % NC) * G + x / NC) * (D + 2)];
+  // the slab's value sums of every (chunk, head), when they fit (G * NC <= 128)
+  const bool staged = G * NC * 32 <= OC;
+  if (staged)
+    for (int x = tid; x < G * NC * 8; x += NT) {  // 8 float4 per (chunk, head)
+      const int cg = x / 8, c4 = x % 8;
+      const float* src = part + cg * (D + 2) + 2 + 32 * slab + 4 * c4;
+      f32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = src[e];  // rows of D + 2 floats: 8-byte aligned only
+      *reinterpret_cast<f32x4*>(os + cg * 32 + 4 * c4) = y;
     }
-    for (int c = 0; c < NC; ++c) wch[g * NCM + c] /= l;
+  __syncthreads();
+  // per head (32 lanes a head): den = sigma(q) . z, the chunks' maximum
+  for (int g0 = 0; g0 < G; g0 += NT / 32) {
+    const int g = g0 + tid / 32, l32 = tid & 31;
+    if (g < G) {
+      float dp = 0.f;
+      for (int k = l32; k < D; k += 32) dp += sq[g * D + k] * zs[k];
+      float m = -INFINITY;
+      for (int c = l32; c < NC; c += 32) m = fmaxf(m, wch[g * NCM + c]);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) {
+        dp += __shfl_xor(dp, o, 32);
+        m = fmaxf(m, __shfl_xor(m, o, 32));
+      }
+      if (l32 == 0) {
+        den[g] = dp;
+        mx[g] = m;
+        gate[g] = 1.f / (1.f + expf(-a.beta[hq0 + g]));
+      }
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < G * NC; x += NT) {
+    const int g = x / NC, c = x % NC;
+    wch[g * NCM + c] = exp2f(wch[g * NCM + c] - mx[g]);
+  }
+  __syncthreads();
+  for (int g0 = 0; g0 < G; g0 += NT / 32) {
+    const int g = g0 + tid / 32, l32 = tid & 31;
+    if (g < G) {
+      float l = 0.f;
+      for (int c = l32; c < NC; c += 32) l += wch[g * NCM + c] * part[(c * G + g) * (D + 2) + 1];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 32);
+      if (l32 == 0) lsum[g] = l;
+    }
   }
   __syncthreads();
 
   T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + hq0) * D;
-  for (int x = tid; x < G * D; x += NT) {
-    const int g = x / D, col = x % D;
+  for (int x = tid; x < G * 32; x += NT) {
+    const int g = x / 32, cs = x % 32, col = 32 * slab + cs;
     float o = 0.f;
-    for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * part[(c * G + g) * (D + 2) + 2 + col];
+    if (staged)
+      for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * os[(c * G + g) * 32 + cs];
+    else
+      for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * part[(c * G + g) * (D + 2) + 2 + col];
     float r = 0.f;
-    for (int k = 0; k < D; ++k) r += sq[g * D + k] * M[(int64_t)k * D + col];
-    out[x] = from_f32<T>(gate[g] * (r / den[g]) + (1.f - gate[g]) * o);
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) r += sq[g * D + k] * ms[k * 32 + cs];
+    out[g * D + col] = from_f32<T>(gate[g] * (r / den[g]) + (1.f - gate[g]) * (o / lsum[g]));
   }
 }
 
@@ -203,8 +245,9 @@ template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)(a.B * a.Hkv);
   hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3(units * (unsigned)a.n_chunks),
+                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(units * (unsigned)(D / 32)),
                      dim3(kDecodeNT), 0, stream, a);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(units), dim3(kDecodeNT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ struct AttnArgs {
 // One streaming decode step (decode.hip): the token at row pos of its
 // segment, for every (batch, head).
 constexpr int kDecodeMaxGroup = 16;   // query heads per KV head
-constexpr int kDecodeMaxChunks = 64;  // 256-row cache chunks (seg_len <= 16384)
+constexpr int kDecodeMaxChunks = 256;  // 64-row cache chunks (seg_len <= 16384)
 struct DecodeArgs {
   const void* q;       // [B][Hq][d]
   const void* k;       // [B][Hkv][d]
@@ -83,7 +83,7 @@ struct DecodeArgs {
   float* part;         // [B*Hkv][n_chunks][G][2 + d]: chunk max, weight sum, value sums
   int64_t seg_len;
   int32_t B, Hq, Hkv, G;
-  int32_t pos, n_chunks;  // n_chunks = ceil((pos + 1) / 256)
+  int32_t pos, n_chunks;  // n_chunks = ceil((pos + 1) / 64)
   float scale_log2;       // log2(e) / sqrt(d)
 };
 

@@ -161,4 +161,33 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// Maximum and sum of x over the whole wave, returned to every lane: DPP
+// butterflies within each 16-lane row, then the four rows combined through
+// lanes 15, 31, 47 and 63 read with v_readlane.
+__device__ __forceinline__ float wave_max(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 decltype(ctrl)::value, 0xf, 0xf,
+                                                                 false));
+  };
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0xB1>{}));
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x4E>{}));
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x141>{}));
+  x = fmaxf(x, dpp(x, std::integral_constant<int, 0x140>{}));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum<16>(x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+  return (r0 + r1) + (r2 + r3);
+}
+
 }  // namespace infini

@@ -211,12 +211,12 @@ def dws(lib, *args):
 
 
 def test_decode_workspace_size(lib):
-    # Llama-3-8B-shaped: 32 units, 8 chunks of 256 rows, 4 query heads a unit,
+    # Llama-3-8B-shaped: 32 units, 32 chunks of 64 rows, 4 query heads a unit,
     # plus the one-segment recurrence workspace of the forward
     st, n = dws(lib, 4, 32, 8, 128, 2048, 1, 1)
     assert st == 0
     _, _, fold = ws(lib, 4, 32, 8, 2048, 128, 2048, 1, 1)
-    part = 32 * 8 * 4 * (128 + 2) * 4
+    part = 32 * 32 * 4 * (128 + 2) * 4
     assert n == (part + 255) // 256 * 256 + fold
 
 
@@ -226,7 +226,7 @@ def test_decode_workspace_size(lib):
     ((1, 1, 1, 32, 0, 0, 0), 1),         # seg_len < 1
     ((1, 1, 1, 48, 16, 0, 0), 2),        # d unsupported
     ((1, 17, 1, 32, 16, 0, 0), 2),       # more than 16 query heads per KV head
-    ((1, 1, 1, 32, 16385, 0, 0), 2),     # segment longer than 64 chunks of 256
+    ((1, 1, 1, 32, 16385, 0, 0), 2),     # segment longer than 256 chunks of 64
     ((1, 1, 1, 32, 16, 2, 0), 1),        # bad rule
 ])
 def test_decode_workspace_size_rejects(lib, args, status):
