@@ -462,17 +462,20 @@ __device__ __forceinline__ void dma_snapshot(const DmaTile<D, NW, BN>& tile, con
 // The iteration loads K(j + 2) over K(j) and V(j + 1) over V(j - 1), both
 // last read before the previous barrier, and waits for them at its end.
 // FULL: the caller knows that tile j + 1 is this wave's too and below its
-// diagonal (every iteration but a workgroup's last few), so the iteration is
-// one straight-line block apart from the rare rescale.
+// diagonal (every iteration but a workgroup's last few), so tile j + 2
+// exists and the iteration is one straight-line block apart from the rare
+// rescale. The loads and the wait are then unconditional, which lets the
+// compiler see that the reads of this iteration touch only the other two
+// buffers (separate arrays) and need not wait for the loads just issued.
 template <int D, int NW, int BN, int P, bool FULL>
 __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile<D, NW, BN>& tile,
-                                         const bf16* K, const bf16* V, bf16 (*Ks)[BN * D],
-                                         bf16 (*Vs)[BN * D], int n_s, int w, int q0,
+                                         const bf16* K, const bf16* V, bf16* const* Ks,
+                                         bf16* const* Vs, int n_s, int w, int q0,
                                          DmaLane<D>& st, f32x16* sacc, float c, int row, int h,
                                          const bf16* Mts, const float* zs, float* Zs) {
   constexpr int NKB = BN / 32, NPC = BN / 16;
-  if (j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
-  if (j + 1 < n_kt) tile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+  if (FULL || j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
+  if (FULL || j + 1 < n_kt) tile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
   if (!FULL && j + 1 == n_kt) dma_snapshot<D, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
   if (FULL || j + 1 < n_w) {
     bf16x8 pf[NPC];
@@ -489,7 +492,7 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile
     dma_probs<D, BN>(sacc, st, c, pf);
     dma_values<D, BN>(Vs[P], st, pf);
   }
-  if (j + 1 < n_kt) {
+  if (FULL || j + 1 < n_kt) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j + 2), V(j + 1) have landed
     __syncthreads();
   }
@@ -499,8 +502,14 @@ template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   constexpr int BM = 32 * NW;
   constexpr int NC = D / 16, NDB = D / 32;
-  __shared__ __align__(1024) bf16 Ks[2][BN * D];
-  __shared__ __align__(1024) bf16 Vs[2][BN * D];
+  // four separate arrays, so that the compiler can tell a tile being loaded
+  // by DMA from the tiles being read and does not wait for the load
+  __shared__ __align__(1024) bf16 Ks0[BN * D];
+  __shared__ __align__(1024) bf16 Ks1[BN * D];
+  __shared__ __align__(1024) bf16 Vs0[BN * D];
+  __shared__ __align__(1024) bf16 Vs1[BN * D];
+  bf16* const Ks[2] = {Ks0, Ks1};
+  bf16* const Vs[2] = {Vs0, Vs1};
   __shared__ __align__(16) float Zs[256];  // z of the segment (one 16-byte DMA per lane of wave 0)
 
   const int tid = threadIdx.x, lane = tid & 63;
