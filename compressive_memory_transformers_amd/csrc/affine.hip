@@ -276,6 +276,7 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   __shared__ __align__(1024) bf16 Vr[NBUF][TC * D];
   __shared__ __align__(1024) bf16 Ph[TC * D];
   __shared__ __align__(1024) bf16 DPh[DELTA ? TC * D : 8];
+  __shared__ __align__(16) float Zs[256];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -286,22 +287,22 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
   const int n_c = (n_s + TC - 1) / TC;
 
-  // staging role (z loaded before the DMA, so the vmcnt waits below count
-  // DMA loads only): token st_t of the chunk, columns 16 st_g .. + 15
+  // staging role: token st_t of the chunk, columns 16 st_g .. + 15. z comes
+  // into LDS by one 16-byte DMA per lane of wave 0 (lanes past d / 4 read
+  // outside the resource, which returns zeros), issued before the tiles, so
+  // the first chunk's wait covers it.
   const int st_t = tid >> 3, st_g = tid & 7;
+  if (w == 0)
+    dma16_asm(Zs, asm_rsrc(a.snapZ + ((int64_t)unit * a.s_count + sl) * D, D * 4),
+              (uint32_t)lane * 16, 0u);
   float zc[16];
-  {
-    const float* z = a.snapZ + ((int64_t)unit * a.s_count + sl) * D + 16 * st_g;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) zc[e] = z[e];
-  }
   Tile tile;
   tile.init(w, lane);
-  tile.template issue<true>(K, Kr[0], 0, n_s, w);
-  tile.template issue<false>(V, Vr[0], 0, n_s, w);
+  tile.template issue_asm<true>(K, Kr[0], 0, n_s, w);
+  tile.template issue_asm<false>(V, Vr[0], 0, n_s, w);
   if (n_c > 1) {
-    tile.template issue<true>(K, Kr[1], TC, n_s, w);
-    tile.template issue<false>(V, Vr[1], TC, n_s, w);
+    tile.template issue_asm<true>(K, Kr[1], TC, n_s, w);
+    tile.template issue_asm<false>(V, Vr[1], TC, n_s, w);
   }
 
   // product role: row tiles rt0, rt0 + 1; column tiles BC cq + c
@@ -326,9 +327,13 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
     else
       wait_vmcnt<0>();
     __syncthreads();  // chunk ch complete everywhere; chunk ch - 1's products done
+    if (ch == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zc[e] = Zs[16 * st_g + e];
+    }
     if (ch + 2 < n_c) {  // into the buffer chunk ch - 1 used
-      tile.template issue<true>(K, Kr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
-      tile.template issue<false>(V, Vr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+      tile.template issue_asm<true>(K, Kr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+      tile.template issue_asm<false>(V, Vr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
     }
     // stage Phi and Phi / den of token st_t (zero past the segment's end)
     {

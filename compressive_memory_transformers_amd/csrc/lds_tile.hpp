@@ -54,6 +54,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16* base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// The same 16-byte LDS-DMA load written as inline assembly. The compiler
+// neither counts these loads nor inserts waits for them (with the builtin it
+// must assume that any later LDS access, or the fence of a barrier, depends
+// on every DMA load in flight), so a kernel that uses them waits for them
+// explicitly (wait_vmcnt, s_waitcnt). Each sets M0, the instruction's LDS
+// base, itself: a kernel must not mix them with the builtin, which expects
+// M0 to be the compiler's.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 asm_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ void dma16_asm(void* lds, u32x4 rsrc, uint32_t voff, uint32_t soff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 template <int D, int NW, int BN>
 struct DmaTile {
   static constexpr int NT = NW * 64;
@@ -107,6 +125,25 @@ struct DmaTile {
         const uint32_t xj = J_INV ? off[0] + j * J_STEP : off[j];
         const uint32_t xo = xj < lim ? xj : last + (xj & (2 * D - 1));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, xo, 0, 0, 0);
+      }
+    }
+  }
+  // issue() through dma16_asm
+  template <bool IS_K>
+  __device__ __forceinline__ void issue_asm(const bf16* X, bf16* Xs, int k0, int n_s, int w) const {
+    const uint32_t* off = IS_K ? k_off : v_off;
+    const int rows = min(BN, n_s - k0);
+    const u32x4 rx = asm_rsrc(X + (int64_t)k0 * D, (uint32_t)rows * D * 2);
+    const uint32_t lim = (uint32_t)rows * (2 * D);
+    const uint32_t last = lim - 2 * D;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = (j * NW + w) * 64 * 8;
+      if (rows == BN) {
+        dma16_asm(Xs + blk, rx, off[J_INV ? 0 : j], J_INV ? j * J_STEP : 0u);
+      } else {
+        const uint32_t xj = J_INV ? off[0] + j * J_STEP : off[j];
+        dma16_asm(Xs + blk, rx, xj < lim ? xj : last + (xj & (2 * D - 1)), 0u);
       }
     }
   }
