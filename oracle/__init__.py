@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Infini-attention block forward.
+"""fp64 CPU oracle for the Infini-attention block forward and its gradients.
 
 This package is TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import or call it. The product
@@ -16,6 +16,9 @@ Sources (page title, then section):
   update of M, the update of z, and the additive (linear) variant.
 * same page, section "Why is the memory footprint bounded?": segments of fixed
   length N, with the state (M, z) carried and nothing else.
+* same page, section "How is an Infini-attention model trained?": gradients
+  flow through the memory recurrence as in truncated backpropagation through
+  time (the backward pass; one call is the truncation window).
 * "Hugging Face Infini-Attention Reproduction Analysis", section
   "Infini-Attention Mechanism", steps 1-6: the per-segment order (segment,
   local attention, retrieval from M_{s-1}, gate, update, carry only the
@@ -44,6 +47,11 @@ Pins (each function is checked against something other than itself in
   ``forward`` on it (every output row, and the state at every segment end);
   the first token of a segment attends to itself alone (closed form); the
   state is unchanged inside a segment.
+* ``backward`` (oracle/backward.py) -- every gradient (Q, K, V, beta, M0,
+  z0) against central finite differences of ``forward``, both rules, ragged,
+  grouped and one-token segments; five planted mistakes (a dropped carry, a
+  dropped term, a wrong derivative) fail that check
+  (``tests/test_oracle_backward.py``).
 
 No function here is "parity unpinned".
 """
@@ -59,4 +67,5 @@ from .infini_attention import (  # noqa: F401
     forward,
     decode_step,
 )
+from .backward import backward  # noqa: F401
 from .compare import max_rel_err, slice_errors  # noqa: F401
