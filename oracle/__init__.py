@@ -47,7 +47,7 @@ Pins (each function is checked against something other than itself in
   ``forward`` on it (every output row, and the state at every segment end);
   the first token of a segment attends to itself alone (closed form); the
   state is unchanged inside a segment.
-* ``backward`` (oracle/backward.py) -- every gradient (Q, K, V, beta, M0,
+* ``backward`` (oracle/gradients.py) -- every gradient (Q, K, V, beta, M0,
   z0) against central finite differences of ``forward``, both rules, ragged,
   grouped and one-token segments; five planted mistakes (a dropped carry, a
   dropped term, a wrong derivative) fail that check
@@ -67,5 +67,5 @@ from .infini_attention import (  # noqa: F401
     forward,
     decode_step,
 )
-from .backward import backward  # noqa: F401
+from .gradients import backward  # noqa: F401
 from .compare import max_rel_err, slice_errors  # noqa: F401

@@ -1,4 +1,4 @@
-"""Pins of the oracle's backward pass (oracle/backward.py).
+"""Pins of the oracle's backward pass (oracle/gradients.py).
 
 The gradients are checked against central finite differences of the oracle
 forward, a definition independent of the chain-rule derivation: for a scalar
@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import backward as bw
+from oracle import gradients as bw
 
 CASES = [
     # B, Hq, Hkv, L, d, seg_len
