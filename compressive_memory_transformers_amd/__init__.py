@@ -1,4 +1,4 @@
-"""Infini-attention block forward on AMD Instinct MI355X (gfx950).
+"""Infini-attention block on AMD Instinct MI355X (gfx950): forward, decode step, backward.
 
 The computation lives in libinfini_attn.so (hand-written HIP kernels behind
 the C ABI of include/infini_attn.h); this package is its thin Python binding.
@@ -9,9 +9,12 @@ from .binding import (  # noqa: F401
     DTYPES,
     RULES,
     InfiniAttnError,
+    backward,
+    backward_workspace_size,
     decode_step,
     decode_workspace_size,
     forward,
+    forward_train,
     load_library,
     status_string,
     version,

@@ -31,6 +31,12 @@ SIGNATURES = {
     "infini_attn_forward_timed": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
+    "infini_attn_forward_train": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 10 + [_c_p, _c_size, _c_p]),
+    "infini_attn_backward_workspace_size": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_backward": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 17 + [_c_p, _c_size, _c_p]),
     "infini_attn_decode_workspace_size": (
         _c_i32, [_c_i64] * 5 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_decode_step": (
@@ -94,7 +100,7 @@ def _ptr(t):
 
 
 def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_final=None,
-            workspace=None, stream=None, events=None):
+            workspace=None, stream=None, events=None, lse=None):
     """Infini-attention block forward on the GPU.
 
     q [B,Hq,L,d], k and v [B,Hkv,L,d] (float32 or bfloat16, contiguous, on one
@@ -104,7 +110,8 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     ``stream`` (a torch.cuda.Stream) or torch's current stream, asynchronously.
     ``events``: optional list of torch.cuda.Event to record around each phase
     (see infini_attn_forward_timed); each must have been recorded once so that
-    its HIP event exists.
+    its HIP event exists. ``lse``: a float32 [B,Hq,L] tensor to receive the
+    softmax statistics (infini_attn_forward_train); not with ``events``.
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -148,7 +155,15 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
             _ptr(out), _ptr(M_final), _ptr(z_final),
             _ptr(workspace), workspace.numel() * workspace.element_size(),
             ctypes.c_void_p(stream.cuda_stream)]
-    if events:
+    if lse is not None:
+        if events:
+            raise ValueError("lse and events cannot be combined")
+        if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                or lse.device != dev:
+            raise ValueError("lse must be a contiguous float32 [B,Hq,L] tensor on the GPU of q")
+        st = lib.infini_attn_forward_train(*args[:17], _ptr(lse), *args[17:])
+        name = "infini_attn_forward_train"
+    elif events:
         handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
         st = lib.infini_attn_forward_timed(*args, handles, len(events))
         name = "infini_attn_forward_timed"
@@ -222,3 +237,78 @@ def decode_step(q, k, v, beta, k_cache, v_cache, M, z, pos, rule, *, out=None, w
     if st != 0:
         raise InfiniAttnError(st, "infini_attn_decode_step")
     return out
+
+
+def forward_train(q, k, v, beta, M0, z0, seg_len, rule, **kw):
+    """forward() that also returns the softmax statistics the backward pass
+    needs: (out, M_final, z_final, lse) with lse [B,Hq,L] float32."""
+    B, Hq, L, _ = q.shape
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=q.device)
+    out, M_final, z_final = forward(q, k, v, beta, M0, z0, seg_len, rule, lse=lse, **kw)
+    return out, M_final, z_final, lse
+
+
+def backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, dtype):
+    """Workspace bytes of a backward call with these sizes."""
+    n = _c_size(0)
+    st = load_library().infini_attn_backward_workspace_size(B, Hq, Hkv, L, d, seg_len, RULES[rule],
+                                                            DTYPES[dtype], ctypes.byref(n))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_backward_workspace_size")
+    return int(n.value)
+
+
+def backward(q, k, v, beta, M0, z0, seg_len, rule, out, lse, d_out, dM_final=None,
+             dz_final=None, *, workspace=None, stream=None):
+    """Gradients of the block (infini_attn_backward).
+
+    The forward's inputs, its out and lse (forward_train), and the gradients
+    d_out (like out), dM_final (like M0) and dz_final (like z0; either may be
+    None for zero). Returns (dq, dk, dv, dbeta, dM0, dz0). Asynchronous on
+    ``stream`` (or torch's current stream).
+    """
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if not (k.shape == v.shape == (B, Hkv, L, d)):
+        raise ValueError("k and v must be [B,Hkv,L,d]")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+        raise ValueError("beta, M0 or z0 has the wrong shape")
+    if out.shape != q.shape or d_out.shape != q.shape or lse.shape != (B, Hq, L):
+        raise ValueError("out and d_out must be like q, lse [B,Hq,L]")
+    if q.dtype not in DTYPES or any(t.dtype != q.dtype for t in (k, v, out, d_out)):
+        raise TypeError("q, k, v, out and d_out must share one dtype, float32 or bfloat16")
+    f32 = [beta, M0, z0, lse] + [t for t in (dM_final, dz_final) if t is not None]
+    if any(t.dtype != torch.float32 for t in f32):
+        raise TypeError("beta, M0, z0, lse, dM_final and dz_final must be float32")
+    if dM_final is not None and dM_final.shape != M0.shape:
+        raise ValueError("dM_final must be like M0")
+    if dz_final is not None and dz_final.shape != z0.shape:
+        raise ValueError("dz_final must be like z0")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    for t in [q, k, v, out, d_out] + f32:
+        if t.device != dev:
+            raise ValueError("all tensors must be on one GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbeta, dM0, dz0 = torch.empty_like(beta), torch.empty_like(M0), torch.empty_like(z0)
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, q.dtype),
+                                dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    opt = lambda t: _ptr(t) if t is not None else ctypes.c_void_p(0)
+    st = load_library().infini_attn_backward(
+        B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[q.dtype],
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+        _ptr(out), _ptr(lse), _ptr(d_out), opt(dM_final), opt(dz_final),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_backward")
+    return dq, dk, dv, dbeta, dM0, dz0

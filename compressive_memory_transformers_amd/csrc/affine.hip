@@ -412,6 +412,11 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
 }
 
 // ---- 4. M_s = M_{s-1} + B_s + A_s M_{s-1}, per 32-column slab ---------------
+//
+// With a.reverse the same step runs over the segments last to first. The
+// backward pass uses it for the gradient of the state: A_s is symmetric
+// (-Phi^T diag(1/den) Phi), so dM_{s-1} = dM_s + A_s dM_s + C_s has this form
+// with B_s = C_s, and the snapshot written before step s is dM_s.
 
 template <typename T, int D, int RULE>
 __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
@@ -431,7 +436,8 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = Min[(32 * w + acc_row(r, h)) * D + col0 + i];
 
-  for (int sl = 0; sl < a.s_count; ++sl) {
+  for (int it = 0; it < a.s_count; ++it) {
+    const int sl = a.reverse ? a.s_count - 1 - it : it;
     const int64_t seg = (int64_t)unit * a.s_count + sl;
     // issue this segment's loads first; they are independent of M
     float bv[16];
@@ -501,7 +507,30 @@ hipError_t launch_affine_d(int d, int rule, const AffineArgs& a, hipStream_t str
   }
 }
 
+template <typename T>
+hipError_t launch_chain_d(int d, int rule, const AffineArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.units * (d / 32))), block(d / 32 * 64);
+#define INFINI_CHAIN(D)                                                                  \
+  if (rule == kRuleDelta)                                                                \
+    hipLaunchKernelGGL((chain_kernel<T, D, kRuleDelta>), grid, block, 0, stream, a);     \
+  else                                                                                   \
+    hipLaunchKernelGGL((chain_kernel<T, D, kRuleLinear>), grid, block, 0, stream, a);
+  switch (d) {
+    case 32: INFINI_CHAIN(32) break;
+    case 64: INFINI_CHAIN(64) break;
+    case 128: INFINI_CHAIN(128) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef INFINI_CHAIN
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {
+  return dtype == kBF16 ? launch_chain_d<bf16>(d, rule, a, stream)
+                        : launch_chain_d<float>(d, rule, a, stream);
+}
 
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {
   return dtype == kBF16 ? launch_affine_d<bf16>(d, rule, a, stream)

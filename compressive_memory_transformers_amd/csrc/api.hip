@@ -169,6 +169,7 @@ hipError_t launch_recurrence(const Plan& p, const Carved& cw, int32_t rule, int3
     fa.units = (int32_t)p.units;
     fa.s_begin = (int32_t)s_begin;
     fa.s_count = (int32_t)s_count;
+    fa.reverse = 0;
     return infini::launch_affine(dtype, (int)p.d, rule, fa, s);
   }
   ScanArgs sa;
@@ -212,7 +213,7 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
                              int64_t seg_len, int32_t rule, int32_t dtype, const void* q,
                              const void* k, const void* v, const float* beta, const float* M0,
                              const float* z0, void* out, float* M_final, float* z_final,
-                             void* workspace, size_t workspace_bytes, void* stream,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream,
                              void* const* events, int32_t n_events) {
   Plan p;
   infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
@@ -247,6 +248,15 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
       overlap(workspace, workspace_bytes, M_final, nM) ||
       overlap(workspace, workspace_bytes, z_final, nz))
     return INFINI_ERR_INVALID_ARG;
+  if (lse != nullptr) {  // written: overlaps no other argument
+    if (!aligned16(lse)) return INFINI_ERR_MISALIGNED;
+    const size_t nl = (size_t)(B * Hq * L) * 4;
+    for (const Range& r : inputs)
+      if (overlap(lse, nl, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+    if (overlap(lse, nl, out, nq) || overlap(lse, nl, M_final, nM) ||
+        overlap(lse, nl, z_final, nz) || overlap(lse, nl, workspace, workspace_bytes))
+      return INFINI_ERR_INVALID_ARG;
+  }
 
   if (workspace_bytes < p.fixed + p.per_seg) return INFINI_ERR_WORKSPACE;
   int64_t W = (int64_t)((workspace_bytes - p.fixed) / p.per_seg);
@@ -308,6 +318,7 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     aa.snapM = snapM;
     aa.snapZ = snapZ;
     aa.out = out;
+    aa.lse = lse;
     aa.L = L;
     aa.seg_len = seg_len;
     aa.Hq = (int32_t)Hq;
@@ -336,7 +347,19 @@ infini_status_t infini_attn_forward(int64_t B, int64_t Hq, int64_t Hkv, int64_t 
                                     void* out, float* M_final, float* z_final,
                                     void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
-                      M_final, z_final, workspace, workspace_bytes, stream, nullptr, 0);
+                      M_final, z_final, nullptr, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+infini_status_t infini_attn_forward_train(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                          int64_t d, int64_t seg_len, int32_t rule,
+                                          int32_t dtype, const void* q, const void* k,
+                                          const void* v, const float* beta, const float* M0,
+                                          const float* z0, void* out, float* M_final,
+                                          float* z_final, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (lse == nullptr) return INFINI_ERR_INVALID_ARG;
+  return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
+                      M_final, z_final, lse, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 infini_status_t infini_attn_forward_timed(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
@@ -348,7 +371,8 @@ infini_status_t infini_attn_forward_timed(int64_t B, int64_t Hq, int64_t Hkv, in
                                           size_t workspace_bytes, void* stream,
                                           void* const* events, int32_t n_events) {
   return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
-                      M_final, z_final, workspace, workspace_bytes, stream, events, n_events);
+                      M_final, z_final, nullptr, workspace, workspace_bytes, stream, events,
+                      n_events);
 }
 
 // ---- streaming decode --------------------------------------------------------
@@ -468,6 +492,357 @@ infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int6
                           1, s) != hipSuccess)
       return INFINI_ERR_HIP;
   }
+  return INFINI_OK;
+}
+
+}  // extern "C"
+
+// ---- backward pass -------------------------------------------------------------
+//
+// Plan (kernels in bwd.hip, affine.hip): one window, the whole call.
+//   1. the forward recurrence in affine form, for the states before each
+//      segment (snapshots) and, with the delta rule, each segment's A_s;
+//   2. retrieval: nm = sigma(Q) M_{s-1} (product), the row step (delta, dg,
+//      dn, dden), nm = dn M_{s-1}^T (product), the retrieval part of dQ;
+//      C_s = sum over the group's heads of sigma(Q)^T dn (products), and the
+//      retrieval part of dL/dz_{s-1};
+//   3. dM_s for every segment by the chain run backwards from dM_final,
+//      dM_{s-1} = dM_s + A_s dM_s + C_s (A_s = 0 with the linear rule); dM0.
+//      In float for every element type, with A_s formed in float: with a
+//      small z_{s-1} the transition has large entries and would amplify bf16
+//      rounding into dM0;
+//   4. local attention: dK, dV (stored in float) and dQ;
+//   5. update: Phi dM_s, the delta rule's Phi M_{s-1} and row step, then
+//      dPhi = (U or V) dM_s^T (+ dP M_{s-1}^T) (products);
+//   6. dz recurrence backwards from dz_final, the final dK, dV, and dbeta.
+
+namespace {
+
+struct BwdLayout {
+  size_t total;
+  size_t stM, stz, zeroM, snapM, snapZ, colsum, Bmat, Amat, dMsnap, e_ret, e_upd, dzs;
+  size_t nm, dn, delta, dg, dden, dk_acc, dv_acc, du_buf, dphi, p_buf, u_el, dp_el, dc;
+  size_t Amat_f, dMsnap_f, phi_f, phic_f;
+};
+
+BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int32_t rule) {
+  BwdLayout b{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = cur;
+    cur += align_up(bytes);
+    return r;
+  };
+  const size_t d = (size_t)p.d, e = (size_t)p.e, units = (size_t)p.units, S = (size_t)p.S;
+  const size_t qrows = (size_t)(B * Hq * L), krows = (size_t)(B * Hkv * L);
+  const bool delta = rule == INFINI_RULE_DELTA;
+  b.stM = take(units * d * d * 4);
+  b.stz = take(units * d * 4);
+  b.zeroM = take(units * d * d * 4);
+  b.snapM = take(units * S * d * d * e);
+  b.snapZ = take(units * S * d * 4);
+  b.colsum = take(units * S * d * 4);
+  b.Bmat = take(units * S * d * d * 4);
+  b.Amat = delta ? take(units * S * d * d * e) : 0;
+  b.dMsnap = take(units * S * d * d * e);
+  b.dMsnap_f = take(units * S * d * d * 4);
+  b.Amat_f = delta ? take(units * S * d * d * 4) : 0;
+  b.e_ret = take(units * S * d * 4);
+  b.e_upd = take(units * S * d * 4);
+  b.dzs = take(units * S * d * 4);
+  b.nm = take(qrows * d * 4);
+  b.dn = take(qrows * d * e);
+  b.delta = take(qrows * 4);
+  b.dg = take(qrows * 4);
+  b.dden = take(qrows * 4);
+  b.dk_acc = take(krows * d * 4);
+  b.dv_acc = take(krows * d * 4);
+  b.du_buf = take(krows * d * 4);
+  b.dphi = take(krows * d * 4);
+  if (delta) {
+    b.p_buf = take(krows * d * 4);
+    b.u_el = take(krows * d * e);
+    b.dp_el = take(krows * d * e);
+    b.dc = take(krows * 4);
+    b.phi_f = take(krows * d * 4);
+    b.phic_f = take(krows * d * 4);
+  }
+  b.total = cur + kAlign;  // slack for an unaligned base
+  return b;
+}
+
+// A product over the (hi, lo) batches: hi = B * heads rows of a [.][L][d]
+// tensor, lo = the segment. Defaults: no transposes, alpha 1, overwrite.
+infini::GemmArgs gemm_args(const void* A, const void* B, float* C, int32_t M, int32_t N,
+                           int32_t K, int64_t hi_count, int64_t S, int64_t L, int64_t seg_len) {
+  infini::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.alpha = 1.f;
+  g.batches = (int32_t)(hi_count * S);
+  g.S = (int32_t)S;
+  g.a_div = g.b_div = g.c_div = 1;
+  g.L = L;
+  g.seg_len = seg_len;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_backward_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                                    int64_t d, int64_t seg_len, int32_t rule,
+                                                    int32_t dtype, size_t* bytes) {
+  Plan p;
+  const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, rule).total;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
+                                     int64_t seg_len, int32_t rule, int32_t dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const float* beta, const float* M0, const float* z0,
+                                     const void* out, const float* lse, const void* d_out,
+                                     const float* dM_final, const float* dz_final, void* dq,
+                                     void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  const void* required[] = {q, k, v, beta, M0, z0, out, lse, d_out, dq, dk, dv, dbeta, dM0, dz0,
+                            workspace};
+  for (const void* ptr : required)
+    if (ptr == nullptr) return INFINI_ERR_INVALID_ARG;
+  for (const void* ptr : required)
+    if (!aligned16(ptr)) return INFINI_ERR_MISALIGNED;
+  if ((dM_final && !aligned16(dM_final)) || (dz_final && !aligned16(dz_final)))
+    return INFINI_ERR_MISALIGNED;
+  const size_t e = (size_t)p.e;
+  const size_t nq = (size_t)(B * Hq * L * d) * e, nkv = (size_t)(B * Hkv * L * d) * e;
+  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  const size_t nrow = (size_t)(B * Hq * L) * 4, nbeta = (size_t)Hq * 4;
+  const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, rule);
+  if (workspace_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  struct Range { const void* p; size_t n; };
+  const Range all[] = {{q, nq},         {k, nkv},         {v, nkv},      {beta, nbeta},
+                       {M0, nM},        {z0, nz},         {out, nq},     {lse, nrow},
+                       {d_out, nq},     {dM_final, nM},   {dz_final, nz}, {dq, nq},
+                       {dk, nkv},       {dv, nkv},        {dbeta, nbeta}, {dM0, nM},
+                       {dz0, nz},       {workspace, workspace_bytes}};
+  // the outputs and the workspace (from entry 11 on) overlap no other argument
+  const int n_all = (int)(sizeof(all) / sizeof(all[0]));
+  for (int x = 11; x < n_all; ++x)
+    for (int y = 0; y < n_all; ++y)
+      if (x != y && all[y].p != nullptr && overlap(all[x].p, all[x].n, all[y].p, all[y].n))
+        return INFINI_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(align_up((size_t)(uintptr_t)workspace) -
+                                     (size_t)(uintptr_t)workspace + static_cast<char*>(workspace));
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto E = [&](size_t off) { return static_cast<void*>(ws + off); };
+  const int64_t S = p.S, units = p.units, G = Hq / Hkv;
+  const int32_t D = (int32_t)d;
+  const int32_t N = (int32_t)(seg_len < L ? seg_len : L);  // rows of the longest segment
+
+  // 1. states before each segment (and A_s)
+  AffineArgs fa{};
+  fa.k = k;
+  fa.v = v;
+  fa.M_in = M0;
+  fa.z_in = z0;
+  fa.M_out = F(lay.stM);
+  fa.z_out = F(lay.stz);
+  fa.snapM = E(lay.snapM);
+  fa.snapZ = F(lay.snapZ);
+  fa.colsum = F(lay.colsum);
+  fa.Amat = rule == INFINI_RULE_DELTA ? E(lay.Amat) : nullptr;
+  fa.Bmat = F(lay.Bmat);
+  fa.L = L;
+  fa.seg_len = seg_len;
+  fa.units = (int32_t)units;
+  fa.s_begin = 0;
+  fa.s_count = (int32_t)S;
+  fa.reverse = 0;
+  if (infini::launch_affine(dtype, D, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
+
+  infini::BwdArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.beta = beta;
+  ba.out = out;
+  ba.lse = lse;
+  ba.dout = d_out;
+  ba.snapM = E(lay.snapM);
+  ba.snapZ = F(lay.snapZ);
+  ba.nm = F(lay.nm);
+  ba.dn = E(lay.dn);
+  ba.delta = F(lay.delta);
+  ba.dg = F(lay.dg);
+  ba.dden = F(lay.dden);
+  ba.dk_acc = F(lay.dk_acc);
+  ba.dv_acc = F(lay.dv_acc);
+  ba.p_buf = rule == INFINI_RULE_DELTA ? F(lay.p_buf) : nullptr;
+  ba.du_buf = F(lay.du_buf);
+  ba.dphi = F(lay.dphi);
+  ba.u_el = rule == INFINI_RULE_DELTA ? E(lay.u_el) : nullptr;
+  ba.dp_el = rule == INFINI_RULE_DELTA ? E(lay.dp_el) : nullptr;
+  ba.dc = rule == INFINI_RULE_DELTA ? F(lay.dc) : nullptr;
+  ba.phi_f = rule == INFINI_RULE_DELTA ? F(lay.phi_f) : nullptr;
+  ba.phic_f = rule == INFINI_RULE_DELTA ? F(lay.phic_f) : nullptr;
+  ba.e_ret = F(lay.e_ret);
+  ba.e_upd = F(lay.e_upd);
+  ba.dzs = F(lay.dzs);
+  ba.dz_final = dz_final;
+  ba.dz0 = dz0;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dbeta = dbeta;
+  ba.L = L;
+  ba.seg_len = seg_len;
+  ba.B = (int32_t)B;
+  ba.Hq = (int32_t)Hq;
+  ba.Hkv = (int32_t)Hkv;
+  ba.S = (int32_t)S;
+  ba.rule = rule;
+  ba.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+
+  const int64_t LD = L * d, ND = seg_len * d, DD = d * d;
+  // 2. retrieval. Query-side products: hi = b * Hq + h, M_{s-1} of unit hi / G.
+  {
+    infini::GemmArgs g = gemm_args(q, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
+    g.lda = g.ldb = g.ldc = D;
+    g.a_hi = g.c_hi = LD;
+    g.a_lo = g.c_lo = ND;
+    g.b_div = (int32_t)G;
+    g.b_hi = S * DD;
+    g.b_lo = DD;
+    g.tb = 1;  // op(B) = M, stored as M^T
+    g.a_sigma = 1;
+    g.clip = 1;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (infini::launch_bwd_retrieval_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  {
+    infini::GemmArgs g = gemm_args(ba.dn, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
+    g.lda = g.ldb = g.ldc = D;
+    g.a_hi = g.c_hi = LD;
+    g.a_lo = g.c_lo = ND;
+    g.b_div = (int32_t)G;
+    g.b_hi = S * DD;
+    g.b_lo = DD;
+    g.tb = 0;  // op(B) = M^T as stored
+    g.clip = 1;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (infini::launch_bwd_retrieval_dq(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
+    const size_t off = (size_t)(hg * LD) * e;
+    infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + off,
+                                   static_cast<const char*>(E(lay.dn)) + off, F(lay.Bmat), D, D,
+                                   (int32_t)seg_len, units, S, L, seg_len);
+    g.lda = g.ldb = g.ldc = D;
+    g.a_hi = g.b_hi = G * LD;
+    g.a_lo = g.b_lo = ND;
+    g.c_hi = S * DD;
+    g.c_lo = DD;
+    g.ta = 1;  // op(A) = sigma(Q)^T
+    g.a_sigma = 1;
+    g.clip = 2;
+    g.accumulate = hg > 0;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (infini::launch_bwd_row_weighted_sum(dtype, D, ba, true, s) != hipSuccess)
+    return INFINI_ERR_HIP;
+
+  // 3. dM_s for every segment, and dM0, in float. A_s = -Phi^T diag(1/c) Phi
+  // from float sigma(K) and sigma(K) / c.
+  if (rule == INFINI_RULE_DELTA) {
+    if (infini::launch_bwd_phi_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+    infini::GemmArgs g = gemm_args(ba.phi_f, ba.phic_f, F(lay.Amat_f), D, D, (int32_t)seg_len,
+                                   units, S, L, seg_len);
+    g.lda = g.ldb = g.ldc = D;
+    g.a_hi = g.b_hi = LD;
+    g.a_lo = g.b_lo = ND;
+    g.c_hi = S * DD;
+    g.c_lo = DD;
+    g.ta = 1;  // op(A) = Phi^T
+    g.alpha = -1.f;
+    g.clip = 2;
+    if (infini::launch_gemm(INFINI_F32, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  const float* dM_in = dM_final;
+  if (dM_in == nullptr) {
+    if (infini::launch_fill_f32(F(lay.zeroM), 0.f, units * d * d, s) != hipSuccess)
+      return INFINI_ERR_HIP;
+    dM_in = F(lay.zeroM);
+  }
+  AffineArgs ra = fa;
+  ra.M_in = dM_in;
+  ra.M_out = dM0;
+  ra.snapM = F(lay.dMsnap_f);
+  ra.Amat = rule == INFINI_RULE_DELTA ? F(lay.Amat_f) : nullptr;
+  ra.reverse = 1;
+  if (infini::launch_chain(INFINI_F32, D, rule, ra, s) != hipSuccess) return INFINI_ERR_HIP;
+  // dM_s^T in the element type for the update's products
+  if (infini::launch_round_f32(dtype, E(lay.dMsnap), F(lay.dMsnap_f), units * S * d * d, s) !=
+      hipSuccess)
+    return INFINI_ERR_HIP;
+
+  // 4. local attention
+  if (infini::launch_bwd_attention(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+
+  // 5. update. Key-side products: hi = unit.
+  auto kside = [&](const void* A, const void* Bm, float* C) {
+    infini::GemmArgs g = gemm_args(A, Bm, C, N, D, D, units, S, L, seg_len);
+    g.lda = g.ldb = g.ldc = D;
+    g.a_hi = g.c_hi = LD;
+    g.a_lo = g.c_lo = ND;
+    g.b_hi = S * DD;
+    g.b_lo = DD;
+    g.clip = 1;
+    return g;
+  };
+  {
+    infini::GemmArgs g = kside(k, E(lay.dMsnap), ba.du_buf);  // Phi dM_s (dM_s^T stored)
+    g.tb = 1;
+    g.a_sigma = 1;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (rule == INFINI_RULE_DELTA) {
+    infini::GemmArgs g = kside(k, E(lay.snapM), ba.p_buf);  // Phi M_{s-1}
+    g.tb = 1;
+    g.a_sigma = 1;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (infini::launch_bwd_update_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  {
+    infini::GemmArgs g = kside(rule == INFINI_RULE_DELTA ? ba.u_el : v, E(lay.dMsnap), ba.dphi);
+    g.tb = 0;  // op(B) = dM_s^T as stored
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
+  if (rule == INFINI_RULE_DELTA) {
+    infini::GemmArgs g = kside(ba.dp_el, E(lay.snapM), ba.dphi);  // + dP M_{s-1}^T
+    g.tb = 0;
+    g.accumulate = 1;
+    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    if (infini::launch_bwd_row_weighted_sum(dtype, D, ba, false, s) != hipSuccess)
+      return INFINI_ERR_HIP;
+  }
+
+  // 6. dz, dK, dV, dbeta
+  if (infini::launch_bwd_finish(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   return INFINI_OK;
 }
 

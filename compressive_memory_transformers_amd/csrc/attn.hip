@@ -273,6 +273,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   if (!wave_on) return;  // no barrier follows
 
   const float l = l_run + __shfl_xor(l_run, 32);
+  if (a.lse != nullptr && h == 0 && row < n_s)
+    a.lse[qh * a.L + seg_start + row] = m_run * c + __log2f(l);
   const int64_t snap = (int64_t)unit * a.s_count + sl;
   const float* zs = a.snapZ + snap * D;
   const T* Mts = static_cast<const T*>(a.snapM) + snap * D * D;
@@ -614,6 +616,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   const bf16* Mb = pl ? Vs[0] : Vs[1];
   float l = st.l0 + st.l1;
   l += __shfl_xor(l, 32);
+  if (a.lse != nullptr && h == 0 && row < n_s)
+    a.lse[qh * a.L + seg_start + row] = st.m_run * c + __log2f(l);
   float sq[NC][8];
   float dp = 0.f;
 #pragma unroll

@@ -1,0 +1,600 @@
+// Backward pass of the Infini-attention block: gradients of out, M_final and
+// z_final with respect to Q, K, V, beta, M0 and z0.
+//
+// "Infini-Attention" (AI Wiki), "How is an Infini-attention model trained?":
+// gradients flow through the memory recurrence from segment to segment, as
+// in truncated backpropagation through time; one call is the window. The
+// derivation is the chain rule through each step of the forward ("What
+// happens inside the Infini-attention block?", "How does the compressive
+// memory work?"), in reverse order:
+//
+//   out = g A_mem + (1 - g) A_dot, g = sigmoid(beta_h):
+//     dg = sum dout . (A_mem - A_dot) = sum dout . (A_mem - out) / (1 - g)
+//   A_mem = X M / (X z), X = sigma(Q):
+//     dn = g dout / den, dden = -g (dout . A_mem) / den,
+//     dX = dn M^T + dden z^T, dM_{s-1} += X^T dn, dz_{s-1} += X^T dden
+//   A_dot = softmax(Q K^T / sqrt(d)) V (causal): the usual softmax gradient
+//     with delta_t = dA_dot,t . A_dot,t = dout_t . out_t - g dout_t . A_mem,t
+//   update, Phi = sigma(K): z_s = z_{s-1} + sum Phi_t gives dPhi += dz_s;
+//     linear M_s = M_{s-1} + Phi^T V: dV += Phi dM_s, dPhi += V dM_s^T;
+//     delta  M_s = M_{s-1} + Phi^T U, U = V - P / c, P = Phi M_{s-1},
+//     c = Phi z_{s-1}: dU = Phi dM_s, dV += dU, dP = -dU / c,
+//     dc = (dU . P / c) / c, dPhi += U dM_s^T + dP M_{s-1}^T + dc z_{s-1}^T,
+//     dM_{s-1} += Phi^T dP (= A_s dM_s), dz_{s-1} += Phi^T dc.
+//
+// The host plan (api.hip) strings these together with the batched matrix
+// product below for every d x d product and the kernels here for the
+// row-wise steps, the local attention, the dz recurrence and the outputs.
+// The recurrence of dM runs in float whatever the element type: with a small
+// z_{s-1} the delta rule's transition I + A_s has large entries, and bf16
+// operands there would be amplified into the state gradients.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "lds_tile.hpp"
+
+namespace infini {
+
+namespace {
+
+// sigma'(x): 1 above zero, e^x at or below (continuous at 0).
+__device__ __forceinline__ float feature_map_grad(float x) {
+  return x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+__device__ __forceinline__ float gate_of(const float* beta, int h) {
+  return 1.f / (1.f + __expf(-beta[h]));
+}
+
+// ---- batched matrix product ---------------------------------------------------
+//
+// 64 x 64 tile of C per workgroup (four waves of 32 x 32), K in steps of 32.
+// op(A) is staged as [m][k], op(B) as [n][k], both with k contiguous, so that
+// each MFMA operand is one 16-byte (bf16) or 32-byte (float) LDS read; a
+// transposed operand is transposed while it is stored.
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  constexpr int TM = 64, TN = 64, TK = 32, LS = TK + pad16<T>();
+  __shared__ __align__(16) T As[TM * LS];
+  __shared__ __align__(16) T Bs[TN * LS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int ntn = (g.N + TN - 1) / TN;
+  const int64_t n_tiles_m = (g.M + TM - 1) / TM;
+  const int64_t per_batch = n_tiles_m * ntn;
+  const int64_t x = blockIdx.x;
+  const int batch = (int)(x / per_batch);
+  const int tile = (int)(x % per_batch);
+  const int m0 = (tile / ntn) * TM, n0 = (tile % ntn) * TN;
+  const int hi = batch / g.S, lo = batch % g.S;
+  int Mv = g.M, Kv = g.K;
+  if (g.clip != 0) {
+    const int64_t rows = min<int64_t>(g.seg_len, g.L - (int64_t)lo * g.seg_len);
+    if (g.clip == 1) Mv = (int)min<int64_t>(Mv, rows); else Kv = (int)min<int64_t>(Kv, rows);
+  }
+  if (m0 >= Mv) return;  // uniform
+  const T* A = static_cast<const T*>(g.A) + (int64_t)(hi / g.a_div) * g.a_hi + (int64_t)lo * g.a_lo;
+  const T* B = static_cast<const T*>(g.B) + (int64_t)(hi / g.b_div) * g.b_hi + (int64_t)lo * g.b_lo;
+  float* C = g.C + (int64_t)(hi / g.c_div) * g.c_hi + (int64_t)lo * g.c_lo;
+
+  const int wm = w >> 1, wn = w & 1;
+  f32x16 acc = zero16();
+  for (int k0 = 0; k0 < Kv; k0 += TK) {
+    {  // A -> As[m][k]
+      frag_t<T> val = zero_frag<T>();
+      if (!g.ta) {
+        const int r = tid >> 2, kc = (tid & 3) * 8;
+        if (m0 + r < Mv && k0 + kc < Kv) val = load8<T>(A + (int64_t)(m0 + r) * g.lda + k0 + kc);
+        if (g.a_sigma)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] = from_f32<T>(feature_map(to_f32<T>(val[e])));
+        store8<T>(As + r * LS + kc, val);
+      } else {
+        const int kr = tid >> 3, mc = (tid & 7) * 8;
+        if (k0 + kr < Kv && m0 + mc < Mv) val = load8<T>(A + (int64_t)(k0 + kr) * g.lda + m0 + mc);
+        if (g.a_sigma && k0 + kr < Kv)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] = from_f32<T>(feature_map(to_f32<T>(val[e])));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) As[(mc + e) * LS + kr] = val[e];
+      }
+    }
+    {  // B -> Bs[n][k]
+      frag_t<T> val = zero_frag<T>();
+      if (g.tb) {
+        const int r = tid >> 2, kc = (tid & 3) * 8;
+        if (n0 + r < g.N && k0 + kc < Kv) val = load8<T>(B + (int64_t)(n0 + r) * g.ldb + k0 + kc);
+        store8<T>(Bs + r * LS + kc, val);
+      } else {
+        const int kr = tid >> 3, nc = (tid & 7) * 8;
+        if (k0 + kr < Kv && n0 + nc < g.N) val = load8<T>(B + (int64_t)(k0 + kr) * g.ldb + n0 + nc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bs[(nc + e) * LS + kr] = val[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 16)
+      mma32(acc, load8<T>(As + (32 * wm + i) * LS + kk + 8 * h),
+            load8<T>(Bs + (32 * wn + i) * LS + kk + 8 * h));
+    __syncthreads();
+  }
+  const int n = n0 + 32 * wn + i;
+  if (n >= g.N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 32 * wm + acc_row(r, h);
+    if (m < Mv) {
+      float* c = C + (int64_t)m * g.ldc + n;
+      *c = g.alpha * acc[r] + (g.accumulate ? *c : 0.f);
+    }
+  }
+}
+
+// ---- row steps (one wave per row, lane l holds elements l, l + 64) -----------
+
+template <int D> struct RowLanes {
+  static constexpr int E = (D + 63) / 64;
+  __device__ static bool ok(int lane, int e) { return 64 * e + lane < D; }
+};
+
+// Retrieval backward, per query row: with nm = sigma(q) M_{s-1} (the
+// numerator of A_mem), writes delta, dg, dden and dn (element type).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
+  using R = RowLanes<D>;
+  const int lane = threadIdx.x & 63;
+  const int G = a.Hq / a.Hkv;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.L;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t bh = row / a.L, t = row % a.L;
+    const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const int s = (int)(t / a.seg_len);
+    const int64_t unit = (int64_t)b * a.Hkv + hq / G;
+    const float* z = a.snapZ + (unit * a.S + s) * D;
+    const T* q = static_cast<const T*>(a.q) + row * D;
+    const T* o = static_cast<const T*>(a.out) + row * D;
+    const T* dO = static_cast<const T*>(a.dout) + row * D;
+    const float* nm = a.nm + row * D;
+    float den = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e)) den += feature_map(to_f32<T>(q[64 * e + lane])) * z[64 * e + lane];
+    den = wave_sum(den);
+    float am[R::E], dov[R::E];
+    float dam = 0.f, doo = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e) {
+      am[e] = dov[e] = 0.f;
+      if (R::ok(lane, e)) {
+        const int c = 64 * e + lane;
+        am[e] = nm[c] / den;
+        dov[e] = to_f32<T>(dO[c]);
+        dam += dov[e] * am[e];
+        doo += dov[e] * to_f32<T>(o[c]);
+      }
+    }
+    dam = wave_sum(dam);
+    doo = wave_sum(doo);
+    const float g = gate_of(a.beta, hq);
+    T* dn = static_cast<T*>(a.dn) + row * D;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e)) dn[64 * e + lane] = from_f32<T>(g * dov[e] / den);
+    if (lane == 0) {
+      a.delta[row] = doo - g * dam;
+      a.dg[row] = (dam - doo) / (1.f - g);
+      a.dden[row] = -g * dam / den;
+    }
+  }
+}
+
+// nm <- (nm + dden z) * sigma'(q): nm held dn M^T, now the retrieval part of
+// dL/dQ.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void retrieval_dq_kernel(BwdArgs a) {
+  const int G = a.Hq / a.Hkv;
+  const int64_t n = (int64_t)a.B * a.Hq * a.L * D;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
+    const int64_t row = x / D;
+    const int c = (int)(x % D);
+    const int64_t bh = row / a.L, t = row % a.L;
+    const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const int64_t unit = (int64_t)b * a.Hkv + hq / G;
+    const int s = (int)(t / a.seg_len);
+    const float z = a.snapZ[(unit * a.S + s) * D + c];
+    const float qv = to_f32<T>(static_cast<const T*>(a.q)[x]);
+    a.nm[x] = (a.nm[x] + a.dden[row] * z) * feature_map_grad(qv);
+  }
+}
+
+// e[unit][s][c] = sum over the segment's rows t (and the group's query heads
+// when of_q) of w_t sigma(x_t[c]): the retrieval (x = q, w = dden) or the
+// delta rule's (x = k, w = dc) part of dL/dz_{s-1}.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void weighted_sum_kernel(BwdArgs a, int of_q) {
+  const int c = threadIdx.x;
+  const int64_t unit = blockIdx.x / a.S;
+  const int s = blockIdx.x % a.S;
+  const int G = a.Hq / a.Hkv;
+  const int64_t t0 = (int64_t)s * a.seg_len;
+  const int64_t t1 = min<int64_t>(t0 + a.seg_len, a.L);
+  float acc = 0.f;
+  if (of_q) {
+    const int64_t b = unit / a.Hkv, j = unit % a.Hkv;
+    for (int hg = 0; hg < G; ++hg) {
+      const int64_t bh = b * a.Hq + j * G + hg;
+      const T* x = static_cast<const T*>(a.q) + bh * a.L * D;
+      const float* wv = a.dden + bh * a.L;
+      for (int64_t t = t0; t < t1; ++t) acc += wv[t] * feature_map(to_f32<T>(x[t * D + c]));
+    }
+    a.e_ret[(unit * a.S + s) * D + c] = acc;
+  } else {
+    const T* x = static_cast<const T*>(a.k) + unit * a.L * D;
+    const float* wv = a.dc + unit * a.L;
+    for (int64_t t = t0; t < t1; ++t) acc += wv[t] * feature_map(to_f32<T>(x[t * D + c]));
+    a.e_upd[(unit * a.S + s) * D + c] = acc;
+  }
+}
+
+// ---- local attention, one wave per row (small shapes and float) -----------
+//
+// P_tu = exp2(c q_t . k_u - lse_t), c = log2(e) / sqrt(d); dA_dot = (1 - g)
+// dout; dS_tu = P_tu ((1 - g) dout_t . v_u - delta_t);
+// dQ_t = sum_u dS_tu k_u / sqrt(d), dK_u = sum_t dS_tu q_t / sqrt(d),
+// dV_u = sum_t P_tu (1 - g) dout_t.
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_dq_rows_kernel(BwdArgs a) {
+  using R = RowLanes<D>;
+  const int lane = threadIdx.x & 63;
+  const int G = a.Hq / a.Hkv;
+  const float c = a.scale_log2, inv_sqrt_d = a.scale_log2 / kLog2e;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.L;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t bh = row / a.L, t = row % a.L;
+    const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const int64_t unit = (int64_t)b * a.Hkv + hq / G;
+    const int64_t t0 = t / a.seg_len * a.seg_len;
+    const float om = 1.f - gate_of(a.beta, hq);
+    const float lse = a.lse[row], dl = a.delta[row];
+    float qv[R::E], dov[R::E], acc[R::E];
+#pragma unroll
+    for (int e = 0; e < R::E; ++e) {
+      const bool ok = R::ok(lane, e);
+      qv[e] = ok ? to_f32<T>(static_cast<const T*>(a.q)[row * D + 64 * e + lane]) : 0.f;
+      dov[e] = ok ? to_f32<T>(static_cast<const T*>(a.dout)[row * D + 64 * e + lane]) : 0.f;
+      acc[e] = 0.f;
+    }
+    const T* K = static_cast<const T*>(a.k) + unit * a.L * D;
+    const T* V = static_cast<const T*>(a.v) + unit * a.L * D;
+    for (int64_t u = t0; u <= t; ++u) {
+      float kv[R::E], sd = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < R::E; ++e) {
+        const bool ok = R::ok(lane, e);
+        kv[e] = ok ? to_f32<T>(K[u * D + 64 * e + lane]) : 0.f;
+        sd += qv[e] * kv[e];
+        dp += dov[e] * (ok ? to_f32<T>(V[u * D + 64 * e + lane]) : 0.f);
+      }
+      sd = wave_sum(sd);
+      dp = wave_sum(dp);
+      const float p = __builtin_amdgcn_exp2f(c * sd - lse);
+      const float ds = p * (om * dp - dl);
+#pragma unroll
+      for (int e = 0; e < R::E; ++e) acc[e] += ds * kv[e];
+    }
+    T* dq = static_cast<T*>(a.dq) + row * D;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e))
+        dq[64 * e + lane] = from_f32<T>(acc[e] * inv_sqrt_d + a.nm[row * D + 64 * e + lane]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_dkdv_rows_kernel(BwdArgs a) {
+  using R = RowLanes<D>;
+  const int lane = threadIdx.x & 63;
+  const int G = a.Hq / a.Hkv;
+  const float c = a.scale_log2, inv_sqrt_d = a.scale_log2 / kLog2e;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t unit = row / a.L, u = row % a.L;
+    const int64_t b = unit / a.Hkv, j = unit % a.Hkv;
+    const int64_t t1 = min<int64_t>((u / a.seg_len + 1) * a.seg_len, a.L);
+    float kv[R::E], vv[R::E], dk[R::E], dv[R::E];
+#pragma unroll
+    for (int e = 0; e < R::E; ++e) {
+      const bool ok = R::ok(lane, e);
+      kv[e] = ok ? to_f32<T>(static_cast<const T*>(a.k)[row * D + 64 * e + lane]) : 0.f;
+      vv[e] = ok ? to_f32<T>(static_cast<const T*>(a.v)[row * D + 64 * e + lane]) : 0.f;
+      dk[e] = dv[e] = 0.f;
+    }
+    for (int hg = 0; hg < G; ++hg) {
+      const int hq = (int)(j * G + hg);
+      const int64_t bh = b * a.Hq + hq;
+      const float om = 1.f - gate_of(a.beta, hq);
+      const T* Q = static_cast<const T*>(a.q) + bh * a.L * D;
+      const T* dO = static_cast<const T*>(a.dout) + bh * a.L * D;
+      for (int64_t t = u; t < t1; ++t) {
+        float qv[R::E], dov[R::E], sd = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < R::E; ++e) {
+          const bool ok = R::ok(lane, e);
+          qv[e] = ok ? to_f32<T>(Q[t * D + 64 * e + lane]) : 0.f;
+          dov[e] = ok ? to_f32<T>(dO[t * D + 64 * e + lane]) : 0.f;
+          sd += qv[e] * kv[e];
+          dp += dov[e] * vv[e];
+        }
+        sd = wave_sum(sd);
+        dp = wave_sum(dp);
+        const float p = __builtin_amdgcn_exp2f(c * sd - a.lse[bh * a.L + t]);
+        const float ds = p * (om * dp - a.delta[bh * a.L + t]);
+#pragma unroll
+        for (int e = 0; e < R::E; ++e) {
+          dk[e] += ds * qv[e];
+          dv[e] += p * om * dov[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e)) {
+        a.dk_acc[row * D + 64 * e + lane] = dk[e] * inv_sqrt_d;
+        a.dv_acc[row * D + 64 * e + lane] = dv[e];
+      }
+  }
+}
+
+// ---- update backward, per key row ----------------------------------------------
+//
+// Linear: dv_acc += du_buf (= Phi dM_s). Delta, with p_buf = Phi M_{s-1}:
+// c = Phi . z_{s-1}, pred = P / c, U = V - pred (u_el), dU = du_buf,
+// dv_acc += dU, dP = -dU / c (dp_el), dc = (dU . pred) / c.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void update_rows_kernel(BwdArgs a) {
+  using R = RowLanes<D>;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    if (a.rule == kRuleLinear) {
+#pragma unroll
+      for (int e = 0; e < R::E; ++e)
+        if (R::ok(lane, e)) a.dv_acc[row * D + 64 * e + lane] += a.du_buf[row * D + 64 * e + lane];
+      continue;
+    }
+    const int64_t unit = row / a.L, t = row % a.L;
+    const int s = (int)(t / a.seg_len);
+    const float* z = a.snapZ + (unit * a.S + s) * D;
+    float cc = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e))
+        cc += feature_map(to_f32<T>(static_cast<const T*>(a.k)[row * D + 64 * e + lane])) *
+              z[64 * e + lane];
+    cc = wave_sum(cc);
+    float dcs = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e)) {
+        const int64_t x = row * D + 64 * e + lane;
+        const float pred = a.p_buf[x] / cc;
+        const float du = a.du_buf[x];
+        static_cast<T*>(a.u_el)[x] = from_f32<T>(to_f32<T>(static_cast<const T*>(a.v)[x]) - pred);
+        static_cast<T*>(a.dp_el)[x] = from_f32<T>(-du / cc);
+        a.dv_acc[x] += du;
+        dcs += du * pred;
+      }
+    dcs = wave_sum(dcs);
+    if (lane == 0) a.dc[row] = dcs / cc;
+  }
+}
+
+// For A_s = -Phi^T diag(1/c) Phi in float (the state gradient's transition):
+// phi_f = sigma(K) and phic_f = sigma(K) / c, c = sigma(k) . z_{s-1}.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void phi_rows_kernel(BwdArgs a) {
+  using R = RowLanes<D>;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
+       row += (int64_t)gridDim.x * 4) {
+    const int64_t unit = row / a.L, t = row % a.L;
+    const float* z = a.snapZ + (unit * a.S + t / a.seg_len) * D;
+    float ph[R::E], cc = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::E; ++e) {
+      ph[e] = R::ok(lane, e)
+                  ? feature_map(to_f32<T>(static_cast<const T*>(a.k)[row * D + 64 * e + lane]))
+                  : 0.f;
+      if (R::ok(lane, e)) cc += ph[e] * z[64 * e + lane];
+    }
+    cc = wave_sum(cc);
+#pragma unroll
+    for (int e = 0; e < R::E; ++e)
+      if (R::ok(lane, e)) {
+        a.phi_f[row * D + 64 * e + lane] = ph[e];
+        a.phic_f[row * D + 64 * e + lane] = ph[e] / cc;
+      }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void round_kernel(T* dst, const float* src, int64_t n) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256)
+    dst[x] = from_f32<T>(src[x]);
+}
+
+// ---- dz recurrence and outputs ---------------------------------------------------
+
+// dz_s for every segment, last to first: dz_{s-1} = dz_s + e_ret_s + e_upd_s.
+template <int D>
+__global__ __launch_bounds__(D) void dz_scan_kernel(BwdArgs a) {
+  const int c = threadIdx.x;
+  const int64_t unit = blockIdx.x;
+  float dz = a.dz_final ? a.dz_final[unit * D + c] : 0.f;
+  for (int s = a.S - 1; s >= 0; --s) {
+    const int64_t x = (unit * a.S + s) * D + c;
+    a.dzs[x] = dz;
+    dz += a.e_ret[x];
+    if (a.rule == kRuleDelta) dz += a.e_upd[x];
+  }
+  a.dz0[unit * D + c] = dz;
+}
+
+// dK = dk_acc + (dphi + dc z_{s-1} + dz_s) sigma'(k), dV = dv_acc.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void kv_out_kernel(BwdArgs a) {
+  const int64_t n = (int64_t)a.B * a.Hkv * a.L * D;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
+    const int64_t row = x / D;
+    const int c = (int)(x % D);
+    const int64_t unit = row / a.L, t = row % a.L;
+    const int s = (int)(t / a.seg_len);
+    const int64_t sx = (unit * a.S + s) * D + c;
+    float dphi = a.dphi[x] + a.dzs[sx];
+    if (a.rule == kRuleDelta) dphi += a.dc[row] * a.snapZ[sx];
+    const float kv = to_f32<T>(static_cast<const T*>(a.k)[x]);
+    static_cast<T*>(a.dk)[x] = from_f32<T>(a.dk_acc[x] + dphi * feature_map_grad(kv));
+    static_cast<T*>(a.dv)[x] = from_f32<T>(a.dv_acc[x]);
+  }
+}
+
+// dbeta_h = g (1 - g) sum over the batch and the stream of dg.
+__global__ __launch_bounds__(256) void dbeta_kernel(BwdArgs a) {
+  __shared__ float part[256];
+  const int hq = blockIdx.x;
+  float acc = 0.f;
+  for (int b = 0; b < a.B; ++b) {
+    const float* dg = a.dg + ((int64_t)b * a.Hq + hq) * a.L;
+    for (int64_t t = threadIdx.x; t < a.L; t += 256) acc += dg[t];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float g = gate_of(a.beta, hq);
+    a.dbeta[hq] = part[0] * g * (1.f - g);
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* p, float v, int64_t n) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256)
+    p[x] = v;
+}
+
+unsigned row_grid(int64_t rows) {  // 4 rows per workgroup, grid-stride beyond
+  const int64_t n = (rows + 3) / 4;
+  return (unsigned)(n < 65536 ? n : 65536);
+}
+unsigned elem_grid(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return (unsigned)(g < 65536 ? g : 65536);
+}
+
+template <typename T, int D>
+hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
+  const int64_t qrows = (int64_t)a.B * a.Hq * a.L, krows = (int64_t)a.B * a.Hkv * a.L;
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  switch (which) {
+    case 0:
+      hipLaunchKernelGGL((retrieval_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
+      break;
+    case 1:
+      hipLaunchKernelGGL((retrieval_dq_kernel<T, D>), dim3(elem_grid(qrows * D)), dim3(256), 0, s, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((weighted_sum_kernel<T, D>), dim3((unsigned)(units * a.S)), dim3(D), 0, s,
+                         a, arg);
+      break;
+    case 3:
+      hipLaunchKernelGGL((attn_dkdv_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_dq_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((update_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
+      break;
+    case 6:
+      hipLaunchKernelGGL((phi_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
+      break;
+    case 5:
+      hipLaunchKernelGGL((dz_scan_kernel<D>), dim3((unsigned)units), dim3(D), 0, s, a);
+      hipLaunchKernelGGL((kv_out_kernel<T, D>), dim3(elem_grid(krows * D)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((dbeta_kernel), dim3((unsigned)a.Hq), dim3(256), 0, s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(int d, int which, const BwdArgs& a, int arg, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_d<T, 32>(which, a, arg, s);
+    case 64: return launch_d<T, 64>(which, a, arg, s);
+    case 128: return launch_d<T, 128>(which, a, arg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch(int dtype, int d, int which, const BwdArgs& a, int arg, hipStream_t s) {
+  return dtype == kBF16 ? launch_t<bf16>(d, which, a, arg, s) : launch_t<float>(d, which, a, arg, s);
+}
+
+}  // namespace
+
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_kernel, dim3(elem_grid(n)), dim3(256), 0, stream, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64) * g.batches;
+  if (tiles <= 0 || tiles > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((gemm_kernel<bf16>), dim3((unsigned)tiles), dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<float>), dim3((unsigned)tiles), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 0, a, 0, s);
+}
+hipError_t launch_bwd_retrieval_dq(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 1, a, 0, s);
+}
+hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
+                                       hipStream_t s) {
+  return launch(dtype, d, 2, a, of_q ? 1 : 0, s);
+}
+hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 3, a, 0, s);
+}
+hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 4, a, 0, s);
+}
+hipError_t launch_bwd_finish(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 5, a, 0, s);
+}
+hipError_t launch_bwd_phi_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, 6, a, 0, s);
+}
+hipError_t launch_round_f32(int dtype, void* dst, const float* src, int64_t n, hipStream_t s) {
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((round_kernel<bf16>), dim3(elem_grid(n)), dim3(256), 0, s,
+                       static_cast<bf16*>(dst), src, n);
+  else
+    hipLaunchKernelGGL((round_kernel<float>), dim3(elem_grid(n)), dim3(256), 0, s,
+                       static_cast<float*>(dst), src, n);
+  return hipGetLastError();
+}
+
+}  // namespace infini

@@ -47,6 +47,7 @@ struct AffineArgs {
   int64_t L, seg_len;
   int32_t units;
   int32_t s_begin, s_count;
+  int32_t reverse;     // chain only: walk the segments last to first
 };
 
 // Local causal attention of every (batch, query head, segment, query tile)
@@ -59,6 +60,8 @@ struct AttnArgs {
   const void* snapM;   // as ScanArgs::snapM
   const float* snapZ;  // as ScanArgs::snapZ
   void* out;           // [B][Hq][L][d]
+  float* lse;          // [B][Hq][L] or null: per query row, log2 of the softmax
+                       // denominator of the scaled scores, c m + log2(l)
   int64_t L, seg_len;
   int32_t Hq, Hkv;
   int32_t s_begin, s_count;
@@ -87,12 +90,98 @@ struct DecodeArgs {
   float scale_log2;       // log2(e) / sqrt(d)
 };
 
+// ---- backward pass (bwd.hip) ------------------------------------------------
+
+// Batched matrix product C = alpha op(A) op(B) (+ C if accumulate) with float
+// accumulation; A, B in the element type (optionally sigma applied to A as it
+// is read), C float. Batch n = hi * S + lo; each operand's offset is
+// (hi / div) * stride_hi + lo * stride_lo elements. clip = 1 (2): M (K) is
+// the row count of segment lo, min(seg_len, L - lo * seg_len).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  float* C;
+  int32_t M, N, K;
+  int32_t lda, ldb, ldc;  // row strides as stored: A is M x K (K x M if ta),
+                          // B is K x N (N x K if tb), C is M x N
+  int32_t ta, tb, a_sigma, accumulate, clip;
+  float alpha;
+  int32_t batches, S;
+  int32_t a_div, b_div, c_div;
+  int64_t a_hi, a_lo, b_hi, b_lo, c_hi, c_lo;
+  int64_t L, seg_len;
+};
+
+// Everything the backward's elementwise, reduction and attention kernels read.
+// Row tensors are [B][H][L] (query heads for q-side, KV heads for k-side).
+struct BwdArgs {
+  const void* q;       // [B][Hq][L][d]
+  const void* k;       // [B][Hkv][L][d]
+  const void* v;       // [B][Hkv][L][d]
+  const float* beta;   // [Hq]
+  const void* out;     // [B][Hq][L][d] forward output
+  const float* lse;    // [B][Hq][L] from the training forward
+  const void* dout;    // [B][Hq][L][d]
+  const void* snapM;   // [B*Hkv][S][d][d] M_{s-1}^T, element type
+  const float* snapZ;  // [B*Hkv][S][d] z_{s-1}
+  float* nm;           // [B][Hq][L][d] sigma(Q) M_{s-1}, then dL/dQ (retrieval part)
+  void* dn;            // [B][Hq][L][d] g dout / den, element type
+  float* delta;        // [B][Hq][L] dout . out - g dout . A_mem
+  float* dg;           // [B][Hq][L] per-row share of dL/dsigmoid(beta)
+  float* dden;         // [B][Hq][L] dL/d(sigma(q) . z)
+  float* dk_acc;       // [B][Hkv][L][d]
+  float* dv_acc;       // [B][Hkv][L][d]
+  float* p_buf;        // [B][Hkv][L][d] sigma(K) M_{s-1} (delta)
+  float* du_buf;       // [B][Hkv][L][d] sigma(K) dM_s
+  float* dphi;         // [B][Hkv][L][d] dL/dsigma(K) from the update
+  void* u_el;          // [B][Hkv][L][d] V - prediction (delta), element type
+  void* dp_el;         // [B][Hkv][L][d] dL/dP (delta), element type
+  float* dc;           // [B][Hkv][L] dL/dc, c = sigma(k) . z_{s-1} (delta)
+  float* phi_f;        // [B][Hkv][L][d] sigma(K) in float (delta)
+  float* phic_f;       // [B][Hkv][L][d] sigma(K) / c in float (delta)
+  float* e_ret;        // [B*Hkv][S][d] retrieval part of dL/dz_{s-1}
+  float* e_upd;        // [B*Hkv][S][d] update part of dL/dz_{s-1}
+  float* dzs;          // [B*Hkv][S][d] dL/dz_s
+  const float* dz_final;  // [B*Hkv][d] or null
+  float* dz0;          // [B*Hkv][d]
+  void* dq;            // outputs, element type
+  void* dk;
+  void* dv;
+  float* dbeta;        // [Hq]
+  int64_t L, seg_len;
+  int32_t B, Hq, Hkv, S;
+  int32_t rule;
+  float scale_log2;    // log2(e) / sqrt(d)
+};
+
+hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
+// Row step of the retrieval backward: delta, dg, dn, dden from nm, out, dout.
+hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+// nm <- (nm + dden z) * sigma'(q): the retrieval part of dL/dQ.
+hipError_t launch_bwd_retrieval_dq(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+// e[unit][s] = sum over the segment's rows (and query heads if of_q) of w_t sigma(x_t).
+hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
+                                       hipStream_t stream);
+// Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
+hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+// Row step of the delta rule's update backward (after p_buf, du_buf).
+hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+// phi_f = sigma(K), phic_f = sigma(K) / (sigma(K) . z_{s-1}), per key row, in float.
+hipError_t launch_bwd_phi_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+// dst[i] = src[i] rounded to the element type (or copied, float).
+hipError_t launch_round_f32(int dtype, void* dst, const float* src, int64_t n, hipStream_t stream);
+// dz suffix scan and the final dK, dV, dbeta.
+hipError_t launch_bwd_finish(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+
 // Wave count of the attention workgroup for a segment length: one wave per 32
 // query rows, at most four.
 int attn_waves(int64_t seg_len);
 
 hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
+// The chain step of the affine form alone (a.reverse honoured).
+hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -1,5 +1,6 @@
 /*
- * infini_attn.h -- C ABI of the Infini-attention block forward on gfx950.
+ * infini_attn.h -- C ABI of the Infini-attention block on gfx950: forward,
+ * streaming decode step and backward pass.
  *
  * The operation ("Infini-Attention" (AI Wiki), sections "What happens inside
  * the Infini-attention block?" and "How does the compressive memory work?";
@@ -176,6 +177,59 @@ infini_status_t infini_attn_decode_step(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* A static, human-readable name of a status code. Never NULL. */
+/*
+ * Training forward: infini_attn_forward, plus the softmax statistics the
+ * backward pass needs.
+ *   lse: [B][Hq][L] float, written: for query row t of its segment,
+ *        lse[t] = log2( sum over visible keys u of exp2(c q_t . k_u) ),
+ *        c = log2(e) / sqrt(d), i.e. the base-2 log of the softmax
+ *        denominator of the scaled scores, as the kernel computed it.
+ * Same workspace, sizes and errors as infini_attn_forward; lse must be
+ * non-NULL, 16-byte aligned and overlap no other argument.
+ */
+infini_status_t infini_attn_forward_train(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass ("Infini-Attention" (AI Wiki), "How is an Infini-attention
+ * model trained?": gradients flow through the memory recurrence from segment
+ * to segment, as in truncated backpropagation through time). One call is the
+ * truncation window: for the loss
+ *   sum(d_out * out) + sum(dM_final * M_final) + sum(dz_final * z_final)
+ * of the forward with the same arguments, it writes the gradients with
+ * respect to every input, through all segments down to (M0, z0).
+ *   q, k, v, beta, M0, z0: the forward's inputs;
+ *   out, lse: the forward's outputs (infini_attn_forward_train);
+ *   d_out: [B][Hq][L][d] element type, the gradient of out;
+ *   dM_final [B][Hkv][d][d], dz_final [B][Hkv][d]: float gradients of the
+ *     final state, or NULL for zero;
+ *   dq, dk, dv: like q, k, v (element type), written;
+ *   dbeta: [Hq] float, written (summed over the batch and the stream);
+ *   dM0, dz0: like M0, z0 (float), written;
+ *   workspace, workspace_bytes: at least infini_attn_backward_workspace_size
+ *     (one window: the whole call).
+ * Sizes and errors as infini_attn_forward. The outputs and the workspace may
+ * overlap no argument. Gradients are accumulated in float and rounded to the
+ * element type once, at the end.
+ */
+infini_status_t infini_attn_backward_workspace_size(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype, size_t* bytes);
+infini_status_t infini_attn_backward(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    const void* out, const float* lse, const void* d_out,
+    const float* dM_final, const float* dz_final,
+    void* dq, void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 const char* infini_attn_status_string(int32_t status);
 
 /* The ABI version: major * 10000 + minor * 100 + patch. */

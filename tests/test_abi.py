@@ -32,9 +32,10 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
+        "infini_attn_backward", "infini_attn_backward_workspace_size",
         "infini_attn_decode_step", "infini_attn_decode_workspace_size",
-        "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_status_string",
-        "infini_attn_version", "infini_attn_workspace_size"])
+        "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_forward_train",
+        "infini_attn_status_string", "infini_attn_version", "infini_attn_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -284,3 +285,95 @@ def test_decode_rejects_small_workspace(lib):
     bufs = FakeDecodeBuffers(2, 4, 2, 64, 40, 2)
     _, need = dws(lib, 2, 4, 2, 64, 40, 1, 1)
     assert dcall(lib, DSHAPE, 3, bufs, workspace_bytes=need - 1) == 4
+
+
+# ---- training forward and backward ---------------------------------------------
+
+def test_forward_train_rejects_bad_lse(lib):
+    bufs = FakeBuffers(2, 4, 2, 64, 32, 2)
+    a = bufs.addr
+    lse = (1 << 43)  # a distinct aligned address
+    args = lambda lse_addr, **over: [2, 4, 2, 64, 32, 16, 1, 1] + [
+        ctypes.c_void_p({**a, **over}[n]) for n in ("q", "k", "v", "beta", "M0", "z0", "out",
+                                                    "M_final", "z_final")] + [
+        ctypes.c_void_p(lse_addr), ctypes.c_void_p(a["workspace"]),
+        over.get("workspace_bytes", bufs.size["workspace"]), None]
+    assert lib.infini_attn_forward_train(*args(None)) == 1
+    assert lib.infini_attn_forward_train(*args(lse + 4)) == 3
+    assert lib.infini_attn_forward_train(*args(a["out"])) == 1     # overlaps out
+    assert lib.infini_attn_forward_train(*args(a["k"] + 64)) == 1  # overlaps an input
+    assert lib.infini_attn_forward_train(*args(lse, workspace_bytes=0)) == 4
+
+
+def bws(lib, *args):
+    n = ctypes.c_size_t(0)
+    st = lib.infini_attn_backward_workspace_size(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_backward_workspace_size(lib):
+    st, n = bws(lib, 2, 4, 2, 64, 32, 16, 1, 1)
+    assert st == 0
+    units, S, d, e, L = 4, 4, 32, 2, 64
+    # at least the float gradient accumulators and the per-segment matrices
+    assert n > 2 * 4 * L * d * 4 + 3 * units * S * d * d * e
+    assert bws(lib, 2, 3, 2, 64, 32, 16, 1, 1)[0] == 1
+    assert bws(lib, 2, 4, 2, 64, 48, 16, 1, 1)[0] == 2
+    # the linear rule needs no delta-rule buffers
+    assert bws(lib, 2, 4, 2, 64, 32, 16, 0, 1)[1] < n
+
+
+BWD_NAMES = ("q", "k", "v", "beta", "M0", "z0", "out", "lse", "d_out", "dM_final", "dz_final",
+             "dq", "dk", "dv", "dbeta", "dM0", "dz0", "workspace")
+
+
+class FakeBwdBuffers:
+    def __init__(self, B, Hq, Hkv, L, d, e):
+        q, kv, M, z = B * Hq * L * d * e, B * Hkv * L * d * e, B * Hkv * d * d * 4, B * Hkv * d * 4
+        sizes = dict(q=q, k=kv, v=kv, beta=Hq * 4, M0=M, z0=z, out=q, lse=B * Hq * L * 4, d_out=q,
+                     dM_final=M, dz_final=z, dq=q, dk=kv, dv=kv, dbeta=Hq * 4, dM0=M, dz0=z,
+                     workspace=1 << 40)
+        base = 1 << 44
+        self.addr, self.size = {}, sizes
+        for name in BWD_NAMES:
+            self.addr[name] = base
+            base += (sizes[name] + 4095) // 4096 * 4096 + 4096
+
+
+def bcall(lib, bufs, **over):
+    a = {**bufs.addr, **over}
+    wsb = over.get("workspace_bytes", bufs.size["workspace"])
+    return lib.infini_attn_backward(2, 4, 2, 64, 32, 16, 1, 1,
+                                    *[ctypes.c_void_p(a[n]) for n in BWD_NAMES], wsb, None)
+
+
+def test_backward_accepts_null_final_gradients_then_checks_the_workspace(lib):
+    bufs = FakeBwdBuffers(2, 4, 2, 64, 32, 2)
+    # dM_final / dz_final may be NULL; the call still fails on the workspace
+    # size, so nothing launches
+    assert bcall(lib, bufs, dM_final=None, dz_final=None, workspace_bytes=16) == 4
+
+
+@pytest.mark.parametrize("name", [n for n in BWD_NAMES if n not in ("dM_final", "dz_final")])
+def test_backward_rejects_null_and_misaligned(lib, name):
+    bufs = FakeBwdBuffers(2, 4, 2, 64, 32, 2)
+    assert bcall(lib, bufs, **{name: None}) == 1
+    assert bcall(lib, bufs, **{name: bufs.addr[name] + 8}) == 3
+
+
+@pytest.mark.parametrize("a,b", [("dq", "q"), ("dk", "dv"), ("dbeta", "beta"), ("dM0", "M0"),
+                                 ("dz0", "dz_final"), ("workspace", "lse"), ("dq", "d_out"),
+                                 ("dk", "workspace")])
+def test_backward_rejects_overlaps(lib, a, b):
+    bufs = FakeBwdBuffers(2, 4, 2, 64, 32, 2)
+    assert bcall(lib, bufs, **{a: bufs.addr[b]}) == 1
+
+
+def test_backward_rejects_small_workspace_and_bad_sizes(lib):
+    bufs = FakeBwdBuffers(2, 4, 2, 64, 32, 2)
+    _, need = bws(lib, 2, 4, 2, 64, 32, 16, 1, 1)
+    assert bcall(lib, bufs, workspace_bytes=need - 1) == 4
+    a = bufs.addr
+    assert lib.infini_attn_backward(2, 3, 2, 64, 32, 16, 1, 1,
+                                    *[ctypes.c_void_p(a[n]) for n in BWD_NAMES], 1 << 40,
+                                    None) == 1
