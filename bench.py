@@ -190,6 +190,91 @@ def bench_decode(lib, w, rule, dev, args):
     }
 
 
+def bwd_flops(w, rule):
+    """Algorithmic matrix-product FLOPs of one backward call: per (query head,
+    segment of n rows) 5 causal products of d n (n + 1) each for the local
+    attention (S, dP, dV, dK, dQ); per query row 6 d^2 for the retrieval
+    (sigma(Q) M, dn M^T, sigma(Q)^T dn); per key row 4 d^2 for the linear
+    update's (Phi dM, V dM^T), 10 d^2 for the delta rule's (also Phi M,
+    dP M^T and A_s); 2 d^3 per (unit, segment) for the delta chain."""
+    d = w.d
+    local = 0
+    for s_ in range(w.segments):
+        n = min(w.seg_len, w.L - s_ * w.seg_len)
+        local += 5 * d * n * (n + 1)
+    local *= w.B * w.Hq
+    retr = 6 * d * d * w.B * w.Hq * w.L
+    upd = (10 if rule == "delta" else 4) * d * d * w.B * w.Hkv * w.L
+    chain = (2 * d ** 3 * w.B * w.Hkv * w.segments) if rule == "delta" else 0
+    return local + retr + upd + chain, local
+
+
+def bench_backward(lib, w, rule, dev, args):
+    """The backward pass over the whole workload: one infini_attn_backward
+    call per step, with the forward's out and lse (one training forward)
+    and a random d_out resident in HBM; no gradient on the final state."""
+    import torch
+
+    inp = synth.make_inputs(w, dev)
+    dt = inp["q"].dtype
+    g = torch.Generator(device="cpu").manual_seed(9)
+    d_out = torch.randn(w.B, w.Hq, w.L, w.d, generator=g).to(dt).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    out, _, _, lse = lib.forward_train(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"],
+                                       inp["z0"], w.seg_len, rule)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1)
+    ws = torch.empty(lib.backward_workspace_size(w.B, w.Hq, w.Hkv, w.L, w.d, w.seg_len, rule, dt),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return lib.backward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                            w.seg_len, rule, out, lse, d_out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        grads = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    finite = all(bool(torch.isfinite(x).all()) for x in grads[:4])
+    flops, local = bwd_flops(w, rule)
+    peak = PEAK_TFLOPS["bf16" if w.dtype == "bf16" else "f32"]
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "metric": "Infini-attn backward tokens/s + TFLOP/s, 1xMI355X",
+        "value": w.B * w.L / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V and d_out in HBM; random beta; M0 = 0, "
+                "z0 = 1e-6)",
+        "config": {"workload": w.name + "/backward", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "L": w.L, "d": w.d, "seg_len": w.seg_len, "rule": rule},
+        "forward_train_ms": fwd_ms,
+        "gradients_finite": finite,
+        "tflops": tf,
+        "roofline": {"kernel": "whole backward call (local-attention gradients dominate)",
+                     "bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tf / peak, "traffic": None,
+                     "algorithmic_flop_per_launch": flops,
+                     "local_attention_flop_per_launch": local},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,9 +285,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "backward"],
                     help="forward: the block forward over the workload (default); decode: "
-                         "the streaming decode step over one full segment of it")
+                         "the streaming decode step over one full segment of it; backward: "
+                         "the gradients of the block over the workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the steps, copy MIB MiB device to device once (a kernel "
                          "of known traffic that calibrates the HBM byte counters)")
@@ -224,6 +310,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "decode":
         print(json.dumps(bench_decode(lib, w, rule, dev, args)), flush=True)
+        return
+    if args.mode == "backward":
+        print(json.dumps(bench_backward(lib, w, rule, dev, args)), flush=True)
         return
     inp = synth.make_inputs(w, dev)
     out = torch.empty_like(inp["q"])

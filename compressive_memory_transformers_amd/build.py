@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "scan.hip", "affine.hip", "attn.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["api.hip", "scan.hip", "affine.hip", "attn.hip", "decode.hip", "bwd.hip",
+           "attn_bwd.hip"]
 ARCH = "gfx950"
 
 COMPILE_FLAGS = [

@@ -522,10 +522,11 @@ struct BwdLayout {
   size_t total;
   size_t stM, stz, zeroM, snapM, snapZ, colsum, Bmat, Amat, dMsnap, e_ret, e_upd, dzs;
   size_t nm, dn, delta, dg, dden, dk_acc, dv_acc, du_buf, dphi, p_buf, u_el, dp_el, dc;
-  size_t Amat_f, dMsnap_f, phi_f, phic_f;
+  size_t Amat_f, dMsnap_f, phi_f, phic_f, wsum_part;
 };
 
-BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int32_t rule) {
+BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                     int64_t seg_len, int32_t rule) {
   BwdLayout b{};
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -550,6 +551,11 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
   b.e_ret = take(units * S * d * 4);
   b.e_upd = take(units * S * d * 4);
   b.dzs = take(units * S * d * 4);
+  {  // chunks of 512 rows of a segment's query rows (all heads of the group)
+    const size_t n = (size_t)(seg_len < L ? seg_len : L);
+    const size_t chunks = ((size_t)(Hq / Hkv) * n + 511) / 512;
+    b.wsum_part = take(units * S * chunks * d * 4);
+  }
   b.nm = take(qrows * d * 4);
   b.dn = take(qrows * d * e);
   b.delta = take(qrows * 4);
@@ -602,7 +608,7 @@ infini_status_t infini_attn_backward_workspace_size(int64_t B, int64_t Hq, int64
   const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
   if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
-  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, rule).total;
+  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule).total;
   return INFINI_OK;
 }
 
@@ -630,7 +636,7 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   const size_t nq = (size_t)(B * Hq * L * d) * e, nkv = (size_t)(B * Hkv * L * d) * e;
   const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
   const size_t nrow = (size_t)(B * Hq * L) * 4, nbeta = (size_t)Hq * 4;
-  const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, rule);
+  const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule);
   if (workspace_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   struct Range { const void* p; size_t n; };
   const Range all[] = {{q, nq},         {k, nkv},         {v, nkv},      {beta, nbeta},
@@ -703,6 +709,7 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ba.e_ret = F(lay.e_ret);
   ba.e_upd = F(lay.e_upd);
   ba.dzs = F(lay.dzs);
+  ba.wsum_part = F(lay.wsum_part);
   ba.dz_final = dz_final;
   ba.dz0 = dz0;
   ba.dq = dq;
@@ -744,9 +751,18 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
     g.b_lo = DD;
     g.tb = 0;  // op(B) = M^T as stored
     g.clip = 1;
+    // epilogue: nm = (dn M^T + dden z^T) sigma'(Q), the retrieval part of dQ
+    g.epi = 1;
+    g.epi_w = ba.dden;
+    g.w_hi = L;
+    g.w_lo = seg_len;
+    g.epi_z = F(lay.snapZ);
+    g.z_div = (int32_t)G;
+    g.z_hi = S * d;
+    g.z_lo = d;
+    g.epi_x = q;
     if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
   }
-  if (infini::launch_bwd_retrieval_dq(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
     const size_t off = (size_t)(hg * LD) * e;
     infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + off,

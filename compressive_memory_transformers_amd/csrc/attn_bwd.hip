@@ -1,0 +1,370 @@
+// Gradients of the local causal attention, bf16 with MFMA (d in {64, 128}).
+//
+// "Infini-Attention" (AI Wiki), "What happens inside the Infini-attention
+// block?" (A_dot) and "How is an Infini-attention model trained?". With the
+// forward's softmax statistics lse (base-2, scaled scores), P_tu =
+// exp2(c q_t . k_u - lse_t), c = log2(e) / sqrt(d); dA_dot = (1 - g) dout;
+// dS_tu = P_tu ((1 - g) dout_t . v_u - delta_t):
+//   dQ_t = sum_u dS_tu k_u / sqrt(d)            (query-major kernel)
+//   dK_u = sum_t dS_tu q_t / sqrt(d), dV_u = sum_t P_tu (1 - g) dout_t
+//                                              (key-major kernel, over the
+//                                               query heads of the group)
+// Tiles come into LDS by DMA in the row-major "K" layout (lds_tile.hpp); a
+// tile is read row-wise for one operand and with transposing reads for the
+// other, so each tensor is staged once.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "lds_tile.hpp"
+
+namespace infini {
+
+namespace {
+
+constexpr int kNW = 4;  // waves per workgroup
+
+// Round-robin rows (query or key) over the waves: row index base + w + 4 i
+// for lane i, so every wave meets the causal diagonal in the same tiles.
+
+// ---- dQ: one workgroup per 128 query rows, key tiles of 64 ---------------------
+
+template <int D>
+struct DqLane {
+  static constexpr int NC = D / 16, NDB = D / 32;
+  bf16x8 qf[NC], dof[NC];  // B operands: query row, k = head dim
+  f32x16 acc[NDB];         // dQ^T
+  uint32_t ko;             // row read offset (as the forward's K reads)
+  uint32_t tk[2][NDB];     // transposing read offsets of K
+};
+
+// One 64-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+template <int D>
+__device__ __forceinline__ void dq_tile(const bf16* Kt, const bf16* Vt, DqLane<D>& st, float c,
+                                        float lse, float dl, float om, int k0, int row, int h,
+                                        bool diag) {
+  constexpr int NC = D / 16, NDB = D / 32;
+  f32x16 sacc[2], pacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    sacc[kb] = zero16();
+    pacc[kb] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint32_t o = (st.ko ^ (32u * cc)) + 2 * 32 * kb * D;
+      mma32(sacc[kb], load8<bf16>(lds_at(Kt, o)), st.qf[cc]);
+      mma32(pacc[kb], load8<bf16>(lds_at(Vt, o)), st.dof[cc]);
+    }
+  }
+  bf16x8 dsf[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -lse));
+      if (diag && k0 + 32 * kb + acc_row(r, h) > row) p = 0.f;
+      dsf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * __builtin_fmaf(om, pacc[kb][r], -dl));
+    }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+      mma32(st.acc[db], tr_frag_k<D>(Kt, st.tk[0][db], st.tk[1][db], pc), dsf[pc]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
+  constexpr int BN = 64, BM = 32 * kNW, NC = D / 16, NDB = D / 32;
+  __shared__ __align__(1024) bf16 Ks0[BN * D];
+  __shared__ __align__(1024) bf16 Ks1[BN * D];
+  __shared__ __align__(1024) bf16 Vs0[BN * D];
+  __shared__ __align__(1024) bf16 Vs1[BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  // XCD-aware order as in the forward: a contiguous range of logical tiles
+  // per XCD, heaviest query tiles of a (unit, segment) group first
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int G = a.Hq / a.Hkv;
+  const int in_grp = n_qt * G;
+  const int grp = t / in_grp, rr = t % in_grp;
+  const int qt = n_qt - 1 - rr / G, hg = rr % G;
+  const int sl = grp % a.S, unit = grp / a.S;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv, hq = kvh * G + hg;
+  const int64_t seg_start = (int64_t)sl * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int q0 = qt * BM;
+  if (q0 >= n_s) return;
+
+  const int64_t qh = (int64_t)b * a.Hq + hq;
+  const int64_t rbase = qh * a.L + seg_start;  // row index of the segment's first query
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  const float om = 1.f - 1.f / (1.f + __expf(-a.beta[hq]));
+  const float c = a.scale_log2;
+  const int row = q0 + w + kNW * i;
+  const bool live = row < n_s;
+  const int n_kt = (min(q0 + BM, n_s) + BN - 1) / BN;
+
+  DmaTile<D, kNW, BN> tile;
+  tile.init(w, lane);
+  tile.template issue<true>(K, Ks0, 0, n_s, w);
+  tile.template issue<true>(V, Vs0, 0, n_s, w);
+
+  DqLane<D> st;
+  st.ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    st.tk[0][db] = tr_offset_k<D>(lane, db, 0);
+    st.tk[1][db] = tr_offset_k<D>(lane, db, 1);
+    st.acc[db] = zero16();
+  }
+  const bf16* Q = static_cast<const bf16*>(a.q) + (rbase + row) * D;
+  const bf16* dO = static_cast<const bf16*>(a.dout) + (rbase + row) * D;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    st.qf[cc] = live ? load8<bf16>(Q + 16 * cc + 8 * h) : zero_frag<bf16>();
+    st.dof[cc] = live ? load8<bf16>(dO + 16 * cc + 8 * h) : zero_frag<bf16>();
+  }
+  // rows past the segment: lse = +inf gives P = 0
+  const float lse = live ? a.lse[rbase + row] : INFINITY;
+  const float dl = live ? a.delta[rbase + row] : 0.f;
+  const int wave_first = q0 + w;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  bf16* const Ks[2] = {Ks0, Ks1};
+  bf16* const Vs[2] = {Vs0, Vs1};
+  auto step = [&](int j, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (j + 1 < n_kt) {
+      tile.template issue<true>(K, Ks[P ^ 1], (j + 1) * BN, n_s, w);
+      tile.template issue<true>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+    }
+    const int k0 = j * BN;
+    dq_tile<D>(Ks[P], Vs[P], st, c, lse, dl, om, k0, row, h, k0 + BN - 1 > wave_first);
+    if (j + 1 < n_kt) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  };
+  for (int j = 0; j < n_kt; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (!live) return;
+  // dq = dQ^T^T / sqrt(d) + the retrieval part (a.nm, float)
+  const float inv_sqrt_d = a.scale_log2 / kLog2e;
+  const float* nm = a.nm + (rbase + row) * D;
+  bf16* dq = static_cast<bf16*>(a.dq) + (rbase + row) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int col = 32 * db + 8 * rq + 4 * h;
+      const f32x4 m = *reinterpret_cast<const f32x4*>(nm + col);
+      bf16x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (bf16)(st.acc[db][4 * rq + j] * inv_sqrt_d + m[j]);
+      store4<bf16>(dq + col, y);
+    }
+}
+
+// ---- dK, dV: one workgroup per 128 keys, query tiles of 32, all G heads -------
+
+template <int D>
+struct KvLane {
+  static constexpr int NC = D / 16, NDB = D / 32;
+  bf16x8 kf[NC];            // B operand: key row, k = head dim (V's is read from LDS)
+  f32x16 dk[NDB], dv[NDB];  // dK^T, dV^T
+  uint32_t ko;              // row read offset in a query tile
+  uint32_t vo;              // row read offset of this lane's key in the V block
+  uint32_t tk[2][NDB];
+};
+
+// One 32-query tile of one head: S = Q K^T, dP = dO V^T, P, dS;
+// dV^T += dO^T P, dK^T += Q^T dS.
+template <int D>
+__device__ __forceinline__ void kv_tile(const bf16* Qt, const bf16* Ot, const bf16* Vb,
+                                        const float* lse_t, const float* dl_t, KvLane<D>& st,
+                                        float c, float om, int q0, int n_s, int key, int h,
+                                        bool diag) {
+  constexpr int NC = D / 16, NDB = D / 32;
+  f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const uint32_t o = st.ko ^ (32u * cc);
+    mma32(sacc, load8<bf16>(lds_at(Qt, o)), st.kf[cc]);
+    mma32(pacc, load8<bf16>(lds_at(Ot, o)), load8<bf16>(lds_at(Vb, st.vo ^ (32u * cc))));
+  }
+  bf16x8 pf[2], dsf[2];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    // rows 8 g4 + 4 h + 0..3 of the tile
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_t + 8 * g4 + 4 * h);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl_t + 8 * g4 + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * g4 + j;
+      const int q = q0 + 8 * g4 + 4 * h + j;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[j]));
+      if ((diag && key > q) || q >= n_s) p = 0.f;
+      pf[r >> 3][r & 7] = (bf16)(p * om);
+      dsf[r >> 3][r & 7] = (bf16)(p * __builtin_fmaf(om, pacc[r], -d4[j]));
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {
+      mma32(st.dv[db], tr_frag_k<D>(Ot, st.tk[0][db], st.tk[1][db], pc), pf[pc]);
+      mma32(st.dk[db], tr_frag_k<D>(Qt, st.tk[0][db], st.tk[1][db], pc), dsf[pc]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
+  constexpr int BQ = 32, BK = 32 * kNW, NC = D / 16, NDB = D / 32;
+  __shared__ __align__(1024) bf16 Qs0[BQ * D];
+  __shared__ __align__(1024) bf16 Qs1[BQ * D];
+  __shared__ __align__(1024) bf16 Os0[BQ * D];
+  __shared__ __align__(1024) bf16 Os1[BQ * D];
+  __shared__ __align__(1024) bf16 Vb[BK * D];  // V of the workgroup's keys
+  __shared__ __align__(16) float Ls0[64], Ls1[64], Ds0[64], Ds1[64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int kt = t % n_kt, grp = t / n_kt;  // key tiles of a segment: heaviest first
+  const int sl = grp % a.S, unit = grp / a.S;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int64_t seg_start = (int64_t)sl * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int k0 = kt * BK;
+  if (k0 >= n_s) return;
+  const int key = k0 + w + kNW * i;
+  const bool live = key < n_s;
+  const float c = a.scale_log2;
+
+  KvLane<D> st;
+  const int64_t krow = (int64_t)unit * a.L + seg_start + key;
+  {  // the V rows of the block, by DMA (rows past the segment repeat its last)
+    DmaTile<D, kNW, BK> vt;
+    vt.init(w, lane);
+    vt.template issue<true>(static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D,
+                            Vb, k0, n_s, w);
+  }
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+    st.kf[cc] = live ? load8<bf16>(static_cast<const bf16*>(a.k) + krow * D + 16 * cc + 8 * h)
+                     : zero_frag<bf16>();
+  st.ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+  {
+    const int r = w + kNW * i;  // this lane's key, relative to the block
+    st.vo = 2 * (r * D + 8 * (h ^ swz_k<D>(r)));
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    st.tk[0][db] = tr_offset_k<D>(lane, db, 0);
+    st.tk[1][db] = tr_offset_k<D>(lane, db, 1);
+    st.dk[db] = zero16();
+    st.dv[db] = zero16();
+  }
+
+  DmaTile<D, kNW, BQ> tile;
+  tile.init(w, lane);
+  bf16* const Qs[2] = {Qs0, Qs1};
+  bf16* const Os[2] = {Os0, Os1};
+  float* const Ls[2] = {Ls0, Ls1};
+  float* const Ds[2] = {Ds0, Ds1};
+  // query tiles q0 = k0, k0 + 32, ... of every head of the group, as one list
+  const int n_q = (n_s - k0 + BQ - 1) / BQ;
+  const int n_items = n_q * G;
+  auto issue = [&](int it, int P) {
+    const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
+    const int64_t rb = ((int64_t)b * a.Hq + kvh * G + hg) * a.L + seg_start;
+    tile.template issue<true>(static_cast<const bf16*>(a.q) + rb * D, Qs[P], q0, n_s, w);
+    tile.template issue<true>(static_cast<const bf16*>(a.dout) + rb * D, Os[P], q0, n_s, w);
+    if (w < 2) {  // 32 floats of lse (wave 0) or delta (wave 1); lanes past 32 read zeros
+      const float* src = (w == 0 ? a.lse : a.delta) + rb + q0;
+      const int rows = min(BQ, n_s - q0);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), 0, rows * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(w == 0 ? Ls[P] : Ds[P]), 4,
+                                               lane * 4, 0, 0, 0);
+    }
+  };
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  auto step = [&](int it, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (it + 1 < n_items) issue(it + 1, P ^ 1);
+    const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
+    const float om = 1.f - 1.f / (1.f + __expf(-a.beta[kvh * G + hg]));
+    kv_tile<D>(Qs[P], Os[P], Vb, Ls[P], Ds[P], st, c, om, q0, n_s, key, h, q0 < k0 + BK);
+    if (it + 1 < n_items) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  };
+  for (int it = 0; it < n_items; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_items) step(it + 1, std::integral_constant<int, 1>{});
+  }
+  if (!live) return;
+  const float inv_sqrt_d = a.scale_log2 / kLog2e;
+  float* dk = a.dk_acc + krow * D;
+  float* dv = a.dv_acc + krow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int col = 32 * db + 8 * rq + 4 * h;
+      f32x4 yk, yv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        yk[j] = st.dk[db][4 * rq + j] * inv_sqrt_d;
+        yv[j] = st.dv[db][4 * rq + j];
+      }
+      *reinterpret_cast<f32x4*>(dk + col) = yk;
+      *reinterpret_cast<f32x4*>(dv + col) = yv;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  const int64_t eff = a.seg_len < a.L ? a.seg_len : a.L;
+  const int n_qt = (int)((eff + 32 * kNW - 1) / (32 * kNW));
+  const int n_kt = n_qt;  // 128 keys per workgroup
+  const int64_t G = a.Hq / a.Hkv;
+  const int64_t kv_grid = units * a.S * n_kt, q_grid = units * a.S * n_qt * G;
+  if (kv_grid > INT32_MAX || q_grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kv_kernel<D>), dim3((unsigned)kv_grid), dim3(kNW * 64), 0, s, a, n_kt);
+  hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)q_grid), dim3(kNW * 64), 0, s, a, n_qt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_mfma_supported(int dtype, int d) { return dtype == kBF16 && (d == 64 || d == 128); }
+
+hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace infini

@@ -120,6 +120,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
   const int n = n0 + 32 * wn + i;
   if (n >= g.N) return;
+  if (g.epi == 1) {
+    const float* wv = g.epi_w + (int64_t)(hi / g.c_div) * g.w_hi + (int64_t)lo * g.w_lo;
+    const float zn = g.epi_z[(int64_t)(hi / g.z_div) * g.z_hi + (int64_t)lo * g.z_lo + n];
+    const T* xv = static_cast<const T*>(g.epi_x) + (int64_t)(hi / g.c_div) * g.c_hi +
+                  (int64_t)lo * g.c_lo;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * wm + acc_row(r, h);
+      if (m < Mv)
+        C[(int64_t)m * g.ldc + n] = (g.alpha * acc[r] + wv[m] * zn) *
+                                    feature_map_grad(to_f32<T>(xv[(int64_t)m * g.ldc + n]));
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = m0 + 32 * wm + acc_row(r, h);
@@ -189,52 +203,60 @@ __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
   }
 }
 
-// nm <- (nm + dden z) * sigma'(q): nm held dn M^T, now the retrieval part of
-// dL/dQ.
+// e[unit][s][c] = sum over the segment's rows t (and the group's query heads
+// when of_q) of w_t sigma(x_t[c]): the retrieval (x = q, w = dden) or the
+// delta rule's (x = k, w = dc) part of dL/dz_{s-1}. Two stages, in a fixed
+// order (no atomics): workgroup ch of a (unit, segment) sums rows
+// [ch R, (ch + 1) R) of the segment's G n or n rows into part, then
+// wsum_final adds the chunks.
+constexpr int kWsumRows = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void retrieval_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void wsum_partial_kernel(BwdArgs a, int of_q, int n_chunks) {
+  constexpr int CG = D / 8, RL = 256 / CG;
+  __shared__ float red[RL * D];
+  const int tid = threadIdx.x, cg = tid % CG, rl = tid / CG;
+  const int ch = blockIdx.x % n_chunks;
+  const int64_t us = blockIdx.x / n_chunks;  // unit * S + s
+  const int64_t unit = us / a.S;
+  const int s = (int)(us % a.S);
   const int G = a.Hq / a.Hkv;
-  const int64_t n = (int64_t)a.B * a.Hq * a.L * D;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
-    const int64_t row = x / D;
-    const int c = (int)(x % D);
-    const int64_t bh = row / a.L, t = row % a.L;
-    const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-    const int64_t unit = (int64_t)b * a.Hkv + hq / G;
-    const int s = (int)(t / a.seg_len);
-    const float z = a.snapZ[(unit * a.S + s) * D + c];
-    const float qv = to_f32<T>(static_cast<const T*>(a.q)[x]);
-    a.nm[x] = (a.nm[x] + a.dden[row] * z) * feature_map_grad(qv);
+  const int64_t t0 = (int64_t)s * a.seg_len;
+  const int n = (int)min<int64_t>(a.seg_len, a.L - t0);
+  const int R = of_q ? G * n : n;
+  const int r1 = min(R, (ch + 1) * kWsumRows);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const int64_t b = unit / a.Hkv, j = unit % a.Hkv;
+  for (int r = ch * kWsumRows + rl; r < r1; r += RL) {
+    int64_t row;  // row of the [.][L] tensor
+    if (of_q)
+      row = (b * a.Hq + j * G + r / n) * a.L + t0 + r % n;
+    else
+      row = unit * a.L + t0 + r;
+    const T* x = static_cast<const T*>(of_q ? a.q : a.k) + row * D + 8 * cg;
+    const float wv = (of_q ? a.dden : a.dc)[row];
+    const frag_t<T> xv = load8<T>(x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += wv * feature_map(to_f32<T>(xv[e]));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl * D + 8 * cg + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int k = 0; k < RL; ++k) t += red[k * D + tid];
+    a.wsum_part[((int64_t)us * n_chunks + ch) * D + tid] = t;
   }
 }
 
-// e[unit][s][c] = sum over the segment's rows t (and the group's query heads
-// when of_q) of w_t sigma(x_t[c]): the retrieval (x = q, w = dden) or the
-// delta rule's (x = k, w = dc) part of dL/dz_{s-1}.
-template <typename T, int D>
-__global__ __launch_bounds__(D) void weighted_sum_kernel(BwdArgs a, int of_q) {
-  const int c = threadIdx.x;
-  const int64_t unit = blockIdx.x / a.S;
-  const int s = blockIdx.x % a.S;
-  const int G = a.Hq / a.Hkv;
-  const int64_t t0 = (int64_t)s * a.seg_len;
-  const int64_t t1 = min<int64_t>(t0 + a.seg_len, a.L);
-  float acc = 0.f;
-  if (of_q) {
-    const int64_t b = unit / a.Hkv, j = unit % a.Hkv;
-    for (int hg = 0; hg < G; ++hg) {
-      const int64_t bh = b * a.Hq + j * G + hg;
-      const T* x = static_cast<const T*>(a.q) + bh * a.L * D;
-      const float* wv = a.dden + bh * a.L;
-      for (int64_t t = t0; t < t1; ++t) acc += wv[t] * feature_map(to_f32<T>(x[t * D + c]));
-    }
-    a.e_ret[(unit * a.S + s) * D + c] = acc;
-  } else {
-    const T* x = static_cast<const T*>(a.k) + unit * a.L * D;
-    const float* wv = a.dc + unit * a.L;
-    for (int64_t t = t0; t < t1; ++t) acc += wv[t] * feature_map(to_f32<T>(x[t * D + c]));
-    a.e_upd[(unit * a.S + s) * D + c] = acc;
-  }
+template <int D>
+__global__ __launch_bounds__(D) void wsum_final_kernel(BwdArgs a, int of_q, int n_chunks) {
+  const int64_t us = blockIdx.x;
+  float t = 0.f;
+  for (int ch = 0; ch < n_chunks; ++ch) t += a.wsum_part[((int64_t)us * n_chunks + ch) * D + threadIdx.x];
+  (of_q ? a.e_ret : a.e_upd)[us * D + threadIdx.x] = t;
 }
 
 // ---- local attention, one wave per row (small shapes and float) -----------
@@ -507,13 +529,16 @@ hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
     case 0:
       hipLaunchKernelGGL((retrieval_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
       break;
-    case 1:
-      hipLaunchKernelGGL((retrieval_dq_kernel<T, D>), dim3(elem_grid(qrows * D)), dim3(256), 0, s, a);
+    case 2: {
+      const int G = a.Hq / a.Hkv;
+      const int64_t n = a.seg_len < a.L ? a.seg_len : a.L;
+      const int n_chunks = (int)(((arg ? G : 1) * n + kWsumRows - 1) / kWsumRows);
+      hipLaunchKernelGGL((wsum_partial_kernel<T, D>), dim3((unsigned)(units * a.S * n_chunks)),
+                         dim3(256), 0, s, a, arg, n_chunks);
+      hipLaunchKernelGGL((wsum_final_kernel<D>), dim3((unsigned)(units * a.S)), dim3(D), 0, s, a,
+                         arg, n_chunks);
       break;
-    case 2:
-      hipLaunchKernelGGL((weighted_sum_kernel<T, D>), dim3((unsigned)(units * a.S)), dim3(D), 0, s,
-                         a, arg);
-      break;
+    }
     case 3:
       hipLaunchKernelGGL((attn_dkdv_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
       hipLaunchKernelGGL((attn_dq_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
@@ -568,15 +593,13 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream) {
 hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
   return launch(dtype, d, 0, a, 0, s);
 }
-hipError_t launch_bwd_retrieval_dq(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 1, a, 0, s);
-}
 hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
                                        hipStream_t s) {
   return launch(dtype, d, 2, a, of_q ? 1 : 0, s);
 }
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 3, a, 0, s);
+  if (attn_bwd_mfma_supported(dtype, d)) return launch_attn_bwd_mfma(d, a, s);
+  return launch(dtype, d, 3, a, 0, s);  // float, or d = 32: one wave per row
 }
 hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
   return launch(dtype, d, 4, a, 0, s);

@@ -110,6 +110,14 @@ struct GemmArgs {
   int32_t a_div, b_div, c_div;
   int64_t a_hi, a_lo, b_hi, b_lo, c_hi, c_lo;
   int64_t L, seg_len;
+  // epi = 1: C = (alpha op(A) op(B) + w[m] z[n]) sigma'(x[m][n]), with w (float)
+  // offset like C's rows (w_hi, w_lo per hi, lo; one value per row), z (float)
+  // offset (hi / z_div) z_hi + lo z_lo, x (element type) offset like C.
+  int32_t epi, z_div;
+  const float* epi_w;
+  const float* epi_z;
+  const void* epi_x;
+  int64_t w_hi, w_lo, z_hi, z_lo;
 };
 
 // Everything the backward's elementwise, reduction and attention kernels read.
@@ -139,6 +147,7 @@ struct BwdArgs {
   float* dc;           // [B][Hkv][L] dL/dc, c = sigma(k) . z_{s-1} (delta)
   float* phi_f;        // [B][Hkv][L][d] sigma(K) in float (delta)
   float* phic_f;       // [B][Hkv][L][d] sigma(K) / c in float (delta)
+  float* wsum_part;    // [B*Hkv][S][chunks][d] partial sums of the dz reductions
   float* e_ret;        // [B*Hkv][S][d] retrieval part of dL/dz_{s-1}
   float* e_upd;        // [B*Hkv][S][d] update part of dL/dz_{s-1}
   float* dzs;          // [B*Hkv][S][d] dL/dz_s
@@ -158,11 +167,12 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 // Row step of the retrieval backward: delta, dg, dn, dden from nm, out, dout.
 hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
-// nm <- (nm + dden z) * sigma'(q): the retrieval part of dL/dQ.
-hipError_t launch_bwd_retrieval_dq(int dtype, int d, const BwdArgs& a, hipStream_t stream);
 // e[unit][s] = sum over the segment's rows (and query heads if of_q) of w_t sigma(x_t).
 hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
                                        hipStream_t stream);
+// MFMA kernels of the local-attention gradients (attn_bwd.hip): bf16, d in {64, 128}.
+bool attn_bwd_mfma_supported(int dtype, int d);
+hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
 // Row step of the delta rule's update backward (after p_buf, du_buf).

@@ -173,6 +173,26 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* tile, uint32_t off, int p)
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same transposing read on a "K"-layout tile (rows swizzled by swz_k, as
+// read row-wise by the 16-byte operand loads), so one tile serves both kinds
+// of operand. The row swizzle of row 16p + 8s + 4h + a depends on s but not
+// on p, so a lane keeps two offsets per 32-column block: tr_offset_k(lane,
+// cb, s), and fragment p reads offset s at + 32 p D bytes.
+template <int D>
+__device__ __forceinline__ uint32_t tr_offset_k(int lane, int cb, int s) {
+  const int h = lane >> 5, G = lane >> 4, a = (lane >> 2) & 3, b = lane & 3;
+  const int r = 8 * s + 4 * h + a;
+  const int col = 32 * cb + 16 * (G & 1) + 4 * b;
+  return 2 * (r * D + 8 * ((col >> 3) ^ swz_k<D>(r)) + (col & 7));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag_k(const bf16* tile, uint32_t off0, uint32_t off1,
+                                            int p) {
+  const bf16x4 lo = lds_read_tr(lds_at(tile, off0 + 2 * 16 * p * D));
+  const bf16x4 hi = lds_read_tr(lds_at(tile, off1 + 2 * 16 * p * D));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (DMA loads into LDS count, in issue order); LDS and export counters free.
 template <int N>
