@@ -20,7 +20,8 @@ namespace infini {
 
 namespace {
 
-constexpr int kNW = 4;  // waves per workgroup
+constexpr int kNW = 4;     // waves per workgroup
+constexpr int kMaxG = 64;  // query heads per KV head in the key-major kernel
 
 // Round-robin rows (query or key) over the waves: row index base + w + 4 i
 // for lane i, so every wave meets the causal diagonal in the same tiles.
@@ -138,18 +139,20 @@ __global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
 
   bf16* const Ks[2] = {Ks0, Ks1};
   bf16* const Vs[2] = {Vs0, Vs1};
+  // Tile j on buffer parity P = j % 2 (a constant). Every tile loads its
+  // successor (the last one reloads itself, in bounds and unused) into the
+  // other buffers first and waits for it at its end: with the load and the
+  // wait unconditional, the compiler sees that a tile's reads touch only
+  // buffers no load is filling, and does not wait for the load.
   auto step = [&](int j, auto par) {
     constexpr int P = decltype(par)::value;
-    if (j + 1 < n_kt) {
-      tile.template issue<true>(K, Ks[P ^ 1], (j + 1) * BN, n_s, w);
-      tile.template issue<true>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
-    }
+    const int jn = min(j + 1, n_kt - 1);
+    tile.template issue<true>(K, Ks[P ^ 1], jn * BN, n_s, w);
+    tile.template issue<true>(V, Vs[P ^ 1], jn * BN, n_s, w);
     const int k0 = j * BN;
     dq_tile<D>(Ks[P], Vs[P], st, c, lse, dl, om, k0, row, h, k0 + BN - 1 > wave_first);
-    if (j + 1 < n_kt) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
   for (int j = 0; j < n_kt; j += 2) {
     step(j, std::integral_constant<int, 0>{});
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
   __shared__ __align__(1024) bf16 Os1[BQ * D];
   __shared__ __align__(1024) bf16 Vb[BK * D];  // V of the workgroup's keys
   __shared__ __align__(16) float Ls0[64], Ls1[64], Ds0[64], Ds1[64];
+  __shared__ float omg[kMaxG];  // 1 - sigmoid(beta) of the group's query heads
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -280,42 +284,46 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
     st.dv[db] = zero16();
   }
 
+  if (tid < G) omg[tid] = 1.f - 1.f / (1.f + __expf(-a.beta[kvh * G + tid]));
   DmaTile<D, kNW, BQ> tile;
   tile.init(w, lane);
   bf16* const Qs[2] = {Qs0, Qs1};
   bf16* const Os[2] = {Os0, Os1};
-  float* const Ls[2] = {Ls0, Ls1};
-  float* const Ds[2] = {Ds0, Ds1};
+  auto Ls = [&](int P) { return P ? Ls1 : Ls0; };
+  auto Ds = [&](int P) { return P ? Ds1 : Ds0; };
   // query tiles q0 = k0, k0 + 32, ... of every head of the group, as one list
   const int n_q = (n_s - k0 + BQ - 1) / BQ;
   const int n_items = n_q * G;
-  auto issue = [&](int it, int P) {
+  auto issue = [&](int it, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
     const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
     const int64_t rb = ((int64_t)b * a.Hq + kvh * G + hg) * a.L + seg_start;
-    tile.template issue<true>(static_cast<const bf16*>(a.q) + rb * D, Qs[P], q0, n_s, w);
-    tile.template issue<true>(static_cast<const bf16*>(a.dout) + rb * D, Os[P], q0, n_s, w);
-    if (w < 2) {  // 32 floats of lse (wave 0) or delta (wave 1); lanes past 32 read zeros
-      const float* src = (w == 0 ? a.lse : a.delta) + rb + q0;
-      const int rows = min(BQ, n_s - q0);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), 0, rows * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(w == 0 ? Ls[P] : Ds[P]), 4,
-                                               lane * 4, 0, 0, 0);
+    tile.template issue<true>(static_cast<const bf16*>(a.q) + rb * D, Qd, q0, n_s, w);
+    tile.template issue<true>(static_cast<const bf16*>(a.dout) + rb * D, Od, q0, n_s, w);
+    // 32 floats of lse (wave 0) and delta (wave 1); lanes past the rows read zeros
+    const int bytes = min(BQ, n_s - q0) * 4;
+    if (w == 0) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.lse + rb + q0), 0, bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)Ld, 4, lane * 4, 0, 0, 0);
+    } else if (w == 1) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          a.delta + rb + q0, 0, bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)Dd, 4, lane * 4, 0, 0, 0);
     }
   };
-  issue(0, 0);
+  issue(0, Qs0, Os0, Ls0, Ds0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // as in dq_kernel: every item loads its successor (the last reloads
+  // itself) and waits for it, unconditionally
   auto step = [&](int it, auto par) {
     constexpr int P = decltype(par)::value;
-    if (it + 1 < n_items) issue(it + 1, P ^ 1);
+    issue(min(it + 1, n_items - 1), Qs[P ^ 1], Os[P ^ 1], Ls(P ^ 1), Ds(P ^ 1));
     const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
-    const float om = 1.f - 1.f / (1.f + __expf(-a.beta[kvh * G + hg]));
-    kv_tile<D>(Qs[P], Os[P], Vb, Ls[P], Ds[P], st, c, om, q0, n_s, key, h, q0 < k0 + BK);
-    if (it + 1 < n_items) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
+    const float om = omg[hg];
+    kv_tile<D>(Qs[P], Os[P], Vb, Ls(P), Ds(P), st, c, om, q0, n_s, key, h, q0 < k0 + BK);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
   for (int it = 0; it < n_items; it += 2) {
     step(it, std::integral_constant<int, 0>{});
@@ -357,7 +365,9 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool attn_bwd_mfma_supported(int dtype, int d) { return dtype == kBF16 && (d == 64 || d == 128); }
+bool attn_bwd_mfma_supported(int dtype, int d, int group) {
+  return dtype == kBF16 && (d == 64 || d == 128) && group <= kMaxG;
+}
 
 hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream) {
   switch (d) {

@@ -598,7 +598,7 @@ hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool 
   return launch(dtype, d, 2, a, of_q ? 1 : 0, s);
 }
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  if (attn_bwd_mfma_supported(dtype, d)) return launch_attn_bwd_mfma(d, a, s);
+  if (attn_bwd_mfma_supported(dtype, d, a.Hq / a.Hkv)) return launch_attn_bwd_mfma(d, a, s);
   return launch(dtype, d, 3, a, 0, s);  // float, or d = 32: one wave per row
 }
 hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {

@@ -170,8 +170,9 @@ hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStre
 // e[unit][s] = sum over the segment's rows (and query heads if of_q) of w_t sigma(x_t).
 hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
                                        hipStream_t stream);
-// MFMA kernels of the local-attention gradients (attn_bwd.hip): bf16, d in {64, 128}.
-bool attn_bwd_mfma_supported(int dtype, int d);
+// MFMA kernels of the local-attention gradients (attn_bwd.hip): bf16, d in {64, 128},
+// at most 64 query heads per KV head.
+bool attn_bwd_mfma_supported(int dtype, int d, int group);
 hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
