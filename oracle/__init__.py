@@ -16,6 +16,9 @@ Sources (page title, then section):
   update of M, the update of z, and the additive (linear) variant.
 * same page, section "Why is the memory footprint bounded?": segments of fixed
   length N, with the state (M, z) carried and nothing else.
+* same page, section "What happens inside the Infini-attention block?" again:
+  the input projections (query, key, value) and the output projection after
+  the gate (oracle/block.py).
 * same page, section "How is an Infini-attention model trained?": gradients
   flow through the memory recurrence as in truncated backpropagation through
   time (the backward pass; one call is the truncation window).
@@ -47,6 +50,12 @@ Pins (each function is checked against something other than itself in
   ``forward`` on it (every output row, and the state at every segment end);
   the first token of a segment attends to itself alone (closed form); the
   state is unchanged inside a segment.
+* ``block_forward``, ``project_qkv``, ``project_out`` (oracle/block.py) --
+  scaled-permutation weights give an element-by-element closed form (each
+  projected value is one input feature times a constant, read by explicit
+  index arithmetic); linearity of y in the output weight; homogeneity in the
+  value weights; four planted mistakes in the head split or the
+  concatenation fail those checks (``tests/test_oracle_block.py``).
 * ``backward`` (oracle/gradients.py) -- every gradient (Q, K, V, beta, M0,
   z0) against central finite differences of ``forward``, both rules, ragged,
   grouped and one-token segments; five planted mistakes (a dropped carry, a
@@ -68,4 +77,5 @@ from .infini_attention import (  # noqa: F401
     decode_step,
 )
 from .gradients import backward  # noqa: F401
+from .block import block_forward, project_out, project_qkv  # noqa: F401
 from .compare import max_rel_err, slice_errors  # noqa: F401

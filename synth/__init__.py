@@ -27,7 +27,8 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "outlier": 4}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "outlier": 4, "x": 5, "w_qkv": 6,
+              "w_o": 7, "M0": 8}
 
 
 @dataclass(frozen=True)
@@ -164,3 +165,43 @@ def hbm_bytes(w):
     e = 4 if w.dtype == "f32" else 2
     return (e * w.d * w.L * w.B * (2 * w.Hq + 2 * w.Hkv)
             + 8 * w.B * w.Hkv * (w.d * w.d + w.d) + 4 * w.Hq)
+
+
+def make_block_inputs(B, L, d_model, Hq, Hkv, d, dtype, device="cpu", seed=0, z0=1e-6,
+                      m0_scale=0.0):
+    """Inputs of the block with its projections, on ``device``.
+
+    x [B, L, d_model] N(0, 1); w_qkv [(Hq + 2 Hkv) d, d_model] and
+    w_o [d_model, Hq d], each N(0, 1 / fan_in) (random weights: the projected
+    values then have unit variance), in ``dtype``; beta [Hq] N(0, 1) float32;
+    M0 [B, Hkv, d, d] float32, N(0, m0_scale^2) (zeros by default); z0
+    [B, Hkv, d] float32, all ``z0``. Slices are seeded per batch element (x)
+    and per head (the weights' row blocks).
+    """
+    x = torch.empty((B, L, d_model), dtype=dtype, device=device)
+    for b in range(B):
+        x[b] = _normal((L, d_model), slice_seed(seed, "x", b, 0), device).to(dtype)
+    w_qkv = torch.empty(((Hq + 2 * Hkv) * d, d_model), dtype=dtype, device=device)
+    for h in range(Hq + 2 * Hkv):
+        w_qkv[h * d:(h + 1) * d] = (_normal((d, d_model), slice_seed(seed, "w_qkv", 0, h), device)
+                                    / math.sqrt(d_model)).to(dtype)
+    w_o = (_normal((d_model, Hq * d), slice_seed(seed, "w_o", 0, 0), device)
+           / math.sqrt(Hq * d)).to(dtype)
+    beta = _normal((Hq,), slice_seed(seed, "beta", 0, 0), device)
+    M0 = torch.zeros((B, Hkv, d, d), dtype=torch.float32, device=device)
+    if m0_scale:
+        for b in range(B):
+            for h in range(Hkv):
+                M0[b, h] = m0_scale * _normal((d, d), slice_seed(seed, "M0", b, h), device)
+    z0 = torch.full((B, Hkv, d), z0, dtype=torch.float32, device=device)
+    return dict(x=x, w_qkv=w_qkv, w_o=w_o, beta=beta, M0=M0, z0=z0)
+
+
+def block_flops(B, L, d_model, Hq, Hkv, d, seg_len, rule):
+    """Algorithmic FLOPs of the block with its projections: the input
+    projection 2 B L d_model (Hq + 2 Hkv) d, the block forward (``flops``),
+    the output projection 2 B L Hq d d_model."""
+    w = Workload("block", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, seg_len=seg_len, dtype="bf16",
+                 rules=(rule,), seed=0)
+    proj = 2 * B * L * d_model * (Hq + 2 * Hkv) * d + 2 * B * L * Hq * d * d_model
+    return proj + flops(w, rule)
