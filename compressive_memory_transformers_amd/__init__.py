@@ -1,4 +1,5 @@
-"""Infini-attention block on AMD Instinct MI355X (gfx950): forward, decode step, backward.
+"""Infini-attention block on AMD Instinct MI355X (gfx950): forward, decode step, backward,
+and the block with its input and output projections.
 
 The computation lives in libinfini_attn.so (hand-written HIP kernels behind
 the C ABI of include/infini_attn.h); this package is its thin Python binding.
@@ -11,6 +12,8 @@ from .binding import (  # noqa: F401
     InfiniAttnError,
     backward,
     backward_workspace_size,
+    block_forward,
+    block_workspace_size,
     decode_step,
     decode_workspace_size,
     forward,

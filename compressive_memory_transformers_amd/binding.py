@@ -41,6 +41,13 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 5 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_decode_step": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_block_workspace_size": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_block_forward": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_block_forward_timed": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
+        + [ctypes.POINTER(_c_p), _c_i32]),
     "infini_attn_status_string": (ctypes.c_char_p, [_c_i32]),
     "infini_attn_version": (_c_i32, []),
 }
@@ -312,3 +319,81 @@ def backward(q, k, v, beta, M0, z0, seg_len, rule, out, lse, d_out, dM_final=Non
     if st != 0:
         raise InfiniAttnError(st, "infini_attn_backward")
     return dq, dk, dv, dbeta, dM0, dz0
+
+
+def block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype=torch.bfloat16):
+    """Workspace bytes of infini_attn_block_forward with these sizes."""
+    n = _c_size(0)
+    st = load_library().infini_attn_block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len,
+                                                         RULES[rule], DTYPES[dtype],
+                                                         ctypes.byref(n))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_block_workspace_size")
+    return int(n.value)
+
+
+def block_forward(x, w_qkv, w_o, beta, M0, z0, seg_len, rule, Hq, Hkv, *, y=None, M_final=None,
+                  z_final=None, workspace=None, stream=None, events=None):
+    """The block with its projections on the GPU (infini_attn_block_forward).
+
+    x [B,L,d_model] bfloat16; w_qkv [(Hq+2Hkv)*d, d_model] and w_o
+    [d_model, Hq*d] bfloat16 (linear-layer layout); beta [Hq], M0 [B,Hkv,d,d],
+    z0 [B,Hkv,d] float32. Returns (y [B,L,d_model], M_final, z_final).
+    ``events`` (up to 4 torch.cuda.Event) are recorded before the input
+    projection, after it, after the block and after the output projection.
+    Asynchronous on ``stream`` (or torch's current stream).
+    """
+    B, L, d_model = x.shape
+    if w_qkv.dim() != 2 or w_qkv.shape[1] != d_model or w_qkv.shape[0] % (Hq + 2 * Hkv):
+        raise ValueError("w_qkv must be [(Hq+2Hkv)*d, d_model]")
+    d = w_qkv.shape[0] // (Hq + 2 * Hkv)
+    if w_o.shape != (d_model, Hq * d):
+        raise ValueError("w_o must be [d_model, Hq*d]")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+        raise ValueError("beta, M0 or z0 has the wrong shape")
+    if any(t.dtype != torch.bfloat16 for t in (x, w_qkv, w_o)):
+        raise TypeError("x, w_qkv and w_o must be bfloat16")
+    if any(t.dtype != torch.float32 for t in (beta, M0, z0)):
+        raise TypeError("beta, M0 and z0 must be float32")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    for t in (x, w_qkv, w_o, beta, M0, z0):
+        if t.device != dev:
+            raise ValueError("all tensors must be on one GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if y is None:
+        y = torch.empty_like(x)
+    if M_final is None:
+        M_final = torch.empty_like(M0)
+    if z_final is None:
+        z_final = torch.empty_like(z0)
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor like x")
+    if workspace is None:
+        workspace = torch.empty(block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule),
+                                dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    args = [B, L, d_model, Hq, Hkv, d, seg_len, RULES[rule], DTYPES[x.dtype],
+            _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(beta), _ptr(M0), _ptr(z0),
+            _ptr(y), _ptr(M_final), _ptr(z_final),
+            _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream.cuda_stream)]
+    if events:
+        if any(e.cuda_event == 0 for e in events):
+            raise ValueError("record every event once before passing it (torch creates the "
+                             "HIP event at its first record)")
+        handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib.infini_attn_block_forward_timed(*args, handles, len(events))
+        name = "infini_attn_block_forward_timed"
+    else:
+        st = lib.infini_attn_block_forward(*args)
+        name = "infini_attn_block_forward"
+    if st != 0:
+        raise InfiniAttnError(st, name)
+    return y, M_final, z_final

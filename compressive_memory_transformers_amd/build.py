@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libinfini_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "scan.hip", "affine.hip", "attn.hip", "decode.hip", "bwd.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "proj.hip"]
 ARCH = "gfx950"
 
 COMPILE_FLAGS = [

@@ -862,6 +862,188 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   return INFINI_OK;
 }
 
+// ---- the block with its projections -------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of infini_attn_block_forward: q, k, v (head-major, bf16), the
+// gated result a (head-major, bf16), then a full forward workspace.
+struct BlockLayout {
+  size_t q, k, v, a, fwd, fwd_bytes, total;
+};
+
+infini_status_t block_layout(int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv,
+                             int64_t d, int64_t seg_len, int32_t rule, int32_t dtype,
+                             BlockLayout* lay) {
+  Plan p;
+  infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  if (d_model < 1) return INFINI_ERR_INVALID_ARG;
+  if (dtype != INFINI_BF16) return INFINI_ERR_UNSUPPORTED;  // the projections are bf16 MFMA
+  if (d_model % 32 != 0) return INFINI_ERR_UNSUPPORTED;     // K steps of 32
+  // 32-bit row and column indices in the projection kernel, 32-bit lane
+  // offsets within its loads (rows of one 256-row tile)
+  const int64_t M = B * L, Nqkv = (Hq + 2 * Hkv) * d;
+  if (M >= INT32_MAX || Nqkv >= INT32_MAX || d_model >= (1 << 22)) return INFINI_ERR_INVALID_ARG;
+  if ((256 * Hq + Hq * L + L) * d * 2 >= (int64_t)UINT32_MAX) return INFINI_ERR_INVALID_ARG;
+  const int64_t tiles = ((M + 255) / 256) * (((Nqkv > d_model ? Nqkv : d_model) + 255) / 256);
+  if (tiles > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  if (lay) {
+    const size_t nq = align_up((size_t)(B * Hq * L * d) * 2);
+    const size_t nkv = align_up((size_t)(B * Hkv * L * d) * 2);
+    lay->q = 0;
+    lay->k = nq;
+    lay->v = nq + nkv;
+    lay->a = nq + 2 * nkv;
+    lay->fwd = 2 * nq + 2 * nkv;
+    lay->fwd_bytes = p.fixed + p.per_seg * (size_t)p.S;
+    lay->total = lay->fwd + lay->fwd_bytes;
+  }
+  return INFINI_OK;
+}
+
+infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv,
+                           int64_t d, int64_t seg_len, int32_t rule, int32_t dtype,
+                           const void* x, const void* w_qkv, const void* w_o, const float* beta,
+                           const float* M0, const float* z0, void* y, float* M_final,
+                           float* z_final, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events, int32_t n_events) {
+  BlockLayout lay;
+  infini_status_t st = block_layout(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, &lay);
+  if (st != INFINI_OK) return st;
+  const void* ptrs[] = {x, w_qkv, w_o, beta, M0, z0, y, M_final, z_final, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr) return INFINI_ERR_INVALID_ARG;
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return INFINI_ERR_MISALIGNED;
+  if (workspace_bytes < lay.total) return INFINI_ERR_WORKSPACE;
+  if (n_events < 0 || (n_events > 0 && events == nullptr)) return INFINI_ERR_INVALID_ARG;
+  for (int32_t e = 0; e < n_events; ++e)
+    if (events[e] == nullptr) return INFINI_ERR_INVALID_ARG;
+
+  const int64_t M = B * L, Nqkv = (Hq + 2 * Hkv) * d;
+  const size_t nx = (size_t)(M * d_model) * 2, ny = nx;
+  const size_t nwq = (size_t)(Nqkv * d_model) * 2, nwo = (size_t)(d_model * Hq * d) * 2;
+  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  struct Range { const void* p; size_t n; };
+  const Range inputs[] = {{x, nx}, {w_qkv, nwq}, {w_o, nwo}, {beta, (size_t)Hq * 4},
+                          {M0, nM}, {z0, nz}};
+  // y and the workspace overlap nothing; M_final / z_final may coincide
+  // exactly with M0 / z0 (the forward checks those among themselves)
+  for (const Range& r : inputs) {
+    if (overlap(y, ny, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+    if (overlap(workspace, workspace_bytes, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+    if (r.p != M0 && overlap(M_final, nM, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+    if (r.p != z0 && overlap(z_final, nz, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+  }
+  if (overlap(y, ny, workspace, workspace_bytes) || overlap(y, ny, M_final, nM) ||
+      overlap(y, ny, z_final, nz) || overlap(workspace, workspace_bytes, M_final, nM) ||
+      overlap(workspace, workspace_bytes, z_final, nz))
+    return INFINI_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  void* q = ws + lay.q;
+  void* k = ws + lay.k;
+  void* v = ws + lay.v;
+  void* a = ws + lay.a;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int slot) -> bool {
+    if (slot >= n_events) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(events[slot]), s) == hipSuccess;
+  };
+
+  // 1. q, k, v = x W_qkv^T, split into heads
+  infini::ProjArgs pa{};
+  pa.a = x;
+  pa.w = w_qkv;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.M = M;
+  pa.N = Nqkv;
+  pa.K = d_model;
+  pa.lda = d_model;
+  pa.a_elems = M * d_model;
+  pa.L = L;
+  pa.d = d;
+  pa.Ha = 1;
+  pa.Hq = Hq;
+  pa.Hkv = Hkv;
+  pa.a_mode = infini::kProjRows;
+  pa.c_mode = infini::kProjHeads;
+  if (!mark(0)) return INFINI_ERR_HIP;
+  if (infini::launch_proj(pa, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (!mark(1)) return INFINI_ERR_HIP;
+
+  // 2. the block: a, M_final, z_final
+  st = forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, a, M_final,
+                    z_final, nullptr, ws + lay.fwd, lay.fwd_bytes, stream, nullptr, 0);
+  if (st != INFINI_OK) return st;
+  if (!mark(2)) return INFINI_ERR_HIP;
+
+  // 3. y = concat_h(a_h) W_o^T, a read in place (head-major)
+  infini::ProjArgs po{};
+  po.a = a;
+  po.w = w_o;
+  po.c = y;
+  po.M = M;
+  po.N = d_model;
+  po.K = Hq * d;
+  po.ldc = d_model;
+  po.a_elems = B * Hq * L * d;
+  po.L = L;
+  po.d = d;
+  po.Ha = Hq;
+  po.Hq = Hq;
+  po.Hkv = Hkv;
+  po.a_mode = infini::kProjGather;
+  po.c_mode = infini::kProjRows;
+  if (infini::launch_proj(po, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (!mark(3)) return INFINI_ERR_HIP;
+  return INFINI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_block_workspace_size(int64_t B, int64_t L, int64_t d_model,
+                                                 int64_t Hq, int64_t Hkv, int64_t d,
+                                                 int64_t seg_len, int32_t rule, int32_t dtype,
+                                                 size_t* bytes) {
+  if (bytes == nullptr) return INFINI_ERR_INVALID_ARG;
+  BlockLayout lay;
+  const infini_status_t st =
+      block_layout(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, &lay);
+  if (st != INFINI_OK) return st;
+  *bytes = lay.total;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_block_forward(int64_t B, int64_t L, int64_t d_model, int64_t Hq,
+                                          int64_t Hkv, int64_t d, int64_t seg_len,
+                                          int32_t rule, int32_t dtype, const void* x,
+                                          const void* w_qkv, const void* w_o, const float* beta,
+                                          const float* M0, const float* z0, void* y,
+                                          float* M_final, float* z_final, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return block_impl(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, x, w_qkv, w_o, beta, M0,
+                    z0, y, M_final, z_final, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+infini_status_t infini_attn_block_forward_timed(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype, const void* x, const void* w_qkv, const void* w_o,
+    const float* beta, const float* M0, const float* z0, void* y, float* M_final,
+    float* z_final, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events) {
+  return block_impl(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, x, w_qkv, w_o, beta, M0,
+                    z0, y, M_final, z_final, workspace, workspace_bytes, stream, events,
+                    n_events);
+}
+
 const char* infini_attn_status_string(int32_t status) {
   switch (status) {
     case INFINI_OK: return "ok";

@@ -197,4 +197,28 @@ hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipSt
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
 
+// The projections around the block (proj.hip): C[m][n] = sum_k A[m][k] W[n][k]
+// in bf16 with float accumulation, W [N][K] row-major. A is read as rows
+// (a_mode kProjRows: A[m][k] = a[m lda + k]) or gathered from a head-major
+// [B][Ha][L][d] tensor (kProjGather: A[b L + t][h d + j] = a[((b Ha + h) L + t)
+// d + j]); C is written as rows (kProjRows: c[m ldc + n]) or split into heads
+// (kProjHeads: column h d + j goes to q, k or v [b][h][t][j], the Hq query
+// heads first, then Hkv key heads, then Hkv value heads). Requires K % 32 == 0,
+// N % 4 == 0 and, for a gathered A, d % 32 == 0.
+constexpr int kProjRows = 0, kProjGather = 1, kProjHeads = 1;
+struct ProjArgs {
+  const void* a;  // bf16 throughout
+  const void* w;
+  void* c;
+  void* q;
+  void* k;
+  void* v;
+  int64_t M, N, K;
+  int64_t lda, ldc;
+  int64_t a_elems;  // elements of the tensor a points into (bounds of its loads)
+  int64_t L, d, Ha, Hq, Hkv;
+  int32_t a_mode, c_mode;
+};
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
+
 }  // namespace infini

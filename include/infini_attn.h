@@ -1,6 +1,7 @@
 /*
  * infini_attn.h -- C ABI of the Infini-attention block on gfx950: forward,
- * streaming decode step and backward pass.
+ * streaming decode step, backward pass, and the block with its input and
+ * output projections.
  *
  * The operation ("Infini-Attention" (AI Wiki), sections "What happens inside
  * the Infini-attention block?" and "How does the compressive memory work?";
@@ -229,6 +230,63 @@ infini_status_t infini_attn_backward(
     const float* dM_final, const float* dz_final,
     void* dq, void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The block with its projections ("Infini-Attention" (AI Wiki), "What happens
+ * inside the Infini-attention block?": the layer forms the usual query, key
+ * and value projections of its input tokens, runs both attention paths on
+ * them, and sends the gated result through the output matrix). Readings of
+ * what the page leaves open: no biases; weights are stored as a linear layer
+ * stores them, (out_features, in_features), and applied as x W^T; w_qkv
+ * stacks the Hq query heads' d rows each, then the Hkv key heads', then the
+ * Hkv value heads'; the output projection reads the heads' gated results
+ * concatenated in head order (feature h d + j is element j of head h).
+ *
+ *   q, k, v            = the heads of x w_qkv^T
+ *   a, M_final, z_final = infini_attn_forward(q, k, v, beta, M0, z0, ...)
+ *   y                  = concat_h(a_h) w_o^T
+ *
+ * Layouts (row-major, contiguous, device memory):
+ *   x, y       [B][L][d_model]         bf16
+ *   w_qkv      [(Hq + 2 Hkv) d][d_model] bf16
+ *   w_o        [d_model][Hq d]         bf16
+ *   beta, M0, z0, M_final, z_final     as in infini_attn_forward.
+ * q, k, v and a are kept in the workspace in bf16 (each rounded once, the
+ * products accumulating in float), head-major as infini_attn_forward takes
+ * them; the output projection reads a in place. The workspace begins with q,
+ * k, v and a, in that order, each region rounded up to a multiple of 256
+ * bytes (so a caller may read the projections back after the call).
+ *
+ * Sizes and errors: dtype must be INFINI_BF16 and d_model a multiple of 32
+ * (else INFINI_ERR_UNSUPPORTED); B L < 2^31 and d_model < 2^22 (else
+ * INFINI_ERR_INVALID_ARG); the rest as infini_attn_forward. The workspace must
+ * hold infini_attn_block_workspace_size bytes (one window: the whole call).
+ * y and the workspace overlap no argument; M_final may be M0 and z_final may
+ * be z0. Asynchronous on `stream`.
+ *
+ * infini_attn_block_forward_timed is the same call; events[0..3], those of
+ * them passed (n_events <= 4 are used), are recorded on `stream` before the
+ * input projection, after it, after the block and after the output
+ * projection.
+ */
+infini_status_t infini_attn_block_workspace_size(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d,
+    int64_t seg_len, int32_t rule, int32_t dtype, size_t* bytes);
+infini_status_t infini_attn_block_forward(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d,
+    int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* x, const void* w_qkv, const void* w_o, const float* beta,
+    const float* M0, const float* z0,
+    void* y, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream);
+infini_status_t infini_attn_block_forward_timed(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d,
+    int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* x, const void* w_qkv, const void* w_o, const float* beta,
+    const float* M0, const float* z0,
+    void* y, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
 
 const char* infini_attn_status_string(int32_t status);
 
