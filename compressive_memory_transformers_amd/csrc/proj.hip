@@ -102,18 +102,17 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
   const bf16* W = static_cast<const bf16*>(a.w);
   const int nk = (int)(a.K / kBK);
 
-  // d is 32, 64 or 128: head and column of a K offset by shift and mask
+  // d is 32, 64 or 128: head and column of an offset by shift and mask
   const int ld = __builtin_ctz((unsigned)a.d);
+  // element offsets of the next stage's slabs, advanced stage by stage: a
+  // gathered A moves 32 columns within a head, then to the next head's rows
+  int64_t a_next = a.a_mode == kProjGather ? b0 * a.Ha * a.L * a.d : m0 * a.lda;
+  int64_t w_next = n0 * a.K;
+  const int64_t a_jump = a.L * a.d - a.d + kBK;
+  int k_next = 0;
   auto issue = [&](int kt) {
-    const int k0 = kt * kBK;
-    int64_t aoff;
-    if (a.a_mode == kProjGather)
-      aoff = (b0 * a.Ha + (k0 >> ld)) * a.L * a.d + (k0 & (a.d - 1));
-    else
-      aoff = m0 * a.lda + k0;
-    const int64_t woff = n0 * a.K + k0;
-    const u32x4 ra = asm_rsrc(A + aoff, rsrc_bytes(a.a_elems * 2, aoff * 2));
-    const u32x4 rw = asm_rsrc(W + woff, rsrc_bytes(a.N * a.K * 2, woff * 2));
+    const u32x4 ra = asm_rsrc(A + a_next, rsrc_bytes(a.a_elems * 2, a_next * 2));
+    const u32x4 rw = asm_rsrc(W + w_next, rsrc_bytes(a.N * a.K * 2, w_next * 2));
     const int buf = kt & (kBuf - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -121,6 +120,9 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
       dma16_asm(&As[buf][16 * g * kBK], ra, va[i], 0u);
       dma16_asm(&Ws[buf][16 * g * kBK], rw, vw[i], 0u);
     }
+    k_next += kBK;
+    a_next += (a.a_mode == kProjGather && (k_next & (a.d - 1)) == 0) ? a_jump : kBK;
+    w_next += kBK;
   };
 
   // ---- compute lanes ----------------------------------------------------------
@@ -145,24 +147,37 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
     else
       wait_vmcnt<0>();
     __syncthreads();  // stage kt complete everywhere; stage kt - 1's reads done
-    if (kt + kBuf - 1 < nk) issue(kt + kBuf - 1);  // into the buffer stage kt - 1 used
 
+    // both k16 steps' fragments at once; the first step's products start as
+    // soon as its six reads land, and the DMA of stage kt + 3 (into the
+    // buffer stage kt - 1 used) goes out between the two steps, its scalar
+    // address work overlapping the products in flight. (Timed against a
+    // barrier between the two steps with the next stage's reads behind it:
+    // this order is faster, the DMA path rather than the barrier being what
+    // limits the loop.)
     const int buf = kt & (kBuf - 1);
     const bf16* Ab = &As[buf][(wm * 64) * kBK];
     const bf16* Wb = &Ws[buf][(wn * 128) * kBK];
+    bf16x8 xf[2][2], wf[2][4];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint32_t fo = kk ? fo1 : fo0;
-      bf16x8 xf[2], wf[4];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) xf[mi] = load8<bf16>(lds_at(Ab, fo + mi * 32 * kBK * 2));
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) wf[ni] = load8<bf16>(lds_at(Wb, fo + ni * 32 * kBK * 2));
+      for (int mi = 0; mi < 2; ++mi)
+        xf[kk][mi] = load8<bf16>(lds_at(Ab, fo + mi * 32 * kBK * 2));
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) mma32(acc[ni][mi], wf[ni], xf[mi]);
+        wf[kk][ni] = load8<bf16>(lds_at(Wb, fo + ni * 32 * kBK * 2));
     }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) mma32(acc[ni][mi], wf[0][ni], xf[0][mi]);
+    if (kt + kBuf - 1 < nk) issue(kt + kBuf - 1);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) mma32(acc[ni][mi], wf[1][ni], xf[1][mi]);
   }
 
   // ---- epilogue: lane holds C[m][n .. n + 3] for each (ni, mi, quad) -----------
