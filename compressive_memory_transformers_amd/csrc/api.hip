@@ -726,42 +726,49 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ba.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
 
   const int64_t LD = L * d, ND = seg_len * d, DD = d * d;
-  // 2. retrieval. Query-side products: hi = b * Hq + h, M_{s-1} of unit hi / G.
-  {
-    infini::GemmArgs g = gemm_args(q, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
-    g.lda = g.ldb = g.ldc = D;
-    g.a_hi = g.c_hi = LD;
-    g.a_lo = g.c_lo = ND;
-    g.b_div = (int32_t)G;
-    g.b_hi = S * DD;
-    g.b_lo = DD;
-    g.tb = 1;  // op(B) = M, stored as M^T
-    g.a_sigma = 1;
-    g.clip = 1;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
-  }
-  if (infini::launch_bwd_retrieval_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
-  {
-    infini::GemmArgs g = gemm_args(ba.dn, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
-    g.lda = g.ldb = g.ldc = D;
-    g.a_hi = g.c_hi = LD;
-    g.a_lo = g.c_lo = ND;
-    g.b_div = (int32_t)G;
-    g.b_hi = S * DD;
-    g.b_lo = DD;
-    g.tb = 0;  // op(B) = M^T as stored
-    g.clip = 1;
-    // epilogue: nm = (dn M^T + dden z^T) sigma'(Q), the retrieval part of dQ
-    g.epi = 1;
-    g.epi_w = ba.dden;
-    g.w_hi = L;
-    g.w_lo = seg_len;
-    g.epi_z = F(lay.snapZ);
-    g.z_div = (int32_t)G;
-    g.z_hi = S * d;
-    g.z_lo = d;
-    g.epi_x = q;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  // 2. retrieval. bf16 with d in {64, 128}: one fused kernel per 128 query
+  // rows. Otherwise two products and a row kernel (query-side products:
+  // hi = b * Hq + h, M_{s-1} of unit hi / G).
+  const bool bwd_mfma = infini::attn_bwd_mfma_supported(dtype, D, (int)G);
+  if (bwd_mfma) {
+    if (infini::launch_bwd_retrieval_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  } else {
+    {
+      infini::GemmArgs g = gemm_args(q, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
+      g.lda = g.ldb = g.ldc = D;
+      g.a_hi = g.c_hi = LD;
+      g.a_lo = g.c_lo = ND;
+      g.b_div = (int32_t)G;
+      g.b_hi = S * DD;
+      g.b_lo = DD;
+      g.tb = 1;  // op(B) = M, stored as M^T
+      g.a_sigma = 1;
+      g.clip = 1;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
+    if (infini::launch_bwd_retrieval_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+    {
+      infini::GemmArgs g = gemm_args(ba.dn, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
+      g.lda = g.ldb = g.ldc = D;
+      g.a_hi = g.c_hi = LD;
+      g.a_lo = g.c_lo = ND;
+      g.b_div = (int32_t)G;
+      g.b_hi = S * DD;
+      g.b_lo = DD;
+      g.tb = 0;  // op(B) = M^T as stored
+      g.clip = 1;
+      // epilogue: nm = (dn M^T + dden z^T) sigma'(Q), the retrieval part of dQ
+      g.epi = 1;
+      g.epi_w = ba.dden;
+      g.w_hi = L;
+      g.w_lo = seg_len;
+      g.epi_z = F(lay.snapZ);
+      g.z_div = (int32_t)G;
+      g.z_hi = S * d;
+      g.z_lo = d;
+      g.epi_x = q;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
   }
   for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
     const size_t off = (size_t)(hg * LD) * e;

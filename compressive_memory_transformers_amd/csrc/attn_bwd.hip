@@ -349,6 +349,180 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
     }
 }
 
+// ---- retrieval, fused: one workgroup per 128 query rows of one head ---------
+//
+// "Infini-Attention" (AI Wiki), "What happens inside the Infini-attention
+// block?": A_mem = sigma(q) M / (sigma(q) . z) with M = M_{s-1}, z = z_{s-1},
+// out = g A_mem + (1 - g) A_dot. For each query row t, from d_out, out and
+// the forward's snapshot (M^T in bf16, z in float):
+//   n = sigma(q) M, den = sigma(q) . z, A_mem = n / den,
+//   dam = d_out . A_mem, doo = d_out . out,
+//   delta_t = doo - g dam (the softmax row term: out - g A_mem = (1 - g) A_dot),
+//   dg_t = (dam - doo) / (1 - g), dden_t = -g dam / den, dn = g d_out / den,
+//   nm_t = (dn M^T + dden_t z) * sigma'(q)  (the retrieval part of dQ),
+// and dn itself (bf16, for the products into dL/dM_{s-1}). Both products run
+// on the matrix cores with M^T in LDS (the K layout): n^T = M^T sigma(q)^T as
+// the query-major kernel forms S^T, then dQ_ret^T = M dn^T through
+// transposing reads, dn in the accumulator-derived fragment order that
+// tr_frag_k expects. sigma(q) enters the product in bf16, den in float.
+template <int D>
+__global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) {
+  constexpr int BM = 32 * kNW, NC = D / 16, NT = D / 64, NJB = D / 32;
+  __shared__ __align__(1024) bf16 Ms0[64 * D];
+  __shared__ __align__(1024) bf16 Ms1[NT > 1 ? 64 * D : 8];
+  __shared__ __align__(16) float zs[D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  // the query-major kernel's tile order: the query tiles and heads of one
+  // (unit, segment), which share its snapshot, run together on one XCD
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int G = a.Hq / a.Hkv;
+  const int in_grp = n_qt * G;
+  const int grp = t / in_grp, rr = t % in_grp;
+  const int qt = rr / G, hg = rr % G;
+  const int sl = grp % a.S, unit = grp / a.S;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv, hq = kvh * G + hg;
+  const int64_t seg_start = (int64_t)sl * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int q0 = qt * BM;
+  if (q0 >= n_s) return;
+  const int64_t rbase = ((int64_t)b * a.Hq + hq) * a.L + seg_start;
+  const int row = q0 + w + kNW * i;
+  const bool live = row < n_s;
+
+  const bf16* Mt = static_cast<const bf16*>(a.snapM) + ((int64_t)unit * a.S + sl) * D * D;
+  DmaTile<D, kNW, 64> tile;
+  tile.init(w, lane);
+  tile.template issue<true>(Mt, Ms0, 0, D, w);
+  if constexpr (NT > 1) tile.template issue<true>(Mt, Ms1, 64, D, w);
+  if (tid < D) zs[tid] = a.snapZ[((int64_t)unit * a.S + sl) * D + tid];
+
+  const bf16* Q = static_cast<const bf16*>(a.q) + (rbase + row) * D;
+  const bf16* O = static_cast<const bf16*>(a.out) + (rbase + row) * D;
+  const bf16* dO = static_cast<const bf16*>(a.dout) + (rbase + row) * D;
+  bf16x8 qf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) qf[cc] = live ? load8<bf16>(Q + 16 * cc + 8 * h) : zero_frag<bf16>();
+  const float g = 1.f / (1.f + __expf(-a.beta[hq]));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // sigma(q): bf16 operand of n^T, float in den (this lane's half of the columns)
+  bf16x8 sqf[NC];
+  float den = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sg = feature_map((float)qf[cc][e]);
+      sqf[cc][e] = (bf16)sg;
+      den += sg * zs[16 * cc + 8 * h + e];
+    }
+  den += __shfl_xor(den, 32);
+
+  bf16* const Ms[2] = {Ms0, NT > 1 ? Ms1 : Ms0};
+  const uint32_t ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+  f32x16 nacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    nacc[jb] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint32_t o = (ko ^ (32u * cc)) + 2 * 32 * (jb & 1) * D;
+      mma32(nacc[jb], load8<bf16>(lds_at(Ms[jb >> 1], o)), sqf[cc]);
+    }
+  }
+
+  // this lane: row `row`, columns j = 32 jb + 8 rq + 4 h + 0..3 of n
+  float dam = 0.f, doo = 0.f;
+  bf16x4 dov[NJB][4];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int col = 32 * jb + 8 * rq + 4 * h;
+      bf16x4 o4;
+      if (live) {
+        dov[jb][rq] = load4<bf16>(dO + col);
+        o4 = load4<bf16>(O + col);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dov[jb][rq][j] = o4[j] = (bf16)0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float dv = (float)dov[jb][rq][j];
+        dam += dv * nacc[jb][4 * rq + j];
+        doo += dv * (float)o4[j];
+      }
+    }
+  dam += __shfl_xor(dam, 32);
+  doo += __shfl_xor(doo, 32);
+  const float inv_den = 1.f / den;
+  dam *= inv_den;
+  const float dden = -g * dam * inv_den;
+  const float gd = g * inv_den;
+  if (live && h == 0) {
+    a.delta[rbase + row] = doo - g * dam;
+    a.dg[rbase + row] = (dam - doo) / (1.f - g);
+    a.dden[rbase + row] = dden;
+  }
+
+  // dn = g d_out / den: stored for the products into dL/dM_{s-1}, and as the
+  // B operand of dQ_ret^T (fragment pc of 64-row tile ts from registers
+  // 8 (pc % 2) .. + 7 of accumulator block 2 ts + pc / 2)
+  bf16* dn = static_cast<bf16*>(a.dn) + (rbase + row) * D;
+  bf16x8 dnf[NT][4];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      bf16x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[j] = (bf16)(gd * (float)dov[jb][rq][j]);
+        const int r = 4 * rq + j;
+        dnf[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = y[j];
+      }
+      if (live) store4<bf16>(dn + 32 * jb + 8 * rq + 4 * h, y);
+    }
+
+  f32x16 dacc[NJB];
+#pragma unroll
+  for (int db = 0; db < NJB; ++db) {
+    dacc[db] = zero16();
+    const uint32_t t0 = tr_offset_k<D>(lane, db, 0), t1 = tr_offset_k<D>(lane, db, 1);
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc)
+        mma32(dacc[db], tr_frag_k<D>(Ms[ts], t0, t1, pc), dnf[ts][pc]);
+  }
+  if (!live) return;
+  float* nm = a.nm + (rbase + row) * D;
+#pragma unroll
+  for (int db = 0; db < NJB; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int col = 32 * db + 8 * rq + 4 * h;
+      const bf16x4 q4 = load4<bf16>(Q + col);
+      f32x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)q4[j];
+        const float ds = x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+        y[j] = (dacc[db][4 * rq + j] + dden * zs[col + j]) * ds;
+      }
+      *reinterpret_cast<f32x4*>(nm + col) = y;
+    }
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const int64_t units = (int64_t)a.B * a.Hkv;
@@ -363,10 +537,29 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_retr_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  const int64_t eff = a.seg_len < a.L ? a.seg_len : a.L;
+  const int n_qt = (int)((eff + 32 * kNW - 1) / (32 * kNW));
+  const int64_t grid = units * a.S * n_qt * (a.Hq / a.Hkv);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((retr_kernel<D>), dim3((unsigned)grid), dim3(kNW * 64), 0, s, a, n_qt);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool attn_bwd_mfma_supported(int dtype, int d, int group) {
   return dtype == kBF16 && (d == 64 || d == 128) && group <= kMaxG;
+}
+
+hipError_t launch_bwd_retrieval_mfma(int d, const BwdArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_retr_d<64>(a, stream);
+    case 128: return launch_retr_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream) {

@@ -174,6 +174,9 @@ hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool 
 // at most 64 query heads per KV head.
 bool attn_bwd_mfma_supported(int dtype, int d, int group);
 hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream);
+// The retrieval's backward in one MFMA kernel (bf16, same support as above):
+// delta, dg, dden, dn and nm from q, out, d_out and the snapshots.
+hipError_t launch_bwd_retrieval_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
 // Row step of the delta rule's update backward (after p_buf, du_buf).

@@ -8,7 +8,8 @@
 // XOR-swizzled within a row instead of padded:
 //   "K" layout: chunk c of row r sits at c ^ swz_k(r), so the 16 rows that a
 //      quarter-wave reads for one MFMA operand (same logical chunk, one row
-//      per lane) hit 16 bank groups;
+//      per lane) hit 16 bank groups, and so do the transposing reads of the
+//      same tile (tr_offset_k);
 //   "V" layout: chunk c of row r sits at c ^ swz_v(r), for operands whose
 //      k index runs down the rows (rows of the tile = k, columns = the
 //      operand's rows): they are read with ds_read_b64_tr_b16, which hands
@@ -25,8 +26,16 @@
 
 namespace infini {
 
+// The K layout's swizzle serves three reads without bank conflicts: 16
+// consecutive rows at one logical chunk (the row-wise operand loads: a
+// bijection of r mod 16 onto the chunks, for d = 64 per row parity); the
+// transposing reads of 4 rows x 4 chunks (rows 4k .. 4k + 3 get distinct
+// values of swz >> 2 for d = 128, rows r and r + 2 distinct bit 2 for d = 64);
+// and, for d = 128, two rows of 8 chunk pairs (rows r, r + 1 of opposite
+// parity). It has period 16 in r.
 template <int D> __device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D == 128 ? 4 * (r & 3) + (((r >> 2) & 3) ^ (r & 1))
+                  : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 template <int D> __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
