@@ -158,20 +158,57 @@ __global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
     step(j, std::integral_constant<int, 0>{});
     if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{});
   }
+  // The retrieval part of dQ, (M dn^T + dden z) sigma'(q): the snapshot M^T
+  // comes into the K buffers (free after the last tile), dn (bf16, written
+  // by the retrieval kernel) is read straight into the B operand in the
+  // accumulator-derived order tr_frag_k expects (fragment pc of 64-row tile
+  // ts holds columns 64 ts + 16 pc + 4 h + 0..3 and + 8 .. + 11).
+  constexpr int NT = D / 64;
+  const bf16* Mt = static_cast<const bf16*>(a.snapM) + ((int64_t)unit * a.S + sl) * D * D;
+  tile.template issue<true>(Mt, Ks0, 0, D, w);
+  if constexpr (NT > 1) tile.template issue<true>(Mt, Ks1, 64, D, w);
+  const bf16* dnr = static_cast<const bf16*>(a.dn) + (rbase + row) * D;
+  bf16x8 dnf[NT][4];
+#pragma unroll
+  for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {
+      const int j0 = 64 * ts + 16 * pc + 4 * h;
+      dnf[ts][pc] = live ? load4x2<bf16>(dnr + j0, dnr + j0 + 8) : zero_frag<bf16>();
+    }
+  const float dden = live ? a.dden[rbase + row] : 0.f;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 racc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    racc[db] = zero16();
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc)
+        mma32(racc[db], tr_frag_k<D>(Ks[ts], st.tk[0][db], st.tk[1][db], pc), dnf[ts][pc]);
+  }
   if (!live) return;
-  // dq = dQ^T^T / sqrt(d) + the retrieval part (a.nm, float)
+  // dq = dQ^T^T / sqrt(d) + (dQ_ret + dden z) sigma'(q)
   const float inv_sqrt_d = a.scale_log2 / kLog2e;
-  const float* nm = a.nm + (rbase + row) * D;
+  const float* z = a.snapZ + ((int64_t)unit * a.S + sl) * D;
   bf16* dq = static_cast<bf16*>(a.dq) + (rbase + row) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int col = 32 * db + 8 * rq + 4 * h;
-      const f32x4 m = *reinterpret_cast<const f32x4*>(nm + col);
+      const bf16x4 q4 = load4<bf16>(Q + col);
+      const f32x4 z4 = *reinterpret_cast<const f32x4*>(z + col);
       bf16x4 y;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = (bf16)(st.acc[db][4 * rq + j] * inv_sqrt_d + m[j]);
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)q4[j];
+        const float ds = x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+        y[j] = (bf16)(st.acc[db][4 * rq + j] * inv_sqrt_d +
+                      (racc[db][4 * rq + j] + dden * z4[j]) * ds);
+      }
       store4<bf16>(dq + col, y);
     }
 }
@@ -359,12 +396,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
 //   dam = d_out . A_mem, doo = d_out . out,
 //   delta_t = doo - g dam (the softmax row term: out - g A_mem = (1 - g) A_dot),
 //   dg_t = (dam - doo) / (1 - g), dden_t = -g dam / den, dn = g d_out / den,
-//   nm_t = (dn M^T + dden_t z) * sigma'(q)  (the retrieval part of dQ),
-// and dn itself (bf16, for the products into dL/dM_{s-1}). Both products run
-// on the matrix cores with M^T in LDS (the K layout): n^T = M^T sigma(q)^T as
-// the query-major kernel forms S^T, then dQ_ret^T = M dn^T through
-// transposing reads, dn in the accumulator-derived fragment order that
-// tr_frag_k expects. sigma(q) enters the product in bf16, den in float.
+// and dn itself (bf16). The query-major kernel then adds the retrieval part
+// of dQ, (dn M^T + dden_t z) * sigma'(q), in its epilogue; dn also feeds the
+// products into dL/dM_{s-1}. n^T = M^T sigma(q)^T runs on the matrix cores
+// with M^T in LDS (the K layout), as the query-major kernel forms S^T.
+// sigma(q) enters the product in bf16, den in float.
 template <int D>
 __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) {
   constexpr int BM = 32 * kNW, NC = D / 16, NT = D / 64, NJB = D / 32;
@@ -474,52 +510,18 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
     a.dden[rbase + row] = dden;
   }
 
-  // dn = g d_out / den: stored for the products into dL/dM_{s-1}, and as the
-  // B operand of dQ_ret^T (fragment pc of 64-row tile ts from registers
-  // 8 (pc % 2) .. + 7 of accumulator block 2 ts + pc / 2)
+  // dn = g d_out / den, stored (bf16) for the query-major kernel, which forms
+  // the retrieval part of dQ from it, and for the products into dL/dM_{s-1}
+  if (!live) return;
   bf16* dn = static_cast<bf16*>(a.dn) + (rbase + row) * D;
-  bf16x8 dnf[NT][4];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       bf16x4 y;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[j] = (bf16)(gd * (float)dov[jb][rq][j]);
-        const int r = 4 * rq + j;
-        dnf[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = y[j];
-      }
-      if (live) store4<bf16>(dn + 32 * jb + 8 * rq + 4 * h, y);
-    }
-
-  f32x16 dacc[NJB];
-#pragma unroll
-  for (int db = 0; db < NJB; ++db) {
-    dacc[db] = zero16();
-    const uint32_t t0 = tr_offset_k<D>(lane, db, 0), t1 = tr_offset_k<D>(lane, db, 1);
-#pragma unroll
-    for (int ts = 0; ts < NT; ++ts)
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc)
-        mma32(dacc[db], tr_frag_k<D>(Ms[ts], t0, t1, pc), dnf[ts][pc]);
-  }
-  if (!live) return;
-  float* nm = a.nm + (rbase + row) * D;
-#pragma unroll
-  for (int db = 0; db < NJB; ++db)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int col = 32 * db + 8 * rq + 4 * h;
-      const bf16x4 q4 = load4<bf16>(Q + col);
-      f32x4 y;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = (float)q4[j];
-        const float ds = x > 0.f ? 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
-        y[j] = (dacc[db][4 * rq + j] + dden * zs[col + j]) * ds;
-      }
-      *reinterpret_cast<f32x4*>(nm + col) = y;
+      for (int j = 0; j < 4; ++j) y[j] = (bf16)(gd * (float)dov[jb][rq][j]);
+      store4<bf16>(dn + 32 * jb + 8 * rq + 4 * h, y);
     }
 }
 
