@@ -283,9 +283,15 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
   const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
   const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
-  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
-  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
+  // rows of `heads` consecutive heads (one in the recurrence), chunk c of
+  // the run being chunk c % n_c of head c / n_c
+  const int heads = a.heads > 1 ? a.heads : 1;
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * heads * a.L + seg_start) * D;
+  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * heads * a.L + seg_start) * D;
   const int n_c = (n_s + TC - 1) / TC;
+  const int n_t = heads * n_c;
+  auto head_off = [&](int c) { return (int64_t)(c / n_c) * a.L * D; };
+  auto chunk0 = [&](int c) { return (c % n_c) * TC; };
 
   // staging role: token st_t of the chunk, columns 16 st_g .. + 15. z comes
   // into LDS by one 16-byte DMA per lane of wave 0 (lanes past d / 4 read
@@ -300,9 +306,9 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   tile.init(w, lane);
   tile.template issue_asm<true>(K, Kr[0], 0, n_s, w);
   tile.template issue_asm<false>(V, Vr[0], 0, n_s, w);
-  if (n_c > 1) {
-    tile.template issue_asm<true>(K, Kr[1], TC, n_s, w);
-    tile.template issue_asm<false>(V, Vr[1], TC, n_s, w);
+  if (n_t > 1) {
+    tile.template issue_asm<true>(K + head_off(1), Kr[1], chunk0(1), n_s, w);
+    tile.template issue_asm<false>(V + head_off(1), Vr[1], chunk0(1), n_s, w);
   }
 
   // product role: row tiles rt0, rt0 + 1; column tiles BC cq + c
@@ -318,11 +324,11 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
 #pragma unroll
     for (int c = 0; c < BC; ++c) acc[r][c] = zero16();
 
-  for (int ch = 0; ch < n_c; ++ch) {
+  for (int ch = 0; ch < n_t; ++ch) {
     const int buf = ch % NBUF;
     // this wave's loads of chunk ch have landed (the 2 PER_WAVE of chunk
     // ch + 1, issued later, may still be in flight)
-    if (ch + 1 < n_c)
+    if (ch + 1 < n_t)
       wait_vmcnt<2 * Tile::PER_WAVE>();
     else
       wait_vmcnt<0>();
@@ -331,13 +337,14 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) zc[e] = Zs[16 * st_g + e];
     }
-    if (ch + 2 < n_c) {  // into the buffer chunk ch - 1 used
-      tile.template issue_asm<true>(K, Kr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
-      tile.template issue_asm<false>(V, Vr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+    if (ch + 2 < n_t) {  // into the buffer chunk ch - 1 used
+      const int cn = ch + 2;
+      tile.template issue_asm<true>(K + head_off(cn), Kr[cn % NBUF], chunk0(cn), n_s, w);
+      tile.template issue_asm<false>(V + head_off(cn), Vr[cn % NBUF], chunk0(cn), n_s, w);
     }
     // stage Phi and Phi / den of token st_t (zero past the segment's end)
     {
-      const bool ok = ch * TC + st_t < n_s;
+      const bool ok = chunk0(ch) + st_t < n_s;
       const bf16* krow = Kr[buf] + st_t * D;
       float ph[16];
       float dp = 0.f;
@@ -530,6 +537,15 @@ hipError_t launch_chain_d(int d, int rule, const AffineArgs& a, hipStream_t stre
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {
   return dtype == kBF16 ? launch_chain_d<bf16>(d, rule, a, stream)
                         : launch_chain_d<float>(d, rule, a, stream);
+}
+
+hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStream_t stream) {
+  if (dtype != kBF16 || d != 128) return hipErrorInvalidValue;
+  const int64_t segs = (int64_t)a.units * a.s_count;
+  if (segs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear>), dim3((unsigned)segs), dim3(512), 0, stream,
+                     a);
+  return hipGetLastError();
 }
 
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {

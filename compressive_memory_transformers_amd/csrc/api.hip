@@ -152,7 +152,7 @@ hipError_t launch_recurrence(const Plan& p, const Carved& cw, int32_t rule, int3
                              float* Mout, float* zout, int64_t L, int64_t seg_len,
                              int64_t s_begin, int64_t s_count, hipStream_t s) {
   if (p.affine) {
-    AffineArgs fa;
+    AffineArgs fa{};
     fa.k = k;
     fa.v = v;
     fa.M_in = Min;
@@ -770,21 +770,39 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
   }
-  for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
-    const size_t off = (size_t)(hg * LD) * e;
-    infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + off,
-                                   static_cast<const char*>(E(lay.dn)) + off, F(lay.Bmat), D, D,
-                                   (int32_t)seg_len, units, S, L, seg_len);
-    g.lda = g.ldb = g.ldc = D;
-    g.a_hi = g.b_hi = G * LD;
-    g.a_lo = g.b_lo = ND;
-    g.c_hi = S * DD;
-    g.c_lo = DD;
-    g.ta = 1;  // op(A) = sigma(Q)^T
-    g.a_sigma = 1;
-    g.clip = 2;
-    g.accumulate = hg > 0;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  // C_s = sum over the group's heads of sigma(Q)^T dn, into Bmat: bf16 with
+  // d = 128 by the recurrence's product kernel (one pass over q and dn),
+  // otherwise one product per head, accumulating
+  if (dtype == INFINI_BF16 && d == 128) {
+    AffineArgs ca{};
+    ca.k = q;
+    ca.v = E(lay.dn);
+    ca.snapZ = F(lay.snapZ);
+    ca.Bmat = F(lay.Bmat);
+    ca.L = L;
+    ca.seg_len = seg_len;
+    ca.units = (int32_t)units;
+    ca.s_begin = 0;
+    ca.s_count = (int32_t)S;
+    ca.heads = (int32_t)G;
+    if (infini::launch_affine_products(dtype, D, ca, s) != hipSuccess) return INFINI_ERR_HIP;
+  } else {
+    for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
+      const size_t off = (size_t)(hg * LD) * e;
+      infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + off,
+                                     static_cast<const char*>(E(lay.dn)) + off, F(lay.Bmat), D, D,
+                                     (int32_t)seg_len, units, S, L, seg_len);
+      g.lda = g.ldb = g.ldc = D;
+      g.a_hi = g.b_hi = G * LD;
+      g.a_lo = g.b_lo = ND;
+      g.c_hi = S * DD;
+      g.c_lo = DD;
+      g.ta = 1;  // op(A) = sigma(Q)^T
+      g.a_sigma = 1;
+      g.clip = 2;
+      g.accumulate = hg > 0;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
   }
   if (infini::launch_bwd_row_weighted_sum(dtype, D, ba, true, s) != hipSuccess)
     return INFINI_ERR_HIP;

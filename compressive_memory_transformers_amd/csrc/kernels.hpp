@@ -48,6 +48,9 @@ struct AffineArgs {
   int32_t units;
   int32_t s_begin, s_count;
   int32_t reverse;     // chain only: walk the segments last to first
+  int32_t heads;       // products only (launch_affine_products): unit u's rows are
+                       // those of heads u * heads .. + heads - 1 of k and v, summed;
+                       // 0 or 1 in the recurrence
 };
 
 // Local causal attention of every (batch, query head, segment, query tile)
@@ -196,6 +199,10 @@ hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 // The chain step of the affine form alone (a.reverse honoured).
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
+// The linear rule's products alone, Bmat = sum over a.heads heads of
+// sigma(K)^T V per (unit, segment), bf16 with d = 128 (hipErrorInvalidValue
+// otherwise: the caller takes another path).
+hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
