@@ -46,6 +46,10 @@ Pins (each function is checked against something other than itself in
 * ``forward``           -- single-segment reduction to causal attention,
   gate extremes, chunked calls with a carried state, GQA equal to MHA on
   repeated K/V, batch/head permutation.
+* ``forward_rows``, ``attend_last_row`` -- equal to ``forward`` (and to the
+  last row of ``local_causal_attention``) on every row of small streams,
+  both rules, grouped heads, ragged segments; the state equals ``forward``'s
+  (``tests/test_oracle_rows.py``).
 * ``decode_step``       -- token-by-token decoding of a stream equals
   ``forward`` on it (every output row, and the state at every segment end);
   the first token of a segment attends to itself alone (closed form); the
@@ -74,6 +78,8 @@ from .infini_attention import (  # noqa: F401
     memory_update,
     num_segments,
     forward,
+    forward_rows,
+    attend_last_row,
     decode_step,
 )
 from .gradients import backward  # noqa: F401

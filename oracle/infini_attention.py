@@ -178,6 +178,69 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, units=None, out_segments=None)
     return out, M_final, z_final
 
 
+
+def attend_last_row(q_t, k_prefix, v_prefix):
+    """A_dot of one query row: softmax(q_t k^T / sqrt(d)) v over the rows of
+    its segment up to and including its own (k_prefix, v_prefix: [t + 1, d]).
+
+    The last row of ``local_causal_attention`` on the same block, computed
+    alone in O(t d): what the causal mask leaves of the segment is exactly
+    this prefix ("Infini-Attention" (AI Wiki), "What happens inside the
+    Infini-attention block?", equation for A_dot).
+    """
+    q_t = np.asarray(q_t, dtype=np.float64)
+    k_prefix = np.asarray(k_prefix, dtype=np.float64)
+    v_prefix = np.asarray(v_prefix, dtype=np.float64)
+    scores = (k_prefix @ q_t) / math.sqrt(q_t.shape[0])
+    weights = np.exp(scores - scores.max())
+    return (weights @ v_prefix) / weights.sum()
+
+
+def forward_rows(q, k, v, beta, M0, z0, seg_len, rule, rows):
+    """``forward`` restricted to the output rows ``rows`` (token indices, the
+    same for every batch element and head), for segments too long for the
+    N x N score matrix.
+
+    Returns (out_rows [B, Hq, len(rows), d_value], M_final, z_final). The
+    state chain runs over every segment as in ``forward``; each requested row
+    t of segment s is the gate of attend_last_row over the segment's rows up
+    to t and of the retrieval of q_t from the state before s.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, Hq, L, _ = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    S = num_segments(L, seg_len)
+    rows = [int(t) for t in rows]
+    if any(t < 0 or t >= L for t in rows):
+        raise ValueError("rows must lie in [0, L)")
+    by_seg = {}
+    for r, t in enumerate(rows):
+        by_seg.setdefault(t // seg_len, []).append((r, t))
+    out = np.full((B, Hq, len(rows), v.shape[3]), np.nan)
+    M_final = np.full(np.shape(M0), np.nan)
+    z_final = np.full(np.shape(z0), np.nan)
+    for b in range(B):
+        for j in range(Hkv):
+            M = np.asarray(M0, dtype=np.float64)[b, j].copy()
+            z = np.asarray(z0, dtype=np.float64)[b, j].copy()
+            for s in range(S):
+                t0, t1 = s * seg_len, min((s + 1) * seg_len, L)
+                for r, t in by_seg.get(s, []):
+                    for h in range(j * group, (j + 1) * group):
+                        q_t = q[b, h, t]
+                        a_dot = attend_last_row(q_t, k[b, j, t0:t + 1], v[b, j, t0:t + 1])
+                        a_mem = memory_retrieval(q_t[None, :], M, z)[0]
+                        g = gate_weight(beta[h])
+                        out[b, h, r] = g * a_mem + (1.0 - g) * a_dot
+                M, z = memory_update(k[b, j, t0:t1], v[b, j, t0:t1], M, z, rule)
+            M_final[b, j] = M
+            z_final[b, j] = z
+    return out, M_final, z_final
+
 def decode_step(q, k, v, beta, M, z, k_cache, v_cache, pos, seg_len, rule):
     """One streaming step: the token at position ``pos`` (0-based) of its segment.
 
