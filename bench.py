@@ -277,7 +277,7 @@ def bench_backward(lib, w, rule, dev, args):
 
 
 BLOCK_D_MODEL = {"llama3_8b": 4096, "hf_repro": 1024, "tiny": 64, "long_stream": 2048,
-                 "small_segment": 4096}
+                 "small_segment": 4096, "long_segment": 2048}
 
 
 def bench_block(lib, w, rule, dev, args):

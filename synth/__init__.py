@@ -83,6 +83,10 @@ WORKLOADS = {
         dtype="bf16", rules=("delta",), seed=4, key_outlier_p=0.05,
         key_outlier_scale=8.0,
         note="B16 H32 d128, 256 segments of 128, 5% of key rows scaled by 8"),
+    "long_segment": Workload(
+        "long_segment", B=1, Hq=16, Hkv=16, L=400000, d=128, seg_len=100000,
+        dtype="bf16", rules=("linear",), seed=5, key_std=1.0 / math.sqrt(128),
+        note="B1 H16 d128, 4 segments of 100000 tokens (very long segments)"),
 }
 
 
