@@ -298,11 +298,24 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
 
   KvLane<D> st;
   const int64_t krow = (int64_t)unit * a.L + seg_start + key;
-  {  // the V rows of the block, by DMA (rows past the segment repeat its last)
-    DmaTile<D, kNW, BK> vt;
-    vt.init(w, lane);
-    vt.template issue<true>(static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D,
-                            Vb, k0, n_s, w);
+  {  // The V rows of the block, by DMA (rows past the segment repeat its
+     // last). LDS row 32 w' + i' holds key w' + NW i', so that the 16 lanes
+     // of a read (one wave, consecutive i) take 16 consecutive rows: with the
+     // K swizzle, no bank conflicts (key order would put them 4 rows apart).
+    constexpr int CPR = D / 8, PER = BK * CPR / 64 / kNW;
+    const int rows = min(BK, n_s - k0);
+    const __amdgpu_buffer_rsrc_t rv = raw_rsrc(
+        static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start + k0) * D,
+        (uint32_t)rows * D * 2);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int p = (j * kNW + w) * 64 + lane;  // physical chunk of the block
+      const int R = p / CPR, phys = p % CPR;
+      const int r = min((R >> 5) + kNW * (R & 31), rows - 1);
+      const uint32_t off = 2 * (r * D + 8 * (phys ^ swz_k<D>(R)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vb + (j * kNW + w) * 64 * 8), 16,
+                                               off, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc)
@@ -310,8 +323,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
                      : zero_frag<bf16>();
   st.ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
   {
-    const int r = w + kNW * i;  // this lane's key, relative to the block
-    st.vo = 2 * (r * D + 8 * (h ^ swz_k<D>(r)));
+    const int R = 32 * w + i;  // LDS row of this lane's key (w + NW i)
+    st.vo = 2 * (R * D + 8 * (h ^ swz_k<D>(R)));
   }
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
