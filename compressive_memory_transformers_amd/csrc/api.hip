@@ -844,43 +844,51 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   // 4. local attention
   if (infini::launch_bwd_attention(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
 
-  // 5. update. Key-side products: hi = unit.
-  auto kside = [&](const void* A, const void* Bm, float* C) {
-    infini::GemmArgs g = gemm_args(A, Bm, C, N, D, D, units, S, L, seg_len);
-    g.lda = g.ldb = g.ldc = D;
-    g.a_hi = g.c_hi = LD;
-    g.a_lo = g.c_lo = ND;
-    g.b_hi = S * DD;
-    g.b_lo = DD;
-    g.clip = 1;
-    return g;
-  };
-  {
-    infini::GemmArgs g = kside(k, E(lay.dMsnap), ba.du_buf);  // Phi dM_s (dM_s^T stored)
-    g.tb = 1;
-    g.a_sigma = 1;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+  // 5. update: dv_acc += sigma(K) dM_s, dphi, dc. bf16 with d in {64, 128}:
+  // one fused kernel per 128 key rows; otherwise key-side products
+  // (hi = unit) and a row kernel.
+  ba.dMsnap = E(lay.dMsnap);
+  if (bwd_mfma) {
+    if (infini::launch_bwd_update_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  } else {
+    auto kside = [&](const void* A, const void* Bm, float* C) {
+      infini::GemmArgs g = gemm_args(A, Bm, C, N, D, D, units, S, L, seg_len);
+      g.lda = g.ldb = g.ldc = D;
+      g.a_hi = g.c_hi = LD;
+      g.a_lo = g.c_lo = ND;
+      g.b_hi = S * DD;
+      g.b_lo = DD;
+      g.clip = 1;
+      return g;
+    };
+    {
+      infini::GemmArgs g = kside(k, E(lay.dMsnap), ba.du_buf);  // Phi dM_s (dM_s^T stored)
+      g.tb = 1;
+      g.a_sigma = 1;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
+    if (rule == INFINI_RULE_DELTA) {
+      infini::GemmArgs g = kside(k, E(lay.snapM), ba.p_buf);  // Phi M_{s-1}
+      g.tb = 1;
+      g.a_sigma = 1;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
+    if (infini::launch_bwd_update_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+    {
+      infini::GemmArgs g = kside(rule == INFINI_RULE_DELTA ? ba.u_el : v, E(lay.dMsnap), ba.dphi);
+      g.tb = 0;  // op(B) = dM_s^T as stored
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
+    if (rule == INFINI_RULE_DELTA) {
+      infini::GemmArgs g = kside(ba.dp_el, E(lay.snapM), ba.dphi);  // + dP M_{s-1}^T
+      g.tb = 0;
+      g.accumulate = 1;
+      if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
+    }
   }
-  if (rule == INFINI_RULE_DELTA) {
-    infini::GemmArgs g = kside(k, E(lay.snapM), ba.p_buf);  // Phi M_{s-1}
-    g.tb = 1;
-    g.a_sigma = 1;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
-  }
-  if (infini::launch_bwd_update_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
-  {
-    infini::GemmArgs g = kside(rule == INFINI_RULE_DELTA ? ba.u_el : v, E(lay.dMsnap), ba.dphi);
-    g.tb = 0;  // op(B) = dM_s^T as stored
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
-  }
-  if (rule == INFINI_RULE_DELTA) {
-    infini::GemmArgs g = kside(ba.dp_el, E(lay.snapM), ba.dphi);  // + dP M_{s-1}^T
-    g.tb = 0;
-    g.accumulate = 1;
-    if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
-    if (infini::launch_bwd_row_weighted_sum(dtype, D, ba, false, s) != hipSuccess)
-      return INFINI_ERR_HIP;
-  }
+  if (rule == INFINI_RULE_DELTA &&
+      infini::launch_bwd_row_weighted_sum(dtype, D, ba, false, s) != hipSuccess)
+    return INFINI_ERR_HIP;
 
   // 6. dz, dK, dV, dbeta
   if (infini::launch_bwd_finish(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;

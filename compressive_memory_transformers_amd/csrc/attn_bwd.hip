@@ -538,6 +538,172 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
     }
 }
 
+// ---- the memory update's backward, fused: one workgroup per 128 key rows ----
+//
+// "Infini-Attention" (AI Wiki), "How does the compressive memory work?": with
+// Phi = sigma(K_s), c_t = Phi_t . z_{s-1},
+//   linear: M_s = M_{s-1} + Phi^T V
+//   delta:  M_s = M_{s-1} + Phi^T R, R = V - P / c, P = Phi M_{s-1}.
+// Given dM_s (the reversed chain's snapshot, dM_s^T in bf16), per key row t:
+//   du_t = Phi_t dM_s                  (dL/dR_t, or dL/dV_t for the linear rule)
+//   dv_acc_t += du_t
+//   delta: dP_t = -du_t / c_t, dc_t = (du_t . P_t / c_t) / c_t,
+//          dphi_t = R_t dM_s^T + dP_t M_{s-1}^T
+//   linear: dphi_t = V_t dM_s^T
+// (dz_s, dc_t z and sigma' are added when dK is assembled). U^T = dM_s^T Phi^T
+// and P^T = M_{s-1}^T Phi^T take row reads of the snapshots (K layout, in
+// LDS) with Phi in the B operand, as the retrieval kernel forms n^T; dphi^T =
+// dM_s R^T + M_{s-1} dP^T takes transposing reads, with R and dP in the
+// accumulator-derived fragment order tr_frag_k expects. R and dP enter the
+// products in bf16, c and everything per element in float.
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kNW * 64, 2) void upd_kernel(BwdArgs a, int n_kt) {
+  constexpr int BK = 32 * kNW, NC = D / 16, NT = D / 64, NJB = D / 32;
+  __shared__ __align__(1024) bf16 Us0[64 * D];  // dM_s^T
+  __shared__ __align__(1024) bf16 Us1[NT > 1 ? 64 * D : 8];
+  __shared__ __align__(1024) bf16 Ps0[DELTA ? 64 * D : 8];  // M_{s-1}^T
+  __shared__ __align__(1024) bf16 Ps1[DELTA && NT > 1 ? 64 * D : 8];
+  __shared__ __align__(16) float zs[D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  int t = blockIdx.x;
+  {
+    const int per = (int)(gridDim.x >> 3);
+    if (t < per * 8) t = (t & 7) * per + (t >> 3);
+  }
+  const int kt = t % n_kt, grp = t / n_kt;
+  const int sl = grp % a.S, unit = grp / a.S;
+  const int64_t seg_start = (int64_t)sl * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const int k0 = kt * BK;
+  if (k0 >= n_s) return;
+  const int key = k0 + w + kNW * i;
+  const bool live = key < n_s;
+  const int64_t row = (int64_t)unit * a.L + seg_start + key;  // [B*Hkv][L] row index
+  const int64_t snap = (int64_t)unit * a.S + sl;
+
+  DmaTile<D, kNW, 64> tile;
+  tile.init(w, lane);
+  const bf16* dMt = static_cast<const bf16*>(a.dMsnap) + snap * D * D;
+  tile.template issue<true>(dMt, Us0, 0, D, w);
+  if constexpr (NT > 1) tile.template issue<true>(dMt, Us1, 64, D, w);
+  if constexpr (DELTA) {
+    const bf16* Mt = static_cast<const bf16*>(a.snapM) + snap * D * D;
+    tile.template issue<true>(Mt, Ps0, 0, D, w);
+    if constexpr (NT > 1) tile.template issue<true>(Mt, Ps1, 64, D, w);
+  }
+  if (tid < D) zs[tid] = a.snapZ[snap * D + tid];
+
+  const bf16* Kr = static_cast<const bf16*>(a.k) + row * D;
+  const bf16* Vr = static_cast<const bf16*>(a.v) + row * D;
+  bf16x8 kf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) kf[cc] = live ? load8<bf16>(Kr + 16 * cc + 8 * h) : zero_frag<bf16>();
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Phi: bf16 B operand; c in float (this lane's half of the columns)
+  bf16x8 pf[NC];
+  float cz = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = live ? feature_map((float)kf[cc][e]) : 0.f;
+      pf[cc][e] = (bf16)f;
+      cz += f * zs[16 * cc + 8 * h + e];
+    }
+  cz += __shfl_xor(cz, 32);
+
+  bf16* const Us[2] = {Us0, NT > 1 ? Us1 : Us0};
+  bf16* const Ps[2] = {Ps0, NT > 1 ? Ps1 : Ps0};
+  const uint32_t ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+  f32x16 uacc[NJB], pacc[DELTA ? NJB : 1];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) {
+    uacc[jb] = zero16();
+    if constexpr (DELTA) pacc[jb] = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const uint32_t o = (ko ^ (32u * cc)) + 2 * 32 * (jb & 1) * D;
+      mma32(uacc[jb], load8<bf16>(lds_at(Us[jb >> 1], o)), pf[cc]);
+      if constexpr (DELTA) mma32(pacc[jb], load8<bf16>(lds_at(Ps[jb >> 1], o)), pf[cc]);
+    }
+  }
+
+  // per element: column j = 32 jb + 8 rq + 4 h + 0..3 of row `key`
+  const float ic = 1.f / cz;
+  float* dva = a.dv_acc + row * D;
+  bf16x8 rf[NT][4], df[NT][4];
+  float dcs = 0.f;
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int col = 32 * jb + 8 * rq + 4 * h;
+      bf16x4 v4;
+      f32x4 dv4;
+      if (live) {
+        v4 = load4<bf16>(Vr + col);
+        dv4 = *reinterpret_cast<const f32x4*>(dva + col);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v4[j] = (bf16)0.f;
+          dv4[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * rq + j;
+        const float du = uacc[jb][r];
+        dv4[j] += du;
+        float rv = (float)v4[j], dp = 0.f;
+        if constexpr (DELTA) {
+          const float pred = pacc[jb][r] * ic;
+          rv -= pred;
+          dp = -du * ic;
+          dcs += du * pred;
+        }
+        rf[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = (bf16)rv;
+        if constexpr (DELTA) df[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = (bf16)dp;
+      }
+      if (live) *reinterpret_cast<f32x4*>(dva + col) = dv4;
+    }
+  if constexpr (DELTA) {
+    dcs += __shfl_xor(dcs, 32);
+    if (live && h == 0) a.dc[row] = dcs * ic;
+  }
+
+  // dphi^T = dM_s R^T (+ M_{s-1} dP^T)
+  f32x16 dacc[NJB];
+#pragma unroll
+  for (int db = 0; db < NJB; ++db) {
+    dacc[db] = zero16();
+    const uint32_t t0 = tr_offset_k<D>(lane, db, 0), t1 = tr_offset_k<D>(lane, db, 1);
+#pragma unroll
+    for (int ts = 0; ts < NT; ++ts)
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        mma32(dacc[db], tr_frag_k<D>(Us[ts], t0, t1, pc), rf[ts][pc]);
+        if constexpr (DELTA) mma32(dacc[db], tr_frag_k<D>(Ps[ts], t0, t1, pc), df[ts][pc]);
+      }
+  }
+  if (!live) return;
+  float* dph = a.dphi + row * D;
+#pragma unroll
+  for (int db = 0; db < NJB; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      f32x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = dacc[db][4 * rq + j];
+      *reinterpret_cast<f32x4*>(dph + 32 * db + 8 * rq + 4 * h) = y;
+    }
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
   const int64_t units = (int64_t)a.B * a.Hkv;
@@ -563,6 +729,21 @@ hipError_t launch_retr_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_upd_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  const int64_t eff = a.seg_len < a.L ? a.seg_len : a.L;
+  const int n_kt = (int)((eff + 32 * kNW - 1) / (32 * kNW));
+  const int64_t grid = units * a.S * n_kt;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (a.rule == kRuleDelta)
+    hipLaunchKernelGGL((upd_kernel<D, true>), dim3((unsigned)grid), dim3(kNW * 64), 0, s, a, n_kt);
+  else
+    hipLaunchKernelGGL((upd_kernel<D, false>), dim3((unsigned)grid), dim3(kNW * 64), 0, s, a,
+                       n_kt);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool attn_bwd_mfma_supported(int dtype, int d, int group) {
@@ -573,6 +754,14 @@ hipError_t launch_bwd_retrieval_mfma(int d, const BwdArgs& a, hipStream_t stream
   switch (d) {
     case 64: return launch_retr_d<64>(a, stream);
     case 128: return launch_retr_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_update_mfma(int d, const BwdArgs& a, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_upd_d<64>(a, stream);
+    case 128: return launch_upd_d<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -135,6 +135,7 @@ struct BwdArgs {
   const void* dout;    // [B][Hq][L][d]
   const void* snapM;   // [B*Hkv][S][d][d] M_{s-1}^T, element type
   const float* snapZ;  // [B*Hkv][S][d] z_{s-1}
+  const void* dMsnap;  // [B*Hkv][S][d][d] dM_s^T (dL/dM_s, transposed), element type
   float* nm;           // [B][Hq][L][d] sigma(Q) M_{s-1}, then dL/dQ (retrieval part)
   void* dn;            // [B][Hq][L][d] g dout / den, element type
   float* delta;        // [B][Hq][L] dout . out - g dout . A_mem
@@ -180,6 +181,9 @@ hipError_t launch_attn_bwd_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // The retrieval's backward in one MFMA kernel (bf16, same support as above):
 // delta, dg, dden, dn and nm from q, out, d_out and the snapshots.
 hipError_t launch_bwd_retrieval_mfma(int d, const BwdArgs& a, hipStream_t stream);
+// The update's backward in one MFMA kernel (bf16, d in {64, 128}): dv_acc +=
+// sigma(K) dM_s, dphi = (V - pred or V) dM_s^T (+ dP M_{s-1}^T), dc.
+hipError_t launch_bwd_update_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
 hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
 // Row step of the delta rule's update backward (after p_buf, du_buf).
