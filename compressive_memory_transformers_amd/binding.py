@@ -49,6 +49,7 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
     "infini_attn_status_string": (ctypes.c_char_p, [_c_i32]),
+    "infini_attn_error_string": (ctypes.c_char_p, [_c_i32]),
     "infini_attn_version": (_c_i32, []),
 }
 

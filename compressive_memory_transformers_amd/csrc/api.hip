@@ -1089,6 +1089,8 @@ const char* infini_attn_status_string(int32_t status) {
   }
 }
 
+const char* infini_attn_error_string(int32_t status) { return infini_attn_status_string(status); }
+
 int32_t infini_attn_version(void) { return kVersion; }
 
 }  // extern "C"

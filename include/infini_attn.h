@@ -288,7 +288,11 @@ infini_status_t infini_attn_block_forward_timed(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);
 
+/* A static, human-readable name of a status code ("unknown status" for any
+ * other value). infini_attn_error_string is the same function under a second
+ * name. */
 const char* infini_attn_status_string(int32_t status);
+const char* infini_attn_error_string(int32_t status);
 
 /* The ABI version: major * 10000 + minor * 100 + patch. */
 int32_t infini_attn_version(void);

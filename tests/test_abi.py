@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "infini_attn_backward", "infini_attn_backward_workspace_size",
         "infini_attn_block_forward", "infini_attn_block_forward_timed",
-        "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_decode_workspace_size",
+        "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_error_string", "infini_attn_decode_workspace_size",
         "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_forward_train",
         "infini_attn_status_string", "infini_attn_version", "infini_attn_workspace_size"])
 
@@ -62,6 +62,8 @@ def test_version_and_status_strings(lib):
     assert names[0] == "ok" and names[4] == "workspace too small"
     assert names[6] == "unknown status"
     assert lib.infini_attn_status_string(-3).decode() == "unknown status"
+    for st in range(-1, 8):  # the second name is the same function
+        assert lib.infini_attn_error_string(st) == lib.infini_attn_status_string(st)
 
 
 def ws(lib, *args):
