@@ -19,8 +19,11 @@
 // order (cost 6 N d^2 per segment on the sequential path, no extra memory).
 // The affine form (affine.hip) computes each segment's d x d transition in
 // parallel and leaves 2 d^3 per segment on the sequential path, at the price
-// of two d x d matrices per segment in the workspace. It is used when
-// seg_len >= 4 d, where its sequential part is at least 12x shorter.
+// of two d x d matrices per segment in the workspace (written once, read
+// once). It is used when seg_len >= d: there its sequential part is at least
+// 3x shorter and the matrices at most 1.5x the segment's K and V, and it was
+// measured faster (2x at 128-token segments of d = 128); below, the
+// matrices' traffic outgrows the tokens' and the direct scan is used.
 #include <stdint.h>
 #include <string.h>
 
@@ -50,7 +53,7 @@ struct Plan {
 
 bool use_affine(int64_t L, int64_t d, int64_t seg_len) {
   const int64_t eff = seg_len < L ? seg_len : L;
-  return eff >= 4 * d;
+  return eff >= d;
 }
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {

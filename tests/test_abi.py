@@ -73,7 +73,7 @@ def ws(lib, *args):
 
 
 def test_workspace_sizes(lib):
-    # Llama-3-8B-shaped, bf16, delta rule: seg_len >= 4 d, so the scan runs in
+    # Llama-3-8B-shaped, bf16, delta rule: seg_len >= d, so the scan runs in
     # affine form. Per segment and unit: snapshots (d*d bf16 + d floats),
     # column sums (d floats), B_s (d*d floats) and A_s (d*d bf16).
     st, full, least = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 1)
@@ -85,9 +85,12 @@ def test_workspace_sizes(lib):
     # the linear rule needs no A_s
     st, full_lin, least_lin = ws(lib, 4, 32, 8, 32768, 128, 2048, 0, 1)
     assert full - full_lin == 16 * 32 * d * d * 2
-    # direct scan (seg_len < 4 d): snapshots only
-    st, full_dir, least_dir = ws(lib, 16, 32, 32, 32768, 128, 128, 1, 1)
-    assert full_dir - least_dir == 255 * 512 * (d * d * 2 + d * 4)
+    # direct scan (seg_len < d): snapshots only
+    st, full_dir, least_dir = ws(lib, 16, 32, 32, 32768, 128, 64, 1, 1)
+    assert full_dir - least_dir == 511 * 512 * (d * d * 2 + d * 4)
+    # from seg_len = d on, the affine form's matrices too
+    st, full_aff, least_aff = ws(lib, 16, 32, 32, 32768, 128, 128, 1, 1)
+    assert full_aff - least_aff == 255 * 512 * (d * d * 2 + d * 4 + d * 4 + d * d * 4 + d * d * 2)
     st, full32, _ = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 0)
     assert st == 0 and full32 > full
     # a ragged final segment counts as a segment

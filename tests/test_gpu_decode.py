@@ -58,7 +58,7 @@ def decode_stream(lib, inp, seg_len, rule):
 
 
 STREAMS = [
-    # B, Hq, Hkv, L, d, seg_len, dtype   (seg_len >= 4 d folds in affine form)
+    # B, Hq, Hkv, L, d, seg_len, dtype   (seg_len >= d folds in affine form)
     (2, 4, 2, 100, 64, 40, torch.float32),
     (2, 4, 2, 100, 64, 40, torch.bfloat16),
     (1, 8, 2, 70, 128, 32, torch.bfloat16),     # GQA 4, d = 128

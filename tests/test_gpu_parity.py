@@ -112,7 +112,9 @@ EDGE = [
     (1, 2, 2, 257, 128, 130, torch.bfloat16), # ragged key tiles and query tiles
     (2, 8, 2, 500, 64, 128, torch.bfloat16),
     (1, 4, 4, 64, 32, 33, torch.bfloat16),
-    # seg_len >= 4 d: the scan runs in affine form
+    (1, 2, 2, 200, 128, 64, torch.bfloat16),  # direct scan (seg_len < d), bf16, d = 128
+    (2, 4, 2, 90, 64, 40, torch.bfloat16),    # direct scan, GQA 2, ragged
+    # seg_len >= d: the scan runs in affine form
     (1, 2, 2, 600, 32, 130, torch.float32),
     (2, 4, 2, 1100, 64, 300, torch.bfloat16),
     (1, 4, 1, 1500, 128, 520, torch.bfloat16),
