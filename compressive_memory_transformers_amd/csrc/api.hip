@@ -528,8 +528,11 @@ struct BwdLayout {
   size_t Amat_f, dMsnap_f, phi_f, phic_f, wsum_part;
 };
 
+// fused: the bf16 kernels that form sigma(Q) M, sigma(K) dM_s and sigma(K)
+// M_{s-1} in registers run (attn_bwd_mfma_supported), so the float row
+// buffers of the product path (nm, du_buf, p_buf, u_el, dp_el) are not taken.
 BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
-                     int64_t seg_len, int32_t rule) {
+                     int64_t seg_len, int32_t rule, bool fused) {
   BwdLayout b{};
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -559,19 +562,21 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
     const size_t chunks = ((size_t)(Hq / Hkv) * n + 511) / 512;
     b.wsum_part = take(units * S * chunks * d * 4);
   }
-  b.nm = take(qrows * d * 4);
+  if (!fused) b.nm = take(qrows * d * 4);
   b.dn = take(qrows * d * e);
   b.delta = take(qrows * 4);
   b.dg = take(qrows * 4);
   b.dden = take(qrows * 4);
   b.dk_acc = take(krows * d * 4);
   b.dv_acc = take(krows * d * 4);
-  b.du_buf = take(krows * d * 4);
+  if (!fused) b.du_buf = take(krows * d * 4);
   b.dphi = take(krows * d * 4);
   if (delta) {
-    b.p_buf = take(krows * d * 4);
-    b.u_el = take(krows * d * e);
-    b.dp_el = take(krows * d * e);
+    if (!fused) {
+      b.p_buf = take(krows * d * 4);
+      b.u_el = take(krows * d * e);
+      b.dp_el = take(krows * d * e);
+    }
     b.dc = take(krows * 4);
     b.phi_f = take(krows * d * 4);
     b.phic_f = take(krows * d * 4);
@@ -611,7 +616,8 @@ infini_status_t infini_attn_backward_workspace_size(int64_t B, int64_t Hq, int64
   const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
   if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
-  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule).total;
+  const bool fused = infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
+  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule, fused).total;
   return INFINI_OK;
 }
 
@@ -639,7 +645,8 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   const size_t nq = (size_t)(B * Hq * L * d) * e, nkv = (size_t)(B * Hkv * L * d) * e;
   const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
   const size_t nrow = (size_t)(B * Hq * L) * 4, nbeta = (size_t)Hq * 4;
-  const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule);
+  const bool bwd_mfma = infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
+  const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule, bwd_mfma);
   if (workspace_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   struct Range { const void* p; size_t n; };
   const Range all[] = {{q, nq},         {k, nkv},         {v, nkv},      {beta, nbeta},
@@ -694,18 +701,19 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ba.dout = d_out;
   ba.snapM = E(lay.snapM);
   ba.snapZ = F(lay.snapZ);
-  ba.nm = F(lay.nm);
+  ba.nm = bwd_mfma ? nullptr : F(lay.nm);
   ba.dn = E(lay.dn);
   ba.delta = F(lay.delta);
   ba.dg = F(lay.dg);
   ba.dden = F(lay.dden);
   ba.dk_acc = F(lay.dk_acc);
   ba.dv_acc = F(lay.dv_acc);
-  ba.p_buf = rule == INFINI_RULE_DELTA ? F(lay.p_buf) : nullptr;
-  ba.du_buf = F(lay.du_buf);
+  const bool rows = !bwd_mfma && rule == INFINI_RULE_DELTA;  // delta rule, product path
+  ba.p_buf = rows ? F(lay.p_buf) : nullptr;
+  ba.du_buf = bwd_mfma ? nullptr : F(lay.du_buf);
   ba.dphi = F(lay.dphi);
-  ba.u_el = rule == INFINI_RULE_DELTA ? E(lay.u_el) : nullptr;
-  ba.dp_el = rule == INFINI_RULE_DELTA ? E(lay.dp_el) : nullptr;
+  ba.u_el = rows ? E(lay.u_el) : nullptr;
+  ba.dp_el = rows ? E(lay.dp_el) : nullptr;
   ba.dc = rule == INFINI_RULE_DELTA ? F(lay.dc) : nullptr;
   ba.phi_f = rule == INFINI_RULE_DELTA ? F(lay.phi_f) : nullptr;
   ba.phic_f = rule == INFINI_RULE_DELTA ? F(lay.phic_f) : nullptr;
@@ -732,7 +740,6 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   // 2. retrieval. bf16 with d in {64, 128}: one fused kernel per 128 query
   // rows. Otherwise two products and a row kernel (query-side products:
   // hi = b * Hq + h, M_{s-1} of unit hi / G).
-  const bool bwd_mfma = infini::attn_bwd_mfma_supported(dtype, D, (int)G);
   if (bwd_mfma) {
     if (infini::launch_bwd_retrieval_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   } else {

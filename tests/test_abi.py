@@ -329,6 +329,23 @@ def test_backward_workspace_size(lib):
     assert bws(lib, 2, 4, 2, 64, 32, 16, 0, 1)[1] < n
 
 
+def test_backward_workspace_of_the_fused_path(lib):
+    """bf16 with d = 64 and at most 64 query heads per KV head runs the fused
+    kernels, which keep sigma(Q) M, sigma(K) dM_s and sigma(K) M_{s-1} in
+    registers: the workspace drops the float row buffers the product path
+    needs. With 65 query heads per KV head the same shape takes them again."""
+    B, L, d, N = 1, 64, 64, 16
+    for rule in (0, 1):
+        fused = bws(lib, B, 64, 1, L, d, N, rule, 1)
+        product = bws(lib, B, 65, 1, L, d, N, rule, 1)
+        assert fused[0] == 0 and product[0] == 0
+        qrows, krows = B * 64 * L, B * L
+        # at least nm (float) and du_buf (float); for delta also p_buf (float)
+        # and u_el, dp_el (bf16); one more query head only adds to the rest
+        saved = qrows * d * 4 + krows * d * 4 + (krows * d * (4 + 2 + 2) if rule else 0)
+        assert product[1] - fused[1] >= saved, (rule, fused, product)
+
+
 BWD_NAMES = ("q", "k", "v", "beta", "M0", "z0", "out", "lse", "d_out", "dM_final", "dz_final",
              "dq", "dk", "dv", "dbeta", "dM0", "dz0", "workspace")
 
