@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     status_string,
     version,
     workspace_size,
+    workspace_size_kv,
 )
 
 load_library()

@@ -28,6 +28,10 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
     "infini_attn_forward": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_workspace_size_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
+    "infini_attn_forward_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
     "infini_attn_forward_timed": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
@@ -103,6 +107,17 @@ def workspace_size(B, Hq, Hkv, L, d, seg_len, rule, dtype):
     return int(full.value), int(least.value)
 
 
+def workspace_size_kv(B, Hq, Hkv, L, d_key, d_value, seg_len, rule, dtype):
+    """(full_bytes, min_bytes) of the workspace with separate key and value widths."""
+    lib = load_library()
+    full, least = _c_size(0), _c_size(0)
+    st = lib.infini_attn_workspace_size_kv(B, Hq, Hkv, L, d_key, d_value, seg_len, RULES[rule],
+                                           DTYPES[dtype], ctypes.byref(full), ctypes.byref(least))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_workspace_size_kv")
+    return int(full.value), int(least.value)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -113,6 +128,8 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
 
     q [B,Hq,L,d], k and v [B,Hkv,L,d] (float32 or bfloat16, contiguous, on one
     GPU), beta [Hq] float32, M0 [B,Hkv,d,d] float32, z0 [B,Hkv,d] float32.
+    v may have another width dv than q and k (then M0 is [B,Hkv,d,dv] and out
+    [B,Hq,L,dv]): infini_attn_forward_kv, without ``events`` or ``lse``.
     Returns (out, M_final, z_final). Output buffers and a workspace (a uint8
     tensor) may be passed in; M_final may be M0 and z_final may be z0. Runs on
     ``stream`` (a torch.cuda.Stream) or torch's current stream, asynchronously.
@@ -123,10 +140,14 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
-    if not (k.shape == v.shape == (B, Hkv, L, d)):
-        raise ValueError(f"k and v must be [B,Hkv,L,d]; got {tuple(k.shape)}, {tuple(v.shape)}")
-    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+    dv = v.shape[-1] if v.dim() == 4 else -1
+    if not (k.shape == (B, Hkv, L, d) and v.shape == (B, Hkv, L, dv)):
+        raise ValueError(f"k must be [B,Hkv,L,d] and v [B,Hkv,L,dv]; got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, dv) or z0.shape != (B, Hkv, d):
         raise ValueError("beta, M0 or z0 has the wrong shape")
+    if dv != d and (events or lse is not None):
+        raise ValueError("events and lse need d_value == d_key")
     if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
     if beta.dtype != torch.float32 or M0.dtype != torch.float32 or z0.dtype != torch.float32:
@@ -143,17 +164,17 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, Hq, L, dv), dtype=q.dtype, device=dev)
     if M_final is None:
         M_final = torch.empty_like(M0)
     if z_final is None:
         z_final = torch.empty_like(z0)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+    if out.shape != (B, Hq, L, dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,L,dv] tensor of q's dtype")
     if M_final.shape != M0.shape or z_final.shape != z0.shape:
         raise ValueError("M_final / z_final must have the shapes of M0 / z0")
     if workspace is None:
-        full, _ = workspace_size(B, Hq, Hkv, L, d, seg_len, rule, q.dtype)
+        full, _ = workspace_size_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, q.dtype)
         workspace = torch.empty(full, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
@@ -175,6 +196,9 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
         handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
         st = lib.infini_attn_forward_timed(*args, handles, len(events))
         name = "infini_attn_forward_timed"
+    elif dv != d:
+        st = lib.infini_attn_forward_kv(*args[:5], dv, *args[5:])
+        name = "infini_attn_forward_kv"
     else:
         st = lib.infini_attn_forward(*args)
         name = "infini_attn_forward"

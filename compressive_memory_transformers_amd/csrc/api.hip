@@ -44,7 +44,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int64_t units, S, d, e;
+  int64_t units, S, d, e;  // d: the key width (the value width too, unless dv says otherwise)
+  int64_t dv;              // the value width
   bool affine;         // scan in affine form
   size_t state_bytes;  // one (M, z) buffer, aligned
   size_t per_seg;      // workspace bytes per segment of a window
@@ -63,13 +64,25 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-infini_status_t check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
-                            int64_t seg_len, int32_t rule, int32_t dtype, Plan* plan) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || seg_len < 1) return INFINI_ERR_INVALID_ARG;
+// Query rows per attention workgroup: the kernel with d_key != d_value
+// always runs four waves.
+int64_t attn_block_rows(int64_t dk, int64_t dv, int64_t eff) {
+  return dk == dv ? 32 * infini::attn_waves(eff) : 128;
+}
+
+// dk: the key width, dv: the value width ("Infini-Attention" (AI Wiki), "How
+// does the compressive memory work?": M is d_key x d_value).
+infini_status_t check_sizes_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t dk,
+                               int64_t dv, int64_t seg_len, int32_t rule, int32_t dtype,
+                               Plan* plan) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || dk < 1 || dv < 1 || seg_len < 1)
+    return INFINI_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return INFINI_ERR_INVALID_ARG;
   if (rule != INFINI_RULE_LINEAR && rule != INFINI_RULE_DELTA) return INFINI_ERR_INVALID_ARG;
   if (dtype != INFINI_F32 && dtype != INFINI_BF16) return INFINI_ERR_INVALID_ARG;
-  if (d != 32 && d != 64 && d != 128) return INFINI_ERR_UNSUPPORTED;
+  if (dk != 32 && dk != 64 && dk != 128) return INFINI_ERR_UNSUPPORTED;
+  if (dv != 32 && dv != 64 && dv != 128) return INFINI_ERR_UNSUPPORTED;
+  const int64_t d = dk > dv ? dk : dv;
   // Every element index must fit in int64 and every grid in 2^31 workgroups.
   int64_t n = 0;
   if (!mul_ok(B, Hq, &n) || !mul_ok(n, L, &n) || !mul_ok(n, d, &n) || n > (INT64_MAX >> 3))
@@ -78,26 +91,33 @@ infini_status_t check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64
   if (units * (d / 32) > INT32_MAX) return INFINI_ERR_INVALID_ARG;
   const int64_t S = (L + seg_len - 1) / seg_len;
   const int64_t eff = seg_len < L ? seg_len : L;
-  const int64_t bm = 32 * infini::attn_waves(eff);
+  const int64_t bm = attn_block_rows(dk, dv, eff);
   const int64_t n_qt = (eff + bm - 1) / bm;
   // one segment per window at the least
   if (!mul_ok(B * Hq, n_qt, &n) || n > INT32_MAX) return INFINI_ERR_INVALID_ARG;
   if (plan) {
     plan->units = units;
     plan->S = S;
-    plan->d = d;
+    plan->d = dk;
+    plan->dv = dv;
     plan->e = dtype == INFINI_BF16 ? 2 : 4;
-    plan->affine = use_affine(L, d, seg_len);
-    plan->state_bytes = align_up((size_t)units * (size_t)(d * d + d) * 4);
+    // d_key != d_value: the direct scan only
+    plan->affine = dk == dv && use_affine(L, dk, seg_len);
+    plan->state_bytes = align_up((size_t)units * (size_t)(dk * dv + dk) * 4);
     // snapshots: M^T in the element type, z in float
-    size_t per = (size_t)(d * d * plan->e + d * 4);
-    // affine form: column sums, B_s in float, A_s in the element type (delta)
+    size_t per = (size_t)(dv * dk * plan->e + dk * 4);
+    // affine form (dk == dv): column sums, B_s in float, A_s in the element type (delta)
     if (plan->affine)
-      per += (size_t)(d * 4 + d * d * 4 + (rule == INFINI_RULE_DELTA ? d * d * plan->e : 0));
+      per += (size_t)(dk * 4 + dk * dk * 4 + (rule == INFINI_RULE_DELTA ? dk * dk * plan->e : 0));
     plan->per_seg = (size_t)units * per;
     plan->fixed = 2 * plan->state_bytes + 6 * kAlign;
   }
   return INFINI_OK;
+}
+
+infini_status_t check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
+                            int64_t seg_len, int32_t rule, int32_t dtype, Plan* plan) {
+  return check_sizes_kv(B, Hq, Hkv, L, d, d, seg_len, rule, dtype, plan);
 }
 
 // Byte ranges [p, p + n) overlap.
@@ -124,8 +144,8 @@ struct Carved {
 Carved carve(const Plan& p, int64_t W, int32_t rule, void* workspace) {
   Carved c{};
   char* ws = static_cast<char*>(workspace);
-  const int64_t d = p.d;
-  const size_t mbytes = (size_t)p.units * (size_t)(d * d) * 4;
+  const int64_t d = p.d, dv = p.dv;
+  const size_t mbytes = (size_t)p.units * (size_t)(d * dv) * 4;
   c.stM[0] = reinterpret_cast<float*>(ws);
   c.stM[1] = reinterpret_cast<float*>(ws + p.state_bytes);
   c.stz[0] = reinterpret_cast<float*>(ws + mbytes);
@@ -137,7 +157,7 @@ Carved carve(const Plan& p, int64_t W, int32_t rule, void* workspace) {
     return r;
   };
   const size_t uW = (size_t)p.units * (size_t)W;
-  c.snapM = take(uW * (size_t)(d * d * p.e));
+  c.snapM = take(uW * (size_t)(dv * d * p.e));
   c.snapZ = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
   if (p.affine) {
     c.colsum = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
@@ -189,6 +209,7 @@ hipError_t launch_recurrence(const Plan& p, const Carved& cw, int32_t rule, int3
   sa.units = (int32_t)p.units;
   sa.s_begin = (int32_t)s_begin;
   sa.s_count = (int32_t)s_count;
+  if (p.dv != p.d) return infini::launch_scan_kv(dtype, (int)p.d, (int)p.dv, rule, sa, s);
   return infini::launch_scan(dtype, (int)p.d, rule, sa, s);
 }
 
@@ -212,14 +233,16 @@ infini_status_t infini_attn_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, i
 
 namespace {
 
+// d: the key width; dv: the value width (d for the square entry points).
 infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
                              int64_t seg_len, int32_t rule, int32_t dtype, const void* q,
                              const void* k, const void* v, const float* beta, const float* M0,
                              const float* z0, void* out, float* M_final, float* z_final,
                              float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* events, int32_t n_events) {
+                             void* const* events, int32_t n_events, int64_t dv_in = 0) {
+  const int64_t dv = dv_in > 0 ? dv_in : d;
   Plan p;
-  infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  infini_status_t st = check_sizes_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
 
   const void* ptrs[] = {q, k, v, beta, M0, z0, out, M_final, z_final, workspace};
@@ -232,22 +255,24 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
 
   const size_t nq = (size_t)(B * Hq * L * d) * (size_t)p.e;
   const size_t nkv = (size_t)(B * Hkv * L * d) * (size_t)p.e;
-  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  const size_t nvv = (size_t)(B * Hkv * L * dv) * (size_t)p.e;
+  const size_t nout = (size_t)(B * Hq * L * dv) * (size_t)p.e;
+  const size_t nM = (size_t)(B * Hkv * d * dv) * 4, nz = (size_t)(B * Hkv * d) * 4;
   const size_t nbeta = (size_t)Hq * 4;
   // out overlaps nothing; M_final / z_final may coincide exactly with M0 / z0;
   // the workspace overlaps nothing.
   struct Range { const void* p; size_t n; };
-  const Range inputs[] = {{q, nq}, {k, nkv}, {v, nkv}, {beta, nbeta}, {M0, nM}, {z0, nz}};
+  const Range inputs[] = {{q, nq}, {k, nkv}, {v, nvv}, {beta, nbeta}, {M0, nM}, {z0, nz}};
   for (const Range& r : inputs) {
-    if (overlap(out, nq, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
+    if (overlap(out, nout, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
     if (overlap(workspace, workspace_bytes, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
     if (r.p != M0 && overlap(M_final, nM, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
     if (r.p != z0 && overlap(z_final, nz, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
   }
   if (M0 != M_final && overlap(M_final, nM, M0, nM)) return INFINI_ERR_INVALID_ARG;
   if (z0 != z_final && overlap(z_final, nz, z0, nz)) return INFINI_ERR_INVALID_ARG;
-  if (overlap(out, nq, M_final, nM) || overlap(out, nq, z_final, nz) ||
-      overlap(M_final, nM, z_final, nz) || overlap(out, nq, workspace, workspace_bytes) ||
+  if (overlap(out, nout, M_final, nM) || overlap(out, nout, z_final, nz) ||
+      overlap(M_final, nM, z_final, nz) || overlap(out, nout, workspace, workspace_bytes) ||
       overlap(workspace, workspace_bytes, M_final, nM) ||
       overlap(workspace, workspace_bytes, z_final, nz))
     return INFINI_ERR_INVALID_ARG;
@@ -256,7 +281,7 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     const size_t nl = (size_t)(B * Hq * L) * 4;
     for (const Range& r : inputs)
       if (overlap(lse, nl, r.p, r.n)) return INFINI_ERR_INVALID_ARG;
-    if (overlap(lse, nl, out, nq) || overlap(lse, nl, M_final, nM) ||
+    if (overlap(lse, nl, out, nout) || overlap(lse, nl, M_final, nM) ||
         overlap(lse, nl, z_final, nz) || overlap(lse, nl, workspace, workspace_bytes))
       return INFINI_ERR_INVALID_ARG;
   }
@@ -265,7 +290,7 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   int64_t W = (int64_t)((workspace_bytes - p.fixed) / p.per_seg);
   if (W > p.S) W = p.S;
   const int64_t eff = seg_len < L ? seg_len : L;
-  const int64_t bm = 32 * infini::attn_waves(eff);
+  const int64_t bm = attn_block_rows(d, dv, eff);
   const int64_t n_qt = (eff + bm - 1) / bm;
   const int64_t tiles_per_seg = B * Hq * n_qt;  // <= INT32_MAX, checked above
   if (W > INT32_MAX / tiles_per_seg) W = INT32_MAX / tiles_per_seg;
@@ -329,8 +354,10 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     aa.s_begin = (int32_t)s_begin;
     aa.s_count = (int32_t)s_count;
     aa.n_qt = (int32_t)n_qt;
-    aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-    if (infini::launch_attn(dtype, (int)d, aa, p.units, s) != hipSuccess) return INFINI_ERR_HIP;
+    aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);  // scores scale with the key width
+    const hipError_t ea = dv == d ? infini::launch_attn(dtype, (int)d, aa, p.units, s)
+                                  : infini::launch_attn_kv(dtype, (int)d, (int)dv, aa, p.units, s);
+    if (ea != hipSuccess) return INFINI_ERR_HIP;
     if (!mark(wi, 2)) return INFINI_ERR_HIP;
 
     Min = Mout;
@@ -351,6 +378,32 @@ infini_status_t infini_attn_forward(int64_t B, int64_t Hq, int64_t Hkv, int64_t 
                                     void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
                       M_final, z_final, nullptr, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+infini_status_t infini_attn_workspace_size_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                              int64_t d_key, int64_t d_value, int64_t seg_len,
+                                              int32_t rule, int32_t dtype, size_t* full_bytes,
+                                              size_t* min_bytes) {
+  Plan p;
+  const infini_status_t st =
+      check_sizes_kv(B, Hq, Hkv, L, d_key, d_value, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  if (full_bytes) *full_bytes = p.fixed + p.per_seg * (size_t)p.S;
+  if (min_bytes) *min_bytes = p.fixed + p.per_seg;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_forward_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                       int64_t d_key, int64_t d_value, int64_t seg_len,
+                                       int32_t rule, int32_t dtype, const void* q, const void* k,
+                                       const void* v, const float* beta, const float* M0,
+                                       const float* z0, void* out, float* M_final,
+                                       float* z_final, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return forward_impl(B, Hq, Hkv, L, d_key, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
+                      M_final, z_final, nullptr, workspace, workspace_bytes, stream, nullptr, 0,
+                      d_value);
 }
 
 infini_status_t infini_attn_forward_train(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,

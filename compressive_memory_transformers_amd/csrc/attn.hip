@@ -36,7 +36,9 @@ namespace {
 // and denominator use the same reference.
 constexpr float kRescaleTau = 8.f;
 
-template <typename T, int D, int NW, int BN>
+// DK: the key width (Q, K, rows of M); DV: the value width (V, the output,
+// columns of M).
+template <typename T, int DK, int DV, int NW, int BN>
 struct AttnTile {
   static constexpr int NT = NW * 64;
   // Row strides (elements). K rows: 16 bytes of padding, so the 16 lanes of a
@@ -44,13 +46,13 @@ struct AttnTile {
   // different 4-bank groups. V^T rows: 4 elements of padding, so 32 lanes
   // reading 4-element runs of 32 consecutive rows, and the transposed stores
   // below, each cover the 64 banks once.
-  static constexpr int KS = D + pad16<T>();
+  static constexpr int KS = DK + pad16<T>();
   static constexpr int VS = BN + 4;
-  static constexpr int K_TOTAL = BN * (D / 8);   // 8-element K chunks per tile
+  static constexpr int K_TOTAL = BN * (DK / 8);  // 8-element K chunks per tile
   static constexpr int K_CHUNKS = (K_TOTAL + NT - 1) / NT;  // per thread
   // V is staged in 4 keys x 4 dims blocks; a group of 32 lanes takes 8
   // consecutive dim-quads x 4 consecutive key-quads.
-  static constexpr int DQ = D / 4, KQ = BN / 4;
+  static constexpr int DQ = DV / 4, KQ = BN / 4;
   static constexpr int V_GROUPS = (DQ / 8) * (KQ / 4);
   static constexpr int V_PER_THREAD = (V_GROUPS * 32 + NT - 1) / NT;
   static_assert(DQ % 8 == 0 && KQ % 4 == 0, "V staging layout");
@@ -59,8 +61,8 @@ struct AttnTile {
 
   __device__ __forceinline__ static bool k_item(int j, int tid, int& r, int& col) {
     const int c = tid + j * NT;
-    r = c / (D / 8);
-    col = (c % (D / 8)) * 8;
+    r = c / (DK / 8);
+    col = (c % (DK / 8)) * 8;
     return K_TOTAL % NT == 0 || c < K_TOTAL;
   }
   __device__ __forceinline__ static bool v_item(int j, int tid, int& d4, int& k4) {
@@ -77,7 +79,7 @@ struct AttnTile {
 #pragma unroll
     for (int j = 0; j < K_CHUNKS; ++j) {
       int r, col;
-      if (k_item(j, tid, r, col)) k[j] = load8<T>(K + (int64_t)min(k0 + r, last) * D + col);
+      if (k_item(j, tid, r, col)) k[j] = load8<T>(K + (int64_t)min(k0 + r, last) * DK + col);
     }
 #pragma unroll
     for (int j = 0; j < V_PER_THREAD; ++j) {
@@ -85,7 +87,7 @@ struct AttnTile {
       if (v_item(j, tid, d4, k4)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          v[j][q] = load4<T>(V + (int64_t)min(k0 + 4 * k4 + q, last) * D + 4 * d4);
+          v[j][q] = load4<T>(V + (int64_t)min(k0 + 4 * k4 + q, last) * DV + 4 * d4);
       }
     }
   }
@@ -115,12 +117,12 @@ struct AttnTile {
 // One key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // MASK: the tile reaches past the wave's first query row, so the causal mask
 // applies (only the tiles on the diagonal).
-template <typename T, int D, int BN, bool MASK>
+template <typename T, int DK, int DV, int BN, bool MASK>
 __device__ __forceinline__ void attn_tile(const T* Kb, const T* Vb, const frag_t<T>* qf,
                                           f32x16* oacc, float& m_run, float& l_run, float c,
                                           int k0, int row, int i, int h) {
-  constexpr int NC = D / 16, NDB = D / 32, NKB = BN / 32, NPC = BN / 16;
-  constexpr int KS = D + pad16<T>();
+  constexpr int NC = DK / 16, NDB = DV / 32, NKB = BN / 32, NPC = BN / 16;
+  constexpr int KS = DK + pad16<T>();
   constexpr int VS = BN + 4;
   f32x16 sacc[NKB];
 #pragma unroll
@@ -176,12 +178,12 @@ __device__ __forceinline__ void attn_tile(const T* Kb, const T* Vb, const frag_t
     }
 }
 
-template <typename T, int D, int NW, int BN>
+template <typename T, int DK, int DV, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
-  using Tile = AttnTile<T, D, NW, BN>;
+  using Tile = AttnTile<T, DK, DV, NW, BN>;
   constexpr int BM = 32 * NW;
-  constexpr int NC = D / 16;    // 16-wide chunks of the head dimension
-  constexpr int NDB = D / 32;   // 32-row blocks of the value dimension
+  constexpr int NC = DK / 16;   // 16-wide chunks of the key dimension
+  constexpr int NDB = DV / 32;  // 32-row blocks of the value dimension
   constexpr int NKB = BN / 32;  // 32-key blocks of a key tile
   constexpr int NPC = BN / 16;  // 16-key chunks of a key tile
   constexpr int KS = Tile::KS;
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
 
   // Two buffers: tile kt+1 is written while tile kt is read.
   __shared__ __align__(16) T Ks[2][BN * KS];  // K tiles, [key][dim]
-  __shared__ __align__(16) T Vt[2][D * VS];   // V tiles transposed, [dim][key]
+  __shared__ __align__(16) T Vt[2][DV * VS];  // V tiles transposed, [dim][key]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 31, h = lane >> 5;
@@ -219,10 +221,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   if (q0 >= n_s) return;  // the tail of a short last segment; uniform per workgroup
 
   const int64_t qh = (int64_t)b * a.Hq + hq;
-  const T* Q = static_cast<const T*>(a.q) + (qh * a.L + seg_start) * D;
-  const T* K = static_cast<const T*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
-  const T* V = static_cast<const T*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
-  T* O = static_cast<T*>(a.out) + (qh * a.L + seg_start) * D;
+  const T* Q = static_cast<const T*>(a.q) + (qh * a.L + seg_start) * DK;
+  const T* K = static_cast<const T*>(a.k) + ((int64_t)unit * a.L + seg_start) * DK;
+  const T* V = static_cast<const T*>(a.v) + ((int64_t)unit * a.L + seg_start) * DV;
+  T* O = static_cast<T*>(a.out) + (qh * a.L + seg_start) * DV;
 
   const int row = q0 + 32 * w + i;  // this lane's query, relative to the segment
   const bool wave_on = q0 + 32 * w < n_s;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     qf[cc] = zero_frag<T>();
-    if (row < n_s) qf[cc] = load8<T>(Q + (int64_t)row * D + 16 * cc + 8 * h);
+    if (row < n_s) qf[cc] = load8<T>(Q + (int64_t)row * DK + 16 * cc + 8 * h);
   }
 
   f32x16 oacc[NDB];
@@ -259,9 +261,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
 
     if (wave_on && k0 <= wave_last) {
       if (k0 + BN - 1 > q0 + 32 * w)
-        attn_tile<T, D, BN, true>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i, h);
+        attn_tile<T, DK, DV, BN, true>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i, h);
       else
-        attn_tile<T, D, BN, false>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i, h);
+        attn_tile<T, DK, DV, BN, false>(Ks[buf], Vt[buf], qf, oacc, m_run, l_run, c, k0, row, i,
+                                        h);
     }
     if (kt + 1 < n_kt) {
       // buffer buf^1 was last read in iteration kt-1, before that iteration's
@@ -276,8 +279,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   if (a.lse != nullptr && h == 0 && row < n_s)
     a.lse[qh * a.L + seg_start + row] = m_run * c + __log2f(l);
   const int64_t snap = (int64_t)unit * a.s_count + sl;
-  const float* zs = a.snapZ + snap * D;
-  const T* Mts = static_cast<const T*>(a.snapM) + snap * D * D;
+  const float* zs = a.snapZ + snap * DK;
+  const T* Mts = static_cast<const T*>(a.snapM) + snap * DV * DK;
 
   float sq[NC][8];
   float dp = 0.f;
@@ -306,10 +309,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      mma32(oacc[db], load8<T>(Mts + (int64_t)(32 * db + i) * D + 16 * cc + 8 * h), sf[cc]);
+      mma32(oacc[db], load8<T>(Mts + (int64_t)(32 * db + i) * DK + 16 * cc + 8 * h), sf[cc]);
 
   if (row < n_s) {
-    T* orow = O + (int64_t)row * D;
+    T* orow = O + (int64_t)row * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -669,7 +672,7 @@ hipError_t launch_attn_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
     hipLaunchKernelGGL((attn_kernel_dma<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
                        stream, a);
   } else {
-    hipLaunchKernelGGL((attn_kernel<T, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attn_kernel<T, D, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
                        stream, a);
   }
   return hipGetLastError();
@@ -701,6 +704,48 @@ int attn_waves(int64_t seg_len) { return seg_len <= 32 ? 1 : (seg_len <= 64 ? 2 
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream) {
   return dtype == kBF16 ? launch_attn_d<bf16>(d, a, units, stream)
                         : launch_attn_d<float>(d, a, units, stream);
+}
+
+namespace {
+
+// d_key != d_value: the register-staged kernel with four waves (rows past a
+// short segment's end are masked), every ordered pair of distinct widths in
+// {32, 64, 128}.
+template <typename T, int DK, int DV>
+hipError_t launch_attn_kv_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
+  constexpr int NW = 4, BN = 64;
+  const int64_t total = units * a.s_count * a.n_qt * (a.Hq / a.Hkv);
+  hipLaunchKernelGGL((attn_kernel<T, DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t launch_attn_kv_v(int dv, const AttnArgs& a, int64_t units, hipStream_t stream) {
+  switch (dv) {
+    case 32: return DK != 32 ? launch_attn_kv_t<T, DK, 32>(a, units, stream) : hipErrorInvalidValue;
+    case 64: return DK != 64 ? launch_attn_kv_t<T, DK, 64>(a, units, stream) : hipErrorInvalidValue;
+    case 128: return DK != 128 ? launch_attn_kv_t<T, DK, 128>(a, units, stream) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_attn_kv_d(int dk, int dv, const AttnArgs& a, int64_t units, hipStream_t stream) {
+  switch (dk) {
+    case 32: return launch_attn_kv_v<T, 32>(dv, a, units, stream);
+    case 64: return launch_attn_kv_v<T, 64>(dv, a, units, stream);
+    case 128: return launch_attn_kv_v<T, 128>(dv, a, units, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_kv(int dtype, int dk, int dv, const AttnArgs& a, int64_t units,
+                          hipStream_t stream) {
+  return dtype == kBF16 ? launch_attn_kv_d<bf16>(dk, dv, a, units, stream)
+                        : launch_attn_kv_d<float>(dk, dv, a, units, stream);
 }
 
 }  // namespace infini

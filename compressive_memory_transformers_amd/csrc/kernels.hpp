@@ -200,6 +200,10 @@ hipError_t launch_bwd_finish(int dtype, int d, const BwdArgs& a, hipStream_t str
 int attn_waves(int64_t seg_len);
 
 hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_t stream);
+// The direct scan with d_key = dk != d_value = dv (both in {32, 64, 128}): M is
+// [dk][dv] per unit, the snapshots M^T [dv][dk], z [dk].
+hipError_t launch_scan_kv(int dtype, int dk, int dv, int rule, const ScanArgs& a,
+                          hipStream_t stream);
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 // The chain step of the affine form alone (a.reverse honoured).
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
@@ -208,6 +212,10 @@ hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStre
 // otherwise: the caller takes another path).
 hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
+// The attention with d_key = dk != d_value = dv: q, k rows of dk, v and out
+// rows of dv, snapshots as launch_scan_kv writes them.
+hipError_t launch_attn_kv(int dtype, int dk, int dv, const AttnArgs& a, int64_t units,
+                          hipStream_t stream);
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
 

@@ -46,23 +46,26 @@ __device__ __forceinline__ void reduce_scatter_step(float* a, int mask, bool upp
   }
 }
 
-template <typename T, int D, int RULE, int NW>
+// DK: the key width (rows of M, length of z); DV: the value width (columns
+// of M, split into 32-column slabs).
+template <typename T, int DK, int DV, int RULE, int NW>
 __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int TOK = 32 * NW;         // tokens per step
-  constexpr int NC = D / 16;           // 16-wide chunks of the key dimension
-  constexpr int NDB = D / 32;          // 32-row blocks of the key dimension
-  constexpr int NZ = NC * 8;           // key-dimension entries a lane touches (D / 2)
-  constexpr int MTS = D + pad16<T>();  // row stride of Mt
+  constexpr int TOK = 32 * NW;          // tokens per step
+  constexpr int NC = DK / 16;           // 16-wide chunks of the key dimension
+  constexpr int NDB = DK / 32;          // 32-row blocks of the key dimension
+  constexpr int NZ = NC * 8;            // key-dimension entries a lane touches (DK / 2)
+  constexpr int MTS = DK + pad16<T>();  // row stride of Mt
   constexpr int PTS = TOK + pad16<T>();  // row stride of PhiT
-  constexpr int MSS = 33;              // row stride of Ms (float)
+  constexpr int MSS = 33;               // row stride of Ms (float)
+  static_assert(NT >= DK, "one thread per entry of z");
 
   __shared__ __align__(16) T Mt[32 * MTS];    // M_{s-1}^T of the slab, element type
-  __shared__ __align__(16) T PhiT[D * PTS];   // sigma(K)^T of the current step
-  __shared__ float Ms[D * MSS];               // the slab of M in float, [key][value]
+  __shared__ __align__(16) T PhiT[DK * PTS];  // sigma(K)^T of the current step
+  __shared__ float Ms[DK * MSS];              // the slab of M in float, [key][value]
   __shared__ float den_s[TOK];
-  __shared__ float zprev[D];
-  __shared__ float zred[NW * D];
+  __shared__ float zprev[DK];
+  __shared__ float zred[NW * DK];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 31, h = lane >> 5;
@@ -70,19 +73,19 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
   const int slab = blockIdx.x / a.units;
   const int col0 = slab * 32;
 
-  const T* K = static_cast<const T*>(a.k) + (int64_t)unit * a.L * D;
-  const T* V = static_cast<const T*>(a.v) + (int64_t)unit * a.L * D;
-  const float* Min = a.M_in + (int64_t)unit * D * D;
-  const float* zin = a.z_in + (int64_t)unit * D;
+  const T* K = static_cast<const T*>(a.k) + (int64_t)unit * a.L * DK;
+  const T* V = static_cast<const T*>(a.v) + (int64_t)unit * a.L * DV;
+  const float* Min = a.M_in + (int64_t)unit * DK * DV;
+  const float* zin = a.z_in + (int64_t)unit * DK;
 
-  for (int idx = tid; idx < D * 32; idx += NT) {
+  for (int idx = tid; idx < DK * 32; idx += NT) {
     const int dk = idx >> 5, c = idx & 31;
-    Ms[dk * MSS + c] = Min[dk * D + col0 + c];
+    Ms[dk * MSS + c] = Min[dk * DV + col0 + c];
   }
-  for (int idx = tid; idx < D; idx += NT) zprev[idx] = zin[idx];
+  for (int idx = tid; idx < DK; idx += NT) zprev[idx] = zin[idx];
   __syncthreads();
-  for (int idx = tid; idx < 32 * D; idx += NT) {
-    const int r = idx / D, dk = idx % D;
+  for (int idx = tid; idx < 32 * DK; idx += NT) {
+    const int r = idx / DK, dk = idx % DK;
     Mt[r * MTS + dk] = from_f32<T>(Ms[dk * MSS + r]);
   }
   __syncthreads();
@@ -93,14 +96,14 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
 
     // The state before this segment, for the retrieval.
     {
-      T* sM = static_cast<T*>(a.snapM) + ((int64_t)unit * a.s_count + sl) * D * D;
-      for (int idx = tid; idx < 32 * (D / 8); idx += NT) {
-        const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-        store8<T>(sM + (int64_t)(col0 + r) * D + c8, load8<T>(Mt + r * MTS + c8));
+      T* sM = static_cast<T*>(a.snapM) + ((int64_t)unit * a.s_count + sl) * DV * DK;
+      for (int idx = tid; idx < 32 * (DK / 8); idx += NT) {
+        const int r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+        store8<T>(sM + (int64_t)(col0 + r) * DK + c8, load8<T>(Mt + r * MTS + c8));
       }
       if (slab == 0) {
-        float* sZ = a.snapZ + ((int64_t)unit * a.s_count + sl) * D;
-        for (int idx = tid; idx < D; idx += NT) sZ[idx] = zprev[idx];
+        float* sZ = a.snapZ + ((int64_t)unit * a.s_count + sl) * DK;
+        for (int idx = tid; idx < DK; idx += NT) sZ[idx] = zprev[idx];
       }
     }
 
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
     for (int t0 = 0; t0 < n_s; t0 += TOK) {
       const int tok = t0 + 32 * w + i;
       const bool valid = tok < n_s;
-      const T* krow = K + (seg_start + tok) * D;
+      const T* krow = K + (seg_start + tok) * DK;
       frag_t<T> phf[NC];
       float dpart = 0.f;
 #pragma unroll
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
         const int tr = acc_row(r, h);
         const int tk = t0 + 32 * w + tr;
         T vv = from_f32<T>(0.f);
-        if (tk < n_s) vv = V[(seg_start + tk) * D + col0 + i];
+        if (tk < n_s) vv = V[(seg_start + tk) * DV + col0 + i];
         vf[r >> 3][r & 7] = vv;
         if constexpr (RULE == kRuleDelta)
           pf[r >> 3][r & 7] = from_f32<T>(-accp[r] / den_s[32 * w + tr]);
@@ -226,54 +229,75 @@ __global__ __launch_bounds__(NW * 64) void scan_kernel(ScanArgs a) {
       if (write) {
         for (int j = 0; j < cnt; ++j) {
           const int q = base + j;
-          zred[w * D + 16 * (q >> 3) + 8 * h + (q & 7)] = zp[j];
+          zred[w * DK + 16 * (q >> 3) + 8 * h + (q & 7)] = zp[j];
         }
       }
       __syncthreads();
-      if (tid < D) {
+      if (tid < DK) {
         float s = zprev[tid];
-        for (int ww = 0; ww < NW; ++ww) s += zred[ww * D + tid];
+        for (int ww = 0; ww < NW; ++ww) s += zred[ww * DK + tid];
         zprev[tid] = s;
       }
     }
-    for (int idx = tid; idx < 32 * D; idx += NT) {
-      const int r = idx / D, dk = idx % D;
+    for (int idx = tid; idx < 32 * DK; idx += NT) {
+      const int r = idx / DK, dk = idx % DK;
       Mt[r * MTS + dk] = from_f32<T>(Ms[dk * MSS + r]);
     }
     __syncthreads();
   }
 
-  float* Mout = a.M_out + (int64_t)unit * D * D;
-  for (int idx = tid; idx < D * 32; idx += NT) {
+  float* Mout = a.M_out + (int64_t)unit * DK * DV;
+  for (int idx = tid; idx < DK * 32; idx += NT) {
     const int dk = idx >> 5, c = idx & 31;
-    Mout[dk * D + col0 + c] = Ms[dk * MSS + c];
+    Mout[dk * DV + col0 + c] = Ms[dk * MSS + c];
   }
   if (slab == 0) {
-    float* zout = a.z_out + (int64_t)unit * D;
-    for (int idx = tid; idx < D; idx += NT) zout[idx] = zprev[idx];
+    float* zout = a.z_out + (int64_t)unit * DK;
+    for (int idx = tid; idx < DK; idx += NT) zout[idx] = zprev[idx];
   }
 }
 
-template <typename T, int D, int RULE>
+template <typename T, int DK, int DV, int RULE>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t stream) {
   constexpr int NW = 4;
-  const dim3 grid((unsigned)(a.units * (D / 32)));
-  hipLaunchKernelGGL((scan_kernel<T, D, RULE, NW>), grid, dim3(NW * 64), 0, stream, a);
+  const dim3 grid((unsigned)(a.units * (DV / 32)));
+  hipLaunchKernelGGL((scan_kernel<T, DK, DV, RULE, NW>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t launch_scan_rule(int rule, const ScanArgs& a, hipStream_t stream) {
-  return rule == kRuleDelta ? launch_scan_t<T, D, kRuleDelta>(a, stream)
-                            : launch_scan_t<T, D, kRuleLinear>(a, stream);
+  return rule == kRuleDelta ? launch_scan_t<T, DK, DV, kRuleDelta>(a, stream)
+                            : launch_scan_t<T, DK, DV, kRuleLinear>(a, stream);
 }
 
 template <typename T>
 hipError_t launch_scan_d(int d, int rule, const ScanArgs& a, hipStream_t stream) {
   switch (d) {
-    case 32: return launch_scan_rule<T, 32>(rule, a, stream);
-    case 64: return launch_scan_rule<T, 64>(rule, a, stream);
-    case 128: return launch_scan_rule<T, 128>(rule, a, stream);
+    case 32: return launch_scan_rule<T, 32, 32>(rule, a, stream);
+    case 64: return launch_scan_rule<T, 64, 64>(rule, a, stream);
+    case 128: return launch_scan_rule<T, 128, 128>(rule, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// d_key != d_value: every ordered pair of distinct widths in {32, 64, 128}
+template <typename T, int DK>
+hipError_t launch_scan_kv_v(int dv, int rule, const ScanArgs& a, hipStream_t stream) {
+  switch (dv) {
+    case 32: return DK != 32 ? launch_scan_rule<T, DK, 32>(rule, a, stream) : hipErrorInvalidValue;
+    case 64: return DK != 64 ? launch_scan_rule<T, DK, 64>(rule, a, stream) : hipErrorInvalidValue;
+    case 128: return DK != 128 ? launch_scan_rule<T, DK, 128>(rule, a, stream) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_scan_kv_d(int dk, int dv, int rule, const ScanArgs& a, hipStream_t stream) {
+  switch (dk) {
+    case 32: return launch_scan_kv_v<T, 32>(dv, rule, a, stream);
+    case 64: return launch_scan_kv_v<T, 64>(dv, rule, a, stream);
+    case 128: return launch_scan_kv_v<T, 128>(dv, rule, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -289,6 +313,12 @@ __global__ void copy_f32_kernel(float* dst, const float* src, int64_t n) {
 hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_t stream) {
   return dtype == kBF16 ? launch_scan_d<bf16>(d, rule, a, stream)
                         : launch_scan_d<float>(d, rule, a, stream);
+}
+
+hipError_t launch_scan_kv(int dtype, int dk, int dv, int rule, const ScanArgs& a,
+                          hipStream_t stream) {
+  return dtype == kBF16 ? launch_scan_kv_d<bf16>(dk, dv, rule, a, stream)
+                        : launch_scan_kv_d<float>(dk, dv, rule, a, stream);
 }
 
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream) {

@@ -113,6 +113,32 @@ infini_status_t infini_attn_forward(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward with a key width different from the value width
+ * ("Infini-Attention" (AI Wiki), "How does the compressive memory work?": the
+ * memory M maps d_key-dimensional features to d_value-dimensional values).
+ * Identical to infini_attn_forward when d_key == d_value (the same call).
+ *   q        [B][Hq][L][d_key]     k [B][Hkv][L][d_key]    element type
+ *   v        [B][Hkv][L][d_value]  out [B][Hq][L][d_value] element type
+ *   M0, M_final [B][Hkv][d_key][d_value] float; z0, z_final [B][Hkv][d_key]
+ * The softmax scale is 1/sqrt(d_key). d_key and d_value are each 32, 64 or
+ * 128 (else INFINI_ERR_UNSUPPORTED). With d_key != d_value the memory runs as
+ * the segment-by-segment scan (not the affine form) and the attention as the
+ * register-staged kernel; numerics as infini_attn_forward. Workspace sizes
+ * from infini_attn_workspace_size_kv, with the same full and minimum
+ * meanings; arguments, overlaps and errors as infini_attn_forward.
+ */
+infini_status_t infini_attn_workspace_size_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype, size_t* full_bytes, size_t* min_bytes);
+infini_status_t infini_attn_forward_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * infini_attn_forward, plus HIP events recorded on `stream` around its
  * kernels, for timing each phase. The segments run in windows (one window
  * when the workspace has the full size); for window w the call records

@@ -54,12 +54,14 @@ def all_units(B, Hkv):
     return [(b, j) for b in range(B) for j in range(Hkv)]
 
 
-def random_inputs(B, Hq, Hkv, L, d, dtype, device, seed=0, m0_scale=0.0, z0=1e-6):
+def random_inputs(B, Hq, Hkv, L, d, dtype, device, seed=0, m0_scale=0.0, z0=1e-6, dv=None):
+    """Seeded Gaussian inputs; ``dv`` gives v (and M0's columns) another width."""
+    dv = d if dv is None else dv
     g = torch.Generator(device="cpu").manual_seed(seed)
     mk = lambda *s: torch.randn(*s, generator=g, dtype=torch.float32)
     inp = dict(
-        q=mk(B, Hq, L, d).to(dtype), k=mk(B, Hkv, L, d).to(dtype), v=mk(B, Hkv, L, d).to(dtype),
-        beta=mk(Hq), M0=m0_scale * mk(B, Hkv, d, d),
+        q=mk(B, Hq, L, d).to(dtype), k=mk(B, Hkv, L, d).to(dtype), v=mk(B, Hkv, L, dv).to(dtype),
+        beta=mk(Hq), M0=m0_scale * mk(B, Hkv, d, dv),
         z0=(torch.full((B, Hkv, d), z0) if m0_scale == 0.0
             else 0.5 + torch.rand(B, Hkv, d, generator=g)),
     )

@@ -35,8 +35,9 @@ def test_header_declares_the_entry_points():
         "infini_attn_backward", "infini_attn_backward_workspace_size",
         "infini_attn_block_forward", "infini_attn_block_forward_timed",
         "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_error_string", "infini_attn_decode_workspace_size",
-        "infini_attn_forward", "infini_attn_forward_timed", "infini_attn_forward_train",
-        "infini_attn_status_string", "infini_attn_version", "infini_attn_workspace_size"])
+        "infini_attn_forward", "infini_attn_forward_kv", "infini_attn_forward_timed",
+        "infini_attn_forward_train", "infini_attn_status_string", "infini_attn_version",
+        "infini_attn_workspace_size", "infini_attn_workspace_size_kv"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -97,6 +98,62 @@ def test_workspace_sizes(lib):
     st, a, _ = ws(lib, 1, 1, 1, 100, 32, 30, 0, 0)
     st, b, _ = ws(lib, 1, 1, 1, 120, 32, 30, 0, 0)
     assert a == b
+
+
+def ws_kv(lib, *args):
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib.infini_attn_workspace_size_kv(*args, ctypes.byref(full), ctypes.byref(least))
+    return st, full.value, least.value
+
+
+def test_workspace_sizes_with_separate_key_and_value_widths(lib):
+    # d_key = d_value: the square call's sizes, affine form included
+    for args in [(4, 32, 8, 32768, 128, 2048, 1, 1), (2, 4, 2, 64, 32, 16, 0, 0)]:
+        B, Hq, Hkv, L, d, N, rule, dt = args
+        assert ws_kv(lib, B, Hq, Hkv, L, d, d, N, rule, dt) == ws(lib, *args)
+    # d_key != d_value: the direct scan's snapshots only, M^T [dv][dk] in the
+    # element type and z [dk] in float, per (unit, segment)
+    for dk, dv, e, dt in [(64, 128, 2, 1), (128, 32, 4, 0), (32, 64, 2, 1)]:
+        st, full, least = ws_kv(lib, 2, 8, 2, 1000, dk, dv, 300, 1, dt)
+        assert st == 0
+        per_seg = 2 * 2 * (dv * dk * e + dk * 4)
+        assert full - least == 3 * per_seg  # 4 segments, the last one ragged
+        assert least >= per_seg + 2 * 4 * (dk * dv + dk) * 4
+
+
+@pytest.mark.parametrize("dk,dv,status", [(64, 48, 2), (96, 64, 2), (64, 256, 2), (0, 64, 1),
+                                          (64, 0, 1)])
+def test_workspace_size_kv_rejects(lib, dk, dv, status):
+    assert ws_kv(lib, 1, 2, 2, 64, dk, dv, 16, 0, 1)[0] == status
+
+
+def test_forward_kv_rejects_before_any_launch(lib):
+    # sizes of q, k (d_key 64) and v, out (d_value 128) in bf16
+    B, Hq, Hkv, L, dk, dv = 1, 2, 1, 64, 64, 128
+    sizes = dict(q=B * Hq * L * dk * 2, k=B * Hkv * L * dk * 2, v=B * Hkv * L * dv * 2,
+                 beta=Hq * 4, M0=B * Hkv * dk * dv * 4, z0=B * Hkv * dk * 4,
+                 out=B * Hq * L * dv * 2, M_final=B * Hkv * dk * dv * 4, z_final=B * Hkv * dk * 4,
+                 workspace=1 << 40)
+    addr, base = {}, 1 << 44
+    for name, n in sizes.items():
+        addr[name] = base
+        base += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(dk_=dk, dv_=dv, wsb=1 << 40, **over):
+        a = {**addr, **over}
+        return lib.infini_attn_forward_kv(
+            B, Hq, Hkv, L, dk_, dv_, 16, 1, 1,
+            *[ctypes.c_void_p(a[n]) for n in ("q", "k", "v", "beta", "M0", "z0", "out",
+                                               "M_final", "z_final", "workspace")], wsb, None)
+    assert call(dv_=48) == 2
+    assert call(dk_=96) == 2
+    assert call(q=None) == 1
+    assert call(v=addr["v"] + 8) == 3
+    # out is [B,Hq,L,dv]: its last bytes reach past a q-sized buffer
+    assert call(out=addr["v"] + sizes["v"] - 64) == 1
+    assert call(M_final=addr["z0"]) == 1
+    _, _, least = ws_kv(lib, B, Hq, Hkv, L, dk, dv, 16, 1, 1)
+    assert call(wsb=least - 1) == 4
 
 
 @pytest.mark.parametrize("args,status", [
