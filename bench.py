@@ -40,18 +40,21 @@ def attn_kernel_bytes(w):
     once, K and V once, and the per-segment state it reads (M^T in the element
     type and z in float, per KV head and segment), beta once."""
     e = 4 if w.dtype == "f32" else 2
-    return (e * w.d * w.L * w.B * (2 * w.Hq + 2 * w.Hkv)
-            + w.B * w.Hkv * w.segments * (w.d * w.d * e + 4 * w.d) + 4 * w.Hq)
+    d, dv = w.d, w.d_value
+    return (e * w.L * w.B * ((d + dv) * w.Hq + (d + dv) * w.Hkv)
+            + w.B * w.Hkv * w.segments * (d * dv * e + 4 * d) + 4 * w.Hq)
 
 
 def attn_kernel_flops(w):
     """Algorithmic matrix-product FLOPs of the attention kernel in one call:
     per (query head, token) 2d(N+1) for the causal QK^T and PV (diagonal
-    counted) and 2d^2 for sigma(Q) M, summed exactly over segments."""
+    counted) and 2d^2 for sigma(Q) M, summed exactly over segments; with a
+    value width dv, (d + dv)(N+1) and 2 d dv."""
+    d, dv = w.d, w.d_value
     total = 0
     for s in range(w.segments):
         n = min(w.seg_len, w.L - s * w.seg_len)
-        total += 2 * w.d * n * (n + 1) + 2 * n * w.d * w.d
+        total += (d + dv) * n * (n + 1) + 2 * n * d * dv
     return w.B * w.Hq * total
 
 
@@ -399,10 +402,11 @@ def main():
         print(json.dumps(bench_block(lib, w, rule, dev, args)), flush=True)
         return
     inp = synth.make_inputs(w, dev)
-    out = torch.empty_like(inp["q"])
+    out = torch.empty((w.B, w.Hq, w.L, w.d_value), dtype=inp["q"].dtype, device=dev)
     M = torch.empty_like(inp["M0"])
     z = torch.empty_like(inp["z0"])
-    full, _ = lib.workspace_size(w.B, w.Hq, w.Hkv, w.L, w.d, w.seg_len, rule, inp["q"].dtype)
+    full, _ = lib.workspace_size_kv(w.B, w.Hq, w.Hkv, w.L, w.d, w.d_value, w.seg_len, rule,
+                                    inp["q"].dtype)
     ws = torch.empty(full, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -452,13 +456,15 @@ def main():
     # the bound is the kernel's: matrix cores above the ridge point
     # (peak FLOP/s / peak bytes/s), HBM below it
     a_bytes = attn_kernel_bytes(w)
+    kname = ("attn_kernel (local causal attention + retrieval + gate)" if w.d_value == w.d else
+             "attn_kernel, register-staged, d_key != d_value (attention + retrieval + gate)")
     if a_flops / a_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roofline = {"kernel": "attn_kernel (local causal attention + retrieval + gate)",
+        roofline = {"kernel": kname,
                     "bound": "mfma", "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s",
                     "frac": a_tflops / peak}
     else:
         gbs = a_bytes / (attn_ms * 1e-3) / 1e9
-        roofline = {"kernel": "attn_kernel (local causal attention + retrieval + gate)",
+        roofline = {"kernel": kname,
                     "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": gbs / PEAK_HBM_GBS}
     roofline.update({"traffic": traffic, "algorithmic_flop_per_launch": a_flops,
@@ -477,7 +483,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian Q/K/V in HBM; random beta; M0 = 0, z0 = 1e-6)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "d": w.d,
-                   "seg_len": w.seg_len, "segments": w.segments, "rule": rule},
+                   "seg_len": w.seg_len, "segments": w.segments, "rule": rule,
+                   **({"d_value": w.d_value} if w.d_value != w.d else {})},
         "tflops": tflops,
         "frac_of_peak": tflops / peak,
         "peak_tflops": peak,

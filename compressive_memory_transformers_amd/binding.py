@@ -32,6 +32,9 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
     "infini_attn_forward_kv": (
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_forward_kv_timed": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
+        + [ctypes.POINTER(_c_p), _c_i32]),
     "infini_attn_forward_timed": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
@@ -129,7 +132,7 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     q [B,Hq,L,d], k and v [B,Hkv,L,d] (float32 or bfloat16, contiguous, on one
     GPU), beta [Hq] float32, M0 [B,Hkv,d,d] float32, z0 [B,Hkv,d] float32.
     v may have another width dv than q and k (then M0 is [B,Hkv,d,dv] and out
-    [B,Hq,L,dv]): infini_attn_forward_kv, without ``events`` or ``lse``.
+    [B,Hq,L,dv]): infini_attn_forward_kv, without ``lse``.
     Returns (out, M_final, z_final). Output buffers and a workspace (a uint8
     tensor) may be passed in; M_final may be M0 and z_final may be z0. Runs on
     ``stream`` (a torch.cuda.Stream) or torch's current stream, asynchronously.
@@ -146,8 +149,8 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
                          f"{tuple(v.shape)}")
     if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, dv) or z0.shape != (B, Hkv, d):
         raise ValueError("beta, M0 or z0 has the wrong shape")
-    if dv != d and (events or lse is not None):
-        raise ValueError("events and lse need d_value == d_key")
+    if dv != d and lse is not None:
+        raise ValueError("lse needs d_value == d_key")
     if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
     if beta.dtype != torch.float32 or M0.dtype != torch.float32 or z0.dtype != torch.float32:
@@ -194,8 +197,12 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
         name = "infini_attn_forward_train"
     elif events:
         handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
-        st = lib.infini_attn_forward_timed(*args, handles, len(events))
-        name = "infini_attn_forward_timed"
+        if dv != d:
+            st = lib.infini_attn_forward_kv_timed(*args[:5], dv, *args[5:], handles, len(events))
+            name = "infini_attn_forward_kv_timed"
+        else:
+            st = lib.infini_attn_forward_timed(*args, handles, len(events))
+            name = "infini_attn_forward_timed"
     elif dv != d:
         st = lib.infini_attn_forward_kv(*args[:5], dv, *args[5:])
         name = "infini_attn_forward_kv"

@@ -406,6 +406,20 @@ infini_status_t infini_attn_forward_kv(int64_t B, int64_t Hq, int64_t Hkv, int64
                       d_value);
 }
 
+infini_status_t infini_attn_forward_kv_timed(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                             int64_t d_key, int64_t d_value, int64_t seg_len,
+                                             int32_t rule, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const float* beta,
+                                             const float* M0, const float* z0, void* out,
+                                             float* M_final, float* z_final, void* workspace,
+                                             size_t workspace_bytes, void* stream,
+                                             void* const* events, int32_t n_events) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return forward_impl(B, Hq, Hkv, L, d_key, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
+                      M_final, z_final, nullptr, workspace, workspace_bytes, stream, events,
+                      n_events, d_value);
+}
+
 infini_status_t infini_attn_forward_train(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
                                           int64_t d, int64_t seg_len, int32_t rule,
                                           int32_t dtype, const void* q, const void* k,

@@ -137,6 +137,15 @@ infini_status_t infini_attn_forward_kv(
     const float* M0, const float* z0,
     void* out, float* M_final, float* z_final,
     void* workspace, size_t workspace_bytes, void* stream);
+/* infini_attn_forward_kv with the events of infini_attn_forward_timed. */
+infini_status_t infini_attn_forward_kv_timed(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
 
 /*
  * infini_attn_forward, plus HIP events recorded on `stream` around its

@@ -47,7 +47,12 @@ class Workload:
     key_outlier_p: float = 0.0
     key_outlier_scale: float = 1.0
     z0: float = 1e-6
+    dv: int = 0  # the value width when it differs from the key width d
     note: str = field(default="", compare=False)
+
+    @property
+    def d_value(self):
+        return self.dv or self.d
 
     @property
     def segments(self):
@@ -87,6 +92,10 @@ WORKLOADS = {
         "long_segment", B=1, Hq=16, Hkv=16, L=400000, d=128, seg_len=100000,
         dtype="bf16", rules=("linear",), seed=5, key_std=1.0 / math.sqrt(128),
         note="B1 H16 d128, 4 segments of 100000 tokens (very long segments)"),
+    "kv_split": Workload(
+        "kv_split", B=4, Hq=32, Hkv=8, L=32768, d=64, dv=128, seg_len=2048,
+        dtype="bf16", rules=("delta",), seed=6,
+        note="the llama3_8b layer with 64-wide keys and 128-wide values (d_key != d_value)"),
 }
 
 
@@ -111,14 +120,15 @@ def _uniform(shape, seed, device):
 def make_inputs(w, device="cpu"):
     """Inputs of workload ``w`` on ``device``.
 
-    Returns a dict with q [B,Hq,L,d], k and v [B,Hkv,L,d] in the workload's
-    dtype, beta [Hq] float32, M0 [B,Hkv,d,d] float32 (zeros) and z0 [B,Hkv,d]
-    float32 (all ``w.z0``).
+    Returns a dict with q [B,Hq,L,d], k [B,Hkv,L,d] and v [B,Hkv,L,dv] in the
+    workload's dtype, beta [Hq] float32, M0 [B,Hkv,d,dv] float32 (zeros) and
+    z0 [B,Hkv,d] float32 (all ``w.z0``); dv is ``w.d_value``.
     """
     dt = w.torch_dtype
+    dv = w.d_value
     q = torch.empty((w.B, w.Hq, w.L, w.d), dtype=dt, device=device)
     k = torch.empty((w.B, w.Hkv, w.L, w.d), dtype=dt, device=device)
-    v = torch.empty((w.B, w.Hkv, w.L, w.d), dtype=dt, device=device)
+    v = torch.empty((w.B, w.Hkv, w.L, dv), dtype=dt, device=device)
     for b in range(w.B):
         for h in range(w.Hq):
             q[b, h] = _normal((w.L, w.d), slice_seed(w.seed, "q", b, h), device).to(dt)
@@ -131,9 +141,9 @@ def make_inputs(w, device="cpu"):
                 kk = torch.where((pick < w.key_outlier_p)[:, None],
                                  kk * w.key_outlier_scale, kk)
             k[b, h] = kk.to(dt)
-            v[b, h] = _normal((w.L, w.d), slice_seed(w.seed, "v", b, h), device).to(dt)
+            v[b, h] = _normal((w.L, dv), slice_seed(w.seed, "v", b, h), device).to(dt)
     beta = _normal((w.Hq,), slice_seed(w.seed, "beta", 0, 0), device)
-    M0 = torch.zeros((w.B, w.Hkv, w.d, w.d), dtype=torch.float32, device=device)
+    M0 = torch.zeros((w.B, w.Hkv, w.d, dv), dtype=torch.float32, device=device)
     z0 = torch.full((w.B, w.Hkv, w.d), w.z0, dtype=torch.float32, device=device)
     return dict(q=q, k=k, v=v, beta=beta, M0=M0, z0=z0)
 
@@ -150,15 +160,16 @@ def flops(w, rule):
     diagonal counted (the mean of 2d per visible key over a segment of N is
     2d(N+1)/2 each for QK^T and PV), 2d^2 for sigma(Q) M, and per (KV head,
     token) 2d^2 (linear) or 4d^2 (delta) for the update. Summed exactly over
-    segments so a short final segment is counted as it is.
+    segments so a short final segment is counted as it is. With a value width
+    dv: (d + dv)(N+1) for the two local products and d dv in place of d^2.
     """
-    d = w.d
+    d, dv = w.d, w.d_value
     per_seg = []
     for s in range(w.segments):
         n = min(w.seg_len, w.L - s * w.seg_len)
-        local = 2 * d * n * (n + 1)  # both products over the causal triangle
-        retrieval = 2 * n * d * d
-        update = (2 if rule == "linear" else 4) * n * d * d
+        local = (d + dv) * n * (n + 1)  # both products over the causal triangle
+        retrieval = 2 * n * d * dv
+        update = (2 if rule == "linear" else 4) * n * d * dv
         per_seg.append(w.Hq * (local + retrieval) + w.Hkv * update)
     return w.B * sum(per_seg)
 
@@ -167,8 +178,9 @@ def hbm_bytes(w):
     """Compulsory HBM bytes of one call: Q, K, V read once, out written once,
     the fp32 state read and written once, beta read once."""
     e = 4 if w.dtype == "f32" else 2
-    return (e * w.d * w.L * w.B * (2 * w.Hq + 2 * w.Hkv)
-            + 8 * w.B * w.Hkv * (w.d * w.d + w.d) + 4 * w.Hq)
+    d, dv = w.d, w.d_value
+    return (e * w.L * w.B * ((d + dv) * w.Hq + (d + dv) * w.Hkv)
+            + 8 * w.B * w.Hkv * (d * dv + d) + 4 * w.Hq)
 
 
 def make_block_inputs(B, L, d_model, Hq, Hkv, d, dtype, device="cpu", seed=0, z0=1e-6,

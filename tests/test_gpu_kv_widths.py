@@ -81,3 +81,19 @@ def test_kv_windows_and_in_place_carry(lib, pair):
     assert torch.equal(o1, o2) and torch.equal(M1, M2) and torch.equal(z1, z2)
     assert torch.equal(o1, o3) and torch.equal(M1, M3) and torch.equal(z1, z3)
     assert M3.data_ptr() == M0c.data_ptr()
+
+
+def test_kv_split_workload(lib):
+    """The kv_split workload at its full size (the launch configuration the
+    benchmark times), checked on two sampled (batch, KV head) units."""
+    import synth
+    w = synth.WORKLOADS["kv_split"]
+    units = [(0, 0), (3, 7)]
+    _say(f"kv_split (d_key {w.d}, d_value {w.d_value}, delta, GQA 32/8), units {units}")
+    inp = synth.make_inputs(w, DEV)
+    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                      w.seg_len, "delta")
+    torch.cuda.synchronize()
+    eo, eM, ez = compare_units(inp, res, w.seg_len, "delta", units)
+    _say(f"errors out={eo:.3e} M={eM:.3e} z={ez:.3e}")
+    assert eo <= 2e-2 and eM <= 2e-2 and ez <= 2e-2, (eo, eM, ez)
