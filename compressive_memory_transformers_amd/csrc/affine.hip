@@ -483,6 +483,99 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
   for (int r = 0; r < 16; ++r) Mout[(32 * w + acc_row(r, h)) * D + col0 + i] = acc[r];
 }
 
+// ---- the same step, bf16, d = 128, delta rule: one workgroup per unit ------
+//
+// The slab kernel above reads A_s whole in each of a unit's four slab
+// workgroups, 32 rows per load instruction; with many units that keeps the
+// texture units busy for most of its time. Here one 16-wave workgroup holds
+// the unit's whole M: wave (rb, cb) owns the 32 x 32 block at rows 32 rb,
+// columns 32 cb. Per step A_s comes into LDS once, by 16-byte DMA in the K
+// tile layout (two 64-row tiles), M_{s-1}^T is written to LDS in bf16 by the
+// waves, and the snapshot goes from there to global memory in 16-byte rows.
+// The next step's A_s and B_s block are loaded as soon as the current ones
+// are consumed, so their latency overlaps the step's barrier and stores.
+// LDS: A_s 32 KiB + M^T 34 KiB; up to 128 registers, one workgroup per CU.
+__global__ __launch_bounds__(1024, 4) void chain_unit_kernel(AffineArgs a) {
+  constexpr int D = 128, NC = D / 16, MTS = D + 8;
+  using Tile = DmaTile<D, 16, 64>;
+  __shared__ __align__(1024) bf16 A0[64 * D];  // A_s rows 0..63, K tile layout
+  __shared__ __align__(1024) bf16 A1[64 * D];  // rows 64..127
+  __shared__ __align__(16) bf16 Mt[D * MTS];   // M_{s-1}^T, [column][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  const int rb = w >> 2, cb = w & 3;
+  const int unit = blockIdx.x;
+  const int r0 = 32 * rb, c0 = 32 * cb;
+
+  Tile tile;
+  tile.init(w, lane);
+  // the A operand: row r0 + i of A_s, k = 16 c + 8 h + e. In the K layout
+  // chunk 2c + h of tile row r sits at chunk (2c + h) ^ swz_k(r): byte offset
+  // ao ^ 32 c, with ao that of chunk h (the row bits lie above the XOR's).
+  const bf16* Ab = rb < 2 ? A0 : A1;
+  const uint32_t ao = 2 * (((r0 & 63) + i) * D + 8 * (h ^ swz_k<D>((r0 & 63) + i)));
+
+  f32x16 acc;
+  const float* Min = a.M_in + (int64_t)unit * D * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = Min[(r0 + acc_row(r, h)) * D + c0 + i];
+
+  const bf16* Amat = static_cast<const bf16*>(a.Amat);
+  auto issue_a = [&](int it) {
+    const bf16* As = Amat + ((int64_t)unit * a.s_count + it) * D * D;
+    tile.template issue<true>(As, A0, 0, 64, w);
+    tile.template issue<true>(As + 64 * D, A1, 0, 64, w);
+  };
+  float bv[16];
+  auto load_b = [&](int it) {
+    const float* Bs = a.Bmat + ((int64_t)unit * a.s_count + it) * D * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bv[r] = Bs[(r0 + acc_row(r, h)) * D + c0 + i];
+  };
+  load_b(0);
+  issue_a(0);
+
+  bf16* snap = static_cast<bf16*>(a.snapM);
+  for (int it = 0; it < a.s_count; ++it) {
+    // M_{s-1}^T of this wave's block into LDS (every wave is past the reads
+    // of the previous step: barrier at the loop's end)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      bf16x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = (bf16)acc[4 * rq + j];
+      store4<bf16>(Mt + (c0 + i) * MTS + r0 + 8 * rq + 4 * h, y);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of A_s, and B_s, have landed
+    __syncthreads();
+    // the snapshot: 16-byte pieces of M^T rows, 32 bytes per thread
+    {
+      bf16* sM = snap + ((int64_t)unit * a.s_count + it) * D * D;
+      const int row = tid >> 3, col = 16 * (tid & 7);
+      store8<bf16>(sM + row * D + col, load8<bf16>(Mt + row * MTS + col));
+      store8<bf16>(sM + row * D + col + 8, load8<bf16>(Mt + row * MTS + col + 8));
+    }
+    // M_s = M_{s-1} + A_s M_{s-1} + B_s for this block
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      mma32(acc, load8<bf16>(lds_at(Ab, ao ^ (32u * c))),
+            load8<bf16>(Mt + (c0 + i) * MTS + 16 * c + 8 * h));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += bv[r];
+    lds_barrier();  // every wave is done with A_s and Mt
+    if (it + 1 < a.s_count) {
+      issue_a(it + 1);
+      load_b(it + 1);
+    }
+  }
+
+  float* Mout = a.M_out + (int64_t)unit * D * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Mout[(r0 + acc_row(r, h)) * D + c0 + i] = acc[r];
+}
+
 template <typename T, int D, int RULE>
 hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
   const unsigned segs = (unsigned)(a.units * a.s_count);
@@ -493,6 +586,18 @@ hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((affine_kernel<T, D, RULE>), dim3(segs),
                        dim3(AffineShape<D, RULE>::NW * 64), 0, stream, a);
+  if constexpr (sizeof(T) == 2 && D == 128 && RULE == kRuleDelta) {
+    // one workgroup per unit once the units alone fill the CUs; with fewer
+    // units the slab kernel's four workgroups per unit keep more CUs busy
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    if (!a.reverse && a.units >= cus) {
+      hipLaunchKernelGGL(chain_unit_kernel, dim3((unsigned)a.units), dim3(1024), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((chain_kernel<T, D, RULE>), dim3((unsigned)(a.units * (D / 32))),
                      dim3(D / 32 * 64), 0, stream, a);
   return hipGetLastError();

@@ -51,6 +51,16 @@ __device__ __forceinline__ f32x16 zero16() {
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
 
+// A workgroup barrier for LDS only: this wave's LDS accesses have completed
+// (lgkmcnt(0)), then s_barrier. Unlike __syncthreads() it does not wait for
+// the wave's global loads and stores in flight (vmcnt), so stores that no
+// other wave of the workgroup reads, and loads issued ahead for later use,
+// stay in flight across it. The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Row of the 32x32 accumulator tile that register r of a lane in half h holds.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return (r >> 2) * 8 + 4 * h + (r & 3); }
 

@@ -208,3 +208,22 @@ def test_streams_and_null_stream(lib):
     s.synchronize()
     for x, y in zip(ref, res):
         assert torch.equal(x, y)
+
+
+def test_many_units_chain_per_unit(lib):
+    """With at least as many (batch, KV head) units as CUs, the affine form's
+    chain runs one workgroup per unit (bf16, d = 128, delta): parity on
+    sampled units, and a one-segment-per-window workspace gives the bits of
+    the full one."""
+    B, Hq, Hkv, L, d, N = 4, 64, 64, 520, 128, 128  # 256 units, 5 segments, ragged
+    _say(f"many units B{B} Hkv{Hkv} L{L} d{d} N{N} delta bf16")
+    inp = random_inputs(B, Hq, Hkv, L, d, torch.bfloat16, DEV, seed=21, m0_scale=0.3)
+    args = [inp[n] for n in ("q", "k", "v", "beta", "M0", "z0")]
+    res = run(lib, inp, N, "delta")
+    units = [(0, 0), (0, 63), (1, 17), (2, 40), (3, 5), (3, 63)]
+    check(inp, res, N, "delta", units, tolerance(torch.bfloat16))
+    _, least = lib.workspace_size(B, Hq, Hkv, L, d, N, "delta", torch.bfloat16)
+    ws = torch.empty(least, dtype=torch.uint8, device=DEV)
+    o2, M2, z2 = lib.forward(*args, N, "delta", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(res[0], o2) and torch.equal(res[1], M2) and torch.equal(res[2], z2)
