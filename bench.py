@@ -457,7 +457,7 @@ def main():
     # (peak FLOP/s / peak bytes/s), HBM below it
     a_bytes = attn_kernel_bytes(w)
     kname = ("attn_kernel (local causal attention + retrieval + gate)" if w.d_value == w.d else
-             "attn_kernel, register-staged, d_key != d_value (attention + retrieval + gate)")
+             f"attn_kernel, d_key {w.d} != d_value {w.d_value} (attention + retrieval + gate)")
     if a_flops / a_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         roofline = {"kernel": kname,
                     "bound": "mfma", "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s",

@@ -336,9 +336,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
 // once: with the swizzles above, a lane's K and V read addresses differ
 // between key blocks, probability chunks and the two LDS buffers only by
 // constants, which the reads take as immediate offsets.
-template <int D>
+template <int DK, int DV>
 struct DmaLane {
-  static constexpr int NC = D / 16, NDB = D / 32;
+  static constexpr int NC = DK / 16, NDB = DV / 32;
   bf16x8 qf[NC];
   f32x16 oacc[NDB];
   float m_run, l0, l1;  // running max (log2 units before scaling) and two partial sums
@@ -347,9 +347,9 @@ struct DmaLane {
 
   __device__ __forceinline__ void init_offsets(int lane) {
     const int i = lane & 31, h = lane >> 5;
-    ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+    ko = 2 * (i * DK + 8 * (h ^ swz_k<DK>(i)));
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vo[db] = tr_offset<D>(lane, db);
+    for (int db = 0; db < NDB; ++db) vo[db] = tr_offset<DV>(lane, db);
   }
 };
 
@@ -361,24 +361,25 @@ struct DmaLane {
 // arguments.
 
 // S^T = K Q^T for one key tile (K in LDS).
-template <int D, int BN>
-__device__ __forceinline__ void dma_scores(const bf16* Kb, const DmaLane<D>& st, f32x16* sacc) {
-  constexpr int NC = D / 16, NKB = BN / 32;
+template <int DK, int DV, int BN>
+__device__ __forceinline__ void dma_scores(const bf16* Kb, const DmaLane<DK, DV>& st,
+                                           f32x16* sacc) {
+  constexpr int NC = DK / 16, NKB = BN / 32;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     sacc[kb] = zero16();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      mma32(sacc[kb], load8<bf16>(lds_at(Kb, (st.ko ^ (32u * cc)) + 2 * 32 * kb * D)), st.qf[cc]);
+      mma32(sacc[kb], load8<bf16>(lds_at(Kb, (st.ko ^ (32u * cc)) + 2 * 32 * kb * DK)), st.qf[cc]);
   }
 }
 
 // Causal mask (on a tile that crosses the wave's diagonal), then the running
 // maximum with the lazy rescale of O and l.
-template <int D, int BN>
-__device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<D>& st, float c, int k0, int row,
-                                        int h, bool diag) {
-  constexpr int NDB = D / 32, NKB = BN / 32;
+template <int DK, int DV, int BN>
+__device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<DK, DV>& st, float c, int k0,
+                                        int row, int h, bool diag) {
+  constexpr int NDB = DV / 32, NKB = BN / 32;
   if (diag) {  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -408,8 +409,8 @@ __device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<D>& st, float c, i
 // Probabilities exp2(c s - c m) of one tile as the bf16 B operand of
 // O^T += V^T P^T, and the row sums of the probabilities as rounded for that
 // product (pairwise, with v_dot2_f32_bf16 against (1, 1)).
-template <int D, int BN>
-__device__ __forceinline__ void dma_probs(const f32x16* sacc, DmaLane<D>& st, float c,
+template <int DK, int DV, int BN>
+__device__ __forceinline__ void dma_probs(const f32x16* sacc, DmaLane<DK, DV>& st, float c,
                                           bf16x8* pf) {
   constexpr int NKB = BN / 32, NPC = BN / 16;
   const float mc = st.m_run * c;
@@ -433,13 +434,14 @@ __device__ __forceinline__ void dma_probs(const f32x16* sacc, DmaLane<D>& st, fl
 }
 
 // O^T += V^T P^T for one key tile (V in LDS, read transposed).
-template <int D, int BN>
-__device__ __forceinline__ void dma_values(const bf16* Vb, DmaLane<D>& st, const bf16x8* pf) {
-  constexpr int NDB = D / 32, NPC = BN / 16;
+template <int DK, int DV, int BN>
+__device__ __forceinline__ void dma_values(const bf16* Vb, DmaLane<DK, DV>& st,
+                                           const bf16x8* pf) {
+  constexpr int NDB = DV / 32, NPC = BN / 16;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int pc = 0; pc < NPC; ++pc) mma32(st.oacc[db], tr_frag<D>(Vb, st.vo[db], pc), pf[pc]);
+    for (int pc = 0; pc < NPC; ++pc) mma32(st.oacc[db], tr_frag<DV>(Vb, st.vo[db], pc), pf[pc]);
 }
 
 // The retrieval's operands, loaded during the workgroup's last key tile into
@@ -448,15 +450,17 @@ __device__ __forceinline__ void dma_values(const bf16* Vb, DmaLane<D>& st, const
 // layout, so the epilogue reads its A operand as it reads K; z (d floats)
 // into Zs by one 16-byte load per lane of wave 0 (lanes past d/4 read
 // outside the resource, which returns zeros).
-template <int D, int NW, int BN>
-__device__ __forceinline__ void dma_snapshot(const DmaTile<D, NW, BN>& tile, const bf16* Mts,
+template <int DK, int DV, int NW, int BN>
+__device__ __forceinline__ void dma_snapshot(const DmaTile<DK, NW, BN>& tile, const bf16* Mts,
                                              const float* zs, bf16* Ma, bf16* Mb, float* Zs,
                                              int w) {
-  static_assert(BN == 64 && D % 64 == 0, "M^T is loaded as d / 64 key tiles");
+  // M^T is d_value rows of d_key: d_value / 64 tiles in the K layout; the
+  // second goes to a V buffer, at least as large when d_value = 128
+  static_assert(BN == 64 && DV % 64 == 0, "M^T is loaded as d_value / 64 key tiles");
   tile.template issue<true>(Mts, Ma, 0, 64, w);
-  if constexpr (D == 128) tile.template issue<true>(Mts + 64 * D, Mb, 0, 64, w);
+  if constexpr (DV == 128) tile.template issue<true>(Mts + 64 * DK, Mb, 0, 64, w);
   if (w == 0) {
-    const __amdgpu_buffer_rsrc_t rz = raw_rsrc(reinterpret_cast<const bf16*>(zs), D * 4);
+    const __amdgpu_buffer_rsrc_t rz = raw_rsrc(reinterpret_cast<const bf16*>(zs), DK * 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)Zs, 16, (threadIdx.x & 63) * 16, 0, 0, 0);
   }
 }
@@ -472,34 +476,37 @@ __device__ __forceinline__ void dma_snapshot(const DmaTile<D, NW, BN>& tile, con
 // rescale. The loads and the wait are then unconditional, which lets the
 // compiler see that the reads of this iteration touch only the other two
 // buffers (separate arrays) and need not wait for the loads just issued.
-template <int D, int NW, int BN, int P, bool FULL>
-__device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile<D, NW, BN>& tile,
-                                         const bf16* K, const bf16* V, bf16* const* Ks,
-                                         bf16* const* Vs, int n_s, int w, int q0,
-                                         DmaLane<D>& st, f32x16* sacc, float c, int row, int h,
-                                         const bf16* Mts, const float* zs, float* Zs) {
+template <int DK, int DV, int NW, int BN, int P, bool FULL>
+__device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
+                                         const DmaTile<DK, NW, BN>& tile,
+                                         const DmaTile<DV, NW, BN>& vtile, const bf16* K,
+                                         const bf16* V, bf16* const* Ks, bf16* const* Vs, int n_s,
+                                         int w, int q0, DmaLane<DK, DV>& st, f32x16* sacc,
+                                         float c, int row, int h, const bf16* Mts,
+                                         const float* zs, float* Zs) {
   constexpr int NKB = BN / 32, NPC = BN / 16;
   if (FULL || j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
-  if (FULL || j + 1 < n_kt) tile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
-  if (!FULL && j + 1 == n_kt) dma_snapshot<D, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
+  if (FULL || j + 1 < n_kt) vtile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+  if (!FULL && j + 1 == n_kt)
+    dma_snapshot<DK, DV, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
   if (FULL || j + 1 < n_w) {
     bf16x8 pf[NPC];
-    dma_probs<D, BN>(sacc, st, c, pf);
+    dma_probs<DK, DV, BN>(sacc, st, c, pf);
     f32x16 snext[NKB];
-    dma_scores<D, BN>(Ks[P ^ 1], st, snext);
-    dma_values<D, BN>(Vs[P], st, pf);
+    dma_scores<DK, DV, BN>(Ks[P ^ 1], st, snext);
+    dma_values<DK, DV, BN>(Vs[P], st, pf);
     // the scheduler's strategy that interleaves LDS reads with the matrix
     // products: 1.3% faster on the full iterations (alternating A/B timing;
     // the strategies for other instruction mixes were slower)
     if constexpr (FULL) __builtin_amdgcn_iglp_opt(0);
     const int k1 = (j + 1) * BN;
-    dma_max<D, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + w);
+    dma_max<DK, DV, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + w);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = snext[kb];
   } else if (!FULL && j < n_w) {  // this wave's last tile
     bf16x8 pf[NPC];
-    dma_probs<D, BN>(sacc, st, c, pf);
-    dma_values<D, BN>(Vs[P], st, pf);
+    dma_probs<DK, DV, BN>(sacc, st, c, pf);
+    dma_values<DK, DV, BN>(Vs[P], st, pf);
   }
   if (FULL || j + 1 < n_kt) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(j + 2), V(j + 1) have landed
@@ -507,16 +514,17 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w, const DmaTile
   }
 }
 
-template <int D, int NW, int BN>
+// DK: the key width (Q, K); DV: the value width (V, the output).
+template <int DK, int DV, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   constexpr int BM = 32 * NW;
-  constexpr int NC = D / 16, NDB = D / 32;
+  constexpr int NC = DK / 16, NDB = DV / 32;
   // four separate arrays, so that the compiler can tell a tile being loaded
   // by DMA from the tiles being read and does not wait for the load
-  __shared__ __align__(1024) bf16 Ks0[BN * D];
-  __shared__ __align__(1024) bf16 Ks1[BN * D];
-  __shared__ __align__(1024) bf16 Vs0[BN * D];
-  __shared__ __align__(1024) bf16 Vs1[BN * D];
+  __shared__ __align__(1024) bf16 Ks0[BN * DK];
+  __shared__ __align__(1024) bf16 Ks1[BN * DK];
+  __shared__ __align__(1024) bf16 Vs0[BN * DV];
+  __shared__ __align__(1024) bf16 Vs1[BN * DV];
   bf16* const Ks[2] = {Ks0, Ks1};
   bf16* const Vs[2] = {Vs0, Vs1};
   __shared__ __align__(16) float Zs[256];  // z of the segment (one 16-byte DMA per lane of wave 0)
@@ -546,10 +554,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
 
   const int64_t qh = (int64_t)b * a.Hq + hq;
   const float g = 1.f / (1.f + __expf(-a.beta[hq]));  // the gate, read early
-  const bf16* Q = static_cast<const bf16*>(a.q) + (qh * a.L + seg_start) * D;
-  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
-  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D;
-  bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * D;
+  const bf16* Q = static_cast<const bf16*>(a.q) + (qh * a.L + seg_start) * DK;
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * DK;
+  const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * DV;
+  bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * DV;
 
   // Rows are dealt to the waves round robin (row q0 + w + NW i for lane i),
   // so every wave spans the whole block and meets the causal diagonal in the
@@ -563,18 +571,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   const int n_kv = min(q0 + BM, n_s);
   const int n_kt = (n_kv + BN - 1) / BN;
 
-  DmaTile<D, NW, BN> tile;
+  DmaTile<DK, NW, BN> tile;  // K tiles (and M^T), rows of d_key
   tile.init(w, lane);
+  DmaTile<DV, NW, BN> vtile;  // V tiles, rows of d_value
+  vtile.init(w, lane);
   tile.template issue<true>(K, Ks[0], 0, n_s, w);
-  tile.template issue<false>(V, Vs[0], 0, n_s, w);
+  vtile.template issue<false>(V, Vs[0], 0, n_s, w);
   if (n_kt > 1) tile.template issue<true>(K, Ks[1], BN, n_s, w);
 
-  DmaLane<D> st;
+  DmaLane<DK, DV> st;
   st.init_offsets(lane);
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     st.qf[cc] = zero_frag<bf16>();
-    if (row < n_s) st.qf[cc] = load8<bf16>(Q + (int64_t)row * D + 16 * cc + 8 * h);
+    if (row < n_s) st.qf[cc] = load8<bf16>(Q + (int64_t)row * DK + 16 * cc + 8 * h);
   }
 #pragma unroll
   for (int db = 0; db < NDB; ++db) st.oacc[db] = zero16();
@@ -588,8 +598,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (n_w > 0) {
-    dma_scores<D, BN>(Ks[0], st, sacc);
-    dma_max<D, BN>(sacc, st, c, 0, row, h, BN - 1 > wave_first);
+    dma_scores<DK, DV, BN>(Ks[0], st, sacc);
+    dma_max<DK, DV, BN>(sacc, st, c, 0, row, h, BN - 1 > wave_first);
   }
   __syncthreads();  // K(0) read by every wave before iteration 0 loads K(2) over it
   // When every row of the block is in the segment, iterations j whose next
@@ -597,20 +607,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   // wave.
   const int n_full = q0 + BM <= n_s ? q0 / BN - 1 : 0;
   const int64_t snap = (int64_t)unit * a.s_count + sl;
-  const float* zs = a.snapZ + snap * D;
-  const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * D * D;
+  const float* zs = a.snapZ + snap * DK;
+  const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * DV * DK;
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
-    dma_iter<D, NW, BN, 0, true>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row, h,
+    dma_iter<DK, DV, NW, BN, 0, true>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row, h,
                                  Mts, zs, Zs);
-    dma_iter<D, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
                                  h, Mts, zs, Zs);
   }
   for (; j < n_kt; j += 2) {  // j is even here
-    dma_iter<D, NW, BN, 0, false>(j, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 0, false>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
                                   h, Mts, zs, Zs);
     if (j + 1 < n_kt)
-      dma_iter<D, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c,
+      dma_iter<DK, DV, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c,
                                     row, h, Mts, zs, Zs);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's part of M^T and z has landed
@@ -651,10 +661,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
       mma32(st.oacc[db],
-            load8<bf16>(lds_at(db >= 2 ? Mb : Ma, (st.ko ^ (32u * cc)) + 2 * 32 * (db & 1) * D)),
+            load8<bf16>(lds_at(db >= 2 ? Mb : Ma, (st.ko ^ (32u * cc)) + 2 * 32 * (db & 1) * DK)),
             sf[cc]);
   if (row < n_s) {
-    bf16* orow = O + (int64_t)row * D;
+    bf16* orow = O + (int64_t)row * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -673,7 +683,7 @@ hipError_t launch_attn_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
   const int64_t G = a.Hq / a.Hkv;
   const int64_t total = units * a.s_count * a.n_qt * G;
   if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
-    hipLaunchKernelGGL((attn_kernel_dma<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attn_kernel_dma<D, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
                        stream, a);
   } else {
     hipLaunchKernelGGL((attn_kernel<T, D, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
@@ -712,15 +722,19 @@ hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipSt
 
 namespace {
 
-// d_key != d_value: the register-staged kernel with four waves (rows past a
-// short segment's end are masked), every ordered pair of distinct widths in
-// {32, 64, 128}.
+// d_key != d_value, four waves (rows past a short segment's end are masked),
+// every ordered pair of distinct widths in {32, 64, 128}: bf16 with both
+// widths in {64, 128} on the DMA kernel, the rest on the register-staged one.
 template <typename T, int DK, int DV>
 hipError_t launch_attn_kv_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
   constexpr int NW = 4, BN = 64;
   const int64_t total = units * a.s_count * a.n_qt * (a.Hq / a.Hkv);
-  hipLaunchKernelGGL((attn_kernel<T, DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
-                     stream, a);
+  if constexpr (sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128))
+    hipLaunchKernelGGL((attn_kernel_dma<DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64),
+                       0, stream, a);
   return hipGetLastError();
 }
 
