@@ -122,8 +122,8 @@ infini_status_t infini_attn_forward(
  *   M0, M_final [B][Hkv][d_key][d_value] float; z0, z_final [B][Hkv][d_key]
  * The softmax scale is 1/sqrt(d_key). d_key and d_value are each 32, 64 or
  * 128 (else INFINI_ERR_UNSUPPORTED). With d_key != d_value the memory runs as
- * the segment-by-segment scan (not the affine form) and the attention as the
- * register-staged kernel; numerics as infini_attn_forward. Workspace sizes
+ * the segment-by-segment scan (not the affine form); numerics as
+ * infini_attn_forward. Workspace sizes
  * from infini_attn_workspace_size_kv, with the same full and minimum
  * meanings; arguments, overlaps and errors as infini_attn_forward.
  */
