@@ -48,6 +48,10 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 5 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_decode_step": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_decode_workspace_size_kv": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_decode_step_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
     "infini_attn_block_workspace_size": (
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_block_forward": (
@@ -234,16 +238,19 @@ def decode_step(q, k, v, beta, k_cache, v_cache, M, z, pos, rule, *, out=None, w
     same dtype; M [B,Hkv,d,d] and z [B,Hkv,d] float32, the state before the
     segment. Writes the token into the caches and, when pos == seg_len - 1,
     folds the segment into M and z in place. Returns out [B,Hq,d].
+    v, v_cache and M's columns may have another width dv than q and k (then
+    out is [B,Hq,dv]: infini_attn_decode_step_kv).
     Asynchronous on ``stream`` (or torch's current stream).
     """
     B, Hq, d = q.shape
     Hkv = k.shape[1]
     seg_len = k_cache.shape[2]
-    if k.shape != (B, Hkv, d) or v.shape != (B, Hkv, d):
-        raise ValueError("k and v must be [B,Hkv,d]")
-    if k_cache.shape != (B, Hkv, seg_len, d) or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [B,Hkv,seg_len,d]")
-    if beta.shape != (Hq,) or M.shape != (B, Hkv, d, d) or z.shape != (B, Hkv, d):
+    dv = v.shape[-1] if v.dim() == 3 else -1
+    if k.shape != (B, Hkv, d) or v.shape != (B, Hkv, dv):
+        raise ValueError("k must be [B,Hkv,d] and v [B,Hkv,dv]")
+    if k_cache.shape != (B, Hkv, seg_len, d) or v_cache.shape != (B, Hkv, seg_len, dv):
+        raise ValueError("k_cache must be [B,Hkv,seg_len,d] and v_cache [B,Hkv,seg_len,dv]")
+    if beta.shape != (Hq,) or M.shape != (B, Hkv, d, dv) or z.shape != (B, Hkv, d):
         raise ValueError("beta, M or z has the wrong shape")
     if q.dtype not in DTYPES or any(t.dtype != q.dtype for t in (k, v, k_cache, v_cache)):
         raise TypeError("q, k, v and the caches must share one dtype, float32 or bfloat16")
@@ -260,21 +267,32 @@ def decode_step(q, k, v, beta, k_cache, v_cache, M, z, pos, rule, *, out=None, w
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+        out = torch.empty((B, Hq, dv), dtype=q.dtype, device=dev)
+    if out.shape != (B, Hq, dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,dv] tensor of q's dtype")
+    lib = load_library()
     if workspace is None:
-        workspace = torch.empty(decode_workspace_size(B, Hq, Hkv, d, seg_len, rule, q.dtype),
-                                dtype=torch.uint8, device=dev)
+        n = _c_size(0)
+        st = lib.infini_attn_decode_workspace_size_kv(B, Hq, Hkv, d, dv, seg_len, RULES[rule],
+                                                      DTYPES[q.dtype], ctypes.byref(n))
+        if st != 0:
+            raise InfiniAttnError(st, "infini_attn_decode_workspace_size_kv")
+        workspace = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = load_library().infini_attn_decode_step(
-        B, Hq, Hkv, d, seg_len, int(pos), RULES[rule], DTYPES[q.dtype],
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_cache), _ptr(v_cache), _ptr(M), _ptr(z),
-        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        ctypes.c_void_p(stream.cuda_stream))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_cache), _ptr(v_cache), _ptr(M),
+            _ptr(z), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream.cuda_stream)]
+    if dv != d:
+        st = lib.infini_attn_decode_step_kv(B, Hq, Hkv, d, dv, seg_len, int(pos), RULES[rule],
+                                            DTYPES[q.dtype], *args)
+        name = "infini_attn_decode_step_kv"
+    else:
+        st = lib.infini_attn_decode_step(B, Hq, Hkv, d, seg_len, int(pos), RULES[rule],
+                                         DTYPES[q.dtype], *args)
+        name = "infini_attn_decode_step"
     if st != 0:
-        raise InfiniAttnError(st, "infini_attn_decode_step")
+        raise InfiniAttnError(st, name)
     return out
 
 

@@ -457,14 +457,17 @@ struct DecodePlan {
   size_t part_bytes;   // chunk partials, aligned
 };
 
+// d: the key width; dv: the value width (d when 0).
 infini_status_t check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t seg_len,
-                             int32_t rule, int32_t dtype, DecodePlan* dp) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || seg_len < 1) return INFINI_ERR_INVALID_ARG;
+                             int32_t rule, int32_t dtype, DecodePlan* dp, int64_t dv = 0) {
+  if (dv == 0) dv = d;
+  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || dv < 1 || seg_len < 1) return INFINI_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return INFINI_ERR_INVALID_ARG;
   if (Hq / Hkv > infini::kDecodeMaxGroup) return INFINI_ERR_UNSUPPORTED;
   if (seg_len > 64 * (int64_t)infini::kDecodeMaxChunks) return INFINI_ERR_UNSUPPORTED;
   Plan fold;
-  const infini_status_t st = check_sizes(B, Hq, Hkv, seg_len, d, seg_len, rule, dtype, &fold);
+  const infini_status_t st =
+      check_sizes_kv(B, Hq, Hkv, seg_len, d, dv, seg_len, rule, dtype, &fold);
   if (st != INFINI_OK) return st;
   if (fold.units * ((seg_len + 63) / 64) > INT32_MAX) return INFINI_ERR_INVALID_ARG;
   if (dp) {
@@ -472,7 +475,7 @@ infini_status_t check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int6
     dp->G = Hq / Hkv;
     dp->n_chunks_max = (seg_len + 63) / 64;
     dp->part_bytes = align_up((size_t)fold.units * (size_t)dp->n_chunks_max * (size_t)dp->G *
-                              (size_t)(d + 2) * 4);
+                              (size_t)(dv + 2) * 4);
   }
   return INFINI_OK;
 }
@@ -491,14 +494,18 @@ infini_status_t infini_attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t
   return INFINI_OK;
 }
 
-infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
-                                        int64_t seg_len, int64_t pos, int32_t rule,
-                                        int32_t dtype, const void* q, const void* k,
-                                        const void* v, const float* beta, void* k_cache,
-                                        void* v_cache, float* M, float* z, void* out,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// d: the key width; dv: the value width.
+infini_status_t decode_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64_t dv,
+                            int64_t seg_len, int64_t pos, int32_t rule, int32_t dtype,
+                            const void* q, const void* k, const void* v, const float* beta,
+                            void* k_cache, void* v_cache, float* M, float* z, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   DecodePlan dp;
-  const infini_status_t st = check_decode(B, Hq, Hkv, d, seg_len, rule, dtype, &dp);
+  const infini_status_t st = check_decode(B, Hq, Hkv, d, seg_len, rule, dtype, &dp, dv);
   if (st != INFINI_OK) return st;
   if (pos < 0 || pos >= seg_len) return INFINI_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, beta, k_cache, v_cache, M, z, out, workspace};
@@ -510,13 +517,15 @@ infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int6
   }
   const Plan& p = dp.fold;
   const size_t e = (size_t)p.e;
-  const size_t nq = (size_t)(B * Hq * d) * e, nkv = (size_t)(B * Hkv * d) * e;
-  const size_t ncache = (size_t)(B * Hkv) * (size_t)seg_len * (size_t)d * e;
-  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  const size_t nq = (size_t)(B * Hq * d) * e, nk = (size_t)(B * Hkv * d) * e;
+  const size_t nv = (size_t)(B * Hkv * dv) * e, nout = (size_t)(B * Hq * dv) * e;
+  const size_t nkc = (size_t)(B * Hkv) * (size_t)seg_len * (size_t)d * e;
+  const size_t nvc = (size_t)(B * Hkv) * (size_t)seg_len * (size_t)dv * e;
+  const size_t nM = (size_t)(B * Hkv * d * dv) * 4, nz = (size_t)(B * Hkv * d) * 4;
   struct Range { const void* p; size_t n; };
-  const Range all[] = {{q, nq},           {k, nkv},           {v, nkv},
-                       {beta, (size_t)Hq * 4}, {k_cache, ncache}, {v_cache, ncache},
-                       {M, nM},           {z, nz},            {out, nq},
+  const Range all[] = {{q, nq},           {k, nk},            {v, nv},
+                       {beta, (size_t)Hq * 4}, {k_cache, nkc}, {v_cache, nvc},
+                       {M, nM},           {z, nz},            {out, nout},
                        {workspace, workspace_bytes}};
   // the caches, the state, the output and the workspace are written: none of
   // them may overlap any other argument
@@ -547,7 +556,7 @@ infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int6
   da.pos = (int32_t)pos;
   da.n_chunks = (int32_t)((pos + 1 + 63) / 64);
   da.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
-  if (infini::launch_decode(dtype, (int)d, da, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (infini::launch_decode_kv(dtype, (int)d, (int)dv, da, s) != hipSuccess) return INFINI_ERR_HIP;
 
   if (pos == seg_len - 1) {
     // the segment is complete: fold the cache into (M, z), in place
@@ -563,6 +572,44 @@ infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int6
       return INFINI_ERR_HIP;
   }
   return INFINI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_decode_step(int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                                        int64_t seg_len, int64_t pos, int32_t rule,
+                                        int32_t dtype, const void* q, const void* k,
+                                        const void* v, const float* beta, void* k_cache,
+                                        void* v_cache, float* M, float* z, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(B, Hq, Hkv, d, d, seg_len, pos, rule, dtype, q, k, v, beta, k_cache,
+                     v_cache, M, z, out, workspace, workspace_bytes, stream);
+}
+
+infini_status_t infini_attn_decode_workspace_size_kv(int64_t B, int64_t Hq, int64_t Hkv,
+                                                     int64_t d_key, int64_t d_value,
+                                                     int64_t seg_len, int32_t rule, int32_t dtype,
+                                                     size_t* bytes) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  DecodePlan dp;
+  const infini_status_t st = check_decode(B, Hq, Hkv, d_key, seg_len, rule, dtype, &dp, d_value);
+  if (st != INFINI_OK) return st;
+  if (bytes) *bytes = dp.part_bytes + dp.fold.fixed + dp.fold.per_seg;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_decode_step_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t d_key,
+                                           int64_t d_value, int64_t seg_len, int64_t pos,
+                                           int32_t rule, int32_t dtype, const void* q,
+                                           const void* k, const void* v, const float* beta,
+                                           void* k_cache, void* v_cache, float* M, float* z,
+                                           void* out, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return decode_impl(B, Hq, Hkv, d_key, d_value, seg_len, pos, rule, dtype, q, k, v, beta,
+                     k_cache, v_cache, M, z, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

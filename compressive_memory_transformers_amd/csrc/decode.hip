@@ -30,10 +30,10 @@ namespace {
 constexpr int kDecodeKC = 64;   // cache rows per partial workgroup (one wave)
 constexpr int kDecodeNT = 256;  // threads per combine workgroup
 
-template <typename T, int D>
+template <typename T, int W>
 __device__ __forceinline__ const T* cache_row(const DecodeArgs& a, const T* cache, const T* fresh,
                                               int t) {
-  return t == a.pos ? fresh : cache + (int64_t)t * D;
+  return t == a.pos ? fresh : cache + (int64_t)t * W;
 }
 
 // One 256-thread workgroup per (batch, KV head, chunk of 64 cache rows).
@@ -42,14 +42,16 @@ __device__ __forceinline__ const T* cache_row(const DecodeArgs& a, const T* cach
 // four quarters' partial scores are summed by DPP; one wave per head takes the
 // chunk maximum and weight sum; the value sums run over (head, 8-column group,
 // quarter of the rows) triples and are added in LDS.
-template <typename T, int D>
+// DK: the key width (q, k, rows of M); DV: the value width (v, the output).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int KC = kDecodeKC, GM = kDecodeMaxGroup, C8 = D / 8;
-  constexpr int QW = D / 4, QC = QW / 8;  // columns, 8-column chunks of a row quarter
-  __shared__ float qs[GM * D];  // the group's queries, scaled by log2(e) / sqrt(d)
-  __shared__ float ps[GM * KC]; // scores, then exp2 weights
-  __shared__ __align__(16) T vs[KC * D];
-  __shared__ float ov[4 * GM * D];  // value sums of the four row quarters
+  constexpr int KC = kDecodeKC, GM = kDecodeMaxGroup, C8 = DV / 8;
+  // columns and 8-column chunks of a row quarter, of K and of V
+  constexpr int QWK = DK / 4, QCK = QWK / 8, QWV = DV / 4, QCV = QWV / 8;
+  __shared__ float qs[GM * DK];  // the group's queries, scaled by log2(e) / sqrt(d_key)
+  __shared__ float ps[GM * KC];  // scores, then exp2 weights
+  __shared__ __align__(16) T vs[KC * DV];
+  __shared__ float ov[4 * GM * DV];  // value sums of the four row quarters
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -58,25 +60,25 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   const int b = unit / a.Hkv, j = unit % a.Hkv;
   const int t0 = ch * KC;
   const int n = min(KC, a.pos + 1 - t0);  // rows of this chunk, >= 1
-  const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + (int64_t)j * G) * D;
-  const T* knew = static_cast<const T*>(a.k) + (int64_t)unit * D;
-  const T* vnew = static_cast<const T*>(a.v) + (int64_t)unit * D;
-  const T* kc = static_cast<const T*>(a.k_cache) + (int64_t)unit * a.seg_len * D;
-  const T* vc = static_cast<const T*>(a.v_cache) + (int64_t)unit * a.seg_len * D;
+  const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + (int64_t)j * G) * DK;
+  const T* knew = static_cast<const T*>(a.k) + (int64_t)unit * DK;
+  const T* vnew = static_cast<const T*>(a.v) + (int64_t)unit * DV;
+  const T* kc = static_cast<const T*>(a.k_cache) + (int64_t)unit * a.seg_len * DK;
+  const T* vc = static_cast<const T*>(a.v_cache) + (int64_t)unit * a.seg_len * DV;
 
   // this thread's quarter row (a row past the chunk repeats row t0: finite, weight 0)
   const int r = tid >> 2, u = tid & 3;
   const int t = t0 + (r < n ? r : 0);
-  const T* krow = cache_row<T, D>(a, kc, knew, t) + QW * u;
-  const T* vrow = cache_row<T, D>(a, vc, vnew, t) + QW * u;
-  frag_t<T> kv[QC], vv[QC];
+  const T* krow = cache_row<T, DK>(a, kc, knew, t) + QWK * u;
+  const T* vrow = cache_row<T, DV>(a, vc, vnew, t) + QWV * u;
+  frag_t<T> kv[QCK], vv[QCV];
 #pragma unroll
-  for (int c = 0; c < QC; ++c) kv[c] = load8<T>(krow + 8 * c);
+  for (int c = 0; c < QCK; ++c) kv[c] = load8<T>(krow + 8 * c);
 #pragma unroll
-  for (int c = 0; c < QC; ++c) vv[c] = load8<T>(vrow + 8 * c);
-  for (int x = tid; x < G * D; x += 256) qs[x] = to_f32<T>(q[x]) * a.scale_log2;
+  for (int c = 0; c < QCV; ++c) vv[c] = load8<T>(vrow + 8 * c);
+  for (int x = tid; x < G * DK; x += 256) qs[x] = to_f32<T>(q[x]) * a.scale_log2;
 #pragma unroll
-  for (int c = 0; c < QC; ++c) store8<T>(vs + r * D + QW * u + 8 * c, vv[c]);
+  for (int c = 0; c < QCV; ++c) store8<T>(vs + r * DV + QWV * u + 8 * c, vv[c]);
   __syncthreads();
 
   // scores: the quarter's partial dot for every head, summed over the quad
@@ -85,16 +87,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     if (g < G) {
       float sp = 0.f;
 #pragma unroll
-      for (int c = 0; c < QC; ++c)
+      for (int c = 0; c < QCK; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sp += to_f32<T>(kv[c][e]) * qs[g * D + QW * u + 8 * c + e];
+        for (int e = 0; e < 8; ++e) sp += to_f32<T>(kv[c][e]) * qs[g * DK + QWK * u + 8 * c + e];
       sp = row_sum<4>(sp);
       if (u == 0) ps[g * KC + r] = r < n ? sp : -INFINITY;
     }
   __syncthreads();
 
   // per head (one wave a head): chunk maximum and weight sum, lane = row
-  float* part = a.part + ((int64_t)unit * a.n_chunks + ch) * G * (D + 2);
+  float* part = a.part + ((int64_t)unit * a.n_chunks + ch) * G * (DV + 2);
   for (int g = w; g < G; g += 4) {
     const float sc = ps[g * KC + lane];
     const float m = wave_max(sc);
@@ -102,8 +104,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     const float l = wave_sum(p);
     ps[g * KC + lane] = p;
     if (lane == 0) {
-      part[g * (D + 2)] = m;
-      part[g * (D + 2) + 1] = l;
+      part[g * (DV + 2)] = m;
+      part[g * (DV + 2) + 1] = l;
     }
   }
   __syncthreads();
@@ -118,41 +120,39 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < KC / 4; ++i) {
       const int tt = kq * (KC / 4) + i;  // rows past n carry weight 0
-      const frag_t<T> vx = load8<T>(vs + tt * D + 8 * c);
+      const frag_t<T> vx = load8<T>(vs + tt * DV + 8 * c);
       const float wgt = ps[g * KC + tt];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += wgt * to_f32<T>(vx[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ov[(kq * G + g) * D + 8 * c + e] = acc[e];
+    for (int e = 0; e < 8; ++e) ov[(kq * G + g) * DV + 8 * c + e] = acc[e];
   }
   __syncthreads();
-  for (int x = tid; x < G * D; x += 256) {
-    const int g = x / D, col = x % D;
-    part[g * (D + 2) + 2 + col] = (ov[(0 * G + g) * D + col] + ov[(1 * G + g) * D + col]) +
-                                  (ov[(2 * G + g) * D + col] + ov[(3 * G + g) * D + col]);
+  for (int x = tid; x < G * DV; x += 256) {
+    const int g = x / DV, col = x % DV;
+    part[g * (DV + 2) + 2 + col] = (ov[(0 * G + g) * DV + col] + ov[(1 * G + g) * DV + col]) +
+                                   (ov[(2 * G + g) * DV + col] + ov[(3 * G + g) * DV + col]);
   }
 
   // append the token to the cache (no workgroup reads row pos from the cache)
   if (t0 <= a.pos && a.pos < t0 + KC) {
-    T* kw = static_cast<T*>(a.k_cache) + ((int64_t)unit * a.seg_len + a.pos) * D;
-    T* vw = static_cast<T*>(a.v_cache) + ((int64_t)unit * a.seg_len + a.pos) * D;
-    for (int x = tid; x < D; x += 256) {
-      kw[x] = knew[x];
-      vw[x] = vnew[x];
-    }
+    T* kw = static_cast<T*>(a.k_cache) + ((int64_t)unit * a.seg_len + a.pos) * DK;
+    T* vw = static_cast<T*>(a.v_cache) + ((int64_t)unit * a.seg_len + a.pos) * DV;
+    for (int x = tid; x < DK; x += 256) kw[x] = knew[x];
+    for (int x = tid; x < DV; x += 256) vw[x] = vnew[x];
   }
 }
 
 // Per (batch, KV head, 32-column slab of the output): merge the chunks,
 // retrieve from the float state, gate. The slab of M, z and the queries are
 // loaded at once into LDS; the small reductions run across the workgroup.
-template <typename T, int D>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a) {
   constexpr int NT = kDecodeNT, GM = kDecodeMaxGroup, NCM = kDecodeMaxChunks;
-  __shared__ float sq[GM * D];    // sigma(q)
-  __shared__ float ms[D * 32];    // M[:, slab]
-  __shared__ float zs[D];
+  __shared__ float sq[GM * DK];   // sigma(q)
+  __shared__ float ms[DK * 32];   // M[:, slab]
+  __shared__ float zs[DK];
   __shared__ float wch[GM * NCM]; // chunk maxima, then weights exp2(m_c - m)
   __shared__ float den[GM], gate[GM], mx[GM], lsum[GM];
   constexpr int OC = 4096;           // staged value sums: chunks x heads x 32 columns
@@ -160,28 +160,28 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
 
   const int tid = threadIdx.x;
   const int G = a.G, NC = a.n_chunks;
-  const int unit = blockIdx.x / (D / 32), slab = blockIdx.x % (D / 32);
+  const int unit = blockIdx.x / (DV / 32), slab = blockIdx.x % (DV / 32);
   const int b = unit / a.Hkv, j = unit % a.Hkv;
   const int hq0 = j * G;
-  const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + hq0) * D;
-  const float* M = a.M + (int64_t)unit * D * D + 32 * slab;
-  const float* z = a.z + (int64_t)unit * D;
-  const float* part = a.part + (int64_t)unit * NC * G * (D + 2);
+  const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + hq0) * DK;
+  const float* M = a.M + (int64_t)unit * DK * DV + 32 * slab;
+  const float* z = a.z + (int64_t)unit * DK;
+  const float* part = a.part + (int64_t)unit * NC * G * (DV + 2);
 
-  for (int x = tid; x < D * 8; x += NT) {  // 8 float4 per row of the slab
+  for (int x = tid; x < DK * 8; x += NT) {  // 8 float4 per row of the slab
     const int k = x / 8, c4 = x % 8;
     *reinterpret_cast<f32x4*>(ms + k * 32 + 4 * c4) =
-        *reinterpret_cast<const f32x4*>(M + (int64_t)k * D + 4 * c4);
+        *reinterpret_cast<const f32x4*>(M + (int64_t)k * DV + 4 * c4);
   }
-  for (int x = tid; x < G * D; x += NT) sq[x] = feature_map(to_f32<T>(q[x]));
-  for (int x = tid; x < D; x += NT) zs[x] = z[x];
-  for (int x = tid; x < G * NC; x += NT) wch[(x / NC) * NCM + x % NC] = part[((x % NC) * G + x / NC) * (D + 2)];
+  for (int x = tid; x < G * DK; x += NT) sq[x] = feature_map(to_f32<T>(q[x]));
+  for (int x = tid; x < DK; x += NT) zs[x] = z[x];
+  for (int x = tid; x < G * NC; x += NT) wch[(x / NC) * NCM + x % NC] = part[((x % NC) * G + x / NC) * (DV + 2)];
   // the slab's value sums of every (chunk, head), when they fit (G * NC <= 128)
   const bool staged = G * NC * 32 <= OC;
   if (staged)
     for (int x = tid; x < G * NC * 8; x += NT) {  // 8 float4 per (chunk, head)
       const int cg = x / 8, c4 = x % 8;
-      const float* src = part + cg * (D + 2) + 2 + 32 * slab + 4 * c4;
+      const float* src = part + cg * (DV + 2) + 2 + 32 * slab + 4 * c4;
       f32x4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = src[e];  // rows of D + 2 floats: 8-byte aligned only
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
     const int g = g0 + tid / 32, l32 = tid & 31;
     if (g < G) {
       float dp = 0.f;
-      for (int k = l32; k < D; k += 32) dp += sq[g * D + k] * zs[k];
+      for (int k = l32; k < DK; k += 32) dp += sq[g * DK + k] * zs[k];
       float m = -INFINITY;
       for (int c = l32; c < NC; c += 32) m = fmaxf(m, wch[g * NCM + c]);
 #pragma unroll
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
     const int g = g0 + tid / 32, l32 = tid & 31;
     if (g < G) {
       float l = 0.f;
-      for (int c = l32; c < NC; c += 32) l += wch[g * NCM + c] * part[(c * G + g) * (D + 2) + 1];
+      for (int c = l32; c < NC; c += 32) l += wch[g * NCM + c] * part[(c * G + g) * (DV + 2) + 1];
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 32);
       if (l32 == 0) lsum[g] = l;
@@ -226,48 +226,60 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + hq0) * D;
+  T* out = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + hq0) * DV;
   for (int x = tid; x < G * 32; x += NT) {
     const int g = x / 32, cs = x % 32, col = 32 * slab + cs;
     float o = 0.f;
     if (staged)
       for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * os[(c * G + g) * 32 + cs];
     else
-      for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * part[(c * G + g) * (D + 2) + 2 + col];
+      for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * part[(c * G + g) * (DV + 2) + 2 + col];
     float r = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < D; ++k) r += sq[g * D + k] * ms[k * 32 + cs];
-    out[g * D + col] = from_f32<T>(gate[g] * (r / den[g]) + (1.f - gate[g]) * (o / lsum[g]));
+    for (int k = 0; k < DK; ++k) r += sq[g * DK + k] * ms[k * 32 + cs];
+    out[g * DV + col] = from_f32<T>(gate[g] * (r / den[g]) + (1.f - gate[g]) * (o / lsum[g]));
   }
 }
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)(a.B * a.Hkv);
-  hipLaunchKernelGGL((decode_partial_kernel<T, D>), dim3(units * (unsigned)a.n_chunks),
+  hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV>), dim3(units * (unsigned)a.n_chunks),
                      dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(units * (unsigned)(D / 32)),
+  hipLaunchKernelGGL((decode_combine_kernel<T, DK, DV>), dim3(units * (unsigned)(DV / 32)),
                      dim3(kDecodeNT), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t launch_decode_v(int dv, const DecodeArgs& a, hipStream_t stream) {
+  switch (dv) {
+    case 32: return launch_decode_t<T, DK, 32>(a, stream);
+    case 64: return launch_decode_t<T, DK, 64>(a, stream);
+    case 128: return launch_decode_t<T, DK, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t launch_decode_kv(int dk, int dv, const DecodeArgs& a, hipStream_t stream) {
+  switch (dk) {
+    case 32: return launch_decode_v<T, 32>(dv, a, stream);
+    case 64: return launch_decode_v<T, 64>(dv, a, stream);
+    case 128: return launch_decode_v<T, 128>(dv, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream) {
-  if (dtype == kBF16) {
-    switch (d) {
-      case 32: return launch_decode_t<bf16, 32>(a, stream);
-      case 64: return launch_decode_t<bf16, 64>(a, stream);
-      case 128: return launch_decode_t<bf16, 128>(a, stream);
-    }
-  } else {
-    switch (d) {
-      case 32: return launch_decode_t<float, 32>(a, stream);
-      case 64: return launch_decode_t<float, 64>(a, stream);
-      case 128: return launch_decode_t<float, 128>(a, stream);
-    }
-  }
-  return hipErrorInvalidValue;
+  return launch_decode_kv(dtype, d, d, a, stream);
+}
+
+hipError_t launch_decode_kv(int dtype, int dk, int dv, const DecodeArgs& a, hipStream_t stream) {
+  return dtype == kBF16 ? launch_decode_kv<bf16>(dk, dv, a, stream)
+                        : launch_decode_kv<float>(dk, dv, a, stream);
 }
 
 }  // namespace infini

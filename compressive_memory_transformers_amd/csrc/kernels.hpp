@@ -217,6 +217,9 @@ hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipSt
 hipError_t launch_attn_kv(int dtype, int dk, int dv, const AttnArgs& a, int64_t units,
                           hipStream_t stream);
 hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stream);
+// The decode step with d_key = dk and d_value = dv (each 32, 64 or 128): q, k
+// and the key cache rows of dk, v, the value cache rows and out of dv, M [dk][dv].
+hipError_t launch_decode_kv(int dtype, int dk, int dv, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
 
 // The projections around the block (proj.hip): C[m][n] = sum_k A[m][k] W[n][k]

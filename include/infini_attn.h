@@ -212,6 +212,28 @@ infini_status_t infini_attn_decode_step(
     void* k_cache, void* v_cache, float* M, float* z, void* out,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The decode step with a key width different from the value width (the
+ * memory M is d_key x d_value, "Infini-Attention" (AI Wiki), "How does the
+ * compressive memory work?"): q [B][Hq][d_key], k [B][Hkv][d_key],
+ * v [B][Hkv][d_value], k_cache [B][Hkv][seg_len][d_key], v_cache
+ * [B][Hkv][seg_len][d_value], M [B][Hkv][d_key][d_value], z [B][Hkv][d_key],
+ * out [B][Hq][d_value]; the scale is 1/sqrt(d_key). The fold of a complete
+ * segment runs the segment-by-segment scan when d_key != d_value. Widths,
+ * sizes, overlaps and errors as infini_attn_decode_step; workspace from
+ * infini_attn_decode_workspace_size_kv. Identical to infini_attn_decode_step
+ * when d_key == d_value.
+ */
+infini_status_t infini_attn_decode_workspace_size_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t d_key, int64_t d_value, int64_t seg_len,
+    int32_t rule, int32_t dtype, size_t* bytes);
+infini_status_t infini_attn_decode_step_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t d_key, int64_t d_value, int64_t seg_len,
+    int64_t pos, int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    void* k_cache, void* v_cache, float* M, float* z, void* out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name of a status code. Never NULL. */
 /*
  * Training forward: infini_attn_forward, plus the softmax statistics the

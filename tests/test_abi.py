@@ -34,7 +34,9 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "infini_attn_backward", "infini_attn_backward_workspace_size",
         "infini_attn_block_forward", "infini_attn_block_forward_timed",
-        "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_error_string", "infini_attn_decode_workspace_size",
+        "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_error_string",
+        "infini_attn_decode_workspace_size", "infini_attn_decode_step_kv",
+        "infini_attn_decode_workspace_size_kv",
         "infini_attn_forward", "infini_attn_forward_kv", "infini_attn_forward_kv_timed",
         "infini_attn_forward_timed",
         "infini_attn_forward_train", "infini_attn_status_string", "infini_attn_version",

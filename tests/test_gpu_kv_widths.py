@@ -97,3 +97,59 @@ def test_kv_split_workload(lib):
     eo, eM, ez = compare_units(inp, res, w.seg_len, "delta", units)
     _say(f"errors out={eo:.3e} M={eM:.3e} z={ez:.3e}")
     assert eo <= 2e-2 and eM <= 2e-2 and ez <= 2e-2, (eo, eM, ez)
+
+
+DECODE_KV = [
+    # B, Hq, Hkv, L, d_key, d_value, seg_len, dtype   (folds by the direct scan)
+    (1, 4, 2, 90, 64, 128, 40, torch.bfloat16),
+    (2, 2, 1, 70, 128, 32, 32, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_KV,
+                         ids=[f"dk{c[4]}dv{c[5]}{str(c[7])[6:]}" for c in DECODE_KV])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_decoded_stream_with_kv_widths_matches_the_forward(lib, case, rule):
+    """infini_attn_decode_step_kv token by token: every output, and the state
+    at every segment end, against the oracle forward on the stream so far."""
+    import ctypes
+
+    import oracle
+    import synth
+    B, Hq, Hkv, L, dk, dv, N, dt = case
+    _say(f"decode stream dk={dk} dv={dv} {dt} {rule} B{B} Hq{Hq} Hkv{Hkv} L{L} N{N}")
+    inp = random_inputs(B, Hq, Hkv, L, dk, dt, DEV, seed=L + dk + dv, m0_scale=0.3, dv=dv)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    kc = torch.zeros(B, Hkv, N, dk, dtype=dt, device=DEV)
+    vc = torch.zeros(B, Hkv, N, dv, dtype=dt, device=DEV)
+    M, z = inp["M0"].clone(), inp["z0"].clone()
+    n = ctypes.c_size_t(0)
+    assert lib.load_library().infini_attn_decode_workspace_size_kv(
+        B, Hq, Hkv, dk, dv, N, lib.RULES[rule], lib.DTYPES[dt], ctypes.byref(n)) == 0
+    ws = torch.empty(int(n.value), dtype=torch.uint8, device=DEV)
+    outs, states = [], {}
+    for t in range(L):
+        pos = t % N
+        o = lib.decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                            v[:, :, t].contiguous(), inp["beta"], kc, vc, M, z, pos, rule,
+                            workspace=ws)
+        assert o.shape == (B, Hq, dv)
+        outs.append(o)
+        if pos == N - 1:
+            states[t + 1] = (M.clone(), z.clone())
+    torch.cuda.synchronize()
+    out = torch.stack(outs, dim=2)
+    f64 = {kk: synth.to_f64(vv) for kk, vv in inp.items()}
+    ref, _, _ = oracle.forward(f64["q"], f64["k"], f64["v"], f64["beta"], f64["M0"], f64["z0"],
+                               N, rule)
+    tol = tolerance(dt)
+    eo = oracle.slice_errors(synth.to_f64(out), ref)
+    _say(f"out error {eo:.3e} (tol {tol:g}); {len(states)} segment ends")
+    assert eo <= tol
+    for nn, (Ms, zs) in states.items():
+        _, M_ref, z_ref = oracle.forward(f64["q"][:, :, :nn], f64["k"][:, :, :nn],
+                                         f64["v"][:, :, :nn], f64["beta"], f64["M0"], f64["z0"],
+                                         N, rule)
+        eM = oracle.slice_errors(synth.to_f64(Ms), M_ref)
+        ez = oracle.slice_errors(synth.to_f64(zs), z_ref, elementwise=True)
+        assert eM <= tol and ez <= tol, (nn, eM, ez)
