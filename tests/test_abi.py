@@ -159,6 +159,47 @@ def test_forward_kv_rejects_before_any_launch(lib):
     assert call(wsb=least - 1) == 4
 
 
+def test_decode_kv_sizes_and_rejections(lib):
+    """The decode step with separate widths: the workspace holds the chunk
+    partials (d_value + 2 floats per head and chunk) and a one-segment fold
+    plan; bad widths and overlaps are refused before any launch."""
+    def dws(*args):
+        n = ctypes.c_size_t(0)
+        return lib.infini_attn_decode_workspace_size_kv(*args, ctypes.byref(n)), n.value
+    st, same = dws(1, 4, 2, 64, 64, 256, 1, 1)
+    n2 = ctypes.c_size_t(0)
+    assert st == 0 and lib.infini_attn_decode_workspace_size(1, 4, 2, 64, 256, 1, 1,
+                                                             ctypes.byref(n2)) == 0
+    assert same == n2.value  # d_key == d_value: the square call's size
+    st, wide = dws(1, 4, 2, 64, 128, 256, 1, 1)
+    assert st == 0 and wide > same
+    assert dws(1, 4, 2, 64, 48, 256, 1, 1)[0] == 2
+    assert dws(1, 4, 2, 64, 0, 256, 1, 1)[0] == 1
+    # q, k: d_key 64; v, caches of v, out: d_value 128 (bf16)
+    B, Hq, Hkv, dk, dv, N = 1, 4, 2, 64, 128, 256
+    sizes = dict(q=B * Hq * dk * 2, k=B * Hkv * dk * 2, v=B * Hkv * dv * 2, beta=Hq * 4,
+                 k_cache=B * Hkv * N * dk * 2, v_cache=B * Hkv * N * dv * 2,
+                 M=B * Hkv * dk * dv * 4, z=B * Hkv * dk * 4, out=B * Hq * dv * 2,
+                 workspace=1 << 30)
+    addr, base = {}, 1 << 44
+    for name, n in sizes.items():
+        addr[name] = base
+        base += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(pos=0, dv_=dv, **over):
+        a = {**addr, **over}
+        return lib.infini_attn_decode_step_kv(
+            B, Hq, Hkv, dk, dv_, N, pos, 1, 1,
+            *[ctypes.c_void_p(a[n]) for n in ("q", "k", "v", "beta", "k_cache", "v_cache", "M",
+                                               "z", "out", "workspace")], 1 << 30, None)
+    assert call(pos=N) == 1
+    assert call(dv_=96) == 2
+    assert call(out=None) == 1
+    assert call(v_cache=addr["v_cache"] + 8) == 3
+    # the value cache is d_value wide: a k_cache-sized buffer after it would overlap
+    assert call(M=addr["v_cache"] + sizes["v_cache"] - 256) == 1
+
+
 @pytest.mark.parametrize("args,status", [
     ((0, 1, 1, 8, 32, 4, 0, 0), 1),     # B < 1
     ((1, 3, 2, 8, 32, 4, 0, 0), 1),     # Hq % Hkv
