@@ -79,37 +79,80 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, rule, inp, target_s):
-    """The fp64 oracle, as it is, on whole (batch, KV head) units of the same
-    workload until about target_s seconds have run."""
-    import numpy as np
+def _oracle_unit(task):
+    """One (batch, KV head) unit of the workload through the fp64 oracle in a
+    pool worker with one BLAS thread; returns the oracle's run time."""
     import threadpoolctl
 
     import oracle
-    from tests.parity import unit_inputs
 
-    G = w.Hq // w.Hkv
-    order = [(b, j) for b in range(w.B) for j in range(w.Hkv)]
-    done, elapsed = 0, 0.0
-    for b, j in order:
-        u = unit_inputs(inp, b, j, G)
+    w, rule, b, j = task
+    with threadpoolctl.threadpool_limits(1):
+        u = synth.make_unit_inputs(w, b, j)
         t0 = time.perf_counter()
         oracle.forward(u["q"], u["k"], u["v"], u["beta"], u["M0"], u["z0"], w.seg_len, rule)
-        elapsed += time.perf_counter() - t0
-        done += 1
-        if elapsed >= target_s:
+        return time.perf_counter() - t0
+
+
+def cpu_pool(procs):
+    """A pool of `procs` worker processes, forked before this process touches
+    the GPU (the workers only run the CPU oracle)."""
+    import multiprocessing
+    return multiprocessing.get_context("fork").Pool(procs)
+
+
+def cpu_baseline(pool, procs, w, rule, target_s):
+    """The fp64 oracle, as it is, on whole (batch, KV head) units of the same
+    workload (inputs drawn on the CPU from the same per-slice seeds), one unit
+    per worker process, in rounds of `procs` units until about target_s
+    seconds of wall time have run (or every unit is done)."""
+    order = [(b, j) for b in range(w.B) for j in range(w.Hkv)]
+    done, t0 = 0, time.perf_counter()
+    while done < len(order):
+        batch = order[done:done + procs]
+        pool.map(_oracle_unit, [(w, rule, b, j) for b, j in batch], chunksize=1)
+        done += len(batch)
+        if time.perf_counter() - t0 >= target_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    wall = time.perf_counter() - t0
+    G = w.Hq // w.Hkv
     tokens = w.B * w.L * done / len(order)
     return {
-        "value": tokens / elapsed,
+        "value": tokens / wall,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": int(min(procs, done)),
         "kind": "oracle",
         "sample": (f"{done} of {len(order)} (batch, KV head) units, each {G} query heads x "
-                   f"{w.segments} segments of {w.seg_len}; fp64 numpy, {elapsed:.1f} s; "
-                   f"value = B*L*{done}/{len(order)} tokens / time"),
+                   f"{w.segments} segments of {w.seg_len}, one unit per process on "
+                   f"{min(procs, done)} processes with one BLAS thread each; fp64 numpy, "
+                   f"{wall:.1f} s wall; value = B*L*{done}/{len(order)} tokens / wall time"),
     }
+
+
+def gpu_sclk_mhz():
+    """The current shader clock of GPU 0 in MHz from rocm-smi, or None."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
+                             text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", txt, flags=re.I)
+    return int(m.group(1)) if m else None
+
+
+# The pages' own numbers for Infini-attention models, for context only: none
+# comes with hardware or a throughput ("Infini-Attention" (AI Wiki), "Results
+# at a glance" and "Can Infini-attention retrieve a passkey at one million
+# tokens?"; "Hugging Face Infini-Attention Reproduction Analysis", "Weight
+# Decay and Rollouts").
+PAGES_CONTEXT = {
+    "passkey": "1B model, passkey retrieval up to 1M tokens, about 100% after fine-tuning",
+    "booksum": "8B model, book summarisation over 500K tokens, ROUGE 40.0 / 8.8 / 17.9",
+    "hf_reproduction": "200M Llama and Llama 3 8B, 64-token segments x 16 rollouts",
+    "hardware": "not stated on the pages; no throughput is published",
+}
 
 
 def decode_bytes(w, pos):
@@ -373,6 +416,16 @@ def main():
                          "the streaming decode step over one full segment of it; backward: "
                          "the gradients of the block over the workload; block: the block "
                          "with its Q/K/V and output projections over the workload")
+    ap.add_argument("--seg-len", type=int, default=0,
+                    help="override the workload's segment length (same L; a sweep point)")
+    ap.add_argument("--plan", default="overlapped", choices=["overlapped", "serial"],
+                    help="overlapped: the full workspace (the scan beside the attention); "
+                         "serial: one byte less (scan, then attention, on one stream)")
+    ap.add_argument("--cold", type=int, default=5, metavar="N",
+                    help="also time N steps each after flushing the caches with a 512 MiB "
+                         "device copy outside the timed events (0: skip)")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="worker processes of the CPU oracle (at most the host's CPUs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the steps, copy MIB MiB device to device once (a kernel "
                          "of known traffic that calibrates the HBM byte counters)")
@@ -384,12 +437,19 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
+    w = synth.WORKLOADS[args.workload]
+    if args.seg_len > 0:
+        w = w.with_(seg_len=args.seg_len)
+    rule = args.rule or w.rules[-1]
+    pool, procs = None, 0
+    if args.mode == "forward" and not args.no_cpu_baseline:
+        procs = max(1, min(args.cpu_procs, os.cpu_count() or 1))
+        pool = cpu_pool(procs)  # before the GPU is touched
+
     import torch
 
     import compressive_memory_transformers_amd as lib
 
-    w = synth.WORKLOADS[args.workload]
-    rule = args.rule or w.rules[-1]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.mode == "decode":
@@ -407,7 +467,8 @@ def main():
     z = torch.empty_like(inp["z0"])
     full, _ = lib.workspace_size_kv(w.B, w.Hq, w.Hkv, w.L, w.d, w.d_value, w.seg_len, rule,
                                     inp["q"].dtype)
-    ws = torch.empty(full, dtype=torch.uint8, device=dev)
+    ws = torch.empty(full if args.plan == "overlapped" else full - 1, dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
@@ -445,6 +506,37 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     scan_ms = sum(e[0].elapsed_time(e[1]) for e in phase) / args.steps
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in phase) / args.steps
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in phase)
+    median_ms = step_ms[len(step_ms) // 2]
+
+    # cold: each step after a 512 MiB device copy (outside its events) that
+    # evicts the inputs from L2 and the 256 MB MALL
+    cold_ms = None
+    if args.cold > 0:
+        a_ = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a_)
+        cold = []
+        for _ in range(args.cold):
+            b_.copy_(a_)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            for e in evs:
+                e.record(stream)
+            step(evs)
+            torch.cuda.synchronize()
+            cold.append(evs[0].elapsed_time(evs[2]))
+        cold_ms = sorted(cold)[len(cold) // 2]
+        del a_, b_
+
+    # the shader clock, sampled while steps keep the GPU busy
+    sclk = []
+    for _ in range(3):
+        for _ in range(max(8, int(200 / max(ms, 1e-3)))):
+            step()
+        v_ = gpu_sclk_mhz()
+        if v_ is not None:
+            sclk.append(v_)
+        torch.cuda.synchronize()
+    sclk_mhz = sorted(sclk)[len(sclk) // 2] if sclk else None
 
     tokens = w.B * w.L
     flops = synth.flops(w, rule)
@@ -490,12 +582,21 @@ def main():
         "peak_tflops": peak,
         "head_tokens_per_s": w.B * w.Hq * w.L / (ms * 1e-3),
         "hbm_gbs_compulsory": synth.hbm_bytes(w) / (ms * 1e-3) / 1e9,
-        "phase_ms": {"scan": scan_ms, "attn": attn_ms},
+        "phase_ms": {"scan_exposed": scan_ms, "attn": attn_ms},
+        "plan": args.plan,
+        "ms_per_step_median": median_ms,
+        "cold_ms_per_step_median": cold_ms,
+        "sclk_mhz": sclk_mhz,
+        "frac_of_clock_adjusted_peak": (tflops / (peak * sclk_mhz / 2400.0)
+                                        if sclk_mhz else None),
         "roofline": roofline,
         "cpu_baseline": None,
+        "pages_context": PAGES_CONTEXT,
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, rule, inp, args.cpu_seconds)
+    if pool is not None:
+        del inp
+        rec["cpu_baseline"] = cpu_baseline(pool, procs, w, rule, args.cpu_seconds)
+        pool.close()
     print(json.dumps(rec), flush=True)
 
 

@@ -186,6 +186,14 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     lib = load_library()
+    with torch.cuda.device(dev):
+        return _forward_call(lib, B, Hq, Hkv, L, d, dv, seg_len, rule, q, k, v, beta, M0, z0,
+                             out, M_final, z_final, workspace, stream, events, lse)
+
+
+def _forward_call(lib, B, Hq, Hkv, L, d, dv, seg_len, rule, q, k, v, beta, M0, z0, out,
+                  M_final, z_final, workspace, stream, events, lse):
+    dev = q.device
     args = [B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[q.dtype],
             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
             _ptr(out), _ptr(M_final), _ptr(z_final),

@@ -27,6 +27,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/infini_attn.h"
@@ -128,20 +130,44 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Workspace regions of a window of W segments: state A, state B (each (M, z)),
-// then the window's snapshots and, for the affine form, its column sums and
-// per-segment matrices.
-struct Carved {
-  float* stM[2];
-  float* stz[2];
+// Workspace layout: state A, state B (each (M, z)), then one or two regions
+// of per-segment data, each for a window of up to W segments: the window's
+// snapshots and, for the affine form, its column sums and per-segment
+// matrices.
+struct Region {
   void* snapM;
   float* snapZ;
   float* colsum;
   float* Bmat;
   void* Amat;
 };
+struct Carved {
+  float* stM[2];
+  float* stz[2];
+  Region r[2];
+  Region head;  // one snapshot slot (overlapped plan): the state before segment 0
+};
 
-Carved carve(const Plan& p, int64_t W, int32_t rule, void* workspace) {
+// Bytes of alignment slack that one region's sub-buffers can add.
+constexpr size_t kRegionSlack = 5 * kAlign;
+
+// Bytes of the head slot: one snapshot per unit, each part aligned.
+size_t head_bytes(const Plan& p) {
+  return align_up((size_t)p.units * (size_t)(p.dv * p.d * p.e)) +
+         align_up((size_t)p.units * (size_t)p.d * 4);
+}
+
+// Workspace bytes for every segment at once: with more than one segment, the
+// overlapped plan's two regions (S segments between them) and the head slot.
+size_t workspace_full(const Plan& p) {
+  if (p.S < 2) return p.fixed + p.per_seg;
+  return p.fixed + kRegionSlack + head_bytes(p) + p.per_seg * (size_t)p.S;
+}
+
+// W0 segments in region 0, W1 (0: none) in region 1, and the head slot if
+// `head`.
+Carved carve(const Plan& p, int64_t W0, int64_t W1, int32_t rule, void* workspace,
+             bool head = false) {
   Carved c{};
   char* ws = static_cast<char*>(workspace);
   const int64_t d = p.d, dv = p.dv;
@@ -156,21 +182,61 @@ Carved carve(const Plan& p, int64_t W, int32_t rule, void* workspace) {
     cur += align_up(bytes);
     return r;
   };
-  const size_t uW = (size_t)p.units * (size_t)W;
-  c.snapM = take(uW * (size_t)(dv * d * p.e));
-  c.snapZ = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
-  if (p.affine) {
-    c.colsum = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
-    c.Bmat = reinterpret_cast<float*>(take(uW * (size_t)(d * d) * 4));
-    if (rule == INFINI_RULE_DELTA) c.Amat = take(uW * (size_t)(d * d * p.e));
+  const int64_t Ws[2] = {W0, W1};
+  for (int ri = 0; ri < 2; ++ri) {
+    if (Ws[ri] <= 0) continue;
+    Region& g = c.r[ri];
+    const size_t uW = (size_t)p.units * (size_t)Ws[ri];
+    g.snapM = take(uW * (size_t)(dv * d * p.e));
+    g.snapZ = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
+    if (p.affine) {
+      g.colsum = reinterpret_cast<float*>(take(uW * (size_t)d * 4));
+      g.Bmat = reinterpret_cast<float*>(take(uW * (size_t)(d * d) * 4));
+      if (rule == INFINI_RULE_DELTA) g.Amat = take(uW * (size_t)(d * d * p.e));
+    }
+  }
+  if (head) {
+    c.head.snapM = take((size_t)p.units * (size_t)(dv * d * p.e));
+    c.head.snapZ = reinterpret_cast<float*>(take((size_t)p.units * (size_t)d * 4));
   }
   return c;
+}
+
+// The auxiliary stream of the overlapped plan and its events, one set per
+// device, created on first use and kept until the process ends (default
+// priority, non-blocking). Calls enqueue under g_aux_mu, so concurrent calls
+// never interleave their records and waits on these events.
+struct Aux {
+  bool tried = false, ok = false;
+  hipStream_t s2 = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t rec[2] = {nullptr, nullptr};
+  hipEvent_t att[2] = {nullptr, nullptr};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;
+Aux g_aux[kMaxDevices];
+
+// The current device's set (null if it cannot be created); g_aux_mu held.
+Aux* aux_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Aux& a = g_aux[dev];
+  if (!a.tried) {
+    a.tried = true;
+    bool ok = hipStreamCreateWithFlags(&a.s2, hipStreamNonBlocking) == hipSuccess;
+    hipEvent_t* evs[] = {&a.start, &a.rec[0], &a.rec[1], &a.att[0], &a.att[1]};
+    for (hipEvent_t* e : evs)
+      ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+    a.ok = ok;
+  }
+  return a.ok ? &a : nullptr;
 }
 
 // The memory recurrence over segments [s_begin, s_begin + s_count) of k / v
 // ([B*Hkv][L][d]), from (Min, zin) to (Mout, zout), writing the snapshots into
 // the carved regions: the direct scan or the affine form, as the plan says.
-hipError_t launch_recurrence(const Plan& p, const Carved& cw, int32_t rule, int32_t dtype,
+hipError_t launch_recurrence(const Plan& p, const Region& cw, int32_t rule, int32_t dtype,
                              const void* k, const void* v, const float* Min, const float* zin,
                              float* Mout, float* zout, int64_t L, int64_t seg_len,
                              int64_t s_begin, int64_t s_count, hipStream_t s) {
@@ -224,7 +290,7 @@ infini_status_t infini_attn_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, i
   Plan p;
   const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
-  if (full_bytes) *full_bytes = p.fixed + p.per_seg * (size_t)p.S;
+  if (full_bytes) *full_bytes = workspace_full(p);
   if (min_bytes) *min_bytes = p.fixed + p.per_seg;
   return INFINI_OK;
 }
@@ -287,33 +353,101 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   }
 
   if (workspace_bytes < p.fixed + p.per_seg) return INFINI_ERR_WORKSPACE;
-  int64_t W = (int64_t)((workspace_bytes - p.fixed) / p.per_seg);
-  if (W > p.S) W = p.S;
+  if (n_events < 0 || (n_events > 0 && events == nullptr)) return INFINI_ERR_INVALID_ARG;
+  for (int32_t e = 0; e < n_events; ++e)
+    if (events[e] == nullptr) return INFINI_ERR_INVALID_ARG;
   const int64_t eff = seg_len < L ? seg_len : L;
   const int64_t bm = attn_block_rows(d, dv, eff);
   const int64_t n_qt = (eff + bm - 1) / bm;
   const int64_t tiles_per_seg = B * Hq * n_qt;  // <= INT32_MAX, checked above
-  if (W > INT32_MAX / tiles_per_seg) W = INT32_MAX / tiles_per_seg;
+  const int64_t max_launch = INT32_MAX / tiles_per_seg;  // segments per attention launch
 
-  const Carved cw = carve(p, W, rule, workspace);
+  // Window plan. Serial: one region of W segments, each window's scan then
+  // its attention on the caller's stream. Overlapped (the call has several
+  // segments and two regions plus the head slot fit): segment 0's attention
+  // starts at once from a snapshot of (M0, z0) in the head slot, while the
+  // windows' scans run on an auxiliary stream into the two regions in turn,
+  // and each window's attention (on the caller's stream) waits only for its
+  // own window's scan. The scan's time on the critical path is then the part
+  // segment 0's attention does not cover. It runs when the workspace has the
+  // full size (workspace_full) and the scan is worth hiding (below): the
+  // first window is S / 4 segments and the
+  // second all the rest (more windows, alternating between the two regions,
+  // only if a launch would exceed 2^31 workgroups). A smaller workspace runs
+  // the serial plan, in one window if every segment's data fits.
+  int64_t W = (int64_t)((workspace_bytes - p.fixed) / p.per_seg);
+  if (W > p.S) W = p.S;
+  if (W > max_launch) W = max_launch;
+  int64_t C[2] = {W, 0};
+  bool overlapped = false;
+  std::unique_lock<std::mutex> lock(g_aux_mu, std::defer_lock);
+  Aux* aux = nullptr;
+  // The overlap pays where the scan is the direct form on a large call: a
+  // latency-bound walk over the segments on few workgroups, which leaves the
+  // attention room to run beside it (measured: d_key 64 / d_value 128 at the
+  // Llama layer's sizes, 3.01 -> 2.68 ms per call). The affine form's scan is
+  // mostly parallel work that competes with the attention for the whole chip
+  // (measured 1-2% slower overlapped at the Llama layer and at 128-token
+  // segments), and on small calls the extra launches and event waits cost
+  // more than they hide; those run the serial plan.
+  const bool worth_overlap = !p.affine && (double)B * Hq * L * d >= (double)(1 << 26);
+  if (p.S >= 2 && worth_overlap && workspace_bytes >= workspace_full(p)) {
+    int64_t c0 = p.S / 4 > 0 ? p.S / 4 : 1;
+    int64_t c1 = p.S - c0;
+    if (c0 > max_launch) c0 = max_launch;
+    if (c1 > max_launch) c1 = max_launch;
+    if (c0 >= 1 && c1 >= 1) {
+      lock.lock();
+      aux = aux_for_current_device();
+      if (aux != nullptr) {
+        overlapped = true;
+        C[0] = c0;
+        C[1] = c1;
+      } else {
+        lock.unlock();
+      }
+    }
+  }
+
+  const Carved cw = carve(p, C[0], C[1], rule, workspace, overlapped);
   float* const* stM = cw.stM;
   float* const* stz = cw.stz;
-  void* snapM = cw.snapM;
-  float* snapZ = cw.snapZ;
-  float* colsum = cw.colsum;
-  float* Bmat = cw.Bmat;
-  void* Amat = cw.Amat;
-
-  if (n_events < 0 || (n_events > 0 && events == nullptr)) return INFINI_ERR_INVALID_ARG;
-  for (int32_t e = 0; e < n_events; ++e)
-    if (events[e] == nullptr) return INFINI_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Record event `slot` of window `wi` if the caller passed that many.
-  auto mark = [&](int64_t wi, int slot) -> bool {
-    const int64_t e = 3 * wi + slot;
-    if (e >= n_events) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(events[e]), s) == hipSuccess;
+  hipStream_t sr = overlapped ? aux->s2 : s;  // the stream the scans run on
+  // Caller event `slot`: 0 at the start, 1 before the first attention
+  // kernel, 2 after the last one.
+  auto mark = [&](int slot) -> bool {
+    if (slot >= n_events) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(events[slot]), s) == hipSuccess;
   };
+  // Segments [sb, sb + sc) of the attention, reading the snapshots of region
+  // `rg` whose first entry is segment sb - first.
+  auto attention = [&](const Region& rg, int64_t sb, int64_t sc, int64_t first,
+                       int64_t count) -> bool {
+    AttnArgs aa;
+    aa.q = q;
+    aa.k = k;
+    aa.v = v;
+    aa.beta = beta;
+    aa.snapM = rg.snapM;
+    aa.snapZ = rg.snapZ;
+    aa.out = out;
+    aa.lse = lse;
+    aa.L = L;
+    aa.seg_len = seg_len;
+    aa.Hq = (int32_t)Hq;
+    aa.Hkv = (int32_t)Hkv;
+    aa.s_begin = (int32_t)sb;
+    aa.s_count = (int32_t)sc;
+    aa.snap_first = (int32_t)first;
+    aa.snap_count = (int32_t)count;
+    aa.n_qt = (int32_t)n_qt;
+    aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);  // scores scale with the key width
+    const hipError_t ea = dv == d ? infini::launch_attn(dtype, (int)d, aa, p.units, s)
+                                  : infini::launch_attn_kv(dtype, (int)d, (int)dv, aa, p.units, s);
+    return ea == hipSuccess;
+  };
+  if (!mark(0)) return INFINI_ERR_HIP;
   const float* Min = M0;
   const float* zin = z0;
   if (z_final == z0 && !p.affine) {
@@ -323,46 +457,49 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
     if (infini::launch_copy_f32(stz[1], z0, B * Hkv * d, s) != hipSuccess) return INFINI_ERR_HIP;
     zin = stz[1];
   }
+  if (overlapped) {
+    // the head slot, read before the scans may overwrite M0 / z0 (in place)
+    if (infini::launch_snapshot(dtype, (int)d, (int)dv, M0, zin, cw.head.snapM, cw.head.snapZ,
+                                p.units, s) != hipSuccess)
+      return INFINI_ERR_HIP;
+    // the auxiliary stream starts after the caller's work so far
+    if (hipEventRecord(aux->start, s) != hipSuccess ||
+        hipStreamWaitEvent(sr, aux->start, 0) != hipSuccess)
+      return INFINI_ERR_HIP;
+    if (!mark(1)) return INFINI_ERR_HIP;
+    if (!attention(cw.head, 0, 1, 0, 1)) return INFINI_ERR_HIP;
+  }
 
-  const int64_t n_windows = (p.S + W - 1) / W;
-  for (int64_t wi = 0; wi < n_windows; ++wi) {
-    const int64_t s_begin = wi * W;
-    const int64_t s_count = (p.S - s_begin) < W ? (p.S - s_begin) : W;
-    const bool last = wi == n_windows - 1;
+  int64_t s_begin = 0;
+  for (int64_t wi = 0; s_begin < p.S; ++wi) {
+    const int ri = overlapped ? (int)(wi & 1) : 0;
+    const int64_t s_count = (p.S - s_begin) < C[ri] ? (p.S - s_begin) : C[ri];
+    const bool last = s_begin + s_count == p.S;
     float* Mout = last ? M_final : stM[wi & 1];
     float* zout = last ? z_final : stz[wi & 1];
+    const Region& rg = cw.r[ri];
 
-    if (!mark(wi, 0)) return INFINI_ERR_HIP;
-    if (launch_recurrence(p, cw, rule, dtype, k, v, Min, zin, Mout, zout, L, seg_len, s_begin,
-                          s_count, s) != hipSuccess)
+    // the region's previous window must have finished its attention
+    if (overlapped && wi >= 2 && hipStreamWaitEvent(sr, aux->att[ri], 0) != hipSuccess)
       return INFINI_ERR_HIP;
-    if (!mark(wi, 1)) return INFINI_ERR_HIP;
-
-    AttnArgs aa;
-    aa.q = q;
-    aa.k = k;
-    aa.v = v;
-    aa.beta = beta;
-    aa.snapM = snapM;
-    aa.snapZ = snapZ;
-    aa.out = out;
-    aa.lse = lse;
-    aa.L = L;
-    aa.seg_len = seg_len;
-    aa.Hq = (int32_t)Hq;
-    aa.Hkv = (int32_t)Hkv;
-    aa.s_begin = (int32_t)s_begin;
-    aa.s_count = (int32_t)s_count;
-    aa.n_qt = (int32_t)n_qt;
-    aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);  // scores scale with the key width
-    const hipError_t ea = dv == d ? infini::launch_attn(dtype, (int)d, aa, p.units, s)
-                                  : infini::launch_attn_kv(dtype, (int)d, (int)dv, aa, p.units, s);
-    if (ea != hipSuccess) return INFINI_ERR_HIP;
-    if (!mark(wi, 2)) return INFINI_ERR_HIP;
+    if (launch_recurrence(p, rg, rule, dtype, k, v, Min, zin, Mout, zout, L, seg_len, s_begin,
+                          s_count, sr) != hipSuccess)
+      return INFINI_ERR_HIP;
+    if (overlapped && (hipEventRecord(aux->rec[ri], sr) != hipSuccess ||
+                       hipStreamWaitEvent(s, aux->rec[ri], 0) != hipSuccess))
+      return INFINI_ERR_HIP;
+    if (!overlapped && wi == 0 && !mark(1)) return INFINI_ERR_HIP;
+    // segment 0 already ran from the head slot in the overlapped plan
+    const int64_t skip = overlapped && wi == 0 ? 1 : 0;
+    if (s_count > skip && !attention(rg, s_begin + skip, s_count - skip, skip, s_count))
+      return INFINI_ERR_HIP;
+    if (overlapped && hipEventRecord(aux->att[ri], s) != hipSuccess) return INFINI_ERR_HIP;
 
     Min = Mout;
     zin = zout;
+    s_begin += s_count;
   }
+  if (!mark(2)) return INFINI_ERR_HIP;
   return INFINI_OK;
 }
 
@@ -388,7 +525,7 @@ infini_status_t infini_attn_workspace_size_kv(int64_t B, int64_t Hq, int64_t Hkv
   const infini_status_t st =
       check_sizes_kv(B, Hq, Hkv, L, d_key, d_value, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
-  if (full_bytes) *full_bytes = p.fixed + p.per_seg * (size_t)p.S;
+  if (full_bytes) *full_bytes = workspace_full(p);
   if (min_bytes) *min_bytes = p.fixed + p.per_seg;
   return INFINI_OK;
 }
@@ -560,14 +697,14 @@ infini_status_t decode_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64
 
   if (pos == seg_len - 1) {
     // the segment is complete: fold the cache into (M, z), in place
-    const Carved cw = carve(p, 1, rule, ws + dp.part_bytes);
+    const Carved cw = carve(p, 1, 0, rule, ws + dp.part_bytes);
     const float* zin = z;
     if (!p.affine) {
       // the direct scan's slab workgroups read z while one of them writes it
       if (infini::launch_copy_f32(cw.stz[1], z, B * Hkv * d, s) != hipSuccess) return INFINI_ERR_HIP;
       zin = cw.stz[1];
     }
-    if (launch_recurrence(p, cw, rule, dtype, k_cache, v_cache, M, zin, M, z, seg_len, seg_len, 0,
+    if (launch_recurrence(p, cw.r[0], rule, dtype, k_cache, v_cache, M, zin, M, z, seg_len, seg_len, 0,
                           1, s) != hipSuccess)
       return INFINI_ERR_HIP;
   }
@@ -1055,7 +1192,7 @@ infini_status_t block_layout(int64_t B, int64_t L, int64_t d_model, int64_t Hq, 
     lay->v = nq + nkv;
     lay->a = nq + 2 * nkv;
     lay->fwd = 2 * nq + 2 * nkv;
-    lay->fwd_bytes = p.fixed + p.per_seg * (size_t)p.S;
+    lay->fwd_bytes = workspace_full(p);
     lay->total = lay->fwd + lay->fwd_bytes;
   }
   return INFINI_OK;

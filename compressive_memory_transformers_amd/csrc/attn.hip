@@ -144,7 +144,7 @@ __device__ __forceinline__ void attn_tile(const T* Kb, const T* Vb, const frag_t
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xhalf_max(mx);
   // Key 0 of the segment is visible to every row, so the first tile sets a
   // finite reference for every lane.
   if (__any((mx - m_run) * c > kRescaleTau)) {
@@ -275,10 +275,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
   }
   if (!wave_on) return;  // no barrier follows
 
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = xhalf_sum(l_run);
   if (a.lse != nullptr && h == 0 && row < n_s)
     a.lse[qh * a.L + seg_start + row] = m_run * c + __log2f(l);
-  const int64_t snap = (int64_t)unit * a.s_count + sl;
+  const int64_t snap = (int64_t)unit * a.snap_count + a.snap_first + sl;
   const float* zs = a.snapZ + snap * DK;
   const T* Mts = static_cast<const T*>(a.snapM) + snap * DV * DK;
 
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(AttnArgs a) {
       sq[cc][e] = s;
       dp += s * zs[16 * cc + 8 * h + e];
     }
-  const float den = dp + __shfl_xor(dp, 32);
+  const float den = xhalf_sum(dp);
   const float g = 1.f / (1.f + __expf(-a.beta[hq]));
   const float ca = (1.f - g) / l, cm = g / den;
 #pragma unroll
@@ -392,7 +392,7 @@ __device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<DK, DV>& st, float
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xhalf_max(mx);
   if (__any((mx - st.m_run) * c > kRescaleTau)) {
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   // tile j + 1 lies wholly below the block's first row are full for every
   // wave.
   const int n_full = q0 + BM <= n_s ? q0 / BN - 1 : 0;
-  const int64_t snap = (int64_t)unit * a.s_count + sl;
+  const int64_t snap = (int64_t)unit * a.snap_count + a.snap_first + sl;
   const float* zs = a.snapZ + snap * DK;
   const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * DV * DK;
   int j = 0;
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   const bf16* Ma = pl ? Ks[1] : Ks[0];
   const bf16* Mb = pl ? Vs[0] : Vs[1];
   float l = st.l0 + st.l1;
-  l += __shfl_xor(l, 32);
+  l = xhalf_sum(l);
   if (a.lse != nullptr && h == 0 && row < n_s)
     a.lse[qh * a.L + seg_start + row] = st.m_run * c + __log2f(l);
   float sq[NC][8];
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
       sq[cc][e] = s;
       dp += s * Zs[16 * cc + 8 * h + e];
     }
-  const float den = dp + __shfl_xor(dp, 32);
+  const float den = xhalf_sum(dp);
   const float ca = (1.f - g) / l, cm = g / den;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

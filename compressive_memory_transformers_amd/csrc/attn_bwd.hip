@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
       sqf[cc][e] = (bf16)sg;
       den += sg * zs[16 * cc + 8 * h + e];
     }
-  den += __shfl_xor(den, 32);
+  den = xhalf_sum(den);
 
   bf16* const Ms[2] = {Ms0, NT > 1 ? Ms1 : Ms0};
   const uint32_t ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
         doo += dv * (float)o4[j];
       }
     }
-  dam += __shfl_xor(dam, 32);
-  doo += __shfl_xor(doo, 32);
+  dam = xhalf_sum(dam);
+  doo = xhalf_sum(doo);
   const float inv_den = 1.f / den;
   dam *= inv_den;
   const float dden = -g * dam * inv_den;
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void upd_kernel(BwdArgs a, int n_kt) {
       pf[cc][e] = (bf16)f;
       cz += f * zs[16 * cc + 8 * h + e];
     }
-  cz += __shfl_xor(cz, 32);
+  cz = xhalf_sum(cz);
 
   bf16* const Us[2] = {Us0, NT > 1 ? Us1 : Us0};
   bf16* const Ps[2] = {Ps0, NT > 1 ? Ps1 : Ps0};
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void upd_kernel(BwdArgs a, int n_kt) {
       if (live) *reinterpret_cast<f32x4*>(dva + col) = dv4;
     }
   if constexpr (DELTA) {
-    dcs += __shfl_xor(dcs, 32);
+    dcs = xhalf_sum(dcs);
     if (live && h == 0) a.dc[row] = dcs * ic;
   }
 

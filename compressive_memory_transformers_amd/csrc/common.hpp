@@ -61,6 +61,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Lanes i and i ^ 32 combined, every lane getting the result: one
+// v_permlane32_swap (gfx950) exchanges the two half-waves' copies in
+// registers, where a shuffle would go through the LDS crossbar. The sum adds
+// the two values in the same order for both halves' lanes as x + x[i ^ 32]
+// would (the lower half's value first in the upper half is the commuted
+// addend), so the results are identical to the shuffle form.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row of the 32x32 accumulator tile that register r of a lane in half h holds.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return (r >> 2) * 8 + 4 * h + (r & 3); }
 

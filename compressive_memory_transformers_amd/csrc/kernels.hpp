@@ -68,6 +68,9 @@ struct AttnArgs {
   int64_t L, seg_len;
   int32_t Hq, Hkv;
   int32_t s_begin, s_count;
+  // the snapshot of segment s_begin + sl (sl < s_count) is entry
+  // unit * snap_count + snap_first + sl of snapM / snapZ
+  int32_t snap_first, snap_count;
   int32_t n_qt;        // query tiles per segment
   float scale_log2;    // log2(e) / sqrt(d)
 };
@@ -221,6 +224,10 @@ hipError_t launch_decode(int dtype, int d, const DecodeArgs& a, hipStream_t stre
 // and the key cache rows of dk, v, the value cache rows and out of dv, M [dk][dv].
 hipError_t launch_decode_kv(int dtype, int dk, int dv, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream);
+// One snapshot per unit from a state: snapM[u] = M[u]^T ([dv][dk], element
+// type), snapZ[u] = z[u]; M [units][dk][dv], z [units][dk] float.
+hipError_t launch_snapshot(int dtype, int dk, int dv, const float* M, const float* z,
+                           void* snapM, float* snapZ, int64_t units, hipStream_t stream);
 
 // The projections around the block (proj.hip): C[m][n] = sum_k A[m][k] W[n][k]
 // in bf16 with float accumulation, W [N][K] row-major. A is read as rows

@@ -321,6 +321,38 @@ hipError_t launch_scan_kv(int dtype, int dk, int dv, int rule, const ScanArgs& a
                         : launch_scan_kv_d<float>(dk, dv, rule, a, stream);
 }
 
+namespace {
+
+// One state as the attention reads it: M^T [dv][dk] in the element type and
+// z [dk] in float, per unit; thread t of the unit's blocks writes element t of
+// M^T (reading M [dk][dv] with stride dv).
+template <typename T>
+__global__ __launch_bounds__(256) void snapshot_kernel(const float* M, const float* z, T* snapM,
+                                                       float* snapZ, int dk, int dv) {
+  const int unit = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx < dk * dv) {
+    const int j = idx / dk, i = idx % dk;  // M^T row j (value column), column i (key row)
+    snapM[(int64_t)unit * dk * dv + idx] = static_cast<T>(M[(int64_t)unit * dk * dv + (int64_t)i * dv + j]);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < dk)
+    snapZ[(int64_t)unit * dk + threadIdx.x] = z[(int64_t)unit * dk + threadIdx.x];
+}
+
+}  // namespace
+
+hipError_t launch_snapshot(int dtype, int dk, int dv, const float* M, const float* z,
+                           void* snapM, float* snapZ, int64_t units, hipStream_t stream) {
+  const dim3 grid((unsigned)((dk * dv + 255) / 256), (unsigned)units);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(snapshot_kernel<bf16>, grid, dim3(256), 0, stream, M, z,
+                       static_cast<bf16*>(snapM), snapZ, dk, dv);
+  else
+    hipLaunchKernelGGL(snapshot_kernel<float>, grid, dim3(256), 0, stream, M, z,
+                       static_cast<float*>(snapM), snapZ, dk, dv);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t stream) {
   const int64_t blocks = (n + 255) / 256;
   const unsigned g = (unsigned)(blocks < 1024 ? (blocks < 1 ? 1 : blocks) : 1024);

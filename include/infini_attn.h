@@ -37,10 +37,25 @@
  *   z0, z_final [B][Hkv][d]        float, every entry > 0 (not checked)
  *
  * Ownership: the caller owns every buffer, including the workspace; the
- * library allocates no device memory and keeps no mutable global state, so
- * calls on different streams with different workspaces may run concurrently.
- * `out` must not overlap any input. M_final may be M0 and z_final may be z0
- * (an in-place carry); any other overlap is rejected.
+ * library allocates no device memory. Calls on different streams with
+ * different workspaces may run concurrently. `out` must not overlap any
+ * input. M_final may be M0 and z_final may be z0 (an in-place carry); any
+ * other overlap is rejected.
+ *
+ * Streams: a forward call with more than one segment, a workspace of the
+ * full size (infini_attn_workspace_size) and a memory scan in the direct form
+ * (seg_len < d, or d_key != d_value) on a large call (B*Hq*L*d >= 2^26)
+ * starts the attention of segment 0 at once and runs the scan of the later
+ * segments on an auxiliary stream beside it, in two windows, each window's
+ * attention on `stream` waiting for its own window's scan (events). Every
+ * other call runs on `stream` alone: each window's scan, then its attention.
+ * The auxiliary stream (default priority) and its five events are created
+ * once per device, on the first such call with that device current, and kept
+ * until the process ends; `stream` must belong to the current device. The
+ * call returns with every output ordered before `stream`'s later work, as if
+ * all of it ran on `stream`; calls that use the auxiliary stream enqueue one
+ * at a time (a host mutex), and their scans share it. Results are the same
+ * bit for bit whichever plan runs.
  *
  * Errors: every check runs on the host before anything is enqueued; on an
  * error nothing is written and nothing launches. Execution is asynchronous on
@@ -81,7 +96,8 @@ typedef enum {
 
 /*
  * Workspace sizes of a forward call with these sizes, in bytes.
- *   *full_bytes: enough to process every segment in one pass (fastest);
+ *   *full_bytes: enough to process every segment in one pass, with the scan
+ *                beside the attention (see Streams above);
  *   *min_bytes:  the least the call accepts; it then walks the segments in
  *                windows that fit, which adds launches but gives the same
  *                result bit for bit.
@@ -148,13 +164,16 @@ infini_status_t infini_attn_forward_kv_timed(
     void* const* events, int32_t n_events);
 
 /*
- * infini_attn_forward, plus HIP events recorded on `stream` around its
- * kernels, for timing each phase. The segments run in windows (one window
- * when the workspace has the full size); for window w the call records
- *   events[3w + 0] before the memory scan of the window,
- *   events[3w + 1] after the scan, before the attention kernel,
- *   events[3w + 2] after the attention kernel,
- * for every index below n_events; later windows record nothing. `events`
+ * infini_attn_forward, plus HIP events recorded on `stream`, for timing its
+ * phases:
+ *   events[0] at the start of the call;
+ *   events[1] when the first attention kernel may start (after the first
+ *             window's memory scan: the part of the scan on the critical path);
+ *   events[2] after the last attention kernel (the later windows' scans run
+ *             beside the attention on the auxiliary stream, or between the
+ *             attention kernels on `stream` when the workspace holds only one
+ *             segment's data).
+ * Indices from n_events on are not recorded (at most 3 are used). `events`
  * holds hipEvent_t handles the caller created (as void*); none may be NULL.
  * Everything else is as in infini_attn_forward.
  */

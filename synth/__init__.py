@@ -148,6 +148,32 @@ def make_inputs(w, device="cpu"):
     return dict(q=q, k=k, v=v, beta=beta, M0=M0, z0=z0)
 
 
+def make_unit_inputs(w, b, j):
+    """The slices of one (batch b, KV head j) unit of workload ``w``, drawn
+    on the CPU from the same per-slice seeds as ``make_inputs`` and rounded to
+    the workload's dtype, as float64 numpy arrays with leading dimensions of
+    size 1: q [1, G, L, d] (the G = Hq / Hkv query heads of KV head j), k
+    [1, 1, L, d], v [1, 1, L, dv], beta [G], M0 [1, 1, d, dv], z0 [1, 1, d]."""
+    dt = w.torch_dtype
+    dv = w.d_value
+    G = w.Hq // w.Hkv
+    q = torch.empty((1, G, w.L, w.d), dtype=dt)
+    for g in range(G):
+        q[0, g] = _normal((w.L, w.d), slice_seed(w.seed, "q", b, j * G + g), "cpu").to(dt)
+    kk = _normal((w.L, w.d), slice_seed(w.seed, "k", b, j), "cpu")
+    if w.key_std != 1.0:
+        kk = kk * w.key_std
+    if w.key_outlier_p > 0.0:
+        pick = _uniform((w.L,), slice_seed(w.seed, "outlier", b, j), "cpu")
+        kk = torch.where((pick < w.key_outlier_p)[:, None], kk * w.key_outlier_scale, kk)
+    k = kk.to(dt)[None, None]
+    v = _normal((w.L, dv), slice_seed(w.seed, "v", b, j), "cpu").to(dt)[None, None]
+    beta = _normal((w.Hq,), slice_seed(w.seed, "beta", 0, 0), "cpu")[j * G:(j + 1) * G]
+    M0 = torch.zeros((1, 1, w.d, dv), dtype=torch.float32)
+    z0 = torch.full((1, 1, w.d), w.z0, dtype=torch.float32)
+    return {n: to_f64(t) for n, t in dict(q=q, k=k, v=v, beta=beta, M0=M0, z0=z0).items()}
+
+
 def to_f64(t):
     """A tensor (any dtype, any device) as a float64 numpy array on the host."""
     return t.detach().to("cpu", torch.float32).double().numpy()

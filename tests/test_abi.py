@@ -76,6 +76,18 @@ def ws(lib, *args):
     return st, full.value, least.value
 
 
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def overlap_extra(units, dk, dv, e):
+    """Bytes the full size adds beyond the per-segment data when there are
+    several segments: the head slot (one snapshot per unit, M^T in the element
+    type and z in float, each aligned to 256 bytes) and the alignment slack
+    of the second region's five sub-buffers."""
+    return _al(units * dk * dv * e) + _al(units * dk * 4) + 5 * 256
+
+
 def test_workspace_sizes(lib):
     # Llama-3-8B-shaped, bf16, delta rule: seg_len >= d, so the scan runs in
     # affine form. Per segment and unit: snapshots (d*d bf16 + d floats),
@@ -84,17 +96,18 @@ def test_workspace_sizes(lib):
     assert st == 0
     d = 128
     per_seg = 32 * (d * d * 2 + d * 4 + d * 4 + d * d * 4 + d * d * 2)
-    assert full - least == 15 * per_seg
+    assert full - least == 15 * per_seg + overlap_extra(32, d, d, 2)
     assert least >= per_seg + 2 * 32 * (d * d + d) * 4
     # the linear rule needs no A_s
     st, full_lin, least_lin = ws(lib, 4, 32, 8, 32768, 128, 2048, 0, 1)
     assert full - full_lin == 16 * 32 * d * d * 2
     # direct scan (seg_len < d): snapshots only
     st, full_dir, least_dir = ws(lib, 16, 32, 32, 32768, 128, 64, 1, 1)
-    assert full_dir - least_dir == 511 * 512 * (d * d * 2 + d * 4)
+    assert full_dir - least_dir == 511 * 512 * (d * d * 2 + d * 4) + overlap_extra(512, d, d, 2)
     # from seg_len = d on, the affine form's matrices too
     st, full_aff, least_aff = ws(lib, 16, 32, 32, 32768, 128, 128, 1, 1)
-    assert full_aff - least_aff == 255 * 512 * (d * d * 2 + d * 4 + d * 4 + d * d * 4 + d * d * 2)
+    assert full_aff - least_aff == (255 * 512 * (d * d * 2 + d * 4 + d * 4 + d * d * 4 + d * d * 2)
+                                    + overlap_extra(512, d, d, 2))
     st, full32, _ = ws(lib, 4, 32, 8, 32768, 128, 2048, 1, 0)
     assert st == 0 and full32 > full
     # a ragged final segment counts as a segment
@@ -120,7 +133,8 @@ def test_workspace_sizes_with_separate_key_and_value_widths(lib):
         st, full, least = ws_kv(lib, 2, 8, 2, 1000, dk, dv, 300, 1, dt)
         assert st == 0
         per_seg = 2 * 2 * (dv * dk * e + dk * 4)
-        assert full - least == 3 * per_seg  # 4 segments, the last one ragged
+        # 4 segments, the last one ragged
+        assert full - least == 3 * per_seg + overlap_extra(4, dk, dv, e)
         assert least >= per_seg + 2 * 4 * (dk * dv + dk) * 4
 
 
