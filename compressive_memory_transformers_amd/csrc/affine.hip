@@ -72,14 +72,31 @@ __global__ __launch_bounds__(256) void colsum_kernel(AffineArgs a) {
 
 // ---- 2. z before each segment, and after the window ------------------------
 
+// The column sums do not depend on z, so their loads run kPrefetch segments
+// ahead of the running sum (a ring of registers, the loop unrolled so every
+// slot index is a constant); only the additions are sequential.
+constexpr int kPrefetch = 16;
+
 template <int D>
 __global__ __launch_bounds__(D) void prefix_kernel(AffineArgs a) {
   const int unit = blockIdx.x, tid = threadIdx.x;
+  const int n = a.s_count;
+  const float* cs = a.colsum + (int64_t)unit * n * D + tid;
+  float* sz = a.snapZ + (int64_t)unit * n * D + tid;
   float z = a.z_in[(int64_t)unit * D + tid];
-  for (int sl = 0; sl < a.s_count; ++sl) {
-    const int64_t idx = ((int64_t)unit * a.s_count + sl) * D + tid;
-    a.snapZ[idx] = z;
-    z += a.colsum[idx];
+  float ring[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) ring[u] = u < n ? cs[(int64_t)u * D] : 0.f;
+  for (int s0 = 0; s0 < n; s0 += kPrefetch) {
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int sl = s0 + u;
+      if (sl < n) {
+        sz[(int64_t)sl * D] = z;
+        z += ring[u];
+        if (sl + kPrefetch < n) ring[u] = cs[(int64_t)(sl + kPrefetch) * D];
+      }
+    }
   }
   a.z_out[(int64_t)unit * D + tid] = z;
 }
@@ -266,7 +283,10 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 // 2 x 2 (delta) or 2 x 1 (linear) block of 32 x 32 output tiles at row tiles
 // 2 (w / 4), + 1 and column tiles 2 (w % 4), + 1 of [Phi/den | V] (delta), or
 // column tile w % 4 of V (linear).
-template <int RULE>
+// COLSUM (linear rule): also the segment's column sums of Phi, from the staged
+// rows (the linear rule's products need no z, so the sums need no pass of
+// their own over K).
+template <int RULE, bool COLSUM = false>
 __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   constexpr int D = 128, NW = 8, TC = 64, NBUF = 3;
   constexpr bool DELTA = RULE == kRuleDelta;
@@ -323,6 +343,9 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < BC; ++c) acc[r][c] = zero16();
+  float csum[16];  // COLSUM: columns 16 st_g .. + 15 over this thread's token slot
+#pragma unroll
+  for (int e = 0; e < 16; ++e) csum[e] = 0.f;
 
   for (int ch = 0; ch < n_t; ++ch) {
     const int buf = ch % NBUF;
@@ -356,6 +379,7 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
           const float f = ok ? feature_map((float)kv[e]) : 0.f;
           ph[8 * hc + e] = f;
           dp += f * zc[8 * hc + e];
+          if constexpr (COLSUM) csum[8 * hc + e] += f;
         }
       }
       bf16* prow = Ph + st_t * D;
@@ -395,6 +419,20 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int c = 0; c < BC; ++c) mma32(acc[r][c], af[r], bf[c]);
+    }
+  }
+
+  if constexpr (COLSUM) {
+    // sum the 64 token slots of each column in LDS (the K ring is free now)
+    float* red = reinterpret_cast<float*>(&Kr[0][0]);  // [64 slots][128 columns]
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[st_t * D + 16 * st_g + e] = csum[e];
+    __syncthreads();
+    if (tid < D) {
+      float cs = 0.f;
+      for (int t = 0; t < TC; ++t) cs += red[t * D + tid];
+      a.colsum[((int64_t)unit * a.s_count + sl) * D + tid] = cs;
     }
   }
 
@@ -481,6 +519,62 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
   float* Mout = a.M_out + (int64_t)unit * D * D;
 #pragma unroll
   for (int r = 0; r < 16; ++r) Mout[(32 * w + acc_row(r, h)) * D + col0 + i] = acc[r];
+}
+
+// ---- the linear rule's chain as a prefix sum over segments -----------------
+//
+// Under the linear rule M_s = M_{s-1} + B_s: the state before segment s is
+// M_0 + sum_{s'<s} B_s', a running sum with no product in it ("Infini-
+// Attention" (AI Wiki), "How does the compressive memory work?", the additive
+// variant). Every entry of M is its own sum, so the work splits into 32 x 32
+// blocks of M, one workgroup per (unit, block); each walks its unit's
+// segments with the B_s loads kPrefetch segments ahead of the additions. The
+// snapshot (M^T in the element type) goes through LDS, transposed, so both
+// the B_s reads and the snapshot writes are whole rows. Same float additions
+// in the same order as the step-by-step chain, so the same results.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void linear_prefix_kernel(AffineArgs a) {
+  constexpr int NB = D / 32;  // blocks per side
+  constexpr int TS = 32 + 4;  // LDS row stride of the transposed block
+  __shared__ __align__(16) T Mt[2][32 * TS];
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x / (NB * NB), blk = blockIdx.x % (NB * NB);
+  const int r0 = 32 * (blk / NB), c0 = 32 * (blk % NB);
+  // float4 of B_s / M: row r0 + rr, columns c0 + 4 cq .. + 3
+  const int rr = tid >> 3, cq = tid & 7;
+  // snapshot piece: M^T row c0 + tr, rows r0 + 4 tq .. + 3 of M
+  const int tr = tid >> 3, tq = tid & 7;
+  const int n = a.s_count;
+  const int64_t moff = (int64_t)(r0 + rr) * D + c0 + 4 * cq;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(a.M_in + (int64_t)unit * D * D + moff);
+  const float* Bu = a.Bmat + (int64_t)unit * n * D * D + moff;
+  T* snap = static_cast<T*>(a.snapM) + (int64_t)unit * n * D * D +
+            (int64_t)(c0 + tr) * D + r0 + 4 * tq;
+  f32x4 ring[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+    if (u < n) ring[u] = *reinterpret_cast<const f32x4*>(Bu + (int64_t)u * D * D);
+  for (int s0 = 0; s0 < n; s0 += kPrefetch) {
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int sl = s0 + u;
+      if (sl < n) {
+        T* buf = Mt[u & 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf[(4 * cq + j) * TS + rr] = from_f32<T>(acc[j]);
+        __syncthreads();
+        vec4_t<T> y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = buf[tr * TS + 4 * tq + j];
+        store4<T>(snap + (int64_t)sl * D * D, y);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += ring[u][j];
+        if (sl + kPrefetch < n)
+          ring[u] = *reinterpret_cast<const f32x4*>(Bu + (int64_t)(sl + kPrefetch) * D * D);
+      }
+    }
+  }
+  *reinterpret_cast<f32x4*>(a.M_out + (int64_t)unit * D * D + moff) = acc;
 }
 
 // ---- the same step, bf16, d = 128, delta rule: one workgroup per unit ------
@@ -576,16 +670,39 @@ __global__ __launch_bounds__(1024, 4) void chain_unit_kernel(AffineArgs a) {
   for (int r = 0; r < 16; ++r) Mout[(r0 + acc_row(r, h)) * D + c0 + i] = acc[r];
 }
 
+// A_s and B_s (B_s only, linear) of every (unit, segment) of the window.
 template <typename T, int D, int RULE>
-hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
+hipError_t launch_products_t(const AffineArgs& a, hipStream_t stream) {
   const unsigned segs = (unsigned)(a.units * a.s_count);
-  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
   if constexpr (sizeof(T) == 2 && D == 128)
     hipLaunchKernelGGL((affine_dma_kernel<RULE>), dim3(segs), dim3(512), 0, stream, a);
   else
     hipLaunchKernelGGL((affine_kernel<T, D, RULE>), dim3(segs),
                        dim3(AffineShape<D, RULE>::NW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int RULE>
+hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
+  const unsigned segs = (unsigned)(a.units * a.s_count);
+  if constexpr (sizeof(T) == 2 && D == 128 && RULE == kRuleLinear) {
+    // the column sums come out of the products' pass over K
+    hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear, true>), dim3(segs), dim3(512), 0, stream,
+                       a);
+    hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
+    const hipError_t e = launch_products_t<T, D, RULE>(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (RULE == kRuleLinear) {
+    if (!a.reverse) {
+      hipLaunchKernelGGL((linear_prefix_kernel<T, D>), dim3((unsigned)(a.units * (D / 32) * (D / 32))),
+                         dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (sizeof(T) == 2 && D == 128 && RULE == kRuleDelta) {
     // one workgroup per unit once the units alone fill the CUs; with fewer
     // units the slab kernel's four workgroups per unit keep more CUs busy
