@@ -58,6 +58,14 @@ def attn_kernel_flops(w):
     return w.B * w.Hq * total
 
 
+def uses_fused_plan(w):
+    """Whether the library runs this workload's forward as the one-pass fused
+    kernel (the condition the library's plan applies: bf16, d_key = d_value
+    in {64, 128}, as many query as KV heads, segments no longer than d)."""
+    return (w.dtype == "bf16" and w.d == w.d_value and w.d in (64, 128) and w.Hq == w.Hkv
+            and min(w.seg_len, w.L) <= w.d)
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for path in paths:
@@ -542,14 +550,21 @@ def main():
     flops = synth.flops(w, rule)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    a_flops = attn_kernel_flops(w)
+    if uses_fused_plan(w):
+        # one kernel does the whole forward: its work is the call's
+        a_flops = synth.flops(w, rule)
+        a_bytes = synth.hbm_bytes(w)
+        kname = "fused_kernel (the whole forward in one pass, state on chip)"
+    else:
+        a_flops = attn_kernel_flops(w)
+        a_bytes = attn_kernel_bytes(w)
+        kname = ("attn_kernel (local causal attention + retrieval + gate)" if w.d_value == w.d
+                 else f"attn_kernel, d_key {w.d} != d_value {w.d_value} (attention + retrieval + "
+                      "gate)")
     a_tflops = a_flops / (attn_ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
     # the bound is the kernel's: matrix cores above the ridge point
     # (peak FLOP/s / peak bytes/s), HBM below it
-    a_bytes = attn_kernel_bytes(w)
-    kname = ("attn_kernel (local causal attention + retrieval + gate)" if w.d_value == w.d else
-             f"attn_kernel, d_key {w.d} != d_value {w.d_value} (attention + retrieval + gate)")
     if a_flops / a_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         roofline = {"kernel": kname,
                     "bound": "mfma", "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s",

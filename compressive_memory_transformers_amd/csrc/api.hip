@@ -362,6 +362,36 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   const int64_t tiles_per_seg = B * Hq * n_qt;  // <= INT32_MAX, checked above
   const int64_t max_launch = INT32_MAX / tiles_per_seg;  // segments per attention launch
 
+  // Short segments (bf16, d in {64, 128}, Hq == Hkv, segments no longer than
+  // d): the whole call in one pass, one workgroup per (batch, head) with the
+  // state resident (fused.hip); the workspace is not used.
+  if (dv == d && infini::fused_supported(dtype, (int)d, eff, Hq, Hkv)) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int slot = 0; slot < 2 && slot < n_events; ++slot)
+      if (hipEventRecord(static_cast<hipEvent_t>(events[slot]), s) != hipSuccess)
+        return INFINI_ERR_HIP;
+    infini::FusedArgs fa;
+    fa.q = q;
+    fa.k = k;
+    fa.v = v;
+    fa.beta = beta;
+    fa.M_in = M0;
+    fa.z_in = z0;
+    fa.M_out = M_final;
+    fa.z_out = z_final;
+    fa.out = out;
+    fa.lse = lse;
+    fa.L = L;
+    fa.seg_len = (int32_t)eff;
+    fa.H = (int32_t)Hq;
+    fa.units = (int32_t)p.units;
+    fa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+    if (infini::launch_fused((int)d, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
+    if (n_events > 2 && hipEventRecord(static_cast<hipEvent_t>(events[2]), s) != hipSuccess)
+      return INFINI_ERR_HIP;
+    return INFINI_OK;
+  }
+
   // Window plan. Serial: one region of W segments, each window's scan then
   // its attention on the caller's stream. Overlapped (the call has several
   // segments and two regions plus the head slot fit): segment 0's attention

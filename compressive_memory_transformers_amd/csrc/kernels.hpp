@@ -75,6 +75,29 @@ struct AttnArgs {
   float scale_log2;    // log2(e) / sqrt(d)
 };
 
+// The whole forward in one pass (fused.hip) for bf16, d in {64, 128},
+// Hq == Hkv and segments no longer than d: one workgroup per (batch, head)
+// walks the segments with the state resident on the chip.
+struct FusedArgs {
+  const void* q;       // [B][H][L][d]
+  const void* k;
+  const void* v;
+  const float* beta;   // [H]
+  const float* M_in;   // [B][H][d][d]
+  const float* z_in;   // [B][H][d]
+  float* M_out;        // may be M_in
+  float* z_out;        // may be z_in
+  void* out;           // [B][H][L][d]
+  float* lse;          // [B][H][L] or null (as AttnArgs::lse)
+  int64_t L;
+  int32_t seg_len;     // <= d
+  int32_t H;
+  int32_t units;       // B * H
+  float scale_log2;    // log2(e) / sqrt(d)
+};
+bool fused_supported(int dtype, int d, int64_t seg_len, int64_t Hq, int64_t Hkv);
+hipError_t launch_fused(int d, int rule, const FusedArgs& a, hipStream_t stream);
+
 // One streaming decode step (decode.hip): the token at row pos of its
 // segment, for every (batch, head).
 constexpr int kDecodeMaxGroup = 16;   // query heads per KV head
