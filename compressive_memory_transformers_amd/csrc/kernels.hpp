@@ -102,21 +102,22 @@ hipError_t launch_fused(int d, int rule, const FusedArgs& a, hipStream_t stream)
 // segment, for every (batch, head).
 constexpr int kDecodeMaxGroup = 16;   // query heads per KV head
 constexpr int kDecodeMaxChunks = 256;  // 64-row cache chunks (seg_len <= 16384)
+// dk: the key width, dv: the value width (both d for launch_decode).
 struct DecodeArgs {
-  const void* q;       // [B][Hq][d]
-  const void* k;       // [B][Hkv][d]
-  const void* v;       // [B][Hkv][d]
+  const void* q;       // [B][Hq][dk]
+  const void* k;       // [B][Hkv][dk]
+  const void* v;       // [B][Hkv][dv]
   const float* beta;   // [Hq]
-  void* k_cache;       // [B][Hkv][seg_len][d]; row pos is written
-  void* v_cache;       // [B][Hkv][seg_len][d]
-  const float* M;      // [B][Hkv][d][d]: the state before the segment
-  const float* z;      // [B][Hkv][d]
-  void* out;           // [B][Hq][d]
-  float* part;         // [B*Hkv][n_chunks][G][2 + d]: chunk max, weight sum, value sums
+  void* k_cache;       // [B][Hkv][seg_len][dk]; row pos is written
+  void* v_cache;       // [B][Hkv][seg_len][dv]; row pos is written
+  const float* M;      // [B][Hkv][dk][dv]: the state before the segment
+  const float* z;      // [B][Hkv][dk]
+  void* out;           // [B][Hq][dv]
+  float* part;         // [B*Hkv][n_chunks][G][2 + dv]: chunk max, weight sum, value sums
   int64_t seg_len;
   int32_t B, Hq, Hkv, G;
   int32_t pos, n_chunks;  // n_chunks = ceil((pos + 1) / 64)
-  float scale_log2;       // log2(e) / sqrt(d)
+  float scale_log2;       // log2(e) / sqrt(dk)
 };
 
 // ---- backward pass (bwd.hip) ------------------------------------------------

@@ -60,6 +60,24 @@ def test_kv_widths_match_the_oracle(lib, pair, dt, rule):
         assert eo <= tol and eM <= tol and ez <= tol, (eo, eM, ez)
 
 
+@pytest.mark.parametrize("pair", [(64, 128), (128, 64)], ids=["dk64dv128", "dk128dv64"])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_kv_long_ragged_segments(lib, pair, rule):
+    """Segments of 320 tokens (several query and key tiles each) with a
+    ragged last one of 160, every (batch, KV head) unit."""
+    dk, dv = pair
+    B, Hq, Hkv, L, N = 2, 4, 2, 800, 320
+    _say(f"long segments dk={dk} dv={dv} {rule} B{B} Hq{Hq} Hkv{Hkv} L{L} N{N}")
+    inp = random_inputs(B, Hq, Hkv, L, dk, torch.bfloat16, DEV, seed=5 * dk + dv, m0_scale=0.2,
+                        dv=dv)
+    res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"], N, rule)
+    torch.cuda.synchronize()
+    eo, eM, ez = compare_units(inp, res, N, rule, all_units(B, Hkv))
+    tol = tolerance(torch.bfloat16)
+    _say(f"errors out={eo:.3e} M={eM:.3e} z={ez:.3e} (tol {tol:g})")
+    assert eo <= tol and eM <= tol and ez <= tol, (eo, eM, ez)
+
+
 @pytest.mark.parametrize("pair", [(64, 128), (128, 32)], ids=["dk64dv128", "dk128dv32"])
 def test_kv_windows_and_in_place_carry(lib, pair):
     """The minimum workspace (one segment per window) gives the bits of the
@@ -103,6 +121,7 @@ DECODE_KV = [
     # B, Hq, Hkv, L, d_key, d_value, seg_len, dtype   (folds by the direct scan)
     (1, 4, 2, 90, 64, 128, 40, torch.bfloat16),
     (2, 2, 1, 70, 128, 32, 32, torch.float32),
+    (1, 4, 2, 300, 64, 128, 130, torch.bfloat16),  # three 64-row cache chunks per segment
 ]
 
 
@@ -153,3 +172,44 @@ def test_decoded_stream_with_kv_widths_matches_the_forward(lib, case, rule):
         eM = oracle.slice_errors(synth.to_f64(Ms), M_ref)
         ez = oracle.slice_errors(synth.to_f64(zs), z_ref, elementwise=True)
         assert eM <= tol and ez <= tol, (nn, eM, ez)
+
+
+@pytest.mark.parametrize("pos", [600, 639])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_decode_kv_step_with_many_group_chunks(lib, pos, rule):
+    """One infini_attn_decode_step_kv step with 16 query heads per KV head and
+    640-row segments (G * n_chunks = 160 partial rows per unit), d_key 64,
+    d_value 128, rows 0..pos-1 of the caches filled, against oracle.decode_step;
+    at pos 639 the segment is folded into the state."""
+    import oracle
+    import synth
+    B, Hq, Hkv, dk, dv, N = 2, 16, 1, 64, 128, 640
+    _say(f"decode_kv step G16 N{N} pos {pos} {rule}")
+    g = torch.Generator(device="cpu").manual_seed(77 + pos)
+    mk = lambda *s: torch.randn(*s, generator=g, dtype=torch.float32)
+    q, k = (mk(B, H, dk).to(torch.bfloat16) for H in (Hq, Hkv))
+    v = mk(B, Hkv, dv).to(torch.bfloat16)
+    kc = mk(B, Hkv, N, dk).to(torch.bfloat16)
+    vc = mk(B, Hkv, N, dv).to(torch.bfloat16)
+    beta = mk(Hq)
+    M = 0.05 * mk(B, Hkv, dk, dv)
+    z = 20.0 + torch.rand(B, Hkv, dk, generator=g)
+    f64 = lambda t: t.to(torch.float64).numpy()
+    ro, rM, rz, _, _ = oracle.decode_step(f64(q), f64(k), f64(v), f64(beta), f64(M), f64(z),
+                                          f64(kc), f64(vc), pos, N, rule)
+    dq, dk_, dv_, dkc, dvc, dbeta, dM, dz = (t.to(DEV).contiguous()
+                                             for t in (q, k, v, kc, vc, beta, M, z))
+    out = lib.decode_step(dq, dk_, dv_, dbeta, dkc, dvc, dM, dz, pos, rule)
+    torch.cuda.synchronize()
+    assert out.shape == (B, Hq, dv)
+    eo = oracle.slice_errors(synth.to_f64(out)[:, :, None], ro[:, :, None])
+    _say(f"out error {eo:.3e}")
+    assert eo <= 2e-2
+    assert torch.equal(dvc[:, :, pos].cpu(), v) and torch.equal(dvc[:, :, :pos].cpu(), vc[:, :, :pos])
+    if pos == N - 1:
+        eM = oracle.slice_errors(synth.to_f64(dM), rM)
+        ez = oracle.slice_errors(synth.to_f64(dz), rz, elementwise=True)
+        _say(f"fold errors M {eM:.3e} z {ez:.3e}")
+        assert eM <= 2e-2 and ez <= 2e-2
+    else:
+        assert torch.equal(dM.cpu(), M) and torch.equal(dz.cpu(), z)
