@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     decode_step,
     decode_workspace_size,
     forward,
+    forward_noalloc,
     forward_train,
     load_library,
     status_string,

@@ -28,6 +28,8 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
     "infini_attn_forward": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_forward_noalloc": (
+        _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p]),
     "infini_attn_workspace_size_kv": (
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size)]),
     "infini_attn_forward_kv": (
@@ -223,6 +225,49 @@ def _forward_call(lib, B, Hq, Hkv, L, d, dv, seg_len, rule, q, k, v, beta, M0, z
         name = "infini_attn_forward"
     if st != 0:
         raise InfiniAttnError(st, name)
+    return out, M_final, z_final
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # INFINI_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(q, k, v, beta, M0, z0, seg_len, rule, *, out, M_final, z_final,
+                    stream=None):
+    """infini_attn_forward_noalloc: the forward with the library's per-GPU
+    scratch array as its workspace. q, k, v share one width d here. Every
+    output buffer is the caller's (nothing is allocated, here or in the
+    library); M_final may be M0 and z_final may be z0. Calls that can run at
+    the same time on one GPU race on the scratch array."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != (B, Hkv, L, d):
+        raise ValueError("k and v must be [B,Hkv,L,d] with q's d")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+        raise ValueError("beta, M0 or z0 has the wrong shape")
+    if out.shape != (B, Hq, L, d) or M_final.shape != M0.shape or z_final.shape != z0.shape:
+        raise ValueError("out, M_final or z_final has the wrong shape")
+    if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or \
+            out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share one dtype, float32 or bfloat16")
+    for t in (beta, M0, z0, M_final, z_final):
+        if t.dtype != torch.float32:
+            raise TypeError("beta, M0, z0, M_final and z_final must be float32")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}")
+    dev = q.device
+    for t in (q, k, v, beta, M0, z0, out, M_final, z_final):
+        if t.device != dev or dev.type != "cuda" or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on one GPU")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.infini_attn_forward_noalloc(
+            B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[q.dtype],
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+            _ptr(out), _ptr(M_final), _ptr(z_final), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise InfiniAttnError(st, "infini_attn_forward_noalloc")
     return out, M_final, z_final
 
 

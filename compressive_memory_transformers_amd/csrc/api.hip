@@ -305,7 +305,8 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
                              const void* k, const void* v, const float* beta, const float* M0,
                              const float* z0, void* out, float* M_final, float* z_final,
                              float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* events, int32_t n_events, int64_t dv_in = 0) {
+                             void* const* events, int32_t n_events, int64_t dv_in = 0,
+                             bool allow_overlap = true) {
   const int64_t dv = dv_in > 0 ? dv_in : d;
   Plan p;
   infini_status_t st = check_sizes_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, dtype, &p);
@@ -421,7 +422,7 @@ infini_status_t forward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int6
   // segments), and on small calls the extra launches and event waits cost
   // more than they hide; those run the serial plan.
   const bool worth_overlap = !p.affine && (double)B * Hq * L * d >= (double)(1 << 26);
-  if (p.S >= 2 && worth_overlap && workspace_bytes >= workspace_full(p)) {
+  if (allow_overlap && p.S >= 2 && worth_overlap && workspace_bytes >= workspace_full(p)) {
     int64_t c0 = p.S / 4 > 0 ? p.S / 4 : 1;
     int64_t c1 = p.S - c0;
     if (c0 > max_launch) c0 = max_launch;
@@ -610,6 +611,61 @@ infini_status_t infini_attn_forward_timed(int64_t B, int64_t Hq, int64_t Hkv, in
   return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
                       M_final, z_final, nullptr, workspace, workspace_bytes, stream, events,
                       n_events);
+}
+
+}  // extern "C"
+
+// ---- the forward without a workspace ------------------------------------------
+//
+// For callers that cannot allocate: the workspace of infini_attn_forward is
+// this array, one copy per GPU the library runs on, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// the kernels get the address hipGetSymbolAddress returns for the current
+// device (looked up on the first call on that device and kept), never the
+// name. Nothing in it needs to start at zero: every workspace byte a forward
+// reads was written earlier in the same call.
+static_assert(INFINI_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[INFINI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; null until looked up
+
+// The current device's address of `scratch`, or null if the runtime cannot
+// give it (then the next call asks again).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_forward_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                            int64_t d, int64_t seg_len, int32_t rule,
+                                            int32_t dtype, const void* q, const void* k,
+                                            const void* v, const float* beta, const float* M0,
+                                            const float* z0, void* out, float* M_final,
+                                            float* z_final, void* stream) {
+  Plan p;
+  const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  // the least workspace the call needs must fit the array
+  if (p.fixed + p.per_seg > (size_t)INFINI_NOALLOC_SCRATCH_BYTES) return INFINI_ERR_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return INFINI_ERR_HIP;
+  // the serial plan only: no auxiliary stream, everything on `stream`
+  return forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
+                      M_final, z_final, nullptr, ws, INFINI_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr, 0, 0, false);
 }
 
 // ---- streaming decode --------------------------------------------------------

@@ -129,6 +129,37 @@ infini_status_t infini_attn_forward(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory or hold a workspace (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): infini_attn_forward with its workspace replaced by a scratch
+ * array of INFINI_NOALLOC_SCRATCH_BYTES (64 MiB) that the library keeps in
+ * each GPU's memory, a static device array present from the library's first
+ * use of that GPU until the process ends.
+ *   Arguments, layouts, overlaps and results as infini_attn_forward, without
+ *   the workspace; the output is the same bit for bit. It always runs on
+ *   `stream` alone (the serial plan, no auxiliary stream) and calls no
+ *   hipMalloc, hipFree or other allocating routine. The first call on a
+ *   device looks up the array's address (hipGetSymbolAddress) with that
+ *   device current and keeps it; make that first call outside graph capture.
+ *   Errors as infini_attn_forward, and INFINI_ERR_WORKSPACE when the call's
+ *   minimum workspace (min_bytes of infini_attn_workspace_size) exceeds
+ *   INFINI_NOALLOC_SCRATCH_BYTES (a full-size workspace beyond it only means
+ *   more windows); INFINI_ERR_HIP when the array's address cannot be had.
+ *   Concurrency: all calls on one GPU share that GPU's one array, which keeps
+ *   the last call's contents (nothing in it needs to start at zero). Calls on
+ *   one stream run one after another; calls that can run at the same time on
+ *   one GPU (different streams, graphs replayed concurrently) race on the
+ *   array and give wrong results.
+ */
+#define INFINI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+infini_status_t infini_attn_forward_noalloc(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
+    int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final, void* stream);
+
+/*
  * The forward with a key width different from the value width
  * ("Infini-Attention" (AI Wiki), "How does the compressive memory work?": the
  * memory M maps d_key-dimensional features to d_value-dimensional values).

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
         "infini_attn_decode_workspace_size", "infini_attn_decode_step_kv",
         "infini_attn_decode_workspace_size_kv",
         "infini_attn_forward", "infini_attn_forward_kv", "infini_attn_forward_kv_timed",
-        "infini_attn_forward_timed",
+        "infini_attn_forward_noalloc", "infini_attn_forward_timed",
         "infini_attn_forward_train", "infini_attn_status_string", "infini_attn_version",
         "infini_attn_workspace_size", "infini_attn_workspace_size_kv"])
 
@@ -291,6 +291,26 @@ def test_forward_rejects_small_workspace(lib):
     _, full, least = ws(lib, 2, 4, 2, 64, 32, 16, 1, 1)
     assert call(lib, SHAPE, bufs, workspace_bytes=least - 1) == 4
     assert call(lib, SHAPE, bufs, workspace_bytes=0) == 4
+
+
+def test_forward_noalloc_rejects_on_the_host(lib):
+    """The scratch-array forward checks sizes like infini_attn_forward and
+    refuses a call whose minimum workspace exceeds the array (64 MiB) before
+    it looks up the array or touches a device."""
+    def noalloc(shape):
+        B, Hq, Hkv, L, d, N, rule, dt = shape
+        bufs = FakeBuffers(B, Hq, Hkv, L, d, 2)
+        return lib.infini_attn_forward_noalloc(
+            B, Hq, Hkv, L, d, N, rule, dt,
+            *[ctypes.c_void_p(bufs.addr[n]) for n in ("q", "k", "v", "beta", "M0", "z0", "out",
+                                                       "M_final", "z_final")], None)
+    assert noalloc((2, 3, 2, 64, 32, 16, 1, 1)) == 1    # Hq % Hkv
+    assert noalloc((2, 4, 2, 64, 40, 16, 1, 1)) == 2    # d unsupported
+    assert noalloc((2, 4, 2, 64, 32, 16, 1, 9)) == 1    # bad dtype
+    big = (64, 64, 64, 64, 128, 16, 1, 1)                # 4096 units: two states alone > 64 MiB
+    _, _, least = ws(lib, *big)
+    assert least > 64 << 20
+    assert noalloc(big) == 4
 
 
 def test_binding_validates_before_the_library():
