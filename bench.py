@@ -30,9 +30,11 @@ METRIC = "Infini-attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), 1×MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# the sources that decide the attention kernel's memory traffic
-ATTN_SOURCES = [os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc", f)
-                for f in ("attn.hip", "lds_tile.hpp")]
+# the sources that decide the dominant kernel's memory traffic: the attention
+# kernel of the split plan, or the one-pass fused kernel
+_CSRC = os.path.join(ROOT, "compressive_memory_transformers_amd", "csrc")
+ATTN_SOURCES = [os.path.join(_CSRC, f) for f in ("attn.hip", "lds_tile.hpp", "common.hpp")]
+FUSED_SOURCES = [os.path.join(_CSRC, f) for f in ("fused.hip", "lds_tile.hpp", "common.hpp")]
 
 
 def attn_kernel_bytes(w):
@@ -74,15 +76,19 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention launch from committed rocprofv3 counters, or
-    None when there are none for this workload or the kernel changed since."""
+def measured_traffic(w, rule):
+    """HBM bytes per launch of the workload's dominant kernel from committed
+    rocprofv3 counters, or None when there are none for this workload and
+    configuration or the kernel's sources changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f).get(w.name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCES):
+    srcs = FUSED_SOURCES if uses_fused_plan(w) else ATTN_SOURCES
+    if (not rec or rec.get("hashed_sources") != [os.path.relpath(p, ROOT) for p in srcs]
+            or rec.get("source_sha256_16") != source_hash(srcs)
+            or rec.get("seg_len") != w.seg_len or rec.get("rule") != rule):
         return None
     return rec.get("bytes_per_launch")
 
@@ -432,6 +438,8 @@ def main():
     ap.add_argument("--cold", type=int, default=5, metavar="N",
                     help="also time N steps each after flushing the caches with a 512 MiB "
                          "device copy outside the timed events (0: skip)")
+    ap.add_argument("--sclk-samples", type=int, default=3, metavar="N",
+                    help="sample the shader clock N times while steps run (0: skip)")
     ap.add_argument("--cpu-procs", type=int, default=16,
                     help="worker processes of the CPU oracle (at most the host's CPUs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -537,7 +545,7 @@ def main():
 
     # the shader clock, sampled while steps keep the GPU busy
     sclk = []
-    for _ in range(3):
+    for _ in range(args.sclk_samples):
         for _ in range(max(8, int(200 / max(ms, 1e-3)))):
             step()
         v_ = gpu_sclk_mhz()
@@ -562,7 +570,7 @@ def main():
                  else f"attn_kernel, d_key {w.d} != d_value {w.d_value} (attention + retrieval + "
                       "gate)")
     a_tflops = a_flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w, rule)
     # the bound is the kernel's: matrix cores above the ridge point
     # (peak FLOP/s / peak bytes/s), HBM below it
     if a_flops / a_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
