@@ -17,34 +17,41 @@ from oracle import block as blk
 RULES = ["linear", "delta"]
 
 
-def perm_weights(rng, Hq, Hkv, d, scales=(0.5, 2.0, -1.5, 3.0)):
-    """d_model = Hq d; W_q a scaled permutation, W_k / W_v scaled selections
-    of distinct input features, W_o a scaled permutation."""
-    dm = Hq * d
+def perm_weights(rng, Hq, Hkv, d, dv=None, scales=(0.5, 2.0, -1.5, 3.0)):
+    """d_model = Hq max(d, dv); W_q and W_k / W_v scaled selections of
+    distinct input features (W_q a permutation when d_model = Hq d), W_o a
+    scaled selection of distinct gated features. Query and key heads are d
+    wide, value heads dv wide."""
+    dv = d if dv is None else dv
+    dm = Hq * max(d, dv)
     a_q, a_k, a_v, a_o = scales
-    perm_q = rng.permutation(dm)
+    perm_q = rng.permutation(dm)[: Hq * d]
     sel_k = rng.permutation(dm)[: Hkv * d]
-    sel_v = rng.permutation(dm)[: Hkv * d]
-    perm_o = rng.permutation(dm)
-    w = np.zeros(((Hq + 2 * Hkv) * d, dm))
+    sel_v = rng.permutation(dm)[: Hkv * dv]
+    perm_o = rng.permutation(Hq * dv)
+    w = np.zeros(((Hq + Hkv) * d + Hkv * dv, dm))
     for r in range(Hq * d):
         w[r, perm_q[r]] = a_q
     for r in range(Hkv * d):
         w[Hq * d + r, sel_k[r]] = a_k
+    for r in range(Hkv * dv):
         w[(Hq + Hkv) * d + r, sel_v[r]] = a_v
-    w_o = np.zeros((dm, dm))
-    for i in range(dm):
+    # output feature i reads gated feature perm_o[i] for i < Hq dv, nothing after
+    w_o = np.zeros((dm, Hq * dv))
+    for i in range(min(dm, Hq * dv)):
         w_o[i, perm_o[i]] = a_o
     return w, w_o, (perm_q, sel_k, sel_v, perm_o)
 
 
-def expected_by_index(x, beta, M0, z0, N, rule, Hq, Hkv, d, idx, scales=(0.5, 2.0, -1.5, 3.0)):
+def expected_by_index(x, beta, M0, z0, N, rule, Hq, Hkv, d, idx, dv=None,
+                      scales=(0.5, 2.0, -1.5, 3.0)):
+    dv = d if dv is None else dv
     perm_q, sel_k, sel_v, perm_o = idx
     a_q, a_k, a_v, a_o = scales
     B, L, dm = x.shape
     q = np.empty((B, Hq, L, d))
     k = np.empty((B, Hkv, L, d))
-    v = np.empty((B, Hkv, L, d))
+    v = np.empty((B, Hkv, L, dv))
     for b in range(B):
         for t in range(L):
             for h in range(Hq):
@@ -53,40 +60,44 @@ def expected_by_index(x, beta, M0, z0, N, rule, Hq, Hkv, d, idx, scales=(0.5, 2.
             for h in range(Hkv):
                 for j in range(d):
                     k[b, h, t, j] = a_k * x[b, t, sel_k[h * d + j]]
-                    v[b, h, t, j] = a_v * x[b, t, sel_v[h * d + j]]
+                for j in range(dv):
+                    v[b, h, t, j] = a_v * x[b, t, sel_v[h * dv + j]]
     out, M, z = oracle.forward(q, k, v, beta, M0, z0, N, rule)
-    y = np.empty((B, L, dm))
+    y = np.zeros((B, L, dm))
     for b in range(B):
         for t in range(L):
-            for i in range(dm):
+            for i in range(min(dm, Hq * dv)):
                 f = perm_o[i]
-                y[b, t, i] = a_o * out[b, f // d, t, f % d]
+                y[b, t, i] = a_o * out[b, f // dv, t, f % dv]
     return y, M, z
 
 
-def make(rng, B, L, Hq, Hkv, d, m0=0.3):
-    x = rng.standard_normal((B, L, Hq * d))
+def make(rng, B, L, Hq, Hkv, d, m0=0.3, dv=None):
+    dv = d if dv is None else dv
+    x = rng.standard_normal((B, L, Hq * max(d, dv)))
     beta = rng.standard_normal(Hq)
-    M0 = m0 * rng.standard_normal((B, Hkv, d, d))
+    M0 = m0 * rng.standard_normal((B, Hkv, d, dv))
     z0 = 0.5 + rng.random((B, Hkv, d))
     return x, beta, M0, z0
 
 
-CASES = [(1, 7, 2, 1, 3, 3), (2, 6, 4, 2, 2, 4)]  # B, L, Hq, Hkv, d, seg_len
+# B, L, Hq, Hkv, d (key width), seg_len, value width
+CASES = [(1, 7, 2, 1, 3, 3, 3), (2, 6, 4, 2, 2, 4, 2), (2, 7, 4, 2, 2, 3, 3),
+         (1, 8, 2, 2, 4, 3, 2)]
 
 
 def check_perm(rule, case, seed=0):
-    B, L, Hq, Hkv, d, N = case
+    B, L, Hq, Hkv, d, N, dv = case
     rng = np.random.default_rng(seed)
-    x, beta, M0, z0 = make(rng, B, L, Hq, Hkv, d)
-    w, w_o, idx = perm_weights(rng, Hq, Hkv, d)
-    y, M, z = blk.block_forward(x, w, w_o, beta, M0, z0, N, rule, Hq, Hkv, d)
-    ye, Me, ze = expected_by_index(x, beta, M0, z0, N, rule, Hq, Hkv, d, idx)
+    x, beta, M0, z0 = make(rng, B, L, Hq, Hkv, d, dv=dv)
+    w, w_o, idx = perm_weights(rng, Hq, Hkv, d, dv)
+    y, M, z = blk.block_forward(x, w, w_o, beta, M0, z0, N, rule, Hq, Hkv, d, dv)
+    ye, Me, ze = expected_by_index(x, beta, M0, z0, N, rule, Hq, Hkv, d, idx, dv)
     return max(np.abs(y - ye).max(), np.abs(M - Me).max(), np.abs(z - ze).max())
 
 
 @pytest.mark.parametrize("rule", RULES)
-@pytest.mark.parametrize("case", CASES, ids=["B1L7Hq2Hkv1", "B2L6Hq4Hkv2"])
+@pytest.mark.parametrize("case", CASES, ids=["B1L7Hq2Hkv1", "B2L6Hq4Hkv2", "dk2dv3", "dk4dv2"])
 def test_permutation_weights_match_index_arithmetic(rule, case):
     assert check_perm(rule, case) < 1e-12
 
@@ -133,12 +144,24 @@ def test_outputs_are_homogeneous_in_the_value_weights(rule):
 
 # ---- planted mistakes: each must fail the permutation check ----------------
 
-def _kv_swapped(x, w_qkv, Hq, Hkv, d, _f=blk.project_qkv):
-    q, k, v = _f(x, w_qkv, Hq, Hkv, d)
+def _kv_swapped(x, w_qkv, Hq, Hkv, d, dv=None, _f=blk.project_qkv):
+    q, k, v = _f(x, w_qkv, Hq, Hkv, d, dv)
     return q, v, k
 
 
-def _split_without_transpose(x, w_qkv, Hq, Hkv, d):
+def _value_heads_key_wide(x, w_qkv, Hq, Hkv, d, dv=None):
+    # value heads cut at the key width: the plausible slip with two widths
+    B, L, _ = x.shape
+    y = np.asarray(x) @ np.asarray(w_qkv).T
+    heads = lambda cols, H, wd: y[..., cols].reshape(B, L, H, wd).transpose(0, 2, 1, 3)
+    q = heads(slice(0, Hq * d), Hq, d)
+    k = heads(slice(Hq * d, (Hq + Hkv) * d), Hkv, d)
+    n = y.shape[-1] - (Hq + Hkv) * d
+    v = y[..., (Hq + Hkv) * d:].reshape(B, L, n // Hkv, Hkv).transpose(0, 3, 1, 2)
+    return q, k, v
+
+
+def _split_without_transpose(x, w_qkv, Hq, Hkv, d, dv=None):
     B, L, _ = x.shape
     y = np.asarray(x) @ np.asarray(w_qkv).T
     q = y[..., : Hq * d].reshape(B, Hq, L, d)
@@ -162,6 +185,7 @@ MUTANTS = {
     "head split without the transpose": ("project_qkv", _split_without_transpose),
     "output weight not transposed": ("project_out", _out_weight_not_transposed),
     "heads concatenated feature-major": ("project_out", _concat_feature_major),
+    "value heads split at the wrong width": ("project_qkv", _value_heads_key_wide),
 }
 
 
@@ -169,4 +193,5 @@ MUTANTS = {
 def test_planted_mistake_fails_the_permutation_check(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(blk, attr, fn)
-    assert check_perm("delta", CASES[1]) > 1e-3, name
+    case = CASES[2] if name == "value heads split at the wrong width" else CASES[1]
+    assert check_perm("delta", case) > 1e-3, name
