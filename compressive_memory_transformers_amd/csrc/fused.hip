@@ -18,18 +18,21 @@
 // transpose sits in LDS for the matrix operands; z lives in LDS. The other
 // half of the waves run the local attention, retrieval and gate of one
 // 32-row query block each. Per segment:
-//   1. the segment's K and V (loaded into registers during the previous
-//      segment) go into LDS; the attention waves take their Q rows;
-//   2. every thread stages sigma(K) into LDS, with den_t = sigma(K_t) . z and
-//      the column sums of sigma(K);
-//   3. attention waves: S^T = K Q^T over the causal key blocks (online
+//   1. the update waves store the segment's K and V (loaded into registers
+//      during the previous segment) into LDS; the attention waves take their
+//      Q rows; one barrier;
+//   2. attention waves: S^T = K Q^T over the causal key blocks (online
 //      softmax), O^T = V^T P^T, R^T = M^T sigma(Q)^T, and the rows
-//      (1 - g)/l O + g/den R written out; update waves, per 32-token block:
-//      P = sigma(K) M for their slab (delta), then M += sigma(K)^T V +
-//      sigma(K)^T (-P / den), with -P/den taken from the accumulator
-//      straight into the second product's operand (never through LDS,
-//      never V - P/den rounded as one value);
-//   4. the update waves write their slab's new M^T to LDS and z += column sums.
+//      (1 - g)/l O + g/den R written out. Beside them the update waves stage
+//      sigma(K) into LDS from the K rows still in their registers, with
+//      den_t = sigma(K_t) . z and the column sums of sigma(K), wait for one
+//      another on an LDS counter (the attention waves read none of it and do
+//      not wait), then, per 32-token block: P = sigma(K) M for their slab
+//      (delta), M += sigma(K)^T V + sigma(K)^T (-P / den), with -P/den taken
+//      from the accumulator straight into the second product's operand
+//      (never through LDS, never V - P/den rounded as one value);
+//   3. after a second barrier the update waves write their slab's new M^T to
+//      LDS and z += column sums.
 // All products run on bf16 MFMA with float accumulation; the state stays
 // float. The arithmetic is the split plan's, operand for operand.
 #include "common.hpp"
@@ -49,6 +52,12 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
   constexpr int MTS = D + 8;        // row stride of M^T in LDS
   constexpr int PF = 2 * NB;        // 16-byte K and V chunks per update-wave thread
   constexpr bool DELTA = RULE == kRuleDelta;
+  // Who stages sigma(K): with two waves per SIMD (d = 128) every wave stages
+  // a share from LDS, so the VALU work spreads over all eight; with one wave
+  // per SIMD (d = 64) the update waves stage alone from the K rows in their
+  // registers while the attention waves run.
+  constexpr bool ALL_STAGE = D == 128;
+  constexpr int RED_ROWS = ALL_STAGE ? 32 : NB;  // column-sum partial rows
   static_assert(NT / CPR == 32, "32 rows per staging pass");
   static_assert((NB * 64) % (16 * CPR) == 0, "prefetch rows keep their swizzle");
 
@@ -56,7 +65,8 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
   __shared__ __align__(1024) bf16 Vs[D * D];  // V, V layout
   __shared__ __align__(1024) bf16 Ph[D * D];  // sigma(K), K layout
   __shared__ __align__(16) bf16 Mt[D * MTS];  // M^T (bf16), [value][key]
-  __shared__ __align__(16) float red[32 * D]; // column-sum partials
+  __shared__ __align__(16) float red[RED_ROWS * D];  // column-sum partials
+  __shared__ uint32_t staged;                 // update waves done staging, over all segments
   __shared__ float rden_s[D];                 // 1 / (sigma(K_t) . z) per token, 0 past the end
   __shared__ float zs[D];                     // z
 
@@ -78,6 +88,7 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
 
   const uint32_t ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));  // row reads of a K-layout tile
   if (tid < D) zs[tid] = a.z_in[(int64_t)unit * D + tid];  // attention-wave threads
+  if (tid == 0) staged = 0u;
 
   // M in float goes through LDS on its way in and out (rows 0 .. d/2 - 1 in
   // the K buffer, the rest in the V buffer, both free then), so every global
@@ -96,16 +107,17 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
   }
   __syncthreads();
 
-  // sigma(K) of the segment into Ph, 1 / den_t into rden_s, column-sum partials
-  // into red (every thread, 32 rows per pass)
-  auto stage = [&](int n) {
+  // sigma(K) of the segment into Ph, 1 / den_t into rden_s, column-sum
+  // partials into red, by every thread from the K tile in LDS (32 rows per
+  // pass): the ALL_STAGE staging
+  auto stage_all = [&](int n) {
     const int tr = tid / CPR, cc = tid % CPR;
-    float zc[8];
+    float zc[8], cs[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zc[e] = zs[8 * cc + e];
-    float cs[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs[e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      zc[e] = zs[8 * cc + e];
+      cs[e] = 0.f;
+    }
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
       const int t = tr + 32 * p;
@@ -126,11 +138,22 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[tr * D + 8 * cc + e] = cs[e];
   };
+  // every staging wave counts itself in on `staged` once its LDS stores are
+  // done (release); the update waves then read the count (acquire) until all
+  // staging waves of the segment are in. The wait is bounded: no staging wave
+  // waits on anything before it counts itself in.
+  auto count_in = [&]() {
+    if (lane == 0)
+      __hip_atomic_fetch_add(&staged, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
 
   // The two roles run separate loops (so neither holds the other's
-  // registers), with the same three barriers per segment:
+  // registers), with the same two barriers per segment:
   //   B1 the segment's K, V in LDS, and M^T and z of the state before it;
-  //   B2 sigma(K) staged; B3 the segment's reads of Ks, Vs, Ph, Mt done.
+  //   B3 the segment's reads of Ks, Vs, Ph, Mt, red done.
+  // Between them the update waves alone also wait for sigma(K) to be staged
+  // (the LDS counter `staged`); the attention waves, which read none of it,
+  // run on.
   if (attn_wave) {
     // ---- attention, retrieval and gate for query block w ----
     bf16x8 qf[NC], qn[NC];
@@ -158,8 +181,10 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
       for (int cc = 0; cc < NC; ++cc) qf[cc] = qn[cc];
       __syncthreads();  // B1
       if (s + 1 < S) load_q(s + 1, qn);
-      stage(n);
-      __syncthreads();  // B2
+      if constexpr (ALL_STAGE) {
+        stage_all(n);
+        count_in();
+      }
       const int row = 32 * w + i;
       if (32 * w < n) {
         f32x16 oacc[NB];
@@ -249,7 +274,8 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
       __syncthreads();  // B3
       if (tid < D) {    // z of the next state
         float cs = 0.f;
-        for (int t = 0; t < 32; ++t) cs += red[t * D + tid];
+#pragma unroll
+        for (int u = 0; u < RED_ROWS; ++u) cs += red[u * D + tid];
         zs[tid] += cs;
       }
     }
@@ -317,9 +343,60 @@ __global__ __launch_bounds__(D / 32 * 128) void fused_kernel(FusedArgs a) {
         }
       }
       __syncthreads();  // B1
-      stage(n);
-      if (s + 1 < S) load_kv(s + 1);  // after the staging: its issue waits for queue room
-      __syncthreads();  // B2
+      if constexpr (ALL_STAGE) {
+        stage_all(n);
+      } else {
+        // sigma(K) into Ph from the K rows in registers (rows r + RSTEP k,
+        // 16-byte chunk cc), 1 / den_t into rden_s (the 8-element partial dot
+        // in order, then summed over the row's CPR lanes), and the column
+        // sums: over this thread's rows, then over the lanes of its chunk,
+        // one row of red per wave
+        const int r = ut / CPR, cc = ut % CPR;
+        float zc[8], cs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          zc[e] = zs[8 * cc + e];
+          cs[e] = 0.f;
+        }
+        bf16* pd = Ph + r * D + 8 * (cc ^ swz_k<D>(r));
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+          const int t = r + k * RSTEP;
+          bf16x8 y;
+          float dp = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = t < n ? feature_map((float)kpre[k][e]) : 0.f;
+            y[e] = (bf16)f;
+            dp += f * zc[e];
+            cs[e] += f;
+          }
+          store8<bf16>(pd + k * RSTEP * D, y);
+          const float den = row_sum<CPR>(dp);
+          if (cc == 0) rden_s[t] = t < n ? 1.f / den : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+#pragma unroll
+          for (int off = CPR; off < 32; off *= 2) cs[e] += __shfl_xor(cs[e], off);
+          cs[e] = xhalf_sum(cs[e]);
+        }
+        if (lane < CPR) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) red[vb * D + 8 * lane + e] = cs[e];
+        }
+      }
+      if (s + 1 < S) load_kv(s + 1);  // the K rows in registers are consumed
+      count_in();
+      {
+        const uint32_t target = (uint32_t)(ALL_STAGE ? 2 * NB : NB) * (uint32_t)(s + 1);
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          const uint32_t v =
+              __hip_atomic_load(&staged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if ((int32_t)(v - target) >= 0) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
       // M += sigma(K)^T V (+ sigma(K)^T (-P / den), delta), one 32-token block
       // at a time. -P / den enters as the B operand straight from P's
       // accumulator: chunk p of 16 tokens, element e = token 16 p +
