@@ -58,6 +58,10 @@ SIGNATURES = {
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_block_forward": (
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
+    "infini_attn_block_workspace_size_kv": (
+        _c_i32, [_c_i64] * 8 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_block_forward_kv": (
+        _c_i32, [_c_i64] * 8 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]),
     "infini_attn_block_forward_timed": (
         _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 9 + [_c_p, _c_size, _c_p]
         + [ctypes.POINTER(_c_p), _c_i32]),
@@ -424,14 +428,23 @@ def backward(q, k, v, beta, M0, z0, seg_len, rule, out, lse, d_out, dM_final=Non
     return dq, dk, dv, dbeta, dM0, dz0
 
 
-def block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype=torch.bfloat16):
-    """Workspace bytes of infini_attn_block_forward with these sizes."""
+def block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype=torch.bfloat16,
+                         d_value=None):
+    """Workspace bytes of infini_attn_block_forward with these sizes (of
+    infini_attn_block_forward_kv when d_value is given and differs from d)."""
     n = _c_size(0)
-    st = load_library().infini_attn_block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len,
-                                                         RULES[rule], DTYPES[dtype],
-                                                         ctypes.byref(n))
+    lib = load_library()
+    if d_value is None or d_value == d:
+        st = lib.infini_attn_block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len,
+                                                  RULES[rule], DTYPES[dtype], ctypes.byref(n))
+        name = "infini_attn_block_workspace_size"
+    else:
+        st = lib.infini_attn_block_workspace_size_kv(B, L, d_model, Hq, Hkv, d, d_value,
+                                                     seg_len, RULES[rule], DTYPES[dtype],
+                                                     ctypes.byref(n))
+        name = "infini_attn_block_workspace_size_kv"
     if st != 0:
-        raise InfiniAttnError(st, "infini_attn_block_workspace_size")
+        raise InfiniAttnError(st, name)
     return int(n.value)
 
 
@@ -442,18 +455,25 @@ def block_forward(x, w_qkv, w_o, beta, M0, z0, seg_len, rule, Hq, Hkv, *, y=None
     x [B,L,d_model] bfloat16; w_qkv [(Hq+2Hkv)*d, d_model] and w_o
     [d_model, Hq*d] bfloat16 (linear-layer layout); beta [Hq], M0 [B,Hkv,d,d],
     z0 [B,Hkv,d] float32. Returns (y [B,L,d_model], M_final, z_final).
+    With a value width dv other than the key width d (M0 [B,Hkv,d,dv]), w_qkv
+    is [(Hq+Hkv)*d + Hkv*dv, d_model] and w_o [d_model, Hq*dv]
+    (infini_attn_block_forward_kv, without ``events``).
     ``events`` (up to 4 torch.cuda.Event) are recorded before the input
     projection, after it, after the block and after the output projection.
     Asynchronous on ``stream`` (or torch's current stream).
     """
     B, L, d_model = x.shape
-    if w_qkv.dim() != 2 or w_qkv.shape[1] != d_model or w_qkv.shape[0] % (Hq + 2 * Hkv):
-        raise ValueError("w_qkv must be [(Hq+2Hkv)*d, d_model]")
-    d = w_qkv.shape[0] // (Hq + 2 * Hkv)
-    if w_o.shape != (d_model, Hq * d):
-        raise ValueError("w_o must be [d_model, Hq*d]")
-    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+    if M0.dim() != 4:
+        raise ValueError("M0 must be [B,Hkv,d,dv]")
+    d, dv = M0.shape[2], M0.shape[3]
+    if w_qkv.shape != ((Hq + Hkv) * d + Hkv * dv, d_model):
+        raise ValueError("w_qkv must be [(Hq+Hkv)*d + Hkv*dv, d_model]")
+    if w_o.shape != (d_model, Hq * dv):
+        raise ValueError("w_o must be [d_model, Hq*dv]")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, dv) or z0.shape != (B, Hkv, d):
         raise ValueError("beta, M0 or z0 has the wrong shape")
+    if dv != d and events:
+        raise ValueError("events need d_value == d_key")
     if any(t.dtype != torch.bfloat16 for t in (x, w_qkv, w_o)):
         raise TypeError("x, w_qkv and w_o must be bfloat16")
     if any(t.dtype != torch.float32 for t in (beta, M0, z0)):
@@ -477,7 +497,8 @@ def block_forward(x, w_qkv, w_o, beta, M0, z0, seg_len, rule, Hq, Hkv, *, y=None
     if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
         raise ValueError("y must be a contiguous tensor like x")
     if workspace is None:
-        workspace = torch.empty(block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule),
+        workspace = torch.empty(block_workspace_size(B, L, d_model, Hq, Hkv, d, seg_len, rule,
+                                                     d_value=dv),
                                 dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
@@ -494,6 +515,9 @@ def block_forward(x, w_qkv, w_o, beta, M0, z0, seg_len, rule, Hq, Hkv, *, y=None
         handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
         st = lib.infini_attn_block_forward_timed(*args, handles, len(events))
         name = "infini_attn_block_forward_timed"
+    elif dv != d:
+        st = lib.infini_attn_block_forward_kv(*args[:6], dv, *args[6:])
+        name = "infini_attn_block_forward_kv"
     else:
         st = lib.infini_attn_block_forward(*args)
         name = "infini_attn_block_forward"

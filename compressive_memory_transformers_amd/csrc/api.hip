@@ -1254,30 +1254,34 @@ struct BlockLayout {
   size_t q, k, v, a, fwd, fwd_bytes, total;
 };
 
+// d: the key width, dv: the value width ("Infini-Attention" (AI Wiki), "How
+// does the compressive memory work?": M is d_key x d_value).
 infini_status_t block_layout(int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv,
-                             int64_t d, int64_t seg_len, int32_t rule, int32_t dtype,
-                             BlockLayout* lay) {
+                             int64_t d, int64_t dv, int64_t seg_len, int32_t rule,
+                             int32_t dtype, BlockLayout* lay) {
   Plan p;
-  infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  infini_status_t st = check_sizes_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
   if (d_model < 1) return INFINI_ERR_INVALID_ARG;
   if (dtype != INFINI_BF16) return INFINI_ERR_UNSUPPORTED;  // the projections are bf16 MFMA
   if (d_model % 32 != 0) return INFINI_ERR_UNSUPPORTED;     // K steps of 32
   // 32-bit row and column indices in the projection kernel, 32-bit lane
   // offsets within its loads (rows of one 256-row tile)
-  const int64_t M = B * L, Nqkv = (Hq + 2 * Hkv) * d;
+  const int64_t M = B * L, Nqkv = (Hq + Hkv) * d + Hkv * dv;
   if (M >= INT32_MAX || Nqkv >= INT32_MAX || d_model >= (1 << 22)) return INFINI_ERR_INVALID_ARG;
-  if ((256 * Hq + Hq * L + L) * d * 2 >= (int64_t)UINT32_MAX) return INFINI_ERR_INVALID_ARG;
+  if ((256 * Hq + Hq * L + L) * dv * 2 >= (int64_t)UINT32_MAX) return INFINI_ERR_INVALID_ARG;
   const int64_t tiles = ((M + 255) / 256) * (((Nqkv > d_model ? Nqkv : d_model) + 255) / 256);
   if (tiles > INT32_MAX) return INFINI_ERR_INVALID_ARG;
   if (lay) {
     const size_t nq = align_up((size_t)(B * Hq * L * d) * 2);
-    const size_t nkv = align_up((size_t)(B * Hkv * L * d) * 2);
+    const size_t nk = align_up((size_t)(B * Hkv * L * d) * 2);
+    const size_t nv = align_up((size_t)(B * Hkv * L * dv) * 2);
+    const size_t na = align_up((size_t)(B * Hq * L * dv) * 2);
     lay->q = 0;
     lay->k = nq;
-    lay->v = nq + nkv;
-    lay->a = nq + 2 * nkv;
-    lay->fwd = 2 * nq + 2 * nkv;
+    lay->v = nq + nk;
+    lay->a = nq + nk + nv;
+    lay->fwd = nq + nk + nv + na;
     lay->fwd_bytes = workspace_full(p);
     lay->total = lay->fwd + lay->fwd_bytes;
   }
@@ -1285,13 +1289,15 @@ infini_status_t block_layout(int64_t B, int64_t L, int64_t d_model, int64_t Hq, 
 }
 
 infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv,
-                           int64_t d, int64_t seg_len, int32_t rule, int32_t dtype,
-                           const void* x, const void* w_qkv, const void* w_o, const float* beta,
-                           const float* M0, const float* z0, void* y, float* M_final,
-                           float* z_final, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events, int32_t n_events) {
+                           int64_t d, int64_t dv, int64_t seg_len, int32_t rule,
+                           int32_t dtype, const void* x, const void* w_qkv, const void* w_o,
+                           const float* beta, const float* M0, const float* z0, void* y,
+                           float* M_final, float* z_final, void* workspace,
+                           size_t workspace_bytes, void* stream, void* const* events,
+                           int32_t n_events) {
   BlockLayout lay;
-  infini_status_t st = block_layout(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, &lay);
+  infini_status_t st =
+      block_layout(B, L, d_model, Hq, Hkv, d, dv, seg_len, rule, dtype, &lay);
   if (st != INFINI_OK) return st;
   const void* ptrs[] = {x, w_qkv, w_o, beta, M0, z0, y, M_final, z_final, workspace};
   for (const void* ptr : ptrs)
@@ -1303,10 +1309,10 @@ infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, in
   for (int32_t e = 0; e < n_events; ++e)
     if (events[e] == nullptr) return INFINI_ERR_INVALID_ARG;
 
-  const int64_t M = B * L, Nqkv = (Hq + 2 * Hkv) * d;
+  const int64_t M = B * L, Nqkv = (Hq + Hkv) * d + Hkv * dv;
   const size_t nx = (size_t)(M * d_model) * 2, ny = nx;
-  const size_t nwq = (size_t)(Nqkv * d_model) * 2, nwo = (size_t)(d_model * Hq * d) * 2;
-  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  const size_t nwq = (size_t)(Nqkv * d_model) * 2, nwo = (size_t)(d_model * Hq * dv) * 2;
+  const size_t nM = (size_t)(B * Hkv * d * dv) * 4, nz = (size_t)(B * Hkv * d) * 4;
   struct Range { const void* p; size_t n; };
   const Range inputs[] = {{x, nx}, {w_qkv, nwq}, {w_o, nwo}, {beta, (size_t)Hq * 4},
                           {M0, nM}, {z0, nz}};
@@ -1348,6 +1354,7 @@ infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, in
   pa.a_elems = M * d_model;
   pa.L = L;
   pa.d = d;
+  pa.dv = dv;
   pa.Ha = 1;
   pa.Hq = Hq;
   pa.Hkv = Hkv;
@@ -1359,7 +1366,7 @@ infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, in
 
   // 2. the block: a, M_final, z_final
   st = forward_impl(B, Hq, Hkv, L, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, a, M_final,
-                    z_final, nullptr, ws + lay.fwd, lay.fwd_bytes, stream, nullptr, 0);
+                    z_final, nullptr, ws + lay.fwd, lay.fwd_bytes, stream, nullptr, 0, dv);
   if (st != INFINI_OK) return st;
   if (!mark(2)) return INFINI_ERR_HIP;
 
@@ -1370,11 +1377,12 @@ infini_status_t block_impl(int64_t B, int64_t L, int64_t d_model, int64_t Hq, in
   po.c = y;
   po.M = M;
   po.N = d_model;
-  po.K = Hq * d;
+  po.K = Hq * dv;
   po.ldc = d_model;
-  po.a_elems = B * Hq * L * d;
+  po.a_elems = B * Hq * L * dv;
   po.L = L;
-  po.d = d;
+  po.d = dv;  // a's heads are d_value wide
+  po.dv = dv;
   po.Ha = Hq;
   po.Hq = Hq;
   po.Hkv = Hkv;
@@ -1396,7 +1404,7 @@ infini_status_t infini_attn_block_workspace_size(int64_t B, int64_t L, int64_t d
   if (bytes == nullptr) return INFINI_ERR_INVALID_ARG;
   BlockLayout lay;
   const infini_status_t st =
-      block_layout(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, &lay);
+      block_layout(B, L, d_model, Hq, Hkv, d, d, seg_len, rule, dtype, &lay);
   if (st != INFINI_OK) return st;
   *bytes = lay.total;
   return INFINI_OK;
@@ -1409,8 +1417,35 @@ infini_status_t infini_attn_block_forward(int64_t B, int64_t L, int64_t d_model,
                                           const float* M0, const float* z0, void* y,
                                           float* M_final, float* z_final, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  return block_impl(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, x, w_qkv, w_o, beta, M0,
-                    z0, y, M_final, z_final, workspace, workspace_bytes, stream, nullptr, 0);
+  return block_impl(B, L, d_model, Hq, Hkv, d, d, seg_len, rule, dtype, x, w_qkv, w_o, beta,
+                    M0, z0, y, M_final, z_final, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+infini_status_t infini_attn_block_workspace_size_kv(int64_t B, int64_t L, int64_t d_model,
+                                                    int64_t Hq, int64_t Hkv, int64_t d_key,
+                                                    int64_t d_value, int64_t seg_len,
+                                                    int32_t rule, int32_t dtype, size_t* bytes) {
+  if (bytes == nullptr || d_value < 1) return INFINI_ERR_INVALID_ARG;
+  BlockLayout lay;
+  const infini_status_t st =
+      block_layout(B, L, d_model, Hq, Hkv, d_key, d_value, seg_len, rule, dtype, &lay);
+  if (st != INFINI_OK) return st;
+  *bytes = lay.total;
+  return INFINI_OK;
+}
+
+infini_status_t infini_attn_block_forward_kv(int64_t B, int64_t L, int64_t d_model, int64_t Hq,
+                                             int64_t Hkv, int64_t d_key, int64_t d_value,
+                                             int64_t seg_len, int32_t rule, int32_t dtype,
+                                             const void* x, const void* w_qkv, const void* w_o,
+                                             const float* beta, const float* M0,
+                                             const float* z0, void* y, float* M_final,
+                                             float* z_final, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return block_impl(B, L, d_model, Hq, Hkv, d_key, d_value, seg_len, rule, dtype, x, w_qkv, w_o,
+                    beta, M0, z0, y, M_final, z_final, workspace, workspace_bytes, stream,
+                    nullptr, 0);
 }
 
 infini_status_t infini_attn_block_forward_timed(
@@ -1419,8 +1454,8 @@ infini_status_t infini_attn_block_forward_timed(
     const float* beta, const float* M0, const float* z0, void* y, float* M_final,
     float* z_final, void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events) {
-  return block_impl(B, L, d_model, Hq, Hkv, d, seg_len, rule, dtype, x, w_qkv, w_o, beta, M0,
-                    z0, y, M_final, z_final, workspace, workspace_bytes, stream, events,
+  return block_impl(B, L, d_model, Hq, Hkv, d, d, seg_len, rule, dtype, x, w_qkv, w_o, beta,
+                    M0, z0, y, M_final, z_final, workspace, workspace_bytes, stream, events,
                     n_events);
 }
 

@@ -272,7 +272,8 @@ struct ProjArgs {
   int64_t M, N, K;
   int64_t lda, ldc;
   int64_t a_elems;  // elements of the tensor a points into (bounds of its loads)
-  int64_t L, d, Ha, Hq, Hkv;
+  int64_t L, d, Ha, Hq, Hkv;  // d: the gathered A's head width; heads of q and k (kProjHeads)
+  int64_t dv;                  // heads of v (kProjHeads)
   int32_t a_mode, c_mode;
 };
 hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);

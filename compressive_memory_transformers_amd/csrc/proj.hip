@@ -102,8 +102,9 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
   const bf16* W = static_cast<const bf16*>(a.w);
   const int nk = (int)(a.K / kBK);
 
-  // d is 32, 64 or 128: head and column of an offset by shift and mask
+  // widths are 32, 64 or 128: head and column of an offset by shift and mask
   const int ld = __builtin_ctz((unsigned)a.d);
+  const int ldv = __builtin_ctz((unsigned)a.dv);
   // element offsets of the next stage's slabs, advanced stage by stage: a
   // gathered A moves 32 columns within a head, then to the next head's rows
   int64_t a_next = a.a_mode == kProjGather ? b0 * a.Ha * a.L * a.d : m0 * a.lda;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
     if (a.c_mode == kProjHeads) {
       rowp[0] = static_cast<bf16*>(a.q) + ((int64_t)b * a.Hq * a.L + tt) * a.d;
       rowp[1] = static_cast<bf16*>(a.k) + ((int64_t)b * a.Hkv * a.L + tt) * a.d;
-      rowp[2] = static_cast<bf16*>(a.v) + ((int64_t)b * a.Hkv * a.L + tt) * a.d;
+      rowp[2] = static_cast<bf16*>(a.v) + ((int64_t)b * a.Hkv * a.L + tt) * a.dv;
     } else {
       rowp[0] = rowp[1] = rowp[2] = static_cast<bf16*>(a.c) + (int64_t)m * a.ldc;
     }
@@ -207,10 +208,17 @@ __global__ __launch_bounds__(512, 1) void proj_kernel(ProjArgs a) {
         for (int e = 0; e < 4; ++e) v4[e] = (bf16)acc[ni][mi][4 * qd + e];
         bf16* dst;
         if (a.c_mode == kProjHeads) {
-          const int hn = n >> ld, j = n & (a.d - 1);
-          const int which = hn < a.Hq ? 0 : (hn < a.Hq + a.Hkv ? 1 : 2);
-          const int hh = which == 0 ? hn : (which == 1 ? hn - (int)a.Hq : hn - (int)(a.Hq + a.Hkv));
-          dst = rowp[which] + (int64_t)hh * a.L * a.d + j;
+          // columns: Hq query heads and Hkv key heads d wide, then Hkv value
+          // heads dv wide (four columns never straddle a head: widths are
+          // multiples of 32)
+          const int nq = (int)a.Hq << ld, nk = nq + ((int)a.Hkv << ld);
+          if (n < nk) {
+            const int which = n < nq ? 0 : 1, c = n - (which ? nq : 0);
+            dst = rowp[which] + (int64_t)(c >> ld) * a.L * a.d + (c & (a.d - 1));
+          } else {
+            const int c = n - nk;
+            dst = rowp[2] + (int64_t)(c >> ldv) * a.L * a.dv + (c & (a.dv - 1));
+          }
         } else {
           dst = rowp[0] + n;
         }

@@ -395,6 +395,34 @@ infini_status_t infini_attn_block_forward_timed(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);
 
+/*
+ * The block with a key width different from the value width ("Infini-
+ * Attention" (AI Wiki), "How does the compressive memory work?": the memory
+ * maps d_key-dimensional keys to d_value-dimensional values). Query and key
+ * heads are d_key wide, value heads and the gated result d_value wide:
+ *   w_qkv      [(Hq + Hkv) d_key + Hkv d_value][d_model] bf16 (the Hq query
+ *              heads' d_key rows each, the Hkv key heads' d_key rows, the Hkv
+ *              value heads' d_value rows)
+ *   w_o        [d_model][Hq d_value] bf16 (feature h d_value + j is element j
+ *              of head h)
+ *   M0, M_final [B][Hkv][d_key][d_value] float; z0, z_final [B][Hkv][d_key].
+ * The workspace holds q [B][Hq][L][d_key], k [B][Hkv][L][d_key],
+ * v [B][Hkv][L][d_value] and a [B][Hq][L][d_value] in bf16 first, in that order,
+ * each rounded up to 256 bytes, then the forward's. d_key and d_value in
+ * {32, 64, 128}; everything else as infini_attn_block_forward, which these
+ * calls equal when d_key == d_value.
+ */
+infini_status_t infini_attn_block_workspace_size_kv(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d_key,
+    int64_t d_value, int64_t seg_len, int32_t rule, int32_t dtype, size_t* bytes);
+infini_status_t infini_attn_block_forward_kv(
+    int64_t B, int64_t L, int64_t d_model, int64_t Hq, int64_t Hkv, int64_t d_key,
+    int64_t d_value, int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* x, const void* w_qkv, const void* w_o, const float* beta,
+    const float* M0, const float* z0,
+    void* y, float* M_final, float* z_final,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name of a status code ("unknown status" for any
  * other value). infini_attn_error_string is the same function under a second
  * name. */

@@ -210,31 +210,36 @@ def hbm_bytes(w):
 
 
 def make_block_inputs(B, L, d_model, Hq, Hkv, d, dtype, device="cpu", seed=0, z0=1e-6,
-                      m0_scale=0.0):
+                      m0_scale=0.0, dv=None):
     """Inputs of the block with its projections, on ``device``.
 
-    x [B, L, d_model] N(0, 1); w_qkv [(Hq + 2 Hkv) d, d_model] and
-    w_o [d_model, Hq d], each N(0, 1 / fan_in) (random weights: the projected
+    x [B, L, d_model] N(0, 1); w_qkv [(Hq + Hkv) d + Hkv dv, d_model] (query
+    and key heads d rows each, value heads dv rows; dv = d unless given) and
+    w_o [d_model, Hq dv], each N(0, 1 / fan_in) (random weights: the projected
     values then have unit variance), in ``dtype``; beta [Hq] N(0, 1) float32;
-    M0 [B, Hkv, d, d] float32, N(0, m0_scale^2) (zeros by default); z0
+    M0 [B, Hkv, d, dv] float32, N(0, m0_scale^2) (zeros by default); z0
     [B, Hkv, d] float32, all ``z0``. Slices are seeded per batch element (x)
     and per head (the weights' row blocks).
     """
+    dv = d if dv is None else dv
     x = torch.empty((B, L, d_model), dtype=dtype, device=device)
     for b in range(B):
         x[b] = _normal((L, d_model), slice_seed(seed, "x", b, 0), device).to(dtype)
-    w_qkv = torch.empty(((Hq + 2 * Hkv) * d, d_model), dtype=dtype, device=device)
-    for h in range(Hq + 2 * Hkv):
-        w_qkv[h * d:(h + 1) * d] = (_normal((d, d_model), slice_seed(seed, "w_qkv", 0, h), device)
-                                    / math.sqrt(d_model)).to(dtype)
-    w_o = (_normal((d_model, Hq * d), slice_seed(seed, "w_o", 0, 0), device)
-           / math.sqrt(Hq * d)).to(dtype)
+    widths = [d] * (Hq + Hkv) + [dv] * Hkv
+    w_qkv = torch.empty((sum(widths), d_model), dtype=dtype, device=device)
+    r0 = 0
+    for h, wd in enumerate(widths):
+        w_qkv[r0:r0 + wd] = (_normal((wd, d_model), slice_seed(seed, "w_qkv", 0, h), device)
+                             / math.sqrt(d_model)).to(dtype)
+        r0 += wd
+    w_o = (_normal((d_model, Hq * dv), slice_seed(seed, "w_o", 0, 0), device)
+           / math.sqrt(Hq * dv)).to(dtype)
     beta = _normal((Hq,), slice_seed(seed, "beta", 0, 0), device)
-    M0 = torch.zeros((B, Hkv, d, d), dtype=torch.float32, device=device)
+    M0 = torch.zeros((B, Hkv, d, dv), dtype=torch.float32, device=device)
     if m0_scale:
         for b in range(B):
             for h in range(Hkv):
-                M0[b, h] = m0_scale * _normal((d, d), slice_seed(seed, "M0", b, h), device)
+                M0[b, h] = m0_scale * _normal((d, dv), slice_seed(seed, "M0", b, h), device)
     z0 = torch.full((B, Hkv, d), z0, dtype=torch.float32, device=device)
     return dict(x=x, w_qkv=w_qkv, w_o=w_o, beta=beta, M0=M0, z0=z0)
 

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "infini_attn_backward", "infini_attn_backward_workspace_size",
         "infini_attn_block_forward", "infini_attn_block_forward_timed",
-        "infini_attn_block_workspace_size", "infini_attn_decode_step", "infini_attn_error_string",
+        "infini_attn_block_workspace_size", "infini_attn_block_forward_kv",
+        "infini_attn_block_workspace_size_kv", "infini_attn_decode_step", "infini_attn_error_string",
         "infini_attn_decode_workspace_size", "infini_attn_decode_step_kv",
         "infini_attn_decode_workspace_size_kv",
         "infini_attn_forward", "infini_attn_forward_kv", "infini_attn_forward_kv_timed",
@@ -575,6 +576,29 @@ def test_block_workspace_size(lib):
     _, fwd_full, _ = ws(lib, B, Hq, Hkv, L, d, N, 1, 1)
     # q and a [B,Hq,L,d], k and v [B,Hkv,L,d] in bf16, then a full forward workspace
     assert n == 2 * B * Hq * L * d * 2 + 2 * B * Hkv * L * d * 2 + fwd_full
+
+
+def test_block_workspace_size_with_separate_widths(lib):
+    def blk_ws_kv(*args):
+        n = ctypes.c_size_t(0)
+        st = lib.infini_attn_block_workspace_size_kv(*args, ctypes.byref(n))
+        return st, n.value
+    B, L, dm, Hq, Hkv, N = 4, 32768, 4096, 32, 8, 2048
+    # equal widths: the square call's size
+    assert blk_ws_kv(B, L, dm, Hq, Hkv, 128, 128, N, 1, 1) == blk_ws(lib, B, L, dm, Hq, Hkv, 128,
+                                                                      N, 1, 1)
+    dk, dv = 64, 128
+    st, n = blk_ws_kv(B, L, dm, Hq, Hkv, dk, dv, N, 1, 1)
+    assert st == 0
+    _, fwd_full, _ = ws_kv(lib, B, Hq, Hkv, L, dk, dv, N, 1, 1)
+    # q [B,Hq,L,dk], k [B,Hkv,L,dk], v [B,Hkv,L,dv], a [B,Hq,L,dv] in bf16, then the forward's
+    assert n == (B * Hq * L * dk + B * Hkv * L * dk + B * Hkv * L * dv + B * Hq * L * dv) * 2 \
+        + fwd_full
+    assert blk_ws_kv(B, L, dm, Hq, Hkv, 64, 96, N, 1, 1)[0] == 2     # d_value unsupported
+    assert blk_ws_kv(B, L, dm, Hq, Hkv, 64, 0, N, 1, 1)[0] == 1      # d_value < 1
+    assert blk_ws_kv(B, L, dm, Hq, Hkv, 64, 128, N, 1, 0)[0] == 2    # float
+    assert lib.infini_attn_block_workspace_size_kv(B, L, dm, Hq, Hkv, 64, 128, N, 1, 1,
+                                                   None) == 1
 
 
 @pytest.mark.parametrize("args,status", [
