@@ -526,17 +526,21 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
 // Under the linear rule M_s = M_{s-1} + B_s: the state before segment s is
 // M_0 + sum_{s'<s} B_s', a running sum with no product in it ("Infini-
 // Attention" (AI Wiki), "How does the compressive memory work?", the additive
-// variant). Every entry of M is its own sum, so the work splits into 32 x 32
-// blocks of M, one workgroup per (unit, block); each walks its unit's
-// segments with the B_s loads kPrefetch segments ahead of the additions. The
-// snapshot (M^T in the element type) goes through LDS, transposed, so both
-// the B_s reads and the snapshot writes are whole rows. Same float additions
-// in the same order as the step-by-step chain, so the same results.
+// variant); z is the running sum of the column sums. Every entry is its own
+// sum, so the work splits into 32 x 32 blocks of M, one workgroup per (unit,
+// block); each walks its unit's segments with the B_s loads kPrefetch
+// segments ahead of the additions, and the blocks of column 0 also carry 32
+// entries of z. The snapshots (M^T in the element type) go through LDS,
+// transposed, four segments per barrier, so both the B_s reads and the
+// snapshot writes are whole rows. Same float additions in the same order as
+// the step-by-step chain and the z prefix, so the same results.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void linear_prefix_kernel(AffineArgs a) {
   constexpr int NB = D / 32;  // blocks per side
-  constexpr int TS = 32 + 4;  // LDS row stride of the transposed block
-  __shared__ __align__(16) T Mt[2][32 * TS];
+  constexpr int TS = 32 + 4;  // LDS row stride of a transposed block
+  constexpr int GS = 4;       // segments per barrier
+  static_assert(kPrefetch % GS == 0, "whole groups per prefetch round");
+  __shared__ __align__(16) T Mt[2 * GS][32 * TS];
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / (NB * NB), blk = blockIdx.x % (NB * NB);
   const int r0 = 32 * (blk / NB), c0 = 32 * (blk % NB);
@@ -550,31 +554,56 @@ __global__ __launch_bounds__(256) void linear_prefix_kernel(AffineArgs a) {
   const float* Bu = a.Bmat + (int64_t)unit * n * D * D + moff;
   T* snap = static_cast<T*>(a.snapM) + (int64_t)unit * n * D * D +
             (int64_t)(c0 + tr) * D + r0 + 4 * tq;
+  // z entries r0 + tid of the unit, in the blocks of column 0 (tid < 32)
+  const bool zl = c0 == 0 && tid < 32;
+  const int zj = zl ? r0 + tid : 0;
+  const float* csu = a.colsum + (int64_t)unit * n * D + zj;
+  float* szu = a.snapZ + (int64_t)unit * n * D + zj;
+  float z = zl ? a.z_in[(int64_t)unit * D + zj] : 0.f;
   f32x4 ring[kPrefetch];
+  float zring[kPrefetch];
 #pragma unroll
-  for (int u = 0; u < kPrefetch; ++u)
+  for (int u = 0; u < kPrefetch; ++u) {
     if (u < n) ring[u] = *reinterpret_cast<const f32x4*>(Bu + (int64_t)u * D * D);
+    zring[u] = zl && u < n ? csu[(int64_t)u * D] : 0.f;
+  }
   for (int s0 = 0; s0 < n; s0 += kPrefetch) {
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int sl = s0 + u;
-      if (sl < n) {
-        T* buf = Mt[u & 1];
+    for (int g0 = 0; g0 < kPrefetch; g0 += GS) {
+      if (s0 + g0 >= n) break;  // uniform
+      T (*buf)[32 * TS] = Mt + GS * ((g0 / GS) & 1);
+      // the states before the group's segments into LDS, transposed
 #pragma unroll
-        for (int j = 0; j < 4; ++j) buf[(4 * cq + j) * TS + rr] = from_f32<T>(acc[j]);
-        __syncthreads();
-        vec4_t<T> y;
+      for (int uu = 0; uu < GS; ++uu) {
+        const int u = g0 + uu, sl = s0 + u;
+        if (sl < n) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = buf[tr * TS + 4 * tq + j];
-        store4<T>(snap + (int64_t)sl * D * D, y);
+          for (int j = 0; j < 4; ++j) buf[uu][(4 * cq + j) * TS + rr] = from_f32<T>(acc[j]);
+          if (zl) szu[(int64_t)sl * D] = z;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += ring[u][j];
-        if (sl + kPrefetch < n)
-          ring[u] = *reinterpret_cast<const f32x4*>(Bu + (int64_t)(sl + kPrefetch) * D * D);
+          for (int j = 0; j < 4; ++j) acc[j] += ring[u][j];
+          z += zring[u];
+          if (sl + kPrefetch < n) {
+            ring[u] = *reinterpret_cast<const f32x4*>(Bu + (int64_t)(sl + kPrefetch) * D * D);
+            zring[u] = zl ? csu[(int64_t)(sl + kPrefetch) * D] : 0.f;
+          }
+        }
+      }
+      __syncthreads();  // the group's blocks are in LDS (and the other half is free again)
+#pragma unroll
+      for (int uu = 0; uu < GS; ++uu) {
+        const int sl = s0 + g0 + uu;
+        if (sl < n) {
+          vec4_t<T> y;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = buf[uu][tr * TS + 4 * tq + j];
+          store4<T>(snap + (int64_t)sl * D * D, y);
+        }
       }
     }
   }
   *reinterpret_cast<f32x4*>(a.M_out + (int64_t)unit * D * D + moff) = acc;
+  if (zl) a.z_out[(int64_t)unit * D + zj] = z;
 }
 
 // ---- the same step, bf16, d = 128, delta rule: one workgroup per unit ------
@@ -685,23 +714,29 @@ hipError_t launch_products_t(const AffineArgs& a, hipStream_t stream) {
 template <typename T, int D, int RULE>
 hipError_t launch_affine_t(const AffineArgs& a, hipStream_t stream) {
   const unsigned segs = (unsigned)(a.units * a.s_count);
-  if constexpr (sizeof(T) == 2 && D == 128 && RULE == kRuleLinear) {
-    // the column sums come out of the products' pass over K
-    hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear, true>), dim3(segs), dim3(512), 0, stream,
-                       a);
-    hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
-    const hipError_t e = launch_products_t<T, D, RULE>(a, stream);
-    if (e != hipSuccess) return e;
-  }
   if constexpr (RULE == kRuleLinear) {
     if (!a.reverse) {
-      hipLaunchKernelGGL((linear_prefix_kernel<T, D>), dim3((unsigned)(a.units * (D / 32) * (D / 32))),
-                         dim3(256), 0, stream, a);
+      // the linear rule forward: B_s and the column sums, then both running
+      // sums (M and z) in one segment-parallel prefix
+      if constexpr (sizeof(T) == 2 && D == 128) {
+        // the column sums come out of the products' pass over K
+        hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear, true>), dim3(segs), dim3(512), 0,
+                           stream, a);
+      } else {
+        hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
+        const hipError_t e = launch_products_t<T, D, RULE>(a, stream);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((linear_prefix_kernel<T, D>),
+                         dim3((unsigned)(a.units * (D / 32) * (D / 32))), dim3(256), 0, stream, a);
       return hipGetLastError();
     }
+  }
+  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3(segs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prefix_kernel<D>), dim3((unsigned)a.units), dim3(D), 0, stream, a);
+  {
+    const hipError_t e = launch_products_t<T, D, RULE>(a, stream);
+    if (e != hipSuccess) return e;
   }
   if constexpr (sizeof(T) == 2 && D == 128 && RULE == kRuleDelta) {
     // one workgroup per unit once the units alone fill the CUs; with fewer
