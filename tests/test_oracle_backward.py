@@ -16,28 +16,31 @@ import oracle
 from oracle import gradients as bw
 
 CASES = [
-    # B, Hq, Hkv, L, d, seg_len
+    # B, Hq, Hkv, L, d (the key width), seg_len[, d_value]
     (1, 2, 1, 7, 3, 3),   # ragged last segment, two query heads on one KV head
     (2, 4, 2, 6, 2, 2),   # GQA 2, batch 2
     (1, 1, 1, 5, 3, 8),   # one segment (seg_len > L)
     (1, 1, 1, 4, 2, 1),   # one-token segments
+    (1, 2, 1, 7, 2, 3, 3),  # values wider than keys, ragged
+    (1, 2, 2, 6, 3, 4, 2),  # values narrower than keys
 ]
 
 
 def make(case, seed):
-    B, Hq, Hkv, L, d, N = case
+    B, Hq, Hkv, L, d, N = case[:6]
+    dv = case[6] if len(case) > 6 else d
     r = np.random.default_rng(seed)
     x = dict(
         q=r.standard_normal((B, Hq, L, d)),
         k=r.standard_normal((B, Hkv, L, d)),
-        v=r.standard_normal((B, Hkv, L, d)),
+        v=r.standard_normal((B, Hkv, L, dv)),
         beta=r.standard_normal(Hq),
-        M0=0.3 * r.standard_normal((B, Hkv, d, d)),
+        M0=0.3 * r.standard_normal((B, Hkv, d, dv)),
         z0=0.5 + r.random((B, Hkv, d)),
     )
     cot = dict(
-        d_out=r.standard_normal((B, Hq, L, d)),
-        dM_final=r.standard_normal((B, Hkv, d, d)),
+        d_out=r.standard_normal((B, Hq, L, dv)),
+        dM_final=r.standard_normal((B, Hkv, d, dv)),
         dz_final=r.standard_normal((B, Hkv, d)),
     )
     return x, cot, N
@@ -87,6 +90,7 @@ def fd_cached(case, rule, seed):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}L{c[3]}d{c[4]}N{c[5]}"
+                                             + (f"dv{c[6]}" if len(c) > 6 else "")
                                              for c in CASES])
 @pytest.mark.parametrize("rule", ["linear", "delta"])
 def test_backward_matches_finite_differences(case, rule):
