@@ -42,6 +42,12 @@ SIGNATURES = {
         + [ctypes.POINTER(_c_p), _c_i32]),
     "infini_attn_forward_train": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32] + [_c_p] * 10 + [_c_p, _c_size, _c_p]),
+    "infini_attn_forward_train_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 10 + [_c_p, _c_size, _c_p]),
+    "infini_attn_backward_workspace_size_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
+    "infini_attn_backward_kv": (
+        _c_i32, [_c_i64] * 7 + [_c_i32, _c_i32] + [_c_p] * 17 + [_c_p, _c_size, _c_p]),
     "infini_attn_backward_workspace_size": (
         _c_i32, [_c_i64] * 6 + [_c_i32, _c_i32, ctypes.POINTER(_c_size)]),
     "infini_attn_backward": (
@@ -149,7 +155,8 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
     ``events``: optional list of torch.cuda.Event to record around each phase
     (see infini_attn_forward_timed); each must have been recorded once so that
     its HIP event exists. ``lse``: a float32 [B,Hq,L] tensor to receive the
-    softmax statistics (infini_attn_forward_train); not with ``events``.
+    softmax statistics (infini_attn_forward_train, _kv with two widths); not
+    with ``events``.
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -159,8 +166,6 @@ def forward(q, k, v, beta, M0, z0, seg_len, rule, *, out=None, M_final=None, z_f
                          f"{tuple(v.shape)}")
     if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, dv) or z0.shape != (B, Hkv, d):
         raise ValueError("beta, M0 or z0 has the wrong shape")
-    if dv != d and lse is not None:
-        raise ValueError("lse needs d_value == d_key")
     if q.dtype not in DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
     if beta.dtype != torch.float32 or M0.dtype != torch.float32 or z0.dtype != torch.float32:
@@ -211,8 +216,13 @@ def _forward_call(lib, B, Hq, Hkv, L, d, dv, seg_len, rule, q, k, v, beta, M0, z
         if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous() \
                 or lse.device != dev:
             raise ValueError("lse must be a contiguous float32 [B,Hq,L] tensor on the GPU of q")
-        st = lib.infini_attn_forward_train(*args[:17], _ptr(lse), *args[17:])
-        name = "infini_attn_forward_train"
+        if dv != d:
+            st = lib.infini_attn_forward_train_kv(*args[:5], dv, *args[5:17], _ptr(lse),
+                                                  *args[17:])
+            name = "infini_attn_forward_train_kv"
+        else:
+            st = lib.infini_attn_forward_train(*args[:17], _ptr(lse), *args[17:])
+            name = "infini_attn_forward_train"
     elif events:
         handles = (_c_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
         if dv != d:
@@ -362,13 +372,22 @@ def forward_train(q, k, v, beta, M0, z0, seg_len, rule, **kw):
     return out, M_final, z_final, lse
 
 
-def backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, dtype):
-    """Workspace bytes of a backward call with these sizes."""
+def backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, dtype, d_value=None):
+    """Workspace bytes of a backward call with these sizes (of
+    infini_attn_backward_kv when d_value is given and differs from d)."""
     n = _c_size(0)
-    st = load_library().infini_attn_backward_workspace_size(B, Hq, Hkv, L, d, seg_len, RULES[rule],
-                                                            DTYPES[dtype], ctypes.byref(n))
+    lib = load_library()
+    if d_value is None or d_value == d:
+        st = lib.infini_attn_backward_workspace_size(B, Hq, Hkv, L, d, seg_len, RULES[rule],
+                                                     DTYPES[dtype], ctypes.byref(n))
+        name = "infini_attn_backward_workspace_size"
+    else:
+        st = lib.infini_attn_backward_workspace_size_kv(B, Hq, Hkv, L, d, d_value, seg_len,
+                                                        RULES[rule], DTYPES[dtype],
+                                                        ctypes.byref(n))
+        name = "infini_attn_backward_workspace_size_kv"
     if st != 0:
-        raise InfiniAttnError(st, "infini_attn_backward_workspace_size")
+        raise InfiniAttnError(st, name)
     return int(n.value)
 
 
@@ -379,16 +398,18 @@ def backward(q, k, v, beta, M0, z0, seg_len, rule, out, lse, d_out, dM_final=Non
     The forward's inputs, its out and lse (forward_train), and the gradients
     d_out (like out), dM_final (like M0) and dz_final (like z0; either may be
     None for zero). Returns (dq, dk, dv, dbeta, dM0, dz0). Asynchronous on
-    ``stream`` (or torch's current stream).
+    ``stream`` (or torch's current stream). v may have another width dv than
+    q and k (out, d_out [B,Hq,L,dv], M0 [B,Hkv,d,dv]): infini_attn_backward_kv.
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
-    if not (k.shape == v.shape == (B, Hkv, L, d)):
-        raise ValueError("k and v must be [B,Hkv,L,d]")
-    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, d) or z0.shape != (B, Hkv, d):
+    dv_w = v.shape[-1] if v.dim() == 4 else -1
+    if not (k.shape == (B, Hkv, L, d) and v.shape == (B, Hkv, L, dv_w)):
+        raise ValueError("k must be [B,Hkv,L,d] and v [B,Hkv,L,dv]")
+    if beta.shape != (Hq,) or M0.shape != (B, Hkv, d, dv_w) or z0.shape != (B, Hkv, d):
         raise ValueError("beta, M0 or z0 has the wrong shape")
-    if out.shape != q.shape or d_out.shape != q.shape or lse.shape != (B, Hq, L):
-        raise ValueError("out and d_out must be like q, lse [B,Hq,L]")
+    if out.shape != (B, Hq, L, dv_w) or d_out.shape != out.shape or lse.shape != (B, Hq, L):
+        raise ValueError("out and d_out must be [B,Hq,L,dv], lse [B,Hq,L]")
     if q.dtype not in DTYPES or any(t.dtype != q.dtype for t in (k, v, out, d_out)):
         raise TypeError("q, k, v, out and d_out must share one dtype, float32 or bfloat16")
     f32 = [beta, M0, z0, lse] + [t for t in (dM_final, dz_final) if t is not None]
@@ -411,20 +432,27 @@ def backward(q, k, v, beta, M0, z0, seg_len, rule, out, lse, d_out, dM_final=Non
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbeta, dM0, dz0 = torch.empty_like(beta), torch.empty_like(M0), torch.empty_like(z0)
     if workspace is None:
-        workspace = torch.empty(backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, q.dtype),
+        workspace = torch.empty(backward_workspace_size(B, Hq, Hkv, L, d, seg_len, rule, q.dtype,
+                                                        d_value=dv_w),
                                 dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     opt = lambda t: _ptr(t) if t is not None else ctypes.c_void_p(0)
-    st = load_library().infini_attn_backward(
-        B, Hq, Hkv, L, d, seg_len, RULES[rule], DTYPES[q.dtype],
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
-        _ptr(out), _ptr(lse), _ptr(d_out), opt(dM_final), opt(dz_final),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0),
-        _ptr(workspace), workspace.numel() * workspace.element_size(),
-        ctypes.c_void_p(stream.cuda_stream))
+    args = [RULES[rule], DTYPES[q.dtype],
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(M0), _ptr(z0),
+            _ptr(out), _ptr(lse), _ptr(d_out), opt(dM_final), opt(dz_final),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dM0), _ptr(dz0),
+            _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream.cuda_stream)]
+    lib = load_library()
+    if dv_w != d:
+        st = lib.infini_attn_backward_kv(B, Hq, Hkv, L, d, dv_w, seg_len, *args)
+        name = "infini_attn_backward_kv"
+    else:
+        st = lib.infini_attn_backward(B, Hq, Hkv, L, d, seg_len, *args)
+        name = "infini_attn_backward"
     if st != 0:
-        raise InfiniAttnError(st, "infini_attn_backward")
+        raise InfiniAttnError(st, name)
     return dq, dk, dv, dbeta, dM0, dz0
 
 

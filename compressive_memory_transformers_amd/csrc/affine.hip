@@ -463,7 +463,9 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
 // (-Phi^T diag(1/den) Phi), so dM_{s-1} = dM_s + A_s dM_s + C_s has this form
 // with B_s = C_s, and the snapshot written before step s is dM_s.
 
-template <typename T, int D, int RULE>
+// D: the rows of M (the key width), DV: its columns (the value width); A_s is
+// D x D.
+template <typename T, int D, int RULE, int DV = D>
 __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
   constexpr int NC = D / 16;
   constexpr int MTS = D + pad16<T>();
@@ -472,23 +474,23 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 31, h = lane >> 5;
-  const int slab = blockIdx.x % (D / 32), unit = blockIdx.x / (D / 32);
+  const int slab = blockIdx.x % (DV / 32), unit = blockIdx.x / (DV / 32);
   const int col0 = 32 * slab;
 
   // this lane's 16 entries of the slab: rows 32w + acc_row(r, h), column col0 + i
   f32x16 acc;
-  const float* Min = a.M_in + (int64_t)unit * D * D;
+  const float* Min = a.M_in + (int64_t)unit * D * DV;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = Min[(32 * w + acc_row(r, h)) * D + col0 + i];
+  for (int r = 0; r < 16; ++r) acc[r] = Min[(32 * w + acc_row(r, h)) * DV + col0 + i];
 
   for (int it = 0; it < a.s_count; ++it) {
     const int sl = a.reverse ? a.s_count - 1 - it : it;
     const int64_t seg = (int64_t)unit * a.s_count + sl;
     // issue this segment's loads first; they are independent of M
     float bv[16];
-    const float* Bs = a.Bmat + seg * D * D;
+    const float* Bs = a.Bmat + seg * D * DV;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bv[r] = Bs[(32 * w + acc_row(r, h)) * D + col0 + i];
+    for (int r = 0; r < 16; ++r) bv[r] = Bs[(32 * w + acc_row(r, h)) * DV + col0 + i];
     frag_t<T> af[NC];
     if constexpr (DELTA) {
       const T* As = static_cast<const T*>(a.Amat) + seg * D * D + (int64_t)(32 * w + i) * D;
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
     }
 
     // the state before segment s: snapshot (M^T, element type)
-    T* sM = static_cast<T*>(a.snapM) + seg * D * D + (int64_t)(col0 + i) * D + 32 * w + 4 * h;
+    T* sM = static_cast<T*>(a.snapM) + seg * D * DV + (int64_t)(col0 + i) * D + 32 * w + 4 * h;
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       vec4_t<T> y;
@@ -516,9 +518,9 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
     if constexpr (DELTA) __syncthreads();
   }
 
-  float* Mout = a.M_out + (int64_t)unit * D * D;
+  float* Mout = a.M_out + (int64_t)unit * D * DV;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) Mout[(32 * w + acc_row(r, h)) * D + col0 + i] = acc[r];
+  for (int r = 0; r < 16; ++r) Mout[(32 * w + acc_row(r, h)) * DV + col0 + i] = acc[r];
 }
 
 // ---- the linear rule's chain as a prefix sum over segments -----------------
@@ -794,6 +796,36 @@ hipError_t launch_chain_d(int d, int rule, const AffineArgs& a, hipStream_t stre
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream) {
   return dtype == kBF16 ? launch_chain_d<bf16>(d, rule, a, stream)
                         : launch_chain_d<float>(d, rule, a, stream);
+}
+
+template <int DK, int DV>
+hipError_t launch_chain_kv_t(int rule, const AffineArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.units * (DV / 32))), block(DK / 32 * 64);
+  if (rule == kRuleDelta)
+    hipLaunchKernelGGL((chain_kernel<float, DK, kRuleDelta, DV>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((chain_kernel<float, DK, kRuleLinear, DV>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_chain_kv_v(int dv, int rule, const AffineArgs& a, hipStream_t stream) {
+  switch (dv) {
+    case 32: return launch_chain_kv_t<DK, 32>(rule, a, stream);
+    case 64: return launch_chain_kv_t<DK, 64>(rule, a, stream);
+    case 128: return launch_chain_kv_t<DK, 128>(rule, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_chain_kv_f32(int dk, int dv, int rule, const AffineArgs& a,
+                               hipStream_t stream) {
+  switch (dk) {
+    case 32: return launch_chain_kv_v<32>(dv, rule, a, stream);
+    case 64: return launch_chain_kv_v<64>(dv, rule, a, stream);
+    case 128: return launch_chain_kv_v<128>(dv, rule, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStream_t stream) {

@@ -600,6 +600,20 @@ infini_status_t infini_attn_forward_train(int64_t B, int64_t Hq, int64_t Hkv, in
                       M_final, z_final, lse, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
+infini_status_t infini_attn_forward_train_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                             int64_t d_key, int64_t d_value, int64_t seg_len,
+                                             int32_t rule, int32_t dtype, const void* q,
+                                             const void* k, const void* v, const float* beta,
+                                             const float* M0, const float* z0, void* out,
+                                             float* M_final, float* z_final, float* lse,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (lse == nullptr || d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return forward_impl(B, Hq, Hkv, L, d_key, seg_len, rule, dtype, q, k, v, beta, M0, z0, out,
+                      M_final, z_final, lse, workspace, workspace_bytes, stream, nullptr, 0,
+                      d_value);
+}
+
 infini_status_t infini_attn_forward_timed(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
                                           int64_t d, int64_t seg_len, int32_t rule,
                                           int32_t dtype, const void* q, const void* k,
@@ -877,19 +891,22 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
     cur += align_up(bytes);
     return r;
   };
-  const size_t d = (size_t)p.d, e = (size_t)p.e, units = (size_t)p.units, S = (size_t)p.S;
+  // d: the key width, dv: the value width; M-shaped buffers are d x dv
+  const size_t d = (size_t)p.d, dv = (size_t)p.dv, e = (size_t)p.e, units = (size_t)p.units,
+               S = (size_t)p.S;
+  const size_t dmax = d > dv ? d : dv;
   const size_t qrows = (size_t)(B * Hq * L), krows = (size_t)(B * Hkv * L);
   const bool delta = rule == INFINI_RULE_DELTA;
-  b.stM = take(units * d * d * 4);
+  b.stM = take(units * d * dv * 4);
   b.stz = take(units * d * 4);
-  b.zeroM = take(units * d * d * 4);
-  b.snapM = take(units * S * d * d * e);
+  b.zeroM = take(units * d * dv * 4);
+  b.snapM = take(units * S * d * dv * e);
   b.snapZ = take(units * S * d * 4);
   b.colsum = take(units * S * d * 4);
-  b.Bmat = take(units * S * d * d * 4);
+  b.Bmat = take(units * S * d * dv * 4);
   b.Amat = delta ? take(units * S * d * d * e) : 0;
-  b.dMsnap = take(units * S * d * d * e);
-  b.dMsnap_f = take(units * S * d * d * 4);
+  b.dMsnap = take(units * S * d * dv * e);
+  b.dMsnap_f = take(units * S * d * dv * 4);
   b.Amat_f = delta ? take(units * S * d * d * 4) : 0;
   b.e_ret = take(units * S * d * 4);
   b.e_upd = take(units * S * d * 4);
@@ -899,20 +916,20 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
     const size_t chunks = ((size_t)(Hq / Hkv) * n + 511) / 512;
     b.wsum_part = take(units * S * chunks * d * 4);
   }
-  if (!fused) b.nm = take(qrows * d * 4);
-  b.dn = take(qrows * d * e);
+  if (!fused) b.nm = take(qrows * dmax * 4);  // sigma(Q) M (dv), then dQ's retrieval part (d)
+  b.dn = take(qrows * dv * e);
   b.delta = take(qrows * 4);
   b.dg = take(qrows * 4);
   b.dden = take(qrows * 4);
   b.dk_acc = take(krows * d * 4);
-  b.dv_acc = take(krows * d * 4);
-  if (!fused) b.du_buf = take(krows * d * 4);
+  b.dv_acc = take(krows * dv * 4);
+  if (!fused) b.du_buf = take(krows * dv * 4);
   b.dphi = take(krows * d * 4);
   if (delta) {
     if (!fused) {
-      b.p_buf = take(krows * d * 4);
-      b.u_el = take(krows * d * e);
-      b.dp_el = take(krows * d * e);
+      b.p_buf = take(krows * dv * 4);
+      b.u_el = take(krows * dv * e);
+      b.dp_el = take(krows * dv * e);
     }
     b.dc = take(krows * 4);
     b.phi_f = take(krows * d * 4);
@@ -942,6 +959,18 @@ infini::GemmArgs gemm_args(const void* A, const void* B, float* C, int32_t M, in
   return g;
 }
 
+infini_status_t backward_workspace_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
+                                       int64_t dv, int64_t seg_len, int32_t rule, int32_t dtype,
+                                       size_t* bytes) {
+  Plan p;
+  const infini_status_t st = check_sizes_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, dtype, &p);
+  if (st != INFINI_OK) return st;
+  if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
+  const bool fused = d == dv && infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
+  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule, fused).total;
+  return INFINI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -949,28 +978,36 @@ extern "C" {
 infini_status_t infini_attn_backward_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
                                                     int64_t d, int64_t seg_len, int32_t rule,
                                                     int32_t dtype, size_t* bytes) {
-  Plan p;
-  const infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
-  if (st != INFINI_OK) return st;
-  if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
-  const bool fused = infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
-  if (bytes) *bytes = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule, fused).total;
-  return INFINI_OK;
+  return backward_workspace_impl(B, Hq, Hkv, L, d, d, seg_len, rule, dtype, bytes);
 }
 
-infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
-                                     int64_t seg_len, int32_t rule, int32_t dtype,
-                                     const void* q, const void* k, const void* v,
-                                     const float* beta, const float* M0, const float* z0,
-                                     const void* out, const float* lse, const void* d_out,
-                                     const float* dM_final, const float* dz_final, void* dq,
-                                     void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+infini_status_t infini_attn_backward_workspace_size_kv(int64_t B, int64_t Hq, int64_t Hkv,
+                                                       int64_t L, int64_t d_key, int64_t d_value,
+                                                       int64_t seg_len, int32_t rule,
+                                                       int32_t dtype, size_t* bytes) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return backward_workspace_impl(B, Hq, Hkv, L, d_key, d_value, seg_len, rule, dtype, bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+// d: the key width, dv: the value width ("Infini-Attention" (AI Wiki), "How
+// does the compressive memory work?": M is d_key x d_value).
+infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t dv,
+                              int64_t seg_len, int32_t rule, int32_t dtype, const void* q,
+                              const void* k, const void* v, const float* beta, const float* M0,
+                              const float* z0, const void* out, const float* lse,
+                              const void* d_out, const float* dM_final, const float* dz_final,
+                              void* dq, void* dk, void* dvv, float* dbeta, float* dM0,
+                              float* dz0, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   Plan p;
-  infini_status_t st = check_sizes(B, Hq, Hkv, L, d, seg_len, rule, dtype, &p);
+  infini_status_t st = check_sizes_kv(B, Hq, Hkv, L, d, dv, seg_len, rule, dtype, &p);
   if (st != INFINI_OK) return st;
   if ((int64_t)p.units * p.S > INT32_MAX || B * Hq * p.S > INT32_MAX) return INFINI_ERR_INVALID_ARG;
-  const void* required[] = {q, k, v, beta, M0, z0, out, lse, d_out, dq, dk, dv, dbeta, dM0, dz0,
+  const void* required[] = {q, k, v, beta, M0, z0, out, lse, d_out, dq, dk, dvv, dbeta, dM0, dz0,
                             workspace};
   for (const void* ptr : required)
     if (ptr == nullptr) return INFINI_ERR_INVALID_ARG;
@@ -979,17 +1016,18 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   if ((dM_final && !aligned16(dM_final)) || (dz_final && !aligned16(dz_final)))
     return INFINI_ERR_MISALIGNED;
   const size_t e = (size_t)p.e;
-  const size_t nq = (size_t)(B * Hq * L * d) * e, nkv = (size_t)(B * Hkv * L * d) * e;
-  const size_t nM = (size_t)(B * Hkv * d * d) * 4, nz = (size_t)(B * Hkv * d) * 4;
+  const size_t nq = (size_t)(B * Hq * L * d) * e, nk = (size_t)(B * Hkv * L * d) * e;
+  const size_t nv = (size_t)(B * Hkv * L * dv) * e, no = (size_t)(B * Hq * L * dv) * e;
+  const size_t nM = (size_t)(B * Hkv * d * dv) * 4, nz = (size_t)(B * Hkv * d) * 4;
   const size_t nrow = (size_t)(B * Hq * L) * 4, nbeta = (size_t)Hq * 4;
-  const bool bwd_mfma = infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
+  const bool bwd_mfma = d == dv && infini::attn_bwd_mfma_supported(dtype, (int)d, (int)(Hq / Hkv));
   const BwdLayout lay = bwd_layout(p, B, Hq, Hkv, L, seg_len, rule, bwd_mfma);
   if (workspace_bytes < lay.total) return INFINI_ERR_WORKSPACE;
   struct Range { const void* p; size_t n; };
-  const Range all[] = {{q, nq},         {k, nkv},         {v, nkv},      {beta, nbeta},
-                       {M0, nM},        {z0, nz},         {out, nq},     {lse, nrow},
-                       {d_out, nq},     {dM_final, nM},   {dz_final, nz}, {dq, nq},
-                       {dk, nkv},       {dv, nkv},        {dbeta, nbeta}, {dM0, nM},
+  const Range all[] = {{q, nq},         {k, nk},          {v, nv},       {beta, nbeta},
+                       {M0, nM},        {z0, nz},         {out, no},     {lse, nrow},
+                       {d_out, no},     {dM_final, nM},   {dz_final, nz}, {dq, nq},
+                       {dk, nk},        {dvv, nv},        {dbeta, nbeta}, {dM0, nM},
                        {dz0, nz},       {workspace, workspace_bytes}};
   // the outputs and the workspace (from entry 11 on) overlap no other argument
   const int n_all = (int)(sizeof(all) / sizeof(all[0]));
@@ -1004,10 +1042,11 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   auto E = [&](size_t off) { return static_cast<void*>(ws + off); };
   const int64_t S = p.S, units = p.units, G = Hq / Hkv;
-  const int32_t D = (int32_t)d;
+  const int32_t D = (int32_t)d, DV = (int32_t)dv;
   const int32_t N = (int32_t)(seg_len < L ? seg_len : L);  // rows of the longest segment
 
-  // 1. states before each segment (and A_s)
+  // 1. states before each segment: the affine form (one width), or the
+  // direct scan (two widths)
   AffineArgs fa{};
   fa.k = k;
   fa.v = v;
@@ -1026,7 +1065,25 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   fa.s_begin = 0;
   fa.s_count = (int32_t)S;
   fa.reverse = 0;
-  if (infini::launch_affine(dtype, D, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (d == dv) {
+    if (infini::launch_affine(dtype, D, rule, fa, s) != hipSuccess) return INFINI_ERR_HIP;
+  } else {
+    ScanArgs sa;
+    sa.k = k;
+    sa.v = v;
+    sa.M_in = M0;
+    sa.z_in = z0;
+    sa.M_out = F(lay.stM);
+    sa.z_out = F(lay.stz);
+    sa.snapM = E(lay.snapM);
+    sa.snapZ = F(lay.snapZ);
+    sa.L = L;
+    sa.seg_len = seg_len;
+    sa.units = (int32_t)units;
+    sa.s_begin = 0;
+    sa.s_count = (int32_t)S;
+    if (infini::launch_scan_kv(dtype, D, DV, rule, sa, s) != hipSuccess) return INFINI_ERR_HIP;
+  }
 
   infini::BwdArgs ba{};
   ba.q = q;
@@ -1062,7 +1119,7 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ba.dz0 = dz0;
   ba.dq = dq;
   ba.dk = dk;
-  ba.dv = dv;
+  ba.dv = dvv;
   ba.dbeta = dbeta;
   ba.L = L;
   ba.seg_len = seg_len;
@@ -1073,35 +1130,45 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ba.rule = rule;
   ba.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
 
-  const int64_t LD = L * d, ND = seg_len * d, DD = d * d;
+  // row strides: key side (q, k) d, value side (v, out, dn, M's columns) dv
+  const int64_t LD = L * d, ND = seg_len * d, LV = L * dv, NV = seg_len * dv, DDV = d * dv;
   // 2. retrieval. bf16 with d in {64, 128}: one fused kernel per 128 query
   // rows. Otherwise two products and a row kernel (query-side products:
   // hi = b * Hq + h, M_{s-1} of unit hi / G).
   if (bwd_mfma) {
     if (infini::launch_bwd_retrieval_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   } else {
-    {
-      infini::GemmArgs g = gemm_args(q, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
-      g.lda = g.ldb = g.ldc = D;
-      g.a_hi = g.c_hi = LD;
-      g.a_lo = g.c_lo = ND;
+    {  // nm = sigma(Q) M, [rows][dv]
+      infini::GemmArgs g = gemm_args(q, E(lay.snapM), ba.nm, N, DV, D, B * Hq, S, L, seg_len);
+      g.lda = D;
+      g.ldb = D;
+      g.ldc = DV;
+      g.a_hi = LD;
+      g.a_lo = ND;
+      g.c_hi = LV;
+      g.c_lo = NV;
       g.b_div = (int32_t)G;
-      g.b_hi = S * DD;
-      g.b_lo = DD;
-      g.tb = 1;  // op(B) = M, stored as M^T
+      g.b_hi = S * DDV;
+      g.b_lo = DDV;
+      g.tb = 1;  // op(B) = M, stored as M^T [dv][d]
       g.a_sigma = 1;
       g.clip = 1;
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
-    if (infini::launch_bwd_retrieval_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
-    {
-      infini::GemmArgs g = gemm_args(ba.dn, E(lay.snapM), ba.nm, N, D, D, B * Hq, S, L, seg_len);
-      g.lda = g.ldb = g.ldc = D;
-      g.a_hi = g.c_hi = LD;
-      g.a_lo = g.c_lo = ND;
+    if (infini::launch_bwd_retrieval_rows(dtype, D, DV, ba, s) != hipSuccess)
+      return INFINI_ERR_HIP;
+    {  // nm = dQ's retrieval part, [rows][d]
+      infini::GemmArgs g = gemm_args(ba.dn, E(lay.snapM), ba.nm, N, D, DV, B * Hq, S, L, seg_len);
+      g.lda = DV;
+      g.ldb = D;
+      g.ldc = D;
+      g.a_hi = LV;
+      g.a_lo = NV;
+      g.c_hi = LD;
+      g.c_lo = ND;
       g.b_div = (int32_t)G;
-      g.b_hi = S * DD;
-      g.b_lo = DD;
+      g.b_hi = S * DDV;
+      g.b_lo = DDV;
       g.tb = 0;  // op(B) = M^T as stored
       g.clip = 1;
       // epilogue: nm = (dn M^T + dden z^T) sigma'(Q), the retrieval part of dQ
@@ -1120,7 +1187,7 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   // C_s = sum over the group's heads of sigma(Q)^T dn, into Bmat: bf16 with
   // d = 128 by the recurrence's product kernel (one pass over q and dn),
   // otherwise one product per head, accumulating
-  if (dtype == INFINI_BF16 && d == 128) {
+  if (dtype == INFINI_BF16 && d == 128 && dv == 128) {
     AffineArgs ca{};
     ca.k = q;
     ca.v = E(lay.dn);
@@ -1135,15 +1202,18 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
     if (infini::launch_affine_products(dtype, D, ca, s) != hipSuccess) return INFINI_ERR_HIP;
   } else {
     for (int64_t hg = 0; hg < G; ++hg) {  // C_s into Bmat, summed over the group's heads
-      const size_t off = (size_t)(hg * LD) * e;
-      infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + off,
-                                     static_cast<const char*>(E(lay.dn)) + off, F(lay.Bmat), D, D,
-                                     (int32_t)seg_len, units, S, L, seg_len);
-      g.lda = g.ldb = g.ldc = D;
-      g.a_hi = g.b_hi = G * LD;
-      g.a_lo = g.b_lo = ND;
-      g.c_hi = S * DD;
-      g.c_lo = DD;
+      infini::GemmArgs g = gemm_args(static_cast<const char*>(q) + (size_t)(hg * LD) * e,
+                                     static_cast<const char*>(E(lay.dn)) + (size_t)(hg * LV) * e,
+                                     F(lay.Bmat), D, DV, (int32_t)seg_len, units, S, L, seg_len);
+      g.lda = D;
+      g.ldb = DV;
+      g.ldc = DV;
+      g.a_hi = G * LD;
+      g.a_lo = ND;
+      g.b_hi = G * LV;
+      g.b_lo = NV;
+      g.c_hi = S * DDV;
+      g.c_lo = DDV;
       g.ta = 1;  // op(A) = sigma(Q)^T
       g.a_sigma = 1;
       g.clip = 2;
@@ -1151,20 +1221,20 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
   }
-  if (infini::launch_bwd_row_weighted_sum(dtype, D, ba, true, s) != hipSuccess)
+  if (infini::launch_bwd_row_weighted_sum(dtype, D, DV, ba, true, s) != hipSuccess)
     return INFINI_ERR_HIP;
 
   // 3. dM_s for every segment, and dM0, in float. A_s = -Phi^T diag(1/c) Phi
   // from float sigma(K) and sigma(K) / c.
   if (rule == INFINI_RULE_DELTA) {
-    if (infini::launch_bwd_phi_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+    if (infini::launch_bwd_phi_rows(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
     infini::GemmArgs g = gemm_args(ba.phi_f, ba.phic_f, F(lay.Amat_f), D, D, (int32_t)seg_len,
                                    units, S, L, seg_len);
     g.lda = g.ldb = g.ldc = D;
     g.a_hi = g.b_hi = LD;
     g.a_lo = g.b_lo = ND;
-    g.c_hi = S * DD;
-    g.c_lo = DD;
+    g.c_hi = S * d * d;
+    g.c_lo = d * d;
     g.ta = 1;  // op(A) = Phi^T
     g.alpha = -1.f;
     g.clip = 2;
@@ -1172,7 +1242,7 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   }
   const float* dM_in = dM_final;
   if (dM_in == nullptr) {
-    if (infini::launch_fill_f32(F(lay.zeroM), 0.f, units * d * d, s) != hipSuccess)
+    if (infini::launch_fill_f32(F(lay.zeroM), 0.f, units * d * dv, s) != hipSuccess)
       return INFINI_ERR_HIP;
     dM_in = F(lay.zeroM);
   }
@@ -1182,14 +1252,16 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   ra.snapM = F(lay.dMsnap_f);
   ra.Amat = rule == INFINI_RULE_DELTA ? F(lay.Amat_f) : nullptr;
   ra.reverse = 1;
-  if (infini::launch_chain(INFINI_F32, D, rule, ra, s) != hipSuccess) return INFINI_ERR_HIP;
+  if ((d == dv ? infini::launch_chain(INFINI_F32, D, rule, ra, s)
+               : infini::launch_chain_kv_f32(D, DV, rule, ra, s)) != hipSuccess)
+    return INFINI_ERR_HIP;
   // dM_s^T in the element type for the update's products
-  if (infini::launch_round_f32(dtype, E(lay.dMsnap), F(lay.dMsnap_f), units * S * d * d, s) !=
+  if (infini::launch_round_f32(dtype, E(lay.dMsnap), F(lay.dMsnap_f), units * S * d * dv, s) !=
       hipSuccess)
     return INFINI_ERR_HIP;
 
   // 4. local attention
-  if (infini::launch_bwd_attention(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (infini::launch_bwd_attention(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
 
   // 5. update: dv_acc += sigma(K) dM_s, dphi, dc. bf16 with d in {64, 128}:
   // one fused kernel per 128 key rows; otherwise key-side products
@@ -1198,48 +1270,99 @@ infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t
   if (bwd_mfma) {
     if (infini::launch_bwd_update_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   } else {
-    auto kside = [&](const void* A, const void* Bm, float* C) {
-      infini::GemmArgs g = gemm_args(A, Bm, C, N, D, D, units, S, L, seg_len);
-      g.lda = g.ldb = g.ldc = D;
-      g.a_hi = g.c_hi = LD;
-      g.a_lo = g.c_lo = ND;
-      g.b_hi = S * DD;
-      g.b_lo = DD;
+    // key-side products, hi = unit: (rows of a d wide) x (M-shaped, stored
+    // transposed [dv][d]) -> rows dv wide, or (rows dv wide) x (the stored
+    // [dv][d] as is) -> rows d wide
+    auto to_v = [&](const void* A, const void* Bm, float* C) {
+      infini::GemmArgs g = gemm_args(A, Bm, C, N, DV, D, units, S, L, seg_len);
+      g.lda = D;
+      g.ldb = D;
+      g.ldc = DV;
+      g.a_hi = LD;
+      g.a_lo = ND;
+      g.c_hi = LV;
+      g.c_lo = NV;
+      g.b_hi = S * DDV;
+      g.b_lo = DDV;
+      g.tb = 1;
+      g.a_sigma = 1;
+      g.clip = 1;
+      return g;
+    };
+    auto to_k = [&](const void* A, const void* Bm, float* C) {
+      infini::GemmArgs g = gemm_args(A, Bm, C, N, D, DV, units, S, L, seg_len);
+      g.lda = DV;
+      g.ldb = D;
+      g.ldc = D;
+      g.a_hi = LV;
+      g.a_lo = NV;
+      g.c_hi = LD;
+      g.c_lo = ND;
+      g.b_hi = S * DDV;
+      g.b_lo = DDV;
+      g.tb = 0;
       g.clip = 1;
       return g;
     };
     {
-      infini::GemmArgs g = kside(k, E(lay.dMsnap), ba.du_buf);  // Phi dM_s (dM_s^T stored)
-      g.tb = 1;
-      g.a_sigma = 1;
+      infini::GemmArgs g = to_v(k, E(lay.dMsnap), ba.du_buf);  // Phi dM_s (dM_s^T stored)
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
     if (rule == INFINI_RULE_DELTA) {
-      infini::GemmArgs g = kside(k, E(lay.snapM), ba.p_buf);  // Phi M_{s-1}
-      g.tb = 1;
-      g.a_sigma = 1;
+      infini::GemmArgs g = to_v(k, E(lay.snapM), ba.p_buf);  // Phi M_{s-1}
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
-    if (infini::launch_bwd_update_rows(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
-    {
-      infini::GemmArgs g = kside(rule == INFINI_RULE_DELTA ? ba.u_el : v, E(lay.dMsnap), ba.dphi);
-      g.tb = 0;  // op(B) = dM_s^T as stored
+    if (infini::launch_bwd_update_rows(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+    {  // (V - pred, or V) dM_s^T
+      infini::GemmArgs g = to_k(rule == INFINI_RULE_DELTA ? ba.u_el : v, E(lay.dMsnap), ba.dphi);
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
     if (rule == INFINI_RULE_DELTA) {
-      infini::GemmArgs g = kside(ba.dp_el, E(lay.snapM), ba.dphi);  // + dP M_{s-1}^T
-      g.tb = 0;
+      infini::GemmArgs g = to_k(ba.dp_el, E(lay.snapM), ba.dphi);  // + dP M_{s-1}^T
       g.accumulate = 1;
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
   }
   if (rule == INFINI_RULE_DELTA &&
-      infini::launch_bwd_row_weighted_sum(dtype, D, ba, false, s) != hipSuccess)
+      infini::launch_bwd_row_weighted_sum(dtype, D, DV, ba, false, s) != hipSuccess)
     return INFINI_ERR_HIP;
 
   // 6. dz, dK, dV, dbeta
-  if (infini::launch_bwd_finish(dtype, D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
+  if (infini::launch_bwd_finish(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   return INFINI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+infini_status_t infini_attn_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d,
+                                     int64_t seg_len, int32_t rule, int32_t dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const float* beta, const float* M0, const float* z0,
+                                     const void* out, const float* lse, const void* d_out,
+                                     const float* dM_final, const float* dz_final, void* dq,
+                                     void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(B, Hq, Hkv, L, d, d, seg_len, rule, dtype, q, k, v, beta, M0, z0, out, lse,
+                       d_out, dM_final, dz_final, dq, dk, dv, dbeta, dM0, dz0, workspace,
+                       workspace_bytes, stream);
+}
+
+infini_status_t infini_attn_backward_kv(int64_t B, int64_t Hq, int64_t Hkv, int64_t L,
+                                        int64_t d_key, int64_t d_value, int64_t seg_len,
+                                        int32_t rule, int32_t dtype, const void* q,
+                                        const void* k, const void* v, const float* beta,
+                                        const float* M0, const float* z0, const void* out,
+                                        const float* lse, const void* d_out,
+                                        const float* dM_final, const float* dz_final, void* dq,
+                                        void* dk, void* dv, float* dbeta, float* dM0,
+                                        float* dz0, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (d_value < 1) return INFINI_ERR_INVALID_ARG;
+  return backward_impl(B, Hq, Hkv, L, d_key, d_value, seg_len, rule, dtype, q, k, v, beta, M0,
+                       z0, out, lse, d_out, dM_final, dz_final, dq, dk, dv, dbeta, dM0, dz0,
+                       workspace, workspace_bytes, stream);
 }
 
 // ---- the block with its projections -------------------------------------------

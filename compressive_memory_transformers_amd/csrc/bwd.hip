@@ -153,9 +153,11 @@ template <int D> struct RowLanes {
 
 // Retrieval backward, per query row: with nm = sigma(q) M_{s-1} (the
 // numerator of A_mem), writes delta, dg, dden and dn (element type).
-template <typename T, int D>
+// DK: the key width (q, z); DV: the value width (out, dout, nm, dn).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
-  using R = RowLanes<D>;
+  using RK = RowLanes<DK>;
+  using R = RowLanes<DV>;
   const int lane = threadIdx.x & 63;
   const int G = a.Hq / a.Hkv;
   const int64_t rows = (int64_t)a.B * a.Hq * a.L;
@@ -165,15 +167,15 @@ __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
     const int hq = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
     const int s = (int)(t / a.seg_len);
     const int64_t unit = (int64_t)b * a.Hkv + hq / G;
-    const float* z = a.snapZ + (unit * a.S + s) * D;
-    const T* q = static_cast<const T*>(a.q) + row * D;
-    const T* o = static_cast<const T*>(a.out) + row * D;
-    const T* dO = static_cast<const T*>(a.dout) + row * D;
-    const float* nm = a.nm + row * D;
+    const float* z = a.snapZ + (unit * a.S + s) * DK;
+    const T* q = static_cast<const T*>(a.q) + row * DK;
+    const T* o = static_cast<const T*>(a.out) + row * DV;
+    const T* dO = static_cast<const T*>(a.dout) + row * DV;
+    const float* nm = a.nm + row * DV;
     float den = 0.f;
 #pragma unroll
-    for (int e = 0; e < R::E; ++e)
-      if (R::ok(lane, e)) den += feature_map(to_f32<T>(q[64 * e + lane])) * z[64 * e + lane];
+    for (int e = 0; e < RK::E; ++e)
+      if (RK::ok(lane, e)) den += feature_map(to_f32<T>(q[64 * e + lane])) * z[64 * e + lane];
     den = wave_sum(den);
     float am[R::E], dov[R::E];
     float dam = 0.f, doo = 0.f;
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
     dam = wave_sum(dam);
     doo = wave_sum(doo);
     const float g = gate_of(a.beta, hq);
-    T* dn = static_cast<T*>(a.dn) + row * D;
+    T* dn = static_cast<T*>(a.dn) + row * DV;
 #pragma unroll
     for (int e = 0; e < R::E; ++e)
       if (R::ok(lane, e)) dn[64 * e + lane] = from_f32<T>(g * dov[e] / den);
@@ -266,9 +268,12 @@ __global__ __launch_bounds__(D) void wsum_final_kernel(BwdArgs a, int of_q, int 
 // dQ_t = sum_u dS_tu k_u / sqrt(d), dK_u = sum_t dS_tu q_t / sqrt(d),
 // dV_u = sum_t P_tu (1 - g) dout_t.
 
-template <typename T, int D>
+// DK: the key width (q, k, dq and its retrieval part in nm); DV: the value
+// width (v, dout).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void attn_dq_rows_kernel(BwdArgs a) {
-  using R = RowLanes<D>;
+  using R = RowLanes<DK>;
+  using RV = RowLanes<DV>;
   const int lane = threadIdx.x & 63;
   const int G = a.Hq / a.Hkv;
   const float c = a.scale_log2, inv_sqrt_d = a.scale_log2 / kLog2e;
@@ -281,25 +286,31 @@ __global__ __launch_bounds__(256) void attn_dq_rows_kernel(BwdArgs a) {
     const int64_t t0 = t / a.seg_len * a.seg_len;
     const float om = 1.f - gate_of(a.beta, hq);
     const float lse = a.lse[row], dl = a.delta[row];
-    float qv[R::E], dov[R::E], acc[R::E];
+    float qv[R::E], dov[RV::E], acc[R::E];
 #pragma unroll
     for (int e = 0; e < R::E; ++e) {
       const bool ok = R::ok(lane, e);
-      qv[e] = ok ? to_f32<T>(static_cast<const T*>(a.q)[row * D + 64 * e + lane]) : 0.f;
-      dov[e] = ok ? to_f32<T>(static_cast<const T*>(a.dout)[row * D + 64 * e + lane]) : 0.f;
+      qv[e] = ok ? to_f32<T>(static_cast<const T*>(a.q)[row * DK + 64 * e + lane]) : 0.f;
       acc[e] = 0.f;
     }
-    const T* K = static_cast<const T*>(a.k) + unit * a.L * D;
-    const T* V = static_cast<const T*>(a.v) + unit * a.L * D;
+#pragma unroll
+    for (int e = 0; e < RV::E; ++e)
+      dov[e] = RV::ok(lane, e)
+                   ? to_f32<T>(static_cast<const T*>(a.dout)[row * DV + 64 * e + lane])
+                   : 0.f;
+    const T* K = static_cast<const T*>(a.k) + unit * a.L * DK;
+    const T* V = static_cast<const T*>(a.v) + unit * a.L * DV;
     for (int64_t u = t0; u <= t; ++u) {
       float kv[R::E], sd = 0.f, dp = 0.f;
 #pragma unroll
       for (int e = 0; e < R::E; ++e) {
         const bool ok = R::ok(lane, e);
-        kv[e] = ok ? to_f32<T>(K[u * D + 64 * e + lane]) : 0.f;
+        kv[e] = ok ? to_f32<T>(K[u * DK + 64 * e + lane]) : 0.f;
         sd += qv[e] * kv[e];
-        dp += dov[e] * (ok ? to_f32<T>(V[u * D + 64 * e + lane]) : 0.f);
       }
+#pragma unroll
+      for (int e = 0; e < RV::E; ++e)
+        dp += dov[e] * (RV::ok(lane, e) ? to_f32<T>(V[u * DV + 64 * e + lane]) : 0.f);
       sd = wave_sum(sd);
       dp = wave_sum(dp);
       const float p = __builtin_amdgcn_exp2f(c * sd - lse);
@@ -307,17 +318,18 @@ __global__ __launch_bounds__(256) void attn_dq_rows_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < R::E; ++e) acc[e] += ds * kv[e];
     }
-    T* dq = static_cast<T*>(a.dq) + row * D;
+    T* dq = static_cast<T*>(a.dq) + row * DK;
 #pragma unroll
     for (int e = 0; e < R::E; ++e)
       if (R::ok(lane, e))
-        dq[64 * e + lane] = from_f32<T>(acc[e] * inv_sqrt_d + a.nm[row * D + 64 * e + lane]);
+        dq[64 * e + lane] = from_f32<T>(acc[e] * inv_sqrt_d + a.nm[row * DK + 64 * e + lane]);
   }
 }
 
-template <typename T, int D>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void attn_dkdv_rows_kernel(BwdArgs a) {
-  using R = RowLanes<D>;
+  using R = RowLanes<DK>;
+  using RV = RowLanes<DV>;
   const int lane = threadIdx.x & 63;
   const int G = a.Hq / a.Hkv;
   const float c = a.scale_log2, inv_sqrt_d = a.scale_log2 / kLog2e;
@@ -327,28 +339,35 @@ __global__ __launch_bounds__(256) void attn_dkdv_rows_kernel(BwdArgs a) {
     const int64_t unit = row / a.L, u = row % a.L;
     const int64_t b = unit / a.Hkv, j = unit % a.Hkv;
     const int64_t t1 = min<int64_t>((u / a.seg_len + 1) * a.seg_len, a.L);
-    float kv[R::E], vv[R::E], dk[R::E], dv[R::E];
+    float kv[R::E], vv[RV::E], dk[R::E], dv[RV::E];
 #pragma unroll
     for (int e = 0; e < R::E; ++e) {
-      const bool ok = R::ok(lane, e);
-      kv[e] = ok ? to_f32<T>(static_cast<const T*>(a.k)[row * D + 64 * e + lane]) : 0.f;
-      vv[e] = ok ? to_f32<T>(static_cast<const T*>(a.v)[row * D + 64 * e + lane]) : 0.f;
-      dk[e] = dv[e] = 0.f;
+      kv[e] = R::ok(lane, e) ? to_f32<T>(static_cast<const T*>(a.k)[row * DK + 64 * e + lane])
+                             : 0.f;
+      dk[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < RV::E; ++e) {
+      vv[e] = RV::ok(lane, e) ? to_f32<T>(static_cast<const T*>(a.v)[row * DV + 64 * e + lane])
+                              : 0.f;
+      dv[e] = 0.f;
     }
     for (int hg = 0; hg < G; ++hg) {
       const int hq = (int)(j * G + hg);
       const int64_t bh = b * a.Hq + hq;
       const float om = 1.f - gate_of(a.beta, hq);
-      const T* Q = static_cast<const T*>(a.q) + bh * a.L * D;
-      const T* dO = static_cast<const T*>(a.dout) + bh * a.L * D;
+      const T* Q = static_cast<const T*>(a.q) + bh * a.L * DK;
+      const T* dO = static_cast<const T*>(a.dout) + bh * a.L * DV;
       for (int64_t t = u; t < t1; ++t) {
-        float qv[R::E], dov[R::E], sd = 0.f, dp = 0.f;
+        float qv[R::E], dov[RV::E], sd = 0.f, dp = 0.f;
 #pragma unroll
         for (int e = 0; e < R::E; ++e) {
-          const bool ok = R::ok(lane, e);
-          qv[e] = ok ? to_f32<T>(Q[t * D + 64 * e + lane]) : 0.f;
-          dov[e] = ok ? to_f32<T>(dO[t * D + 64 * e + lane]) : 0.f;
+          qv[e] = R::ok(lane, e) ? to_f32<T>(Q[t * DK + 64 * e + lane]) : 0.f;
           sd += qv[e] * kv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < RV::E; ++e) {
+          dov[e] = RV::ok(lane, e) ? to_f32<T>(dO[t * DV + 64 * e + lane]) : 0.f;
           dp += dov[e] * vv[e];
         }
         sd = wave_sum(sd);
@@ -356,18 +375,17 @@ __global__ __launch_bounds__(256) void attn_dkdv_rows_kernel(BwdArgs a) {
         const float p = __builtin_amdgcn_exp2f(c * sd - a.lse[bh * a.L + t]);
         const float ds = p * (om * dp - a.delta[bh * a.L + t]);
 #pragma unroll
-        for (int e = 0; e < R::E; ++e) {
-          dk[e] += ds * qv[e];
-          dv[e] += p * om * dov[e];
-        }
+        for (int e = 0; e < R::E; ++e) dk[e] += ds * qv[e];
+#pragma unroll
+        for (int e = 0; e < RV::E; ++e) dv[e] += p * om * dov[e];
       }
     }
 #pragma unroll
     for (int e = 0; e < R::E; ++e)
-      if (R::ok(lane, e)) {
-        a.dk_acc[row * D + 64 * e + lane] = dk[e] * inv_sqrt_d;
-        a.dv_acc[row * D + 64 * e + lane] = dv[e];
-      }
+      if (R::ok(lane, e)) a.dk_acc[row * DK + 64 * e + lane] = dk[e] * inv_sqrt_d;
+#pragma unroll
+    for (int e = 0; e < RV::E; ++e)
+      if (RV::ok(lane, e)) a.dv_acc[row * DV + 64 * e + lane] = dv[e];
   }
 }
 
@@ -376,9 +394,12 @@ __global__ __launch_bounds__(256) void attn_dkdv_rows_kernel(BwdArgs a) {
 // Linear: dv_acc += du_buf (= Phi dM_s). Delta, with p_buf = Phi M_{s-1}:
 // c = Phi . z_{s-1}, pred = P / c, U = V - pred (u_el), dU = du_buf,
 // dv_acc += dU, dP = -dU / c (dp_el), dc = (dU . pred) / c.
-template <typename T, int D>
+// DK: the key width (k, z); DV: the value width (v, p_buf, du_buf, u_el,
+// dp_el, dv_acc).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void update_rows_kernel(BwdArgs a) {
-  using R = RowLanes<D>;
+  using RK = RowLanes<DK>;
+  using R = RowLanes<DV>;
   const int lane = threadIdx.x & 63;
   const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
   for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
@@ -386,24 +407,25 @@ __global__ __launch_bounds__(256) void update_rows_kernel(BwdArgs a) {
     if (a.rule == kRuleLinear) {
 #pragma unroll
       for (int e = 0; e < R::E; ++e)
-        if (R::ok(lane, e)) a.dv_acc[row * D + 64 * e + lane] += a.du_buf[row * D + 64 * e + lane];
+        if (R::ok(lane, e))
+          a.dv_acc[row * DV + 64 * e + lane] += a.du_buf[row * DV + 64 * e + lane];
       continue;
     }
     const int64_t unit = row / a.L, t = row % a.L;
     const int s = (int)(t / a.seg_len);
-    const float* z = a.snapZ + (unit * a.S + s) * D;
+    const float* z = a.snapZ + (unit * a.S + s) * DK;
     float cc = 0.f;
 #pragma unroll
-    for (int e = 0; e < R::E; ++e)
-      if (R::ok(lane, e))
-        cc += feature_map(to_f32<T>(static_cast<const T*>(a.k)[row * D + 64 * e + lane])) *
+    for (int e = 0; e < RK::E; ++e)
+      if (RK::ok(lane, e))
+        cc += feature_map(to_f32<T>(static_cast<const T*>(a.k)[row * DK + 64 * e + lane])) *
               z[64 * e + lane];
     cc = wave_sum(cc);
     float dcs = 0.f;
 #pragma unroll
     for (int e = 0; e < R::E; ++e)
       if (R::ok(lane, e)) {
-        const int64_t x = row * D + 64 * e + lane;
+        const int64_t x = row * DV + 64 * e + lane;
         const float pred = a.p_buf[x] / cc;
         const float du = a.du_buf[x];
         static_cast<T*>(a.u_el)[x] = from_f32<T>(to_f32<T>(static_cast<const T*>(a.v)[x]) - pred);
@@ -468,22 +490,26 @@ __global__ __launch_bounds__(D) void dz_scan_kernel(BwdArgs a) {
   a.dz0[unit * D + c] = dz;
 }
 
-// dK = dk_acc + (dphi + dc z_{s-1} + dz_s) sigma'(k), dV = dv_acc.
-template <typename T, int D>
+// dK = dk_acc + (dphi + dc z_{s-1} + dz_s) sigma'(k) (DK wide), dV = dv_acc
+// (DV wide).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void kv_out_kernel(BwdArgs a) {
-  const int64_t n = (int64_t)a.B * a.Hkv * a.L * D;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
+  const int64_t n = rows * DK;
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
-    const int64_t row = x / D;
-    const int c = (int)(x % D);
+    const int64_t row = x / DK;
+    const int c = (int)(x % DK);
     const int64_t unit = row / a.L, t = row % a.L;
     const int s = (int)(t / a.seg_len);
-    const int64_t sx = (unit * a.S + s) * D + c;
+    const int64_t sx = (unit * a.S + s) * DK + c;
     float dphi = a.dphi[x] + a.dzs[sx];
     if (a.rule == kRuleDelta) dphi += a.dc[row] * a.snapZ[sx];
     const float kv = to_f32<T>(static_cast<const T*>(a.k)[x]);
     static_cast<T*>(a.dk)[x] = from_f32<T>(a.dk_acc[x] + dphi * feature_map_grad(kv));
-    static_cast<T*>(a.dv)[x] = from_f32<T>(a.dv_acc[x]);
   }
+  const int64_t nv = rows * DV;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nv; x += (int64_t)gridDim.x * 256)
+    static_cast<T*>(a.dv)[x] = from_f32<T>(a.dv_acc[x]);
 }
 
 // dbeta_h = g (1 - g) sum over the batch and the stream of dg.
@@ -521,13 +547,15 @@ unsigned elem_grid(int64_t n) {
   return (unsigned)(g < 65536 ? g : 65536);
 }
 
-template <typename T, int D>
+// D: the key width; DV: the value width.
+template <typename T, int D, int DV>
 hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
   const int64_t qrows = (int64_t)a.B * a.Hq * a.L, krows = (int64_t)a.B * a.Hkv * a.L;
   const int64_t units = (int64_t)a.B * a.Hkv;
   switch (which) {
     case 0:
-      hipLaunchKernelGGL((retrieval_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((retrieval_rows_kernel<T, D, DV>), dim3(row_grid(qrows)), dim3(256), 0, s,
+                         a);
       break;
     case 2: {
       const int G = a.Hq / a.Hkv;
@@ -540,18 +568,21 @@ hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
       break;
     }
     case 3:
-      hipLaunchKernelGGL((attn_dkdv_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
-      hipLaunchKernelGGL((attn_dq_rows_kernel<T, D>), dim3(row_grid(qrows)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_dkdv_rows_kernel<T, D, DV>), dim3(row_grid(krows)), dim3(256), 0, s,
+                         a);
+      hipLaunchKernelGGL((attn_dq_rows_kernel<T, D, DV>), dim3(row_grid(qrows)), dim3(256), 0, s,
+                         a);
       break;
     case 4:
-      hipLaunchKernelGGL((update_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((update_rows_kernel<T, D, DV>), dim3(row_grid(krows)), dim3(256), 0, s, a);
       break;
     case 6:
       hipLaunchKernelGGL((phi_rows_kernel<T, D>), dim3(row_grid(krows)), dim3(256), 0, s, a);
       break;
     case 5:
       hipLaunchKernelGGL((dz_scan_kernel<D>), dim3((unsigned)units), dim3(D), 0, s, a);
-      hipLaunchKernelGGL((kv_out_kernel<T, D>), dim3(elem_grid(krows * D)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((kv_out_kernel<T, D, DV>), dim3(elem_grid(krows * (D > DV ? D : DV))),
+                         dim3(256), 0, s, a);
       hipLaunchKernelGGL((dbeta_kernel), dim3((unsigned)a.Hq), dim3(256), 0, s, a);
       break;
     default: return hipErrorInvalidValue;
@@ -559,18 +590,30 @@ hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_t(int d, int which, const BwdArgs& a, int arg, hipStream_t s) {
-  switch (d) {
-    case 32: return launch_d<T, 32>(which, a, arg, s);
-    case 64: return launch_d<T, 64>(which, a, arg, s);
-    case 128: return launch_d<T, 128>(which, a, arg, s);
+template <typename T, int D>
+hipError_t launch_v(int dv, int which, const BwdArgs& a, int arg, hipStream_t s) {
+  switch (dv) {
+    case 32: return launch_d<T, D, 32>(which, a, arg, s);
+    case 64: return launch_d<T, D, 64>(which, a, arg, s);
+    case 128: return launch_d<T, D, 128>(which, a, arg, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch(int dtype, int d, int which, const BwdArgs& a, int arg, hipStream_t s) {
-  return dtype == kBF16 ? launch_t<bf16>(d, which, a, arg, s) : launch_t<float>(d, which, a, arg, s);
+template <typename T>
+hipError_t launch_t(int d, int dv, int which, const BwdArgs& a, int arg, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_v<T, 32>(dv, which, a, arg, s);
+    case 64: return launch_v<T, 64>(dv, which, a, arg, s);
+    case 128: return launch_v<T, 128>(dv, which, a, arg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// d: the key width, dv: the value width
+hipError_t launch(int dtype, int d, int dv, int which, const BwdArgs& a, int arg, hipStream_t s) {
+  return dtype == kBF16 ? launch_t<bf16>(d, dv, which, a, arg, s)
+                        : launch_t<float>(d, dv, which, a, arg, s);
 }
 
 }  // namespace
@@ -590,25 +633,26 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 0, a, 0, s);
+hipError_t launch_bwd_retrieval_rows(int dtype, int d, int dv, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, dv, 0, a, 0, s);
 }
-hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
+hipError_t launch_bwd_row_weighted_sum(int dtype, int d, int dv, const BwdArgs& a, bool of_q,
                                        hipStream_t s) {
-  return launch(dtype, d, 2, a, of_q ? 1 : 0, s);
+  return launch(dtype, d, dv, 2, a, of_q ? 1 : 0, s);
 }
-hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  if (attn_bwd_mfma_supported(dtype, d, a.Hq / a.Hkv)) return launch_attn_bwd_mfma(d, a, s);
-  return launch(dtype, d, 3, a, 0, s);  // float, or d = 32: one wave per row
+hipError_t launch_bwd_attention(int dtype, int d, int dv, const BwdArgs& a, hipStream_t s) {
+  if (d == dv && attn_bwd_mfma_supported(dtype, d, a.Hq / a.Hkv))
+    return launch_attn_bwd_mfma(d, a, s);
+  return launch(dtype, d, dv, 3, a, 0, s);  // float, d = 32 or two widths: one wave per row
 }
-hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 4, a, 0, s);
+hipError_t launch_bwd_update_rows(int dtype, int d, int dv, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, dv, 4, a, 0, s);
 }
-hipError_t launch_bwd_finish(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 5, a, 0, s);
+hipError_t launch_bwd_finish(int dtype, int d, int dv, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, dv, 5, a, 0, s);
 }
-hipError_t launch_bwd_phi_rows(int dtype, int d, const BwdArgs& a, hipStream_t s) {
-  return launch(dtype, d, 6, a, 0, s);
+hipError_t launch_bwd_phi_rows(int dtype, int d, int dv, const BwdArgs& a, hipStream_t s) {
+  return launch(dtype, d, dv, 6, a, 0, s);
 }
 hipError_t launch_round_f32(int dtype, void* dst, const float* src, int64_t n, hipStream_t s) {
   if (dtype == kBF16)

@@ -196,10 +196,16 @@ struct BwdArgs {
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
+// The row steps below take the key width d and the value width dv (both in
+// {32, 64, 128}); rows of q, k, z, dk_acc, dphi, phi are d wide, rows of v,
+// out, dout, dn, dv_acc, du_buf, p_buf, u_el, dp_el dv wide; nm holds
+// sigma(q) M (dv wide) until the retrieval row step, then the retrieval part
+// of dQ (d wide).
 // Row step of the retrieval backward: delta, dg, dn, dden from nm, out, dout.
-hipError_t launch_bwd_retrieval_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_retrieval_rows(int dtype, int d, int dv, const BwdArgs& a,
+                                     hipStream_t stream);
 // e[unit][s] = sum over the segment's rows (and query heads if of_q) of w_t sigma(x_t).
-hipError_t launch_bwd_row_weighted_sum(int dtype, int d, const BwdArgs& a, bool of_q,
+hipError_t launch_bwd_row_weighted_sum(int dtype, int d, int dv, const BwdArgs& a, bool of_q,
                                        hipStream_t stream);
 // MFMA kernels of the local-attention gradients (attn_bwd.hip): bf16, d in {64, 128},
 // at most 64 query heads per KV head.
@@ -212,15 +218,15 @@ hipError_t launch_bwd_retrieval_mfma(int d, const BwdArgs& a, hipStream_t stream
 // sigma(K) dM_s, dphi = (V - pred or V) dM_s^T (+ dP M_{s-1}^T), dc.
 hipError_t launch_bwd_update_mfma(int d, const BwdArgs& a, hipStream_t stream);
 // Local-attention gradients: dk_acc, dv_acc (stored) and dq = nm + attention part.
-hipError_t launch_bwd_attention(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_attention(int dtype, int d, int dv, const BwdArgs& a, hipStream_t stream);
 // Row step of the delta rule's update backward (after p_buf, du_buf).
-hipError_t launch_bwd_update_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_update_rows(int dtype, int d, int dv, const BwdArgs& a, hipStream_t stream);
 // phi_f = sigma(K), phic_f = sigma(K) / (sigma(K) . z_{s-1}), per key row, in float.
-hipError_t launch_bwd_phi_rows(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_phi_rows(int dtype, int d, int dv, const BwdArgs& a, hipStream_t stream);
 // dst[i] = src[i] rounded to the element type (or copied, float).
 hipError_t launch_round_f32(int dtype, void* dst, const float* src, int64_t n, hipStream_t stream);
 // dz suffix scan and the final dK, dV, dbeta.
-hipError_t launch_bwd_finish(int dtype, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_finish(int dtype, int d, int dv, const BwdArgs& a, hipStream_t stream);
 
 // Wave count of the attention workgroup for a segment length: one wave per 32
 // query rows, at most four.
@@ -234,6 +240,10 @@ hipError_t launch_scan_kv(int dtype, int dk, int dv, int rule, const ScanArgs& a
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 // The chain step of the affine form alone (a.reverse honoured).
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
+// The same step in float with d_key = dk != d_value = dv: M, B_s [dk][dv] per
+// (unit, segment), A_s [dk][dk], snapshots M^T [dv][dk].
+hipError_t launch_chain_kv_f32(int dk, int dv, int rule, const AffineArgs& a,
+                               hipStream_t stream);
 // The linear rule's products alone, Bmat = sum over a.heads heads of
 // sigma(K)^T V per (unit, segment), bf16 with d = 128 (hipErrorInvalidValue
 // otherwise: the caller takes another path).

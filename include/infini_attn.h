@@ -303,6 +303,16 @@ infini_status_t infini_attn_forward_train(
     void* out, float* M_final, float* z_final, float* lse,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* infini_attn_forward_train with a key width different from the value width
+ * (the sizes and layouts of infini_attn_forward_kv, lse as above). */
+infini_status_t infini_attn_forward_train_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    void* out, float* M_final, float* z_final, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Backward pass ("Infini-Attention" (AI Wiki), "How is an Infini-attention
  * model trained?": gradients flow through the memory recurrence from segment
@@ -331,6 +341,32 @@ infini_status_t infini_attn_backward_workspace_size(
 infini_status_t infini_attn_backward(
     int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t seg_len,
     int32_t rule, int32_t dtype,
+    const void* q, const void* k, const void* v, const float* beta,
+    const float* M0, const float* z0,
+    const void* out, const float* lse, const void* d_out,
+    const float* dM_final, const float* dz_final,
+    void* dq, void* dk, void* dv, float* dbeta, float* dM0, float* dz0,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward with a key width different from the value width ("Infini-
+ * Attention" (AI Wiki), "How does the compressive memory work?": M maps
+ * d_key-dimensional keys to d_value-dimensional values), for the forward of
+ * infini_attn_forward_kv trained with the same loss. q, k, dq, dk are
+ * [.][L][d_key]; v, dv, out, d_out [.][L][d_value]; M0, dM_final, dM0
+ * [B][Hkv][d_key][d_value]; z0, dz_final, dz0 [B][Hkv][d_key]; lse from
+ * infini_attn_forward_train_kv.
+ * d_key, d_value in {32, 64, 128}; the rest as infini_attn_backward, which
+ * these calls equal when d_key == d_value. Two widths run the product path
+ * (float accumulation, one wave per row for the local attention): correct at
+ * every width pair, not tuned.
+ */
+infini_status_t infini_attn_backward_workspace_size_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype, size_t* bytes);
+infini_status_t infini_attn_backward_kv(
+    int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d_key, int64_t d_value,
+    int64_t seg_len, int32_t rule, int32_t dtype,
     const void* q, const void* k, const void* v, const float* beta,
     const float* M0, const float* z0,
     const void* out, const float* lse, const void* d_out,

@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
         "infini_attn_decode_workspace_size_kv",
         "infini_attn_forward", "infini_attn_forward_kv", "infini_attn_forward_kv_timed",
         "infini_attn_forward_noalloc", "infini_attn_forward_timed",
-        "infini_attn_forward_train", "infini_attn_status_string", "infini_attn_version",
+        "infini_attn_forward_train", "infini_attn_forward_train_kv",
+        "infini_attn_backward_kv", "infini_attn_backward_workspace_size_kv", "infini_attn_status_string", "infini_attn_version",
         "infini_attn_workspace_size", "infini_attn_workspace_size_kv"])
 
 

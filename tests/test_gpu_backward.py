@@ -53,12 +53,13 @@ CASES = [
 IDS = [f"B{c[0]}Hq{c[1]}Hkv{c[2]}L{c[3]}d{c[4]}N{c[5]}{str(c[6])[6:]}" for c in CASES]
 
 
-def run_case(lib, case, rule, seed, with_final=True):
+def run_case(lib, case, rule, seed, with_final=True, dv=None):
     B, Hq, Hkv, L, d, N, dt = case
-    inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=seed, m0_scale=0.3)
+    dv = d if dv is None else dv
+    inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=seed, m0_scale=0.3, dv=dv)
     g = torch.Generator(device="cpu").manual_seed(seed + 1)
-    d_out = torch.randn(B, Hq, L, d, generator=g).to(dt).to(DEV)
-    dM_f = torch.randn(B, Hkv, d, d, generator=g).to(DEV) if with_final else None
+    d_out = torch.randn(B, Hq, L, dv, generator=g).to(dt).to(DEV)
+    dM_f = torch.randn(B, Hkv, d, dv, generator=g).to(DEV) if with_final else None
     dz_f = torch.randn(B, Hkv, d, generator=g).to(DEV) if with_final else None
     out, _, _, lse = lib.forward_train(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"],
                                        inp["z0"], N, rule)
@@ -88,6 +89,26 @@ def test_gradients_match_the_oracle(lib, case, rule):
     errs, _ = run_case(lib, case, rule, seed=case[3] + case[5])
     _say("errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     tol = TOL[case[6]]
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (bad, tol)
+
+
+KV_PAIRS = [(32, 64), (32, 128), (64, 32), (64, 128), (128, 32), (128, 64)]
+
+
+@pytest.mark.parametrize("pair", KV_PAIRS, ids=[f"dk{a}dv{b}" for a, b in KV_PAIRS])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("rule", ["linear", "delta"])
+def test_gradients_with_kv_widths_match_the_oracle(lib, pair, dt, rule):
+    """infini_attn_backward_kv (after infini_attn_forward_train_kv): every
+    gradient against the oracle, for every ordered pair of widths, with GQA,
+    a ragged last segment and final-state gradients."""
+    dk, dv = pair
+    case = (1, 4, 2, 70, dk, 32, dt)
+    _say(f"kv widths {case} d_value {dv} {rule}")
+    errs, _ = run_case(lib, case, rule, seed=dk + 7 * dv, dv=dv)
+    _say("errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    tol = TOL[dt]
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, (bad, tol)
 
