@@ -481,12 +481,17 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
                                          const DmaTile<DK, NW, BN>& tile,
                                          const DmaTile<DV, NW, BN>& vtile, const bf16* K,
                                          const bf16* V, bf16* const* Ks, bf16* const* Vs, int n_s,
-                                         int w, int q0, DmaLane<DK, DV>& st, f32x16* sacc,
+                                         int w, int wfirst, DmaLane<DK, DV>& st, f32x16* sacc,
                                          float c, int row, int h, const bf16* Mts,
                                          const float* zs, float* Zs) {
   constexpr int NKB = BN / 32, NPC = BN / 16;
-  if (FULL || j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
-  if (FULL || j + 1 < n_kt) vtile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+  if (FULL) {
+    tile.template issue_full<true>(K, Ks[P], (j + 2) * BN, w);
+    vtile.template issue_full<false>(V, Vs[P ^ 1], (j + 1) * BN, w);
+  } else {
+    if (j + 2 < n_kt) tile.template issue<true>(K, Ks[P], (j + 2) * BN, n_s, w);
+    if (j + 1 < n_kt) vtile.template issue<false>(V, Vs[P ^ 1], (j + 1) * BN, n_s, w);
+  }
   if (!FULL && j + 1 == n_kt)
     dma_snapshot<DK, DV, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
   if (FULL || j + 1 < n_w) {
@@ -500,7 +505,7 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
     // the strategies for other instruction mixes were slower)
     if constexpr (FULL) __builtin_amdgcn_iglp_opt(0);
     const int k1 = (j + 1) * BN;
-    dma_max<DK, DV, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > q0 + w);
+    dma_max<DK, DV, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > wfirst);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = snext[kb];
   } else if (!FULL && j < n_w) {  // this wave's last tile
@@ -515,9 +520,17 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
 }
 
 // DK: the key width (Q, K); DV: the value width (V, the output).
-template <int DK, int DV, int NW, int BN>
+// PACK (NW query heads of one KV head per workgroup, the group size a
+// multiple of NW): wave w takes 32 consecutive positions of the group's head
+// w (lane i: position p0 + i), so the four waves share one diagonal, 32 keys
+// wide, where 128 rows of one head span 128. The key tiles past the diagonal
+// that a block computes and masks fall from 17 of a 2048-token segment's 64-key
+// tiles (128-row blocks, mean) to 16.5, and the masked diagonal work from two
+// tiles per block to one. The K and V tiles, M^T and z are the KV head's, shared by
+// the four heads as they are by four one-head blocks.
+template <int DK, int DV, int NW, int BN, bool PACK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
-  constexpr int BM = 32 * NW;
+  constexpr int BM = PACK ? 32 : 32 * NW;  // positions per block
   constexpr int NC = DK / 16, NDB = DV / 32;
   // four separate arrays, so that the compiler can tell a tile being loaded
   // by DMA from the tiles being read and does not wait for the load
@@ -539,34 +552,48 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
     if (t < per * 8) t = (t & 7) * per + (t >> 3);
   }
   const int G = a.Hq / a.Hkv;
+  // n_qt G blocks per (unit, segment), heaviest first: n_qt query tiles of
+  // 32 NW rows times G heads, or (PACK) NW n_qt position blocks of 32 times
+  // G / NW head groups; blocks past the segment's end return at once
   const int in_grp = a.n_qt * G;
   const int grp = t / in_grp, rr = t % in_grp;
-  const int qt = a.n_qt - 1 - rr / G;
-  const int hg = rr % G;
+  int q0, hg;
+  if constexpr (PACK) {
+    const int n_sub = G / NW;
+    q0 = (a.n_qt * NW - 1 - rr / n_sub) * BM;
+    hg = (rr % n_sub) * NW + w;
+  } else {
+    q0 = (a.n_qt - 1 - rr / G) * BM;
+    hg = rr % G;
+  }
   const int sl = grp % a.s_count;
   const int unit = grp / a.s_count;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int hq = kvh * G + hg;
   const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
   const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
-  const int q0 = qt * BM;
   if (q0 >= n_s) return;
 
   const int64_t qh = (int64_t)b * a.Hq + hq;
-  const float g = 1.f / (1.f + __expf(-a.beta[hq]));  // the gate, read early
   const bf16* Q = static_cast<const bf16*>(a.q) + (qh * a.L + seg_start) * DK;
   const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * DK;
   const bf16* V = static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * DV;
-  bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * DV;
 
-  // Rows are dealt to the waves round robin (row q0 + w + NW i for lane i),
-  // so every wave spans the whole block and meets the causal diagonal in the
-  // same key tiles: the waves run the same number of iterations and none
-  // idles at the barriers of the block's last tiles.
-  const int row = q0 + w + NW * i;  // this lane's query, relative to the segment
-  const int wave_first = q0 + w;
+  // Without PACK the rows are dealt to the waves round robin (row q0 + w +
+  // NW i for lane i), so every wave spans the whole block and meets the
+  // causal diagonal in the same key tiles: the waves run the same number of
+  // iterations and none idles at the barriers of the block's last tiles.
+  // With PACK every wave holds the same 32 positions (of its own head).
+  const int row = PACK ? q0 + i : q0 + w + NW * i;  // this lane's query, relative to the segment
+  int wave_first = PACK ? q0 : q0 + w;
+  // Opaque to the optimiser: with PACK, knowing wave_first == q0 (so every
+  // wave active) led it to keep about 32 more registers live through the key
+  // loop, which spilled at d = 128.
+  asm volatile("" : "+s"(wave_first));
   const bool wave_on = wave_first < n_s;
-  const int wave_last = wave_on ? wave_first + NW * min(31, (n_s - 1 - wave_first) / NW) : -1;
+  const int wave_last = !wave_on ? -1
+                        : PACK   ? min(q0 + 31, n_s - 1)
+                                 : wave_first + NW * min(31, (n_s - 1 - wave_first) / NW);
   const float c = a.scale_log2;
   const int n_kv = min(q0 + BM, n_s);
   const int n_kt = (n_kv + BN - 1) / BN;
@@ -605,28 +632,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   // When every row of the block is in the segment, iterations j whose next
   // tile j + 1 lies wholly below the block's first row are full for every
   // wave.
-  const int n_full = q0 + BM <= n_s ? q0 / BN - 1 : 0;
+  const int n_full = q0 + BM <= n_s ? min(q0 / BN - 1, n_s / BN - 2) : 0;
   const int64_t snap = (int64_t)unit * a.snap_count + a.snap_first + sl;
   const float* zs = a.snapZ + snap * DK;
   const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * DV * DK;
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
-    dma_iter<DK, DV, NW, BN, 0, true>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row, h,
+    dma_iter<DK, DV, NW, BN, 0, true>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row, h,
                                  Mts, zs, Zs);
-    dma_iter<DK, DV, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row,
                                  h, Mts, zs, Zs);
   }
   for (; j < n_kt; j += 2) {  // j is even here
-    dma_iter<DK, DV, NW, BN, 0, false>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 0, false>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row,
                                   h, Mts, zs, Zs);
     if (j + 1 < n_kt)
-      dma_iter<DK, DV, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, q0, st, sacc, c,
+      dma_iter<DK, DV, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c,
                                     row, h, Mts, zs, Zs);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's part of M^T and z has landed
   __syncthreads();
   if (!wave_on) return;
 
+  // the gate and the output rows, formed after the key loop so that they
+  // hold no registers through it
+  const float g = 1.f / (1.f + __expf(-a.beta[hq]));
+  bf16* O = static_cast<bf16*>(a.out) + (qh * a.L + seg_start) * DV;
   // M^T sits in the buffers the last tile (parity (n_kt - 1) % 2) freed
   const bool pl = ((n_kt - 1) & 1) != 0;
   const bf16* Ma = pl ? Ks[1] : Ks[0];
@@ -683,8 +714,17 @@ hipError_t launch_attn_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
   const int64_t G = a.Hq / a.Hkv;
   const int64_t total = units * a.s_count * a.n_qt * G;
   if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
-    hipLaunchKernelGGL((attn_kernel_dma<D, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
-                       stream, a);
+    bool packed = false;
+    if constexpr (NW == 4) {
+      if (G % NW == 0) {
+        packed = true;
+        hipLaunchKernelGGL((attn_kernel_dma<D, D, NW, BN, true>), dim3((unsigned)total),
+                           dim3(NW * 64), 0, stream, a);
+      }
+    }
+    if (!packed)
+      hipLaunchKernelGGL((attn_kernel_dma<D, D, NW, BN, false>), dim3((unsigned)total),
+                         dim3(NW * 64), 0, stream, a);
   } else {
     hipLaunchKernelGGL((attn_kernel<T, D, D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0,
                        stream, a);
@@ -728,11 +768,16 @@ namespace {
 template <typename T, int DK, int DV>
 hipError_t launch_attn_kv_t(const AttnArgs& a, int64_t units, hipStream_t stream) {
   constexpr int NW = 4, BN = 64;
-  const int64_t total = units * a.s_count * a.n_qt * (a.Hq / a.Hkv);
-  if constexpr (sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128))
-    hipLaunchKernelGGL((attn_kernel_dma<DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64),
-                       0, stream, a);
-  else
+  const int64_t G = a.Hq / a.Hkv;
+  const int64_t total = units * a.s_count * a.n_qt * G;
+  if constexpr (sizeof(T) == 2 && (DK == 64 || DK == 128) && (DV == 64 || DV == 128)) {
+    if (G % NW == 0)
+      hipLaunchKernelGGL((attn_kernel_dma<DK, DV, NW, BN, true>), dim3((unsigned)total),
+                         dim3(NW * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel_dma<DK, DV, NW, BN, false>), dim3((unsigned)total),
+                         dim3(NW * 64), 0, stream, a);
+  } else
     hipLaunchKernelGGL((attn_kernel<T, DK, DV, NW, BN>), dim3((unsigned)total), dim3(NW * 64),
                        0, stream, a);
   return hipGetLastError();

@@ -137,6 +137,19 @@ struct DmaTile {
       }
     }
   }
+  // issue() for a tile known to hold BN rows of the segment: every lane's
+  // offset is its fixed one plus a scalar step, with no clamping
+  template <bool IS_K>
+  __device__ __forceinline__ void issue_full(const bf16* X, bf16* Xs, int k0, int w) const {
+    const uint32_t* off = IS_K ? k_off : v_off;
+    const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + (int64_t)k0 * D, (uint32_t)BN * D * 2);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = (j * NW + w) * 64 * 8;
+      const uint32_t sj = J_INV ? j * J_STEP : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, off[J_INV ? 0 : j], sj, 0, 0);
+    }
+  }
   // issue() through dma16_asm
   template <bool IS_K>
   __device__ __forceinline__ void issue_asm(const bf16* X, bf16* Xs, int k0, int n_s, int w) const {

@@ -128,6 +128,9 @@ EDGE = [
     (2, 4, 2, 1100, 64, 300, torch.bfloat16),
     (1, 4, 1, 1500, 128, 520, torch.bfloat16),
     (1, 2, 2, 1200, 128, 600, torch.float32),
+    # GQA blocks of four heads per position block (bf16, d in {64, 128})
+    (1, 16, 2, 650, 128, 300, torch.bfloat16),  # GQA 8: two head groups per block, ragged
+    (1, 8, 2, 333, 64, 333, torch.bfloat16),    # GQA 4, the last position block past the end
 ]
 
 
