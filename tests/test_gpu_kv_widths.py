@@ -62,14 +62,17 @@ def test_kv_widths_match_the_oracle(lib, pair, dt, rule):
 
 @pytest.mark.parametrize("pair", [(64, 128), (128, 64)], ids=["dk64dv128", "dk128dv64"])
 @pytest.mark.parametrize("rule", ["linear", "delta"])
-def test_kv_long_ragged_segments(lib, pair, rule):
+@pytest.mark.parametrize("heads", [(2, 4, 2, 800), (1, 8, 2, 700)], ids=["gqa2", "gqa4"])
+def test_kv_long_ragged_segments(lib, pair, rule, heads):
     """Segments of 320 tokens (several query and key tiles each) with a
-    ragged last one of 160, every (batch, KV head) unit."""
+    ragged last one, every (batch, KV head) unit; group size 2 (one query
+    head per block) and 4 (four query heads of a KV head per block)."""
     dk, dv = pair
-    B, Hq, Hkv, L, N = 2, 4, 2, 800, 320
+    B, Hq, Hkv, L = heads
+    N = 320
     _say(f"long segments dk={dk} dv={dv} {rule} B{B} Hq{Hq} Hkv{Hkv} L{L} N{N}")
-    inp = random_inputs(B, Hq, Hkv, L, dk, torch.bfloat16, DEV, seed=5 * dk + dv, m0_scale=0.2,
-                        dv=dv)
+    inp = random_inputs(B, Hq, Hkv, L, dk, torch.bfloat16, DEV, seed=5 * dk + dv + L,
+                        m0_scale=0.2, dv=dv)
     res = lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"], N, rule)
     torch.cuda.synchronize()
     eo, eM, ez = compare_units(inp, res, N, rule, all_units(B, Hkv))
