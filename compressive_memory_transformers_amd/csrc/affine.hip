@@ -483,20 +483,32 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = Min[(32 * w + acc_row(r, h)) * DV + col0 + i];
 
-  for (int it = 0; it < a.s_count; ++it) {
-    const int sl = a.reverse ? a.s_count - 1 - it : it;
-    const int64_t seg = (int64_t)unit * a.s_count + sl;
-    // issue this segment's loads first; they are independent of M
-    float bv[16];
+  // B_s (this lane's 16 entries of the slab) and A_s (row 32 w + i) of step
+  // `it`; they do not depend on M, so each step's loads are issued a step
+  // ahead (the last step reloads its own, in bounds and unused)
+  auto seg_of = [&](int it) {
+    return (int64_t)unit * a.s_count + (a.reverse ? a.s_count - 1 - it : it);
+  };
+  auto load_step = [&](int it, float* bv, frag_t<T>* af) {
+    const int64_t seg = seg_of(it);
     const float* Bs = a.Bmat + seg * D * DV;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bv[r] = Bs[(32 * w + acc_row(r, h)) * DV + col0 + i];
-    frag_t<T> af[NC];
     if constexpr (DELTA) {
       const T* As = static_cast<const T*>(a.Amat) + seg * D * D + (int64_t)(32 * w + i) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) af[c] = load8<T>(As + 16 * c + 8 * h);
     }
+  };
+  float bvs[2][16];
+  frag_t<T> afs[2][NC];
+  if (a.s_count > 0) load_step(0, bvs[0], afs[0]);
+  auto step = [&](int it, auto par) {
+    constexpr int P = decltype(par)::value;
+    load_step(min(it + 1, a.s_count - 1), bvs[P ^ 1], afs[P ^ 1]);
+    const float* bv = bvs[P];
+    const frag_t<T>* af = afs[P];
+    const int64_t seg = seg_of(it);
 
     // the state before segment s: snapshot (M^T, element type)
     T* sM = static_cast<T*>(a.snapM) + seg * D * DV + (int64_t)(col0 + i) * D + 32 * w + 4 * h;
@@ -516,6 +528,10 @@ __global__ __launch_bounds__(D / 32 * 64) void chain_kernel(AffineArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] += bv[r];
     if constexpr (DELTA) __syncthreads();
+  };
+  for (int it = 0; it < a.s_count; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < a.s_count) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   float* Mout = a.M_out + (int64_t)unit * D * DV;
