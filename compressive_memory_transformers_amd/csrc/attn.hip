@@ -522,12 +522,12 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
 // DK: the key width (Q, K); DV: the value width (V, the output).
 // PACK (NW query heads of one KV head per workgroup, the group size a
 // multiple of NW): wave w takes 32 consecutive positions of the group's head
-// w (lane i: position p0 + i), so the four waves share one diagonal, 32 keys
-// wide, where 128 rows of one head span 128. The key tiles past the diagonal
-// that a block computes and masks fall from 17 of a 2048-token segment's 64-key
-// tiles (128-row blocks, mean) to 16.5, and the masked diagonal work from two
-// tiles per block to one. The K and V tiles, M^T and z are the KV head's, shared by
-// the four heads as they are by four one-head blocks.
+// w (lane i: position q0 + i), so the four waves share one causal diagonal,
+// 32 keys wide, where 128 rows of one head span 128 keys. At 2048-token
+// segments a block then runs 16.5 64-key tiles on average instead of 17, and
+// the tiles it masks drop from two to one. The K and V tiles, M^T and z are
+// the KV head's, shared by the four heads as they are by four one-head
+// blocks.
 template <int DK, int DV, int NW, int BN, bool PACK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   constexpr int BM = PACK ? 32 : 32 * NW;  // positions per block
