@@ -49,6 +49,7 @@ CASES = [
     (1, 4, 2, 100, 64, 32, torch.bfloat16),  # ragged, GQA 2
     (1, 2, 1, 150, 128, 64, torch.bfloat16),  # d = 128, ragged
     (1, 1, 1, 300, 64, 300, torch.bfloat16),  # one segment
+    (1, 8, 2, 300, 128, 130, torch.bfloat16),  # GQA 4 (four query heads per block), ragged
 ]
 IDS = [f"B{c[0]}Hq{c[1]}Hkv{c[2]}L{c[3]}d{c[4]}N{c[5]}{str(c[6])[6:]}" for c in CASES]
 
@@ -133,10 +134,11 @@ def test_llama_head_shape_two_segments(lib):
 
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("d,N,L", [(32, 16, 40), (128, 64, 150), (64, 256, 300)])
-def test_lse_is_the_log2_sum_exp_of_the_scaled_scores(lib, dt, d, N, L):
-    _say(f"lse d{d} N{N} L{L} {dt}")
-    B, Hq, Hkv = 1, 2, 1
+@pytest.mark.parametrize("d,N,L,Hq", [(32, 16, 40, 2), (128, 64, 150, 2), (64, 256, 300, 2),
+                                      (128, 320, 700, 4)])
+def test_lse_is_the_log2_sum_exp_of_the_scaled_scores(lib, dt, d, N, L, Hq):
+    _say(f"lse d{d} N{N} L{L} Hq{Hq} {dt}")
+    B, Hkv = 1, 1
     inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=d + N, m0_scale=0.3)
     _, _, _, lse = lib.forward_train(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"],
                                      inp["z0"], N, "linear")
