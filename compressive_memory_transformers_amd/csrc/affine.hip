@@ -274,21 +274,23 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 
 // ---- 3'. the same products for bf16, d = 128, from DMA-fed LDS tiles ---------
 //
-// Chunks of 64 tokens of K and V stream into a 3-deep LDS ring (K in the "K"
+// Chunks of 32 tokens of K and V stream into a 3-deep LDS ring (K in the "K"
 // layout, V in the "V" layout, lds_tile.hpp). All 512 threads then stage the
-// chunk in place, row major: 8 threads per token, 16 columns each, form
-// sigma(K) and its dot with z (the 8 partial dots summed by DPP), and write
+// chunk in place, row major: 16 threads per token, 8 columns each, form
+// sigma(K) and its dot with z (the 16 partial dots summed by DPP), and write
 // Phi and Phi / den in the "V" layout. The products read every operand with
 // transposing LDS reads (the token index is the k index): wave w owns the
 // 2 x 2 (delta) or 2 x 1 (linear) block of 32 x 32 output tiles at row tiles
 // 2 (w / 4), + 1 and column tiles 2 (w % 4), + 1 of [Phi/den | V] (delta), or
-// column tile w % 4 of V (linear).
+// column tile w % 4 of V (linear). The LDS (64 KB) leaves room for two
+// workgroups per CU, so one's staging (VALU) runs beside the other's
+// products (MFMA).
 // COLSUM (linear rule): also the segment's column sums of Phi, from the staged
 // rows (the linear rule's products need no z, so the sums need no pass of
 // their own over K).
 template <int RULE, bool COLSUM = false>
-__global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
-  constexpr int D = 128, NW = 8, TC = 64, NBUF = 3;
+__global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
+  constexpr int D = 128, NW = 8, TC = 32, NBUF = 3;
   constexpr bool DELTA = RULE == kRuleDelta;
   constexpr int BC = DELTA ? 2 : 1;  // column tiles per wave (row tiles: 2)
   using Tile = DmaTile<D, NW, TC>;
@@ -313,15 +315,15 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   auto head_off = [&](int c) { return (int64_t)(c / n_c) * a.L * D; };
   auto chunk0 = [&](int c) { return (c % n_c) * TC; };
 
-  // staging role: token st_t of the chunk, columns 16 st_g .. + 15. z comes
+  // staging role: token st_t of the chunk, columns 8 st_g .. + 7. z comes
   // into LDS by one 16-byte DMA per lane of wave 0 (lanes past d / 4 read
   // outside the resource, which returns zeros), issued before the tiles, so
   // the first chunk's wait covers it.
-  const int st_t = tid >> 3, st_g = tid & 7;
+  const int st_t = tid >> 4, st_g = tid & 15;
   if (w == 0)
     dma16_asm(Zs, asm_rsrc(a.snapZ + ((int64_t)unit * a.s_count + sl) * D, D * 4),
               (uint32_t)lane * 16, 0u);
-  float zc[16];
+  float zc[8];
   Tile tile;
   tile.init(w, lane);
   tile.template issue_asm<true>(K, Kr[0], 0, n_s, w);
@@ -343,9 +345,9 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < BC; ++c) acc[r][c] = zero16();
-  float csum[16];  // COLSUM: columns 16 st_g .. + 15 over this thread's token slot
+  float csum[8];  // COLSUM: columns 8 st_g .. + 7 over this thread's token slot
 #pragma unroll
-  for (int e = 0; e < 16; ++e) csum[e] = 0.f;
+  for (int e = 0; e < 8; ++e) csum[e] = 0.f;
 
   for (int ch = 0; ch < n_t; ++ch) {
     const int buf = ch % NBUF;
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
     __syncthreads();  // chunk ch complete everywhere; chunk ch - 1's products done
     if (ch == 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) zc[e] = Zs[16 * st_g + e];
+      for (int e = 0; e < 8; ++e) zc[e] = Zs[8 * st_g + e];
     }
     if (ch + 2 < n_t) {  // into the buffer chunk ch - 1 used
       const int cn = ch + 2;
@@ -368,43 +370,34 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
     // stage Phi and Phi / den of token st_t (zero past the segment's end)
     {
       const bool ok = chunk0(ch) + st_t < n_s;
-      const bf16* krow = Kr[buf] + st_t * D;
-      float ph[16];
+      const bf16x8 kv = load8<bf16>(Kr[buf] + st_t * D + 8 * (st_g ^ swz_k<D>(st_t)));
+      float ph[8];
       float dp = 0.f;
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
-        const bf16x8 kv = load8<bf16>(krow + 8 * ((2 * st_g + hc) ^ swz_k<D>(st_t)));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = ok ? feature_map((float)kv[e]) : 0.f;
-          ph[8 * hc + e] = f;
-          dp += f * zc[8 * hc + e];
-          if constexpr (COLSUM) csum[8 * hc + e] += f;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float f = ok ? feature_map((float)kv[e]) : 0.f;
+        ph[e] = f;
+        dp += f * zc[e];
+        if constexpr (COLSUM) csum[e] += f;
       }
-      bf16* prow = Ph + st_t * D;
-#pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
+      const int po = st_t * D + 8 * (st_g ^ swz_v<D>(st_t));
+      {
         bf16x8 y;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (bf16)ph[8 * hc + e];
-        store8<bf16>(prow + 8 * ((2 * st_g + hc) ^ swz_v<D>(st_t)), y);
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)ph[e];
+        store8<bf16>(Ph + po, y);
       }
       if constexpr (DELTA) {
-        const float den = row_sum<8>(dp);
+        const float den = row_sum<16>(dp);
         const float rd = ok ? 1.f / den : 0.f;
-        bf16* drow = DPh + st_t * D;
+        bf16x8 y;
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-          bf16x8 y;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = (bf16)(ph[8 * hc + e] * rd);
-          store8<bf16>(drow + 8 * ((2 * st_g + hc) ^ swz_v<D>(st_t)), y);
-        }
+        for (int e = 0; e < 8; ++e) y[e] = (bf16)(ph[e] * rd);
+        store8<bf16>(DPh + po, y);
       }
     }
     __syncthreads();
-    // products over the chunk's 4 k chunks of 16 tokens
+    // products over the chunk's TC / 16 k chunks of 16 tokens
 #pragma unroll
     for (int p = 0; p < TC / 16; ++p) {
       bf16x8 af[2], bf[BC];
@@ -423,11 +416,13 @@ __global__ __launch_bounds__(512, 1) void affine_dma_kernel(AffineArgs a) {
   }
 
   if constexpr (COLSUM) {
-    // sum the 64 token slots of each column in LDS (the K ring is free now)
-    float* red = reinterpret_cast<float*>(&Kr[0][0]);  // [64 slots][128 columns]
+    // sum the TC token slots of each column in LDS (the K ring, contiguous
+    // and free now: [TC slots][128 columns] floats, 16 KB over Kr[0], Kr[1])
+    static_assert(TC * D * 4 <= 2 * TC * D * 2, "the sums fit in two ring buffers");
+    float* red = reinterpret_cast<float*>(&Kr[0][0]);
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 16; ++e) red[st_t * D + 16 * st_g + e] = csum[e];
+    for (int e = 0; e < 8; ++e) red[st_t * D + 8 * st_g + e] = csum[e];
     __syncthreads();
     if (tid < D) {
       float cs = 0.f;
