@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
   __shared__ float ms[DK * 32];   // M[:, slab]
   __shared__ float zs[DK];
   __shared__ float wch[GM * NCM]; // chunk maxima, then weights exp2(m_c - m)
-  __shared__ float den[GM], gate[GM], mx[GM], lsum[GM];
+  __shared__ float lch[GM * NCM]; // chunk weight sums
+  __shared__ float den[GM], gate[GM], lsum[GM];
   constexpr int OC = 4096;           // staged value sums: chunks x heads x 32 columns
   __shared__ float os[OC];
 
@@ -175,7 +176,11 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
   }
   for (int x = tid; x < G * DK; x += NT) sq[x] = feature_map(to_f32<T>(q[x]));
   for (int x = tid; x < DK; x += NT) zs[x] = z[x];
-  for (int x = tid; x < G * NC; x += NT) wch[(x / NC) * NCM + x % NC] = part[((x % NC) * G + x / NC) * (DV + 2)];
+  for (int x = tid; x < G * NC; x += NT) {  // chunk maxima and weight sums
+    const float* pc = part + ((x % NC) * G + x / NC) * (DV + 2);
+    wch[(x / NC) * NCM + x % NC] = pc[0];
+    lch[(x / NC) * NCM + x % NC] = pc[1];
+  }
   // the slab's value sums of every (chunk, head), when they fit (G * NC <= 128)
   const bool staged = G * NC * 32 <= OC;
   if (staged)
@@ -188,7 +193,9 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
       *reinterpret_cast<f32x4*>(os + cg * 32 + 4 * c4) = y;
     }
   __syncthreads();
-  // per head (32 lanes a head): den = sigma(q) . z, the chunks' maximum
+  // per head (32 lanes a head): den = sigma(q) . z, the chunks' maximum m
+  // (every lane gets it from the butterfly), the weights exp2(m_c - m) and
+  // the weight sum l = sum_c exp2(m_c - m) l_c
   for (int g0 = 0; g0 < G; g0 += NT / 32) {
     const int g = g0 + tid / 32, l32 = tid & 31;
     if (g < G) {
@@ -201,27 +208,19 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
         dp += __shfl_xor(dp, o, 32);
         m = fmaxf(m, __shfl_xor(m, o, 32));
       }
-      if (l32 == 0) {
-        den[g] = dp;
-        mx[g] = m;
-        gate[g] = 1.f / (1.f + expf(-a.beta[hq0 + g]));
-      }
-    }
-  }
-  __syncthreads();
-  for (int x = tid; x < G * NC; x += NT) {
-    const int g = x / NC, c = x % NC;
-    wch[g * NCM + c] = exp2f(wch[g * NCM + c] - mx[g]);
-  }
-  __syncthreads();
-  for (int g0 = 0; g0 < G; g0 += NT / 32) {
-    const int g = g0 + tid / 32, l32 = tid & 31;
-    if (g < G) {
       float l = 0.f;
-      for (int c = l32; c < NC; c += 32) l += wch[g * NCM + c] * part[(c * G + g) * (DV + 2) + 1];
+      for (int c = l32; c < NC; c += 32) {
+        const float wc = exp2f(wch[g * NCM + c] - m);
+        wch[g * NCM + c] = wc;
+        l += wc * lch[g * NCM + c];
+      }
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 32);
-      if (l32 == 0) lsum[g] = l;
+      if (l32 == 0) {
+        den[g] = dp;
+        lsum[g] = l;
+        gate[g] = 1.f / (1.f + expf(-a.beta[hq0 + g]));
+      }
     }
   }
   __syncthreads();
