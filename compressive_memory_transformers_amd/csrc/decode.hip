@@ -43,9 +43,11 @@ __device__ __forceinline__ const T* cache_row(const DecodeArgs& a, const T* cach
 // chunk maximum and weight sum; the value sums run over (head, 8-column group,
 // quarter of the rows) triples and are added in LDS.
 // DK: the key width (q, k, rows of M); DV: the value width (v, the output).
-template <typename T, int DK, int DV>
+// GM: the largest group the instantiation serves (its LDS is sized for it).
+template <typename T, int DK, int DV, int GM>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int KC = kDecodeKC, GM = kDecodeMaxGroup, C8 = DV / 8;
+  constexpr int KC = kDecodeKC, C8 = DV / 8;
+  static_assert(GM <= kDecodeMaxGroup, "group bucket");
   // columns and 8-column chunks of a row quarter, of K and of V
   constexpr int QWK = DK / 4, QCK = QWK / 8, QWV = DV / 4, QCV = QWV / 8;
   __shared__ float qs[GM * DK];  // the group's queries, scaled by log2(e) / sqrt(d_key)
@@ -82,9 +84,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   __syncthreads();
 
   // scores: the quarter's partial dot for every head, summed over the quad
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-    if (g < G) {
+  for (int g = 0; g < G; ++g) {
       float sp = 0.f;
 #pragma unroll
       for (int c = 0; c < QCK; ++c)
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
+#pragma unroll 4
     for (int i = 0; i < KC / 4; ++i) {
       const int tt = kq * (KC / 4) + i;  // rows past n carry weight 0
       const frag_t<T> vx = load8<T>(vs + tt * DV + 8 * c);
@@ -243,8 +243,14 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
 template <typename T, int DK, int DV>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)(a.B * a.Hkv);
-  hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV>), dim3(units * (unsigned)a.n_chunks),
-                     dim3(256), 0, stream, a);
+  // groups of up to 4 query heads take the instantiation with LDS for 4,
+  // so more workgroups share a CU
+  if (a.G <= 4)
+    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, 4>), dim3(units * (unsigned)a.n_chunks),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, kDecodeMaxGroup>),
+                       dim3(units * (unsigned)a.n_chunks), dim3(256), 0, stream, a);
   hipLaunchKernelGGL((decode_combine_kernel<T, DK, DV>), dim3(units * (unsigned)(DV / 32)),
                      dim3(kDecodeNT), 0, stream, a);
   return hipGetLastError();
