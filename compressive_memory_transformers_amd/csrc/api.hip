@@ -691,7 +691,8 @@ namespace {
 struct DecodePlan {
   Plan fold;           // the recurrence over one segment of the cache
   int64_t G, n_chunks_max;
-  size_t part_bytes;   // chunk partials, aligned
+  size_t retr_off, rden_off;  // the retrieval's numerators and denominators
+  size_t part_bytes;   // chunk partials and the retrieval, aligned
 };
 
 // d: the key width; dv: the value width (d when 0).
@@ -711,8 +712,10 @@ infini_status_t check_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int6
     dp->fold = fold;
     dp->G = Hq / Hkv;
     dp->n_chunks_max = (seg_len + 63) / 64;
-    dp->part_bytes = align_up((size_t)fold.units * (size_t)dp->n_chunks_max * (size_t)dp->G *
-                              (size_t)(dv + 2) * 4);
+    dp->retr_off = align_up((size_t)fold.units * (size_t)dp->n_chunks_max * (size_t)dp->G *
+                            (size_t)(dv + 2) * 4);
+    dp->rden_off = dp->retr_off + align_up((size_t)fold.units * (size_t)dp->G * (size_t)dv * 4);
+    dp->part_bytes = dp->rden_off + align_up((size_t)fold.units * (size_t)dp->G * 4);
   }
   return INFINI_OK;
 }
@@ -785,6 +788,8 @@ infini_status_t decode_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t d, int64
   da.z = z;
   da.out = out;
   da.part = reinterpret_cast<float*>(ws);
+  da.retr = reinterpret_cast<float*>(ws + dp.retr_off);
+  da.rden = reinterpret_cast<float*>(ws + dp.rden_off);
   da.seg_len = seg_len;
   da.B = (int32_t)B;
   da.Hq = (int32_t)Hq;

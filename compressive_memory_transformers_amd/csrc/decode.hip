@@ -58,6 +58,42 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int G = a.G;
+  const int n_part = a.B * a.Hkv * a.n_chunks;
+  if ((int)blockIdx.x >= n_part) {
+    // the retrieval workgroups, one per (batch, KV head, 32-column slab):
+    // numerator sigma(q) M[:, slab] and denominator sigma(q) . z of the
+    // group's heads, from the state before the segment (the combine reads
+    // them after this launch)
+    const int rb = (int)blockIdx.x - n_part;
+    const int ru = rb / (DV / 32), slab = rb % (DV / 32);
+    const int b = ru / a.Hkv, j = ru % a.Hkv;
+    const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + (int64_t)j * G) * DK;
+    const float* M = a.M + (int64_t)ru * DK * DV + 32 * slab;
+    const float* z = a.z + (int64_t)ru * DK;
+    float* sq = qs;  // sigma(q) of the group, [G][DK]
+    for (int x = tid; x < G * DK; x += 256) sq[x] = feature_map(to_f32<T>(q[x]));
+    __syncthreads();
+    if (slab == 0) {  // per head (32 lanes a head): den
+      for (int g0 = 0; g0 < G; g0 += 8) {
+        const int g = g0 + tid / 32, l32 = tid & 31;
+        if (g < G) {
+          float dp = 0.f;
+          for (int k = l32; k < DK; k += 32) dp += sq[g * DK + k] * z[k];
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) dp += __shfl_xor(dp, o, 32);
+          if (l32 == 0) a.rden[ru * G + g] = dp;
+        }
+      }
+    }
+    for (int x = tid; x < G * 32; x += 256) {
+      const int g = x / 32, cs = x % 32;
+      float r = 0.f;
+#pragma unroll 16
+      for (int k = 0; k < DK; ++k) r += sq[g * DK + k] * M[(int64_t)k * DV + cs];
+      a.retr[((int64_t)ru * G + g) * DV + 32 * slab + cs] = r;
+    }
+    return;
+  }
   const int unit = blockIdx.x / a.n_chunks, ch = blockIdx.x % a.n_chunks;
   const int b = unit / a.Hkv, j = unit % a.Hkv;
   const int t0 = ch * KC;
@@ -144,18 +180,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Per (batch, KV head, 32-column slab of the output): merge the chunks,
-// retrieve from the float state, gate. The slab of M, z and the queries are
-// loaded at once into LDS; the small reductions run across the workgroup.
+// Per (batch, KV head, 32-column slab of the output): merge the chunks by
+// their maxima, add the retrieval the partial launch formed, gate. The
+// chunks' maxima, weight sums and value sums are loaded at once into LDS;
+// the small reductions run across the workgroup.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a) {
   constexpr int NT = kDecodeNT, GM = kDecodeMaxGroup, NCM = kDecodeMaxChunks;
-  __shared__ float sq[GM * DK];   // sigma(q)
-  __shared__ float ms[DK * 32];   // M[:, slab]
-  __shared__ float zs[DK];
   __shared__ float wch[GM * NCM]; // chunk maxima, then weights exp2(m_c - m)
   __shared__ float lch[GM * NCM]; // chunk weight sums
-  __shared__ float den[GM], gate[GM], lsum[GM];
+  __shared__ float gate[GM], lsum[GM];
   constexpr int OC = 4096;           // staged value sums: chunks x heads x 32 columns
   __shared__ float os[OC];
 
@@ -164,18 +198,8 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
   const int unit = blockIdx.x / (DV / 32), slab = blockIdx.x % (DV / 32);
   const int b = unit / a.Hkv, j = unit % a.Hkv;
   const int hq0 = j * G;
-  const T* q = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + hq0) * DK;
-  const float* M = a.M + (int64_t)unit * DK * DV + 32 * slab;
-  const float* z = a.z + (int64_t)unit * DK;
   const float* part = a.part + (int64_t)unit * NC * G * (DV + 2);
 
-  for (int x = tid; x < DK * 8; x += NT) {  // 8 float4 per row of the slab
-    const int k = x / 8, c4 = x % 8;
-    *reinterpret_cast<f32x4*>(ms + k * 32 + 4 * c4) =
-        *reinterpret_cast<const f32x4*>(M + (int64_t)k * DV + 4 * c4);
-  }
-  for (int x = tid; x < G * DK; x += NT) sq[x] = feature_map(to_f32<T>(q[x]));
-  for (int x = tid; x < DK; x += NT) zs[x] = z[x];
   for (int x = tid; x < G * NC; x += NT) {  // chunk maxima and weight sums
     const float* pc = part + ((x % NC) * G + x / NC) * (DV + 2);
     wch[(x / NC) * NCM + x % NC] = pc[0];
@@ -193,21 +217,16 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
       *reinterpret_cast<f32x4*>(os + cg * 32 + 4 * c4) = y;
     }
   __syncthreads();
-  // per head (32 lanes a head): den = sigma(q) . z, the chunks' maximum m
-  // (every lane gets it from the butterfly), the weights exp2(m_c - m) and
-  // the weight sum l = sum_c exp2(m_c - m) l_c
+  // per head (32 lanes a head): the chunks' maximum m (every lane gets it
+  // from the butterfly), the weights exp2(m_c - m) and the weight sum
+  // l = sum_c exp2(m_c - m) l_c
   for (int g0 = 0; g0 < G; g0 += NT / 32) {
     const int g = g0 + tid / 32, l32 = tid & 31;
     if (g < G) {
-      float dp = 0.f;
-      for (int k = l32; k < DK; k += 32) dp += sq[g * DK + k] * zs[k];
       float m = -INFINITY;
       for (int c = l32; c < NC; c += 32) m = fmaxf(m, wch[g * NCM + c]);
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) {
-        dp += __shfl_xor(dp, o, 32);
-        m = fmaxf(m, __shfl_xor(m, o, 32));
-      }
+      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
       float l = 0.f;
       for (int c = l32; c < NC; c += 32) {
         const float wc = exp2f(wch[g * NCM + c] - m);
@@ -217,7 +236,6 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 32);
       if (l32 == 0) {
-        den[g] = dp;
         lsum[g] = l;
         gate[g] = 1.f / (1.f + expf(-a.beta[hq0 + g]));
       }
@@ -233,10 +251,9 @@ __global__ __launch_bounds__(kDecodeNT) void decode_combine_kernel(DecodeArgs a)
       for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * os[(c * G + g) * 32 + cs];
     else
       for (int c = 0; c < NC; ++c) o += wch[g * NCM + c] * part[(c * G + g) * (DV + 2) + 2 + col];
-    float r = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < DK; ++k) r += sq[g * DK + k] * ms[k * 32 + cs];
-    out[g * DV + col] = from_f32<T>(gate[g] * (r / den[g]) + (1.f - gate[g]) * (o / lsum[g]));
+    const float r = a.retr[((int64_t)unit * G + g) * DV + col];
+    const float den = a.rden[unit * G + g];
+    out[g * DV + col] = from_f32<T>(gate[g] * (r / den) + (1.f - gate[g]) * (o / lsum[g]));
   }
 }
 
@@ -245,12 +262,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const unsigned units = (unsigned)(a.B * a.Hkv);
   // groups of up to 4 query heads take the instantiation with LDS for 4,
   // so more workgroups share a CU
+  const unsigned grid = units * (unsigned)a.n_chunks + units * (unsigned)(DV / 32);
   if (a.G <= 4)
-    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, 4>), dim3(units * (unsigned)a.n_chunks),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, 4>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, kDecodeMaxGroup>),
-                       dim3(units * (unsigned)a.n_chunks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<T, DK, DV, kDecodeMaxGroup>), dim3(grid),
+                       dim3(256), 0, stream, a);
   hipLaunchKernelGGL((decode_combine_kernel<T, DK, DV>), dim3(units * (unsigned)(DV / 32)),
                      dim3(kDecodeNT), 0, stream, a);
   return hipGetLastError();

@@ -114,6 +114,8 @@ struct DecodeArgs {
   const float* z;      // [B][Hkv][dk]
   void* out;           // [B][Hq][dv]
   float* part;         // [B*Hkv][n_chunks][G][2 + dv]: chunk max, weight sum, value sums
+  float* retr;         // [B*Hkv][G][dv]: sigma(q) M of the group's heads
+  float* rden;         // [B*Hkv][G]: sigma(q) . z
   int64_t seg_len;
   int32_t B, Hq, Hkv, G;
   int32_t pos, n_chunks;  // n_chunks = ceil((pos + 1) / 64)

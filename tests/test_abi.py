@@ -356,12 +356,15 @@ def dws(lib, *args):
 
 def test_decode_workspace_size(lib):
     # Llama-3-8B-shaped: 32 units, 32 chunks of 64 rows, 4 query heads a unit,
-    # plus the one-segment recurrence workspace of the forward
+    # the retrieval's numerators and denominators of the group's heads, plus
+    # the one-segment recurrence workspace of the forward
     st, n = dws(lib, 4, 32, 8, 128, 2048, 1, 1)
     assert st == 0
     _, _, fold = ws(lib, 4, 32, 8, 2048, 128, 2048, 1, 1)
+    up = lambda x: (x + 255) // 256 * 256
     part = 32 * 32 * 4 * (128 + 2) * 4
-    assert n == (part + 255) // 256 * 256 + fold
+    retr, rden = 32 * 4 * 128 * 4, 32 * 4 * 4
+    assert n == up(part) + up(retr) + up(rden) + fold
 
 
 @pytest.mark.parametrize("args,status", [
