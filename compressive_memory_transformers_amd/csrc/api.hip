@@ -881,7 +881,7 @@ struct BwdLayout {
   size_t total;
   size_t stM, stz, zeroM, snapM, snapZ, colsum, Bmat, Amat, dMsnap, e_ret, e_upd, dzs;
   size_t nm, dn, delta, dg, dden, dk_acc, dv_acc, du_buf, dphi, p_buf, u_el, dp_el, dc;
-  size_t Amat_f, dMsnap_f, phi_f, phic_f, wsum_part;
+  size_t Amat_f, dMsnap_f, phi_f, phic_f, wsum_part, dbeta_part;
 };
 
 // fused: the bf16 kernels that form sigma(Q) M, sigma(K) dM_s and sigma(K)
@@ -921,6 +921,8 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
     const size_t chunks = ((size_t)(Hq / Hkv) * n + 511) / 512;
     b.wsum_part = take(units * S * chunks * d * 4);
   }
+  b.dbeta_part =
+      take((size_t)(Hq * B) * (size_t)((L + infini::kDbetaChunk - 1) / infini::kDbetaChunk) * 4);
   if (!fused) b.nm = take(qrows * dmax * 4);  // sigma(Q) M (dv), then dQ's retrieval part (d)
   b.dn = take(qrows * dv * e);
   b.delta = take(qrows * 4);
@@ -1120,6 +1122,7 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
   ba.e_upd = F(lay.e_upd);
   ba.dzs = F(lay.dzs);
   ba.wsum_part = F(lay.wsum_part);
+  ba.dbeta_part = F(lay.dbeta_part);
   ba.dz_final = dz_final;
   ba.dz0 = dz0;
   ba.dq = dq;

@@ -512,24 +512,35 @@ __global__ __launch_bounds__(256) void kv_out_kernel(BwdArgs a) {
     static_cast<T*>(a.dv)[x] = from_f32<T>(a.dv_acc[x]);
 }
 
-// dbeta_h = g (1 - g) sum over the batch and the stream of dg.
-__global__ __launch_bounds__(256) void dbeta_kernel(BwdArgs a) {
-  __shared__ float part[256];
-  const int hq = blockIdx.x;
+// dbeta_h = g (1 - g) sum over the batch and the stream of dg, in two
+// passes with a fixed order (no atomics): workgroup (h, b, c) sums positions
+// [c kDbetaChunk, (c + 1) kDbetaChunk) of row (b, h) into dbeta_part, then
+// one thread per head adds that head's partials in (b, c) order.
+__global__ __launch_bounds__(256) void dbeta_partial_kernel(BwdArgs a, int n_ch) {
+  __shared__ float part[4];
+  const int c = blockIdx.x % n_ch;
+  const int64_t hb = blockIdx.x / n_ch;  // hq * B + b
+  const int hq = (int)(hb / a.B), b = (int)(hb % a.B);
+  const float* dg = a.dg + ((int64_t)b * a.Hq + hq) * a.L;
+  const int64_t t1 = min<int64_t>(a.L, (int64_t)(c + 1) * kDbetaChunk);
   float acc = 0.f;
-  for (int b = 0; b < a.B; ++b) {
-    const float* dg = a.dg + ((int64_t)b * a.Hq + hq) * a.L;
-    for (int64_t t = threadIdx.x; t < a.L; t += 256) acc += dg[t];
-  }
-  part[threadIdx.x] = acc;
+#pragma unroll 4
+  for (int64_t t = (int64_t)c * kDbetaChunk + threadIdx.x; t < t1; t += 256) acc += dg[t];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) a.dbeta_part[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+__global__ __launch_bounds__(256) void dbeta_final_kernel(BwdArgs a, int n_ch) {
+  const int n = a.B * n_ch;
+  for (int hq = threadIdx.x; hq < a.Hq; hq += 256) {
+    const float* p = a.dbeta_part + (int64_t)hq * n;
+    float t = 0.f;
+    for (int i = 0; i < n; ++i) t += p[i];
     const float g = gate_of(a.beta, hq);
-    a.dbeta[hq] = part[0] * g * (1.f - g);
+    a.dbeta[hq] = t * g * (1.f - g);
   }
 }
 
@@ -583,7 +594,12 @@ hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
       hipLaunchKernelGGL((dz_scan_kernel<D>), dim3((unsigned)units), dim3(D), 0, s, a);
       hipLaunchKernelGGL((kv_out_kernel<T, D, DV>), dim3(elem_grid(krows * (D > DV ? D : DV))),
                          dim3(256), 0, s, a);
-      hipLaunchKernelGGL((dbeta_kernel), dim3((unsigned)a.Hq), dim3(256), 0, s, a);
+      {
+        const int n_ch = (int)((a.L + kDbetaChunk - 1) / kDbetaChunk);
+        hipLaunchKernelGGL((dbeta_partial_kernel), dim3((unsigned)((int64_t)a.Hq * a.B * n_ch)),
+                           dim3(256), 0, s, a, n_ch);
+        hipLaunchKernelGGL((dbeta_final_kernel), dim3(1), dim3(256), 0, s, a, n_ch);
+      }
       break;
     default: return hipErrorInvalidValue;
   }

@@ -190,11 +190,15 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dbeta;        // [Hq]
+  float* dbeta_part;   // [Hq][B][ceil(L / kDbetaChunk)] partial sums of dg
   int64_t L, seg_len;
   int32_t B, Hq, Hkv, S;
   int32_t rule;
   float scale_log2;    // log2(e) / sqrt(d)
 };
+
+// Positions of one dg row that one workgroup of the d(beta) reduction sums.
+constexpr int64_t kDbetaChunk = 4096;
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t stream);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
