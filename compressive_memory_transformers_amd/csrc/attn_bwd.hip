@@ -226,12 +226,16 @@ struct KvLane {
 };
 
 // One 32-query tile of one head: S = Q K^T, dP = dO V^T, P, dS;
-// dV^T += dO^T P, dK^T += Q^T dS.
+// dV^T += dO^T P, dK^T += Q^T dS. Rows past the segment's end come in as
+// zeros (Q, dO, lse, delta): P = 1 there but dP = dS = 0 and dO = 0, so they
+// add nothing and need no mask. The causal mask drops P where key > q, i.e.
+// where this lane's threshold kq = key - q0 - 4 h exceeds the row's offset
+// 8 g4 + j in the tile; off the diagonal (every row after every key of the
+// block) kq is negative, below every offset.
 template <int D>
 __device__ __forceinline__ void kv_tile(const bf16* Qt, const bf16* Ot, const bf16* Vb,
                                         const float* lse_t, const float* dl_t, KvLane<D>& st,
-                                        float c, float om, int q0, int n_s, int key, int h,
-                                        bool diag) {
+                                        float c, float om, int h, int kq) {
   constexpr int NC = D / 16, NDB = D / 32;
   f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
@@ -249,9 +253,8 @@ __device__ __forceinline__ void kv_tile(const bf16* Qt, const bf16* Ot, const bf
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * g4 + j;
-      const int q = q0 + 8 * g4 + 4 * h + j;
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[j]));
-      if ((diag && key > q) || q >= n_s) p = 0.f;
+      if (kq > 8 * g4 + j) p = 0.f;
       pf[r >> 3][r & 7] = (bf16)(p * om);
       dsf[r >> 3][r & 7] = (bf16)(p * __builtin_fmaf(om, pacc[r], -d4[j]));
     }
@@ -341,14 +344,20 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
   bf16* const Os[2] = {Os0, Os1};
   auto Ls = [&](int P) { return P ? Ls1 : Ls0; };
   auto Ds = [&](int P) { return P ? Ds1 : Ds0; };
-  // query tiles q0 = k0, k0 + 32, ... of every head of the group, as one list
+  // query tiles q0 = k0, k0 + 32, ... of every head of the group, as one
+  // list of items (head hg, tile qi), head-major. The position is carried as
+  // scalar counters: dividing the item index would put hg and qi in vector
+  // registers, and every DMA built from them would become a waterfall loop.
   const int n_q = (n_s - k0 + BQ - 1) / BQ;
-  const int n_items = n_q * G;
-  auto issue = [&](int it, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
-    const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
-    const int64_t rb = ((int64_t)b * a.Hq + kvh * G + hg) * a.L + seg_start;
-    tile.template issue<true>(static_cast<const bf16*>(a.q) + rb * D, Qd, q0, n_s, w);
-    tile.template issue<true>(static_cast<const bf16*>(a.dout) + rb * D, Od, q0, n_s, w);
+  // The group's first query head row, made explicitly scalar: the same
+  // product also indexes beta under the divergent branch above, and merged
+  // through that branch it would reach the DMA descriptors in a vector register.
+  const int hrow0 = __builtin_amdgcn_readfirstlane(b * a.Hq + kvh * G);
+  auto issue = [&](int hg, int qi, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
+    const int q0 = k0 + qi * BQ;
+    const int64_t rb = (int64_t)(hrow0 + hg) * a.L + seg_start;
+    tile.template issue_zero_tail<true>(static_cast<const bf16*>(a.q) + rb * D, Qd, q0, n_s, w);
+    tile.template issue_zero_tail<true>(static_cast<const bf16*>(a.dout) + rb * D, Od, q0, n_s, w);
     // 32 floats of lse (wave 0) and delta (wave 1); lanes past the rows read zeros
     const int bytes = min(BQ, n_s - q0) * 4;
     if (w == 0) {
@@ -361,23 +370,33 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)Dd, 4, lane * 4, 0, 0, 0);
     }
   };
-  issue(0, Qs0, Os0, Ls0, Ds0);
+  issue(0, 0, Qs0, Os0, Ls0, Ds0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const int kq0 = key - 4 * h - k0;  // the causal threshold of tile qi is kq0 - BQ qi
+  int hg = 0, qi = 0;
   // as in dq_kernel: every item loads its successor (the last reloads
   // itself) and waits for it, unconditionally
-  auto step = [&](int it, auto par) {
+  auto step = [&](auto par) {
     constexpr int P = decltype(par)::value;
-    issue(min(it + 1, n_items - 1), Qs[P ^ 1], Os[P ^ 1], Ls(P ^ 1), Ds(P ^ 1));
-    const int hg = it / n_q, q0 = k0 + (it % n_q) * BQ;
-    const float om = omg[hg];
-    kv_tile<D>(Qs[P], Os[P], Vb, Ls(P), Ds(P), st, c, om, q0, n_s, key, h, q0 < k0 + BK);
+    int hn = hg, qn = qi;
+    if (qn + 1 < n_q) {
+      ++qn;
+    } else if (hn + 1 < G) {
+      ++hn;
+      qn = 0;
+    }
+    issue(hn, qn, Qs[P ^ 1], Os[P ^ 1], Ls(P ^ 1), Ds(P ^ 1));
+    kv_tile<D>(Qs[P], Os[P], Vb, Ls(P), Ds(P), st, c, omg[hg], h, kq0 - BQ * qi);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    hg = hn;
+    qi = qn;
   };
+  const int n_items = n_q * G;
   for (int it = 0; it < n_items; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_items) step(it + 1, std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 0>{});
+    if (it + 1 < n_items) step(std::integral_constant<int, 1>{});
   }
   if (!live) return;
   const float inv_sqrt_d = a.scale_log2 / kLog2e;
