@@ -38,10 +38,12 @@ struct DqLane {
 };
 
 // One 64-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
-template <int D>
+// MASK: the tile reaches the causal diagonal. Key k0 + 32 kb + acc_row(r, h)
+// lies after the lane's row where 32 kb + 8 (r / 4) + r % 4 exceeds the
+// lane's threshold kt = row - 4 h - k0.
+template <int D, bool MASK>
 __device__ __forceinline__ void dq_tile(const bf16* Kt, const bf16* Vt, DqLane<D>& st, float c,
-                                        float lse, float dl, float om, int k0, int row, int h,
-                                        bool diag) {
+                                        float lse, float dl, float om, int kt) {
   constexpr int NC = D / 16, NDB = D / 32;
   f32x16 sacc[2], pacc[2];
 #pragma unroll
@@ -61,7 +63,7 @@ __device__ __forceinline__ void dq_tile(const bf16* Kt, const bf16* Vt, DqLane<D
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -lse));
-      if (diag && k0 + 32 * kb + acc_row(r, h) > row) p = 0.f;
+      if (MASK && 32 * kb + 8 * (r >> 2) + (r & 3) > kt) p = 0.f;
       dsf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * __builtin_fmaf(om, pacc[kb][r], -dl));
     }
 #pragma unroll
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
   // rows past the segment: lse = +inf gives P = 0
   const float lse = live ? a.lse[rbase + row] : INFINITY;
   const float dl = live ? a.delta[rbase + row] : 0.f;
-  const int wave_first = q0 + w;
+  const int kt0 = row - 4 * h;  // the causal threshold of key tile k0 is kt0 - k0
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -144,19 +146,29 @@ __global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
   // other buffers first and waits for it at its end: with the load and the
   // wait unconditional, the compiler sees that a tile's reads touch only
   // buffers no load is filling, and does not wait for the load.
-  auto step = [&](int j, auto par) {
+  auto step = [&](int j, auto par, auto mask) {
     constexpr int P = decltype(par)::value;
     const int jn = min(j + 1, n_kt - 1);
     tile.template issue<true>(K, Ks[P ^ 1], jn * BN, n_s, w);
     tile.template issue<true>(V, Vs[P ^ 1], jn * BN, n_s, w);
     const int k0 = j * BN;
-    dq_tile<D>(Ks[P], Vs[P], st, c, lse, dl, om, k0, row, h, k0 + BN - 1 > wave_first);
+    dq_tile<D, decltype(mask)::value>(Ks[P], Vs[P], st, c, lse, dl, om, kt0 - k0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int j = 0; j < n_kt; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{});
+  // Key tiles that end before the block's first query row (k0 + BN <= q0)
+  // lie below every row's diagonal and take no mask. Their count q0 / BN is
+  // even (q0 is a multiple of 2 BN) and below n_kt, so the masked tiles
+  // start on buffer parity 0.
+  static_assert(BM % (2 * BN) == 0, "even count of unmasked key tiles");
+  const int n_free = q0 / BN;
+  for (int j = 0; j < n_free; j += 2) {
+    step(j, std::integral_constant<int, 0>{}, std::false_type{});
+    step(j + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  for (int j = n_free; j < n_kt; j += 2) {
+    step(j, std::integral_constant<int, 0>{}, std::true_type{});
+    if (j + 1 < n_kt) step(j + 1, std::integral_constant<int, 1>{}, std::true_type{});
   }
   // The retrieval part of dQ, (M dn^T + dden z) sigma'(q): the snapshot M^T
   // comes into the K buffers (free after the last tile), dn (bf16, written
