@@ -242,9 +242,9 @@ struct KvLane {
 // zeros (Q, dO, lse, delta): P = 1 there but dP = dS = 0 and dO = 0, so they
 // add nothing and need no mask. The causal mask drops P where key > q, i.e.
 // where this lane's threshold kq = key - q0 - 4 h exceeds the row's offset
-// 8 g4 + j in the tile; off the diagonal (every row after every key of the
-// block) kq is negative, below every offset.
-template <int D>
+// 8 g4 + j in the tile; MASK: the tile reaches the diagonal (off it every
+// row follows every key of the block and the mask is left out).
+template <int D, bool MASK>
 __device__ __forceinline__ void kv_tile(const bf16* Qt, const bf16* Ot, const bf16* Vb,
                                         const float* lse_t, const float* dl_t, KvLane<D>& st,
                                         float c, float om, int h, int kq) {
@@ -266,7 +266,7 @@ __device__ __forceinline__ void kv_tile(const bf16* Qt, const bf16* Ot, const bf
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * g4 + j;
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -l4[j]));
-      if (kq > 8 * g4 + j) p = 0.f;
+      if (MASK && kq > 8 * g4 + j) p = 0.f;
       pf[r >> 3][r & 7] = (bf16)(p * om);
       dsf[r >> 3][r & 7] = (bf16)(p * __builtin_fmaf(om, pacc[r], -d4[j]));
     }
@@ -386,29 +386,48 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int kq0 = key - 4 * h - k0;  // the causal threshold of tile qi is kq0 - BQ qi
-  int hg = 0, qi = 0;
-  // as in dq_kernel: every item loads its successor (the last reloads
-  // itself) and waits for it, unconditionally
-  auto step = [&](auto par) {
-    constexpr int P = decltype(par)::value;
-    int hn = hg, qn = qi;
-    if (qn + 1 < n_q) {
+  // Item order: the tiles that reach the diagonal (qi < n_d) of every head,
+  // then the interior tiles of every head, each part head-major; the second
+  // part takes no mask.
+  const int n_d = min(BK / BQ, n_q);
+  auto succ = [&](int& hn, int& qn) {  // (hn, qn) <- its successor; the last item keeps itself
+    const bool d = qn < n_d;
+    if (qn + 1 < (d ? n_d : n_q)) {
       ++qn;
     } else if (hn + 1 < G) {
       ++hn;
-      qn = 0;
+      qn = d ? 0 : n_d;
+    } else if (d && n_d < n_q) {
+      hn = 0;
+      qn = n_d;
     }
+  };
+  int hg = 0, qi = 0;
+  // as in dq_kernel: every item loads its successor (the last reloads
+  // itself) and waits for it, unconditionally
+  auto step = [&](auto par, auto mask) {
+    constexpr int P = decltype(par)::value;
+    int hn = hg, qn = qi;
+    succ(hn, qn);
     issue(hn, qn, Qs[P ^ 1], Os[P ^ 1], Ls(P ^ 1), Ds(P ^ 1));
-    kv_tile<D>(Qs[P], Os[P], Vb, Ls(P), Ds(P), st, c, omg[hg], h, kq0 - BQ * qi);
+    kv_tile<D, decltype(mask)::value>(Qs[P], Os[P], Vb, Ls(P), Ds(P), st, c, omg[hg], h,
+                                      kq0 - BQ * qi);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     hg = hn;
     qi = qn;
   };
-  const int n_items = n_q * G;
-  for (int it = 0; it < n_items; it += 2) {
-    step(std::integral_constant<int, 0>{});
-    if (it + 1 < n_items) step(std::integral_constant<int, 1>{});
+  // There are interior tiles only when n_d = BK / BQ, an even number, so the
+  // first part's item count is then even and the second starts on parity 0.
+  static_assert((BK / BQ) % 2 == 0, "even count of diagonal items");
+  const int n1 = G * n_d, n2 = G * (n_q - n_d);
+  for (int it = 0; it < n1; it += 2) {
+    step(std::integral_constant<int, 0>{}, std::true_type{});
+    if (it + 1 < n1) step(std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  for (int it = 0; it < n2; it += 2) {
+    step(std::integral_constant<int, 0>{}, std::false_type{});
+    if (it + 1 < n2) step(std::integral_constant<int, 1>{}, std::false_type{});
   }
   if (!live) return;
   const float inv_sqrt_d = a.scale_log2 / kLog2e;
