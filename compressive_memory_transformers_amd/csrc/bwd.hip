@@ -491,25 +491,49 @@ __global__ __launch_bounds__(D) void dz_scan_kernel(BwdArgs a) {
 }
 
 // dK = dk_acc + (dphi + dc z_{s-1} + dz_s) sigma'(k) (DK wide), dV = dv_acc
-// (DV wide).
+// (DV wide). Each thread takes eight consecutive elements of a row (16-byte
+// stores of the outputs; every pointer is 16-byte aligned and the widths are
+// multiples of 8), so the row and segment are decoded once per eight.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void kv_out_kernel(BwdArgs a) {
+  constexpr int CK = DK / 8, CV = DV / 8;
   const int64_t rows = (int64_t)a.B * a.Hkv * a.L;
-  const int64_t n = rows * DK;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) {
-    const int64_t row = x / DK;
-    const int c = (int)(x % DK);
-    const int64_t unit = row / a.L, t = row % a.L;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t nk = rows * CK;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nk; x += stride) {
+    const int64_t row = x / CK;
+    const int c = (int)(x % CK) * 8;
+    const int64_t unit = row / a.L, t = row - unit * a.L;
     const int s = (int)(t / a.seg_len);
+    const int64_t e = row * DK + c;
     const int64_t sx = (unit * a.S + s) * DK + c;
-    float dphi = a.dphi[x] + a.dzs[sx];
-    if (a.rule == kRuleDelta) dphi += a.dc[row] * a.snapZ[sx];
-    const float kv = to_f32<T>(static_cast<const T*>(a.k)[x]);
-    static_cast<T*>(a.dk)[x] = from_f32<T>(a.dk_acc[x] + dphi * feature_map_grad(kv));
+    const frag_t<float> dphi = load8<float>(a.dphi + e);
+    const frag_t<float> dz = load8<float>(a.dzs + sx);
+    const frag_t<float> acc = load8<float>(a.dk_acc + e);
+    const frag_t<T> kv = load8<T>(static_cast<const T*>(a.k) + e);
+    frag_t<float> zc;
+    float dcr = 0.f;
+    if (a.rule == kRuleDelta) {
+      zc = load8<float>(a.snapZ + sx);
+      dcr = a.dc[row];
+    }
+    frag_t<T> y;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float g = dphi[j] + dz[j];
+      if (a.rule == kRuleDelta) g += dcr * zc[j];
+      y[j] = from_f32<T>(acc[j] + g * feature_map_grad(to_f32<T>(kv[j])));
+    }
+    store8<T>(static_cast<T*>(a.dk) + e, y);
   }
-  const int64_t nv = rows * DV;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nv; x += (int64_t)gridDim.x * 256)
-    static_cast<T*>(a.dv)[x] = from_f32<T>(a.dv_acc[x]);
+  const int64_t nv = rows * CV;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nv; x += stride) {
+    const frag_t<float> acc = load8<float>(a.dv_acc + 8 * x);
+    frag_t<T> y;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = from_f32<T>(acc[j]);
+    store8<T>(static_cast<T*>(a.dv) + 8 * x, y);
+  }
 }
 
 // dbeta_h = g (1 - g) sum over the batch and the stream of dg, in two
@@ -592,7 +616,7 @@ hipError_t launch_d(int which, const BwdArgs& a, int arg, hipStream_t s) {
       break;
     case 5:
       hipLaunchKernelGGL((dz_scan_kernel<D>), dim3((unsigned)units), dim3(D), 0, s, a);
-      hipLaunchKernelGGL((kv_out_kernel<T, D, DV>), dim3(elem_grid(krows * (D > DV ? D : DV))),
+      hipLaunchKernelGGL((kv_out_kernel<T, D, DV>), dim3(elem_grid(krows * (D > DV ? D : DV) / 8)),
                          dim3(256), 0, s, a);
       {
         const int n_ch = (int)((a.L + kDbetaChunk - 1) / kDbetaChunk);
