@@ -1272,10 +1272,12 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
   if (infini::launch_bwd_attention(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
 
   // 5. update: dv_acc += sigma(K) dM_s, dphi, dc. bf16 with d in {64, 128}:
-  // one fused kernel per 128 key rows; otherwise key-side products
-  // (hi = unit) and a row kernel.
+  // one fused kernel per 128 key rows, which writes dv = dv_acc + sigma(K)
+  // dM_s as the output itself; otherwise key-side products (hi = unit) and a
+  // row kernel.
   ba.dMsnap = E(lay.dMsnap);
   if (bwd_mfma) {
+    ba.dv_final = 1;  // the kernel writes dv itself
     if (infini::launch_bwd_update_mfma(D, ba, s) != hipSuccess) return INFINI_ERR_HIP;
   } else {
     // key-side products, hi = unit: (rows of a d wide) x (M-shaped, stored

@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
 //   delta:  M_s = M_{s-1} + Phi^T R, R = V - P / c, P = Phi M_{s-1}.
 // Given dM_s (the reversed chain's snapshot, dM_s^T in bf16), per key row t:
 //   du_t = Phi_t dM_s                  (dL/dR_t, or dL/dV_t for the linear rule)
-//   dv_acc_t += du_t
+//   dv_t = dv_acc_t + du_t             (the output itself)
 //   delta: dP_t = -du_t / c_t, dc_t = (du_t . P_t / c_t) / c_t,
 //          dphi_t = R_t dM_s^T + dP_t M_{s-1}^T
 //   linear: dphi_t = V_t dM_s^T
@@ -683,9 +683,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void upd_kernel(BwdArgs a, int n_kt) {
     }
   }
 
-  // per element: column j = 32 jb + 8 rq + 4 h + 0..3 of row `key`
+  // per element: column j = 32 jb + 8 rq + 4 h + 0..3 of row `key`. The
+  // update is dv's last term: dv_acc + du goes out as dv itself, rounded once.
   const float ic = 1.f / cz;
-  float* dva = a.dv_acc + row * D;
+  const float* dva = a.dv_acc + row * D;
+  bf16* dvo = static_cast<bf16*>(a.dv) + row * D;
   bf16x8 rf[NT][4], df[NT][4];
   float dcs = 0.f;
 #pragma unroll
@@ -720,7 +722,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void upd_kernel(BwdArgs a, int n_kt) {
         rf[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = (bf16)rv;
         if constexpr (DELTA) df[jb >> 1][2 * (jb & 1) + (r >> 3)][r & 7] = (bf16)dp;
       }
-      if (live) *reinterpret_cast<f32x4*>(dva + col) = dv4;
+      if (live) {
+        bf16x4 y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = from_f32<bf16>(dv4[j]);
+        store4<bf16>(dvo + col, y);
+      }
     }
   if constexpr (DELTA) {
     dcs = xhalf_sum(dcs);

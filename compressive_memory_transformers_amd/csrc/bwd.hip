@@ -491,7 +491,7 @@ __global__ __launch_bounds__(D) void dz_scan_kernel(BwdArgs a) {
 }
 
 // dK = dk_acc + (dphi + dc z_{s-1} + dz_s) sigma'(k) (DK wide), dV = dv_acc
-// (DV wide). Each thread takes eight consecutive elements of a row (16-byte
+// (DV wide; unless the fused update kernel already wrote it). Each thread takes eight consecutive elements of a row (16-byte
 // stores of the outputs; every pointer is 16-byte aligned and the widths are
 // multiples of 8), so the row and segment are decoded once per eight.
 template <typename T, int DK, int DV>
@@ -526,6 +526,7 @@ __global__ __launch_bounds__(256) void kv_out_kernel(BwdArgs a) {
     }
     store8<T>(static_cast<T*>(a.dk) + e, y);
   }
+  if (a.dv_final) return;  // the fused update kernel wrote dv
   const int64_t nv = rows * CV;
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nv; x += stride) {
     const frag_t<float> acc = load8<float>(a.dv_acc + 8 * x);

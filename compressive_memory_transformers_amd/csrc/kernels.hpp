@@ -191,6 +191,7 @@ struct BwdArgs {
   void* dv;
   float* dbeta;        // [Hq]
   float* dbeta_part;   // [Hq][B][ceil(L / kDbetaChunk)] partial sums of dg
+  int32_t dv_final;    // the fused update kernel writes dv itself (dv_acc is not read after it)
   int64_t L, seg_len;
   int32_t B, Hq, Hkv, S;
   int32_t rule;
