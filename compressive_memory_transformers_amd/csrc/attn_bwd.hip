@@ -227,6 +227,24 @@ __global__ __launch_bounds__(kNW * 64, 2) void dq_kernel(BwdArgs a, int n_qt) {
 
 // ---- dK, dV: one workgroup per 128 keys, query tiles of 32, all G heads -------
 
+// A tile load as DmaTile::issue<true>, but with rows past the segment's end
+// read as zeros: the resource covers only the valid rows and the buffer's
+// range check zero-fills the rest. The whole offset goes in the lane's
+// register, since the range check leaves out the scalar offset.
+template <int D, int NW, int BN>
+__device__ __forceinline__ void issue_zero_tail(const DmaTile<D, NW, BN>& t, const bf16* X,
+                                                bf16* Xs, int k0, int n_s, int w) {
+  using Tile = DmaTile<D, NW, BN>;
+  const int rows = min(BN, n_s - k0);
+  const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + (int64_t)k0 * D, (uint32_t)rows * D * 2);
+#pragma unroll
+  for (int j = 0; j < Tile::PER_WAVE; ++j) {
+    const int blk = (j * NW + w) * 64 * 8;
+    const uint32_t xj = Tile::J_INV ? t.k_off[0] + j * Tile::J_STEP : t.k_off[j];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, xj, 0, 0, 0);
+  }
+}
+
 template <int D>
 struct KvLane {
   static constexpr int NC = D / 16, NDB = D / 32;
@@ -368,8 +386,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
   auto issue = [&](int hg, int qi, bf16* Qd, bf16* Od, float* Ld, float* Dd) {
     const int q0 = k0 + qi * BQ;
     const int64_t rb = (int64_t)(hrow0 + hg) * a.L + seg_start;
-    tile.template issue_zero_tail<true>(static_cast<const bf16*>(a.q) + rb * D, Qd, q0, n_s, w);
-    tile.template issue_zero_tail<true>(static_cast<const bf16*>(a.dout) + rb * D, Od, q0, n_s, w);
+    issue_zero_tail(tile, static_cast<const bf16*>(a.q) + rb * D, Qd, q0, n_s, w);
+    issue_zero_tail(tile, static_cast<const bf16*>(a.dout) + rb * D, Od, q0, n_s, w);
     // 32 floats of lse (wave 0) and delta (wave 1); lanes past the rows read zeros
     const int bytes = min(BQ, n_s - q0) * 4;
     if (w == 0) {

@@ -150,23 +150,6 @@ struct DmaTile {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, off[J_INV ? 0 : j], sj, 0, 0);
     }
   }
-  // issue() with rows past the segment's end read as zeros (the resource
-  // covers only the valid rows and the buffer's range check zero-fills the
-  // rest). The whole offset goes in the lane's register: the range check
-  // leaves out the scalar offset.
-  template <bool IS_K>
-  __device__ __forceinline__ void issue_zero_tail(const bf16* X, bf16* Xs, int k0, int n_s,
-                                                  int w) const {
-    const uint32_t* off = IS_K ? k_off : v_off;
-    const int rows = min(BN, n_s - k0);
-    const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + (int64_t)k0 * D, (uint32_t)rows * D * 2);
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int blk = (j * NW + w) * 64 * 8;
-      const uint32_t xj = J_INV ? off[0] + j * J_STEP : off[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(Xs + blk), 16, xj, 0, 0, 0);
-    }
-  }
   // issue() through dma16_asm
   template <bool IS_K>
   __device__ __forceinline__ void issue_asm(const bf16* X, bf16* Xs, int k0, int n_s, int w) const {
