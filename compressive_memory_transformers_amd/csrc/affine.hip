@@ -451,6 +451,121 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
     }
 }
 
+// ---- 3''. A_s in float, for the backward's state gradient -------------------
+//
+// The transition I + A_s of the delta rule has entries of order 1 / z, so the
+// state gradient's reversed chain needs A_s = -Phi^T diag(1/den) Phi to about
+// float accuracy (one bf16 product leaves each term 2^-8 off). The staging is
+// affine_dma_kernel's (chunks of 32 tokens of K through a 3-deep DMA ring,
+// 16 threads per token), but Phi and Phi / den are each staged as a pair of
+// bf16 values, hi = bf16(x) and lo = bf16(x - hi), and every output tile takes
+// three bf16 products per k step: hi^T hi + hi^T lo + lo^T hi, summed in float.
+// Each term is then within about 2^-16 of its float value (the split and the
+// dropped lo^T lo), and the terms are all positive (Phi > 0, den > 0), so the
+// sums do not cancel. Wave w owns the output row tile w / 2 and the column
+// tiles 2 (w % 2) and + 1.
+__global__ __launch_bounds__(512, 2) void affine_af32_kernel(AffineArgs a) {
+  constexpr int D = 128, NW = 8, TC = 32, NBUF = 3;
+  using Tile = DmaTile<D, NW, TC>;
+  __shared__ __align__(1024) bf16 Kr[NBUF][TC * D];
+  __shared__ __align__(1024) bf16 Ph[TC * D];  // Phi, hi and lo parts
+  __shared__ __align__(1024) bf16 Pl[TC * D];
+  __shared__ __align__(1024) bf16 Qh[TC * D];  // Phi / den, hi and lo parts
+  __shared__ __align__(1024) bf16 Ql[TC * D];
+  __shared__ __align__(16) float Zs[256];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
+  const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
+  const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const bf16* K = static_cast<const bf16*>(a.k) + ((int64_t)unit * a.L + seg_start) * D;
+  const int n_c = (n_s + TC - 1) / TC;
+
+  // staging role: token st_t of the chunk, columns 8 st_g .. + 7; z by one
+  // 16-byte DMA per lane of wave 0 (lanes past d / 4 read zeros), issued
+  // before the tiles, so the first chunk's wait covers it
+  const int st_t = tid >> 4, st_g = tid & 15;
+  if (w == 0)
+    dma16_asm(Zs, asm_rsrc(a.snapZ + ((int64_t)unit * a.s_count + sl) * D, D * 4),
+              (uint32_t)lane * 16, 0u);
+  Tile tile;
+  tile.init(w, lane);
+  tile.template issue_asm<true>(K, Kr[0], 0, n_s, w);
+  if (n_c > 1) tile.template issue_asm<true>(K, Kr[1], TC, n_s, w);
+
+  const int rt = w >> 1, c0 = 2 * (w & 1);
+  const uint32_t ao = tr_offset<D>(lane, rt);
+  const uint32_t bo[2] = {tr_offset<D>(lane, c0), tr_offset<D>(lane, c0 + 1)};
+  f32x16 acc[2] = {zero16(), zero16()};
+  float zc[8];
+
+  for (int ch = 0; ch < n_c; ++ch) {
+    const int buf = ch % NBUF;
+    // this wave's load of chunk ch has landed (chunk ch + 1's may be in flight)
+    if (ch + 1 < n_c)
+      wait_vmcnt<Tile::PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // chunk ch complete everywhere; chunk ch - 1's products done
+    if (ch == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zc[e] = Zs[8 * st_g + e];
+    }
+    if (ch + 2 < n_c)  // into the buffer chunk ch - 1 used
+      tile.template issue_asm<true>(K, Kr[(ch + 2) % NBUF], (ch + 2) * TC, n_s, w);
+    {  // stage the splits of token st_t (zero past the segment's end)
+      const bool ok = ch * TC + st_t < n_s;
+      const bf16x8 kv = load8<bf16>(Kr[buf] + st_t * D + 8 * (st_g ^ swz_k<D>(st_t)));
+      float ph[8];
+      float dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = ok ? feature_map((float)kv[e]) : 0.f;
+        ph[e] = f;
+        dp += f * zc[e];
+      }
+      const float den = row_sum<16>(dp);
+      const float rd = ok ? 1.f / den : 0.f;
+      bf16x8 h1, l1, h2, l2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        h1[e] = (bf16)ph[e];
+        l1[e] = (bf16)(ph[e] - (float)h1[e]);
+        const float x = ph[e] * rd;
+        h2[e] = (bf16)x;
+        l2[e] = (bf16)(x - (float)h2[e]);
+      }
+      const int po = st_t * D + 8 * (st_g ^ swz_v<D>(st_t));
+      store8<bf16>(Ph + po, h1);
+      store8<bf16>(Pl + po, l1);
+      store8<bf16>(Qh + po, h2);
+      store8<bf16>(Ql + po, l2);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < TC / 16; ++p) {
+      const bf16x8 ah = tr_frag<D>(Ph, ao, p), al = tr_frag<D>(Pl, ao, p);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 bh = tr_frag<D>(Qh, bo[c], p), bl = tr_frag<D>(Ql, bo[c], p);
+        mma32(acc[c], ah, bh);
+        mma32(acc[c], ah, bl);
+        mma32(acc[c], al, bh);
+      }
+    }
+  }
+
+  const int i = lane & 31, h = lane >> 5;
+  float* A = a.Amat_f + ((int64_t)unit * a.s_count + sl) * D * D;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int col = 32 * (c0 + c) + i;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) A[(32 * rt + acc_row(q, h)) * D + col] = -acc[c][q];
+  }
+}
+
 // ---- 4. M_s = M_{s-1} + B_s + A_s M_{s-1}, per 32-column slab ---------------
 //
 // With a.reverse the same step runs over the segments last to first. The
@@ -845,6 +960,15 @@ hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStre
   if (segs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear>), dim3((unsigned)segs), dim3(512), 0, stream,
                      a);
+  return hipGetLastError();
+}
+
+bool affine_a_f32_supported(int dtype, int d) { return dtype == kBF16 && d == 128; }
+
+hipError_t launch_affine_a_f32(const AffineArgs& a, hipStream_t stream) {
+  const int64_t segs = (int64_t)a.units * a.s_count;
+  if (segs <= 0 || segs > INT32_MAX || a.Amat_f == nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(affine_af32_kernel, dim3((unsigned)segs), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -939,8 +939,10 @@ BwdLayout bwd_layout(const Plan& p, int64_t B, int64_t Hq, int64_t Hkv, int64_t 
       b.dp_el = take(krows * dv * e);
     }
     b.dc = take(krows * 4);
-    b.phi_f = take(krows * d * 4);
-    b.phic_f = take(krows * d * 4);
+    if (!infini::affine_a_f32_supported(p.e == 2 ? infini::kBF16 : infini::kF32, (int)d)) {
+      b.phi_f = take(krows * d * 4);
+      b.phic_f = take(krows * d * 4);
+    }
   }
   b.total = cur + kAlign;  // slack for an unaligned base
   return b;
@@ -1116,8 +1118,8 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
   ba.u_el = rows ? E(lay.u_el) : nullptr;
   ba.dp_el = rows ? E(lay.dp_el) : nullptr;
   ba.dc = rule == INFINI_RULE_DELTA ? F(lay.dc) : nullptr;
-  ba.phi_f = rule == INFINI_RULE_DELTA ? F(lay.phi_f) : nullptr;
-  ba.phic_f = rule == INFINI_RULE_DELTA ? F(lay.phic_f) : nullptr;
+  ba.phi_f = rule == INFINI_RULE_DELTA && lay.phi_f ? F(lay.phi_f) : nullptr;
+  ba.phic_f = rule == INFINI_RULE_DELTA && lay.phic_f ? F(lay.phic_f) : nullptr;
   ba.e_ret = F(lay.e_ret);
   ba.e_upd = F(lay.e_upd);
   ba.dzs = F(lay.dzs);
@@ -1233,8 +1235,15 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
     return INFINI_ERR_HIP;
 
   // 3. dM_s for every segment, and dM0, in float. A_s = -Phi^T diag(1/c) Phi
-  // from float sigma(K) and sigma(K) / c.
-  if (rule == INFINI_RULE_DELTA) {
+  // from float sigma(K) and sigma(K) / c (bf16 with d = 128: from bf16 hi/lo
+  // pairs of both, formed on the fly from K).
+  if (rule == INFINI_RULE_DELTA && infini::affine_a_f32_supported(dtype, D)) {
+    // bf16, d = 128: one pass over K, Phi and Phi / den split into bf16
+    // pairs on three bf16 products per tile (affine.hip)
+    AffineArgs aa = fa;
+    aa.Amat_f = F(lay.Amat_f);
+    if (infini::launch_affine_a_f32(aa, s) != hipSuccess) return INFINI_ERR_HIP;
+  } else if (rule == INFINI_RULE_DELTA) {
     if (infini::launch_bwd_phi_rows(dtype, D, DV, ba, s) != hipSuccess) return INFINI_ERR_HIP;
     infini::GemmArgs g = gemm_args(ba.phi_f, ba.phic_f, F(lay.Amat_f), D, D, (int32_t)seg_len,
                                    units, S, L, seg_len);

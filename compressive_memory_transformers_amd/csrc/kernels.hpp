@@ -44,6 +44,7 @@ struct AffineArgs {
   float* colsum;       // [B*Hkv][s_count][d]
   void* Amat;          // [B*Hkv][s_count][d][d], element type (delta rule only)
   float* Bmat;         // [B*Hkv][s_count][d][d]
+  float* Amat_f;       // [B*Hkv][s_count][d][d] A_s in float (launch_affine_a_f32 only)
   int64_t L, seg_len;
   int32_t units;
   int32_t s_begin, s_count;
@@ -245,6 +246,11 @@ hipError_t launch_scan(int dtype, int d, int rule, const ScanArgs& a, hipStream_
 hipError_t launch_scan_kv(int dtype, int dk, int dv, int rule, const ScanArgs& a,
                           hipStream_t stream);
 hipError_t launch_affine(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
+// A_s = -Phi^T diag(1/den) Phi in float into a.Amat_f, for every (unit,
+// segment) of a.s_count, from K (bf16, d = 128) and the z before each segment
+// (a.snapZ): the delta rule's transition as the backward's state gradient needs it.
+bool affine_a_f32_supported(int dtype, int d);
+hipError_t launch_affine_a_f32(const AffineArgs& a, hipStream_t stream);
 // The chain step of the affine form alone (a.reverse honoured).
 hipError_t launch_chain(int dtype, int d, int rule, const AffineArgs& a, hipStream_t stream);
 // The same step in float with d_key = dk != d_value = dv: M, B_s [dk][dv] per

@@ -54,10 +54,10 @@ CASES = [
 IDS = [f"B{c[0]}Hq{c[1]}Hkv{c[2]}L{c[3]}d{c[4]}N{c[5]}{str(c[6])[6:]}" for c in CASES]
 
 
-def run_case(lib, case, rule, seed, with_final=True, dv=None):
+def run_case(lib, case, rule, seed, with_final=True, dv=None, m0_scale=0.3):
     B, Hq, Hkv, L, d, N, dt = case
     dv = d if dv is None else dv
-    inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=seed, m0_scale=0.3, dv=dv)
+    inp = random_inputs(B, Hq, Hkv, L, d, dt, DEV, seed=seed, m0_scale=m0_scale, dv=dv)
     g = torch.Generator(device="cpu").manual_seed(seed + 1)
     d_out = torch.randn(B, Hq, L, dv, generator=g).to(dt).to(DEV)
     dM_f = torch.randn(B, Hkv, d, dv, generator=g).to(DEV) if with_final else None
@@ -121,6 +121,24 @@ def test_without_final_state_gradients(lib, dt):
     errs, _ = run_case(lib, case, "delta", seed=5, with_final=False)
     _say("errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL[dt], errs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_small_initial_z(lib, d):
+    """M0 = 0 and z0 = 1e-6: the delta rule's transition I + A_s, A_s =
+    -Phi^T diag(1/den) Phi with den = Phi z_{s-1}, has entries of order 1e6 in
+    the first segment, so the state gradient's reversed chain is as sensitive
+    to how A_s is formed as it gets (bf16, GQA 4, four segments, ragged).
+
+    dM0 takes a bound of its own, 1e-3: with A_s formed from float operands
+    (d = 64) or from bf16 hi/lo pairs (d = 128) it comes out near 3.4e-4; A_s
+    from one bf16 product per term puts it near 3e-3."""
+    case = (1, 4, 1, 200, d, 56, torch.bfloat16)
+    _say(f"small z0 {case}")
+    errs, _ = run_case(lib, case, "delta", seed=3 * d, m0_scale=0.0)
+    _say("errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL[torch.bfloat16], errs
+    assert errs["dM0"] <= 1e-3, errs
 
 
 def test_llama_head_shape_two_segments(lib):
