@@ -272,6 +272,14 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
   }
 }
 
+// One 4-byte LDS-DMA load per lane as inline assembly, like dma16_asm (the
+// kernel waits for it explicitly): lane l's dword lands at lds + 4 l.
+__device__ __forceinline__ void dma4_asm(void* lds, u32x4 rsrc, uint32_t voff) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // ---- 3'. the same products for bf16, d = 128, from DMA-fed LDS tiles ---------
 //
 // Chunks of 32 tokens of K and V stream into a 3-deep LDS ring (K in the "K"
@@ -287,7 +295,10 @@ __global__ __launch_bounds__((AffineShape<D, RULE>::NW * 64)) void affine_kernel
 // products (MFMA).
 // COLSUM (linear rule): also the segment's column sums of Phi, from the staged
 // rows (the linear rule's products need no z, so the sums need no pass of
-// their own over K).
+// their own over K); with a.colsum_w set, the sums weight each row by it
+// (the backward's sum over the group's query rows of dden_t sigma(q_t), beside
+// C_s in the same pass over q). The weights of a chunk come into an LDS ring
+// by one 4-byte DMA per lane of wave 0, counted in that wave's waits.
 template <int RULE, bool COLSUM = false>
 __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
   constexpr int D = 128, NW = 8, TC = 32, NBUF = 3;
@@ -299,12 +310,14 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
   __shared__ __align__(1024) bf16 Ph[TC * D];
   __shared__ __align__(1024) bf16 DPh[DELTA ? TC * D : 8];
   __shared__ __align__(16) float Zs[256];
+  __shared__ __align__(16) float Ws[COLSUM ? NBUF * 64 : 4];  // row weights, a ring
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x / a.s_count, sl = blockIdx.x % a.s_count;
   const int64_t seg_start = (int64_t)(a.s_begin + sl) * a.seg_len;
   const int n_s = (int)min<int64_t>(a.seg_len, a.L - seg_start);
+  const bool weighted = COLSUM && a.colsum_w != nullptr;  // uniform
   // rows of `heads` consecutive heads (one in the recurrence), chunk c of
   // the run being chunk c % n_c of head c / n_c
   const int heads = a.heads > 1 ? a.heads : 1;
@@ -326,11 +339,23 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
   float zc[8];
   Tile tile;
   tile.init(w, lane);
+  // chunk c's weights into ring slot c % NBUF (lanes past the chunk's rows
+  // read zeros; the slot holds all 64 lanes)
+  auto issue_w = [&](int c) {
+    if (weighted && w == 0) {
+      const int64_t r0 = ((int64_t)unit * heads + c / n_c) * a.L + seg_start + chunk0(c);
+      const int rows = min(TC, n_s - chunk0(c));
+      dma4_asm(Ws + (c % NBUF) * 64, asm_rsrc(a.colsum_w + r0, (uint32_t)rows * 4),
+               (uint32_t)lane * 4);
+    }
+  };
   tile.template issue_asm<true>(K, Kr[0], 0, n_s, w);
   tile.template issue_asm<false>(V, Vr[0], 0, n_s, w);
+  issue_w(0);
   if (n_t > 1) {
     tile.template issue_asm<true>(K + head_off(1), Kr[1], chunk0(1), n_s, w);
     tile.template issue_asm<false>(V + head_off(1), Vr[1], chunk0(1), n_s, w);
+    issue_w(1);
   }
 
   // product role: row tiles rt0, rt0 + 1; column tiles BC cq + c
@@ -352,11 +377,16 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
   for (int ch = 0; ch < n_t; ++ch) {
     const int buf = ch % NBUF;
     // this wave's loads of chunk ch have landed (the 2 PER_WAVE of chunk
-    // ch + 1, issued later, may still be in flight)
-    if (ch + 1 < n_t)
-      wait_vmcnt<2 * Tile::PER_WAVE>();
-    else
+    // ch + 1, issued later, and wave 0's weight load of it may still be in
+    // flight)
+    if (ch + 1 < n_t) {
+      if (weighted && w == 0)
+        wait_vmcnt<2 * Tile::PER_WAVE + 1>();
+      else
+        wait_vmcnt<2 * Tile::PER_WAVE>();
+    } else {
       wait_vmcnt<0>();
+    }
     __syncthreads();  // chunk ch complete everywhere; chunk ch - 1's products done
     if (ch == 0) {
 #pragma unroll
@@ -366,10 +396,12 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
       const int cn = ch + 2;
       tile.template issue_asm<true>(K + head_off(cn), Kr[cn % NBUF], chunk0(cn), n_s, w);
       tile.template issue_asm<false>(V + head_off(cn), Vr[cn % NBUF], chunk0(cn), n_s, w);
+      issue_w(cn);
     }
     // stage Phi and Phi / den of token st_t (zero past the segment's end)
     {
       const bool ok = chunk0(ch) + st_t < n_s;
+      const float wt = weighted ? Ws[buf * 64 + st_t] : 1.f;
       const bf16x8 kv = load8<bf16>(Kr[buf] + st_t * D + 8 * (st_g ^ swz_k<D>(st_t)));
       float ph[8];
       float dp = 0.f;
@@ -378,7 +410,7 @@ __global__ __launch_bounds__(512, 2) void affine_dma_kernel(AffineArgs a) {
         const float f = ok ? feature_map((float)kv[e]) : 0.f;
         ph[e] = f;
         dp += f * zc[e];
-        if constexpr (COLSUM) csum[e] += f;
+        if constexpr (COLSUM) csum[e] += wt * f;
       }
       const int po = st_t * D + 8 * (st_g ^ swz_v<D>(st_t));
       {
@@ -958,8 +990,12 @@ hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStre
   if (dtype != kBF16 || d != 128) return hipErrorInvalidValue;
   const int64_t segs = (int64_t)a.units * a.s_count;
   if (segs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear>), dim3((unsigned)segs), dim3(512), 0, stream,
-                     a);
+  if (a.colsum != nullptr)
+    hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear, true>), dim3((unsigned)segs), dim3(512), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((affine_dma_kernel<kRuleLinear>), dim3((unsigned)segs), dim3(512), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

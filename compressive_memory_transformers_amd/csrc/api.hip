@@ -1195,14 +1195,18 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
     }
   }
   // C_s = sum over the group's heads of sigma(Q)^T dn, into Bmat: bf16 with
-  // d = 128 by the recurrence's product kernel (one pass over q and dn),
-  // otherwise one product per head, accumulating
+  // d = 128 by the recurrence's product kernel (one pass over q and dn, which
+  // also forms the retrieval part of dL/dz_{s-1}, sum of dden_t sigma(q_t),
+  // from the rows it stages), otherwise one product per head, accumulating,
+  // and a row reduction for the dz part
   if (dtype == INFINI_BF16 && d == 128 && dv == 128) {
     AffineArgs ca{};
     ca.k = q;
     ca.v = E(lay.dn);
     ca.snapZ = F(lay.snapZ);
     ca.Bmat = F(lay.Bmat);
+    ca.colsum = F(lay.e_ret);
+    ca.colsum_w = ba.dden;
     ca.L = L;
     ca.seg_len = seg_len;
     ca.units = (int32_t)units;
@@ -1230,9 +1234,9 @@ infini_status_t backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int
       g.accumulate = hg > 0;
       if (infini::launch_gemm(dtype, g, s) != hipSuccess) return INFINI_ERR_HIP;
     }
+    if (infini::launch_bwd_row_weighted_sum(dtype, D, DV, ba, true, s) != hipSuccess)
+      return INFINI_ERR_HIP;
   }
-  if (infini::launch_bwd_row_weighted_sum(dtype, D, DV, ba, true, s) != hipSuccess)
-    return INFINI_ERR_HIP;
 
   // 3. dM_s for every segment, and dM0, in float. A_s = -Phi^T diag(1/c) Phi
   // from float sigma(K) and sigma(K) / c (bf16 with d = 128: from bf16 hi/lo

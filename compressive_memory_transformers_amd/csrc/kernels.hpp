@@ -42,6 +42,8 @@ struct AffineArgs {
   void* snapM;         // as ScanArgs::snapM
   float* snapZ;        // as ScanArgs::snapZ
   float* colsum;       // [B*Hkv][s_count][d]
+  const float* colsum_w;  // products with column sums only: per-row weights of the
+                          // sums ([rows of k], laid out as k's rows), or null
   void* Amat;          // [B*Hkv][s_count][d][d], element type (delta rule only)
   float* Bmat;         // [B*Hkv][s_count][d][d]
   float* Amat_f;       // [B*Hkv][s_count][d][d] A_s in float (launch_affine_a_f32 only)
@@ -259,7 +261,9 @@ hipError_t launch_chain_kv_f32(int dk, int dv, int rule, const AffineArgs& a,
                                hipStream_t stream);
 // The linear rule's products alone, Bmat = sum over a.heads heads of
 // sigma(K)^T V per (unit, segment), bf16 with d = 128 (hipErrorInvalidValue
-// otherwise: the caller takes another path).
+// otherwise: the caller takes another path). With a.colsum set, also the
+// column sums of sigma(K) over the same rows, weighted by a.colsum_w when
+// that is set.
 hipError_t launch_affine_products(int dtype, int d, const AffineArgs& a, hipStream_t stream);
 hipError_t launch_attn(int dtype, int d, const AttnArgs& a, int64_t units, hipStream_t stream);
 // The attention with d_key = dk != d_value = dv: q, k rows of dk, v and out
