@@ -481,9 +481,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void kv_kernel(BwdArgs a, int n_kt) {
 // of dQ, (dn M^T + dden_t z) * sigma'(q), in its epilogue; dn also feeds the
 // products into dL/dM_{s-1}. n^T = M^T sigma(q)^T runs on the matrix cores
 // with M^T in LDS (the K layout), as the query-major kernel forms S^T.
-// sigma(q) enters the product in bf16, den in float.
+// sigma(q) enters the product in bf16, den in float. Three waves per SIMD:
+// at d = 128 that leaves 168 registers, and a few row indices of the final
+// stores go to scratch, which costs less than the third wave gains.
 template <int D>
-__global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) {
+__global__ __launch_bounds__(kNW * 64, 3) void retr_kernel(BwdArgs a, int n_qt) {
   constexpr int BM = 32 * kNW, NC = D / 16, NT = D / 64, NJB = D / 32;
   __shared__ __align__(1024) bf16 Ms0[64 * D];
   __shared__ __align__(1024) bf16 Ms1[NT > 1 ? 64 * D : 8];
@@ -543,8 +545,16 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
     }
   den = xhalf_sum(den);
 
+  // n^T = M^T sigma(q)^T with the rows of each 32-row block of M^T read in
+  // the order pi(i) = i ^ 12 where bits 2 and 3 of i differ (row groups
+  // 4..7 <-> 8..11, 20..23 <-> 24..27): accumulator register 8 m + e of lane
+  // (i, h) then holds column 32 jb + 16 m + 8 h + e of n, the columns of the
+  // lane's 16-byte d_out chunks below. pi keeps each 16-row half's set of
+  // rows, so the swizzle's reads stay free of bank conflicts.
+  __builtin_amdgcn_sched_barrier(0);  // sigma(q) complete before the product
   bf16* const Ms[2] = {Ms0, NT > 1 ? Ms1 : Ms0};
-  const uint32_t ko = 2 * (i * D + 8 * (h ^ swz_k<D>(i)));
+  const int pi = i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 12);
+  const uint32_t ko = 2 * (pi * D + 8 * (h ^ swz_k<D>(pi)));
   f32x16 nacc[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) {
@@ -556,54 +566,50 @@ __global__ __launch_bounds__(kNW * 64, 2) void retr_kernel(BwdArgs a, int n_qt) 
     }
   }
 
-  // this lane: row `row`, columns j = 32 jb + 8 rq + 4 h + 0..3 of n
-  float dam = 0.f, doo = 0.f;
-  bf16x4 dov[NJB][4];
+  // d_out and out come in 16-byte chunks: lane (i, h) loads columns
+  // 32 jb + 16 m + 8 h + 0..7 of row `row` (32 contiguous bytes of the row
+  // per lane pair and instruction), the columns of its n accumulators 8 m ..
+  // 8 m + 7. dn = g d_out / den is stored (bf16) for the query-major kernel,
+  // which forms the retrieval part of dQ from it, and for the products into
+  // dL/dM_{s-1}.
+  const float inv_den = 1.f / den;
+  const float gd = g * inv_den;
+  bf16* dn = static_cast<bf16*>(a.dn) + (rbase + row) * D;
+  // every load before the first store (the stores could alias them as far
+  // as the compiler knows, so it would not move a load above one)
+  bf16x8 d8[NJB][2], o8[NJB][2];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int col = 32 * jb + 8 * rq + 4 * h;
-      bf16x4 o4;
-      if (live) {
-        dov[jb][rq] = load4<bf16>(dO + col);
-        o4 = load4<bf16>(O + col);
-      } else {
+    for (int m = 0; m < 2; ++m) {
+      const int col = 32 * jb + 16 * m + 8 * h;
+      d8[jb][m] = live ? load8<bf16>(dO + col) : zero_frag<bf16>();
+      o8[jb][m] = live ? load8<bf16>(O + col) : zero_frag<bf16>();
+    }
+  float dam = 0.f, doo = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dov[jb][rq][j] = o4[j] = (bf16)0.f;
-      }
+  for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float dv = (float)dov[jb][rq][j];
-        dam += dv * nacc[jb][4 * rq + j];
-        doo += dv * (float)o4[j];
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dv = (float)d8[jb][m][e];
+        dam += dv * nacc[jb][8 * m + e];
+        doo += dv * (float)o8[jb][m][e];
+        y[e] = (bf16)(gd * dv);
       }
+      if (live) store8<bf16>(dn + 32 * jb + 16 * m + 8 * h, y);
     }
   dam = xhalf_sum(dam);
   doo = xhalf_sum(doo);
-  const float inv_den = 1.f / den;
   dam *= inv_den;
   const float dden = -g * dam * inv_den;
-  const float gd = g * inv_den;
   if (live && h == 0) {
     a.delta[rbase + row] = doo - g * dam;
     a.dg[rbase + row] = (dam - doo) / (1.f - g);
     a.dden[rbase + row] = dden;
   }
-
-  // dn = g d_out / den, stored (bf16) for the query-major kernel, which forms
-  // the retrieval part of dQ from it, and for the products into dL/dM_{s-1}
-  if (!live) return;
-  bf16* dn = static_cast<bf16*>(a.dn) + (rbase + row) * D;
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      bf16x4 y;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = (bf16)(gd * (float)dov[jb][rq][j]);
-      store4<bf16>(dn + 32 * jb + 8 * rq + 4 * h, y);
-    }
 }
 
 // ---- the memory update's backward, fused: one workgroup per 128 key rows ----
