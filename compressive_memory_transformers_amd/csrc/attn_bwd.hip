@@ -575,6 +575,14 @@ __global__ __launch_bounds__(kNW * 64, 3) void retr_kernel(BwdArgs a, int n_qt) 
   const float inv_den = 1.f / den;
   const float gd = g * inv_den;
   bf16* dn = static_cast<bf16*>(a.dn) + (rbase + row) * D;
+  // The segment's first row (row 0) attends to its own key alone, so A_dot
+  // is v_0 and out = g A_mem + (1 - g) v_0: that row reads v_0 in place of
+  // its output row and forms delta = (1 - g) d_out . v_0 and d(gate) =
+  // d_out . A_mem - d_out . v_0 exactly. From the stored output, whose
+  // rounding would not cancel against (1 - g) d_out . v_0 in dS (exactly
+  // zero there), the rounding would land whole in that row's dQ.
+  const bf16* Or = row == 0 ? static_cast<const bf16*>(a.v) + ((int64_t)unit * a.L + seg_start) * D
+                            : O;
   // every load before the first store (the stores could alias them as far
   // as the compiler knows, so it would not move a load above one)
   bf16x8 d8[NJB][2], o8[NJB][2];
@@ -584,7 +592,7 @@ __global__ __launch_bounds__(kNW * 64, 3) void retr_kernel(BwdArgs a, int n_qt) 
     for (int m = 0; m < 2; ++m) {
       const int col = 32 * jb + 16 * m + 8 * h;
       d8[jb][m] = live ? load8<bf16>(dO + col) : zero_frag<bf16>();
-      o8[jb][m] = live ? load8<bf16>(O + col) : zero_frag<bf16>();
+      o8[jb][m] = live ? load8<bf16>(Or + col) : zero_frag<bf16>();
     }
   float dam = 0.f, doo = 0.f;
 #pragma unroll
@@ -606,8 +614,9 @@ __global__ __launch_bounds__(kNW * 64, 3) void retr_kernel(BwdArgs a, int n_qt) 
   dam *= inv_den;
   const float dden = -g * dam * inv_den;
   if (live && h == 0) {
-    a.delta[rbase + row] = doo - g * dam;
-    a.dg[rbase + row] = (dam - doo) / (1.f - g);
+    // row 0 (doo = d_out . v_0): out = g A_mem + (1 - g) v_0 exactly
+    a.delta[rbase + row] = row == 0 ? (1.f - g) * doo : doo - g * dam;
+    a.dg[rbase + row] = row == 0 ? dam - doo : (dam - doo) / (1.f - g);
     a.dden[rbase + row] = dden;
   }
 }

@@ -169,7 +169,15 @@ __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
     const int64_t unit = (int64_t)b * a.Hkv + hq / G;
     const float* z = a.snapZ + (unit * a.S + s) * DK;
     const T* q = static_cast<const T*>(a.q) + row * DK;
-    const T* o = static_cast<const T*>(a.out) + row * DV;
+    // The segment's first row attends to its own key alone, so A_dot = v_t
+    // and out = g A_mem + (1 - g) v_t: that row reads v_t in place of its
+    // output row and forms delta = (1 - g) dout . v_t and d(gate) =
+    // dout . A_mem - dout . v_t exactly. From the stored output, whose
+    // rounding would not cancel against (1 - g) dout . v_t in dS (exactly
+    // zero there), the rounding would land whole in that row's dQ.
+    const bool first = t % a.seg_len == 0;  // wave-uniform
+    const T* o = first ? static_cast<const T*>(a.v) + (unit * a.L + t) * DV
+                       : static_cast<const T*>(a.out) + row * DV;
     const T* dO = static_cast<const T*>(a.dout) + row * DV;
     const float* nm = a.nm + row * DV;
     float den = 0.f;
@@ -198,8 +206,9 @@ __global__ __launch_bounds__(256) void retrieval_rows_kernel(BwdArgs a) {
     for (int e = 0; e < R::E; ++e)
       if (R::ok(lane, e)) dn[64 * e + lane] = from_f32<T>(g * dov[e] / den);
     if (lane == 0) {
-      a.delta[row] = doo - g * dam;
-      a.dg[row] = (dam - doo) / (1.f - g);
+      // first row: doo = dout . v_t
+      a.delta[row] = first ? (1.f - g) * doo : doo - g * dam;
+      a.dg[row] = first ? dam - doo : (dam - doo) / (1.f - g);
       a.dden[row] = -g * dam / den;
     }
   }
