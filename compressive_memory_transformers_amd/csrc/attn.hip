@@ -35,6 +35,7 @@ namespace {
 // accumulator is rescaled rarely. The result is exact either way: numerator
 // and denominator use the same reference.
 constexpr float kRescaleTau = 8.f;
+constexpr float kRescaleBound = 256.f;  // 2^kRescaleTau
 
 // DK: the key width (Q, K, rows of M); DV: the value width (V, the output,
 // columns of M).
@@ -354,11 +355,10 @@ struct DmaLane {
 };
 
 // The key loop is software-pipelined by one tile, so that each wave has
-// matrix work to issue beside its softmax arithmetic: iteration j turns the
-// exp2 arguments of tile j into probabilities while S(j+1) = K(j+1) Q^T runs
-// on the matrix cores, then issues O += V(j) P(j) while it takes the row
-// maxima of S(j+1), decides the lazy rescale and forms the next exp2
-// arguments.
+// matrix work to issue beside its softmax arithmetic: iteration j issues
+// S(j+1) = K(j+1) Q^T and O += V(j) P(j) (P(j) formed in the iteration
+// before) back to back on the matrix cores, then forms P(j+1) from S(j+1)
+// while O's products run.
 
 // S^T = K Q^T for one key tile (K in LDS).
 template <int DK, int DV, int BN>
@@ -374,26 +374,56 @@ __device__ __forceinline__ void dma_scores(const bf16* Kb, const DmaLane<DK, DV>
   }
 }
 
-// Causal mask (on a tile that crosses the wave's diagonal), then the running
-// maximum with the lazy rescale of O and l.
+// Causal mask (on a tile that crosses the wave's diagonal), then the
+// probabilities exp2(c s - c m) of the tile against the running maximum m as
+// the bf16 B operand of O^T += V^T P^T, with their row sums as rounded for
+// that product (pairwise, v_dot2_f32_bf16 against (1, 1)). The lazy rescale
+// is decided from the sums: each lane's sum over its 32 probabilities of the
+// tile bounds every one of them, so while no lane's sum exceeds
+// 2^kRescaleTau (and none is not a number, as with the first tile's
+// m = -inf) no probability does, and the stale m stands. Otherwise (rarely)
+// the wave takes the tile's row maxima, rescales O and l, and forms the
+// probabilities again. No row maximum is taken on the common path.
 template <int DK, int DV, int BN>
-__device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<DK, DV>& st, float c, int k0,
-                                        int row, int h, bool diag) {
-  constexpr int NDB = DV / 32, NKB = BN / 32;
+__device__ __forceinline__ void dma_probs_lazy(f32x16* s, DmaLane<DK, DV>& st, float c, int k0,
+                                               int row, int h, bool diag, bf16x8* pf) {
+  constexpr int NDB = DV / 32, NKB = BN / 32, NPC = BN / 16;
   if (diag) {  // wave-uniform
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (k0 + 32 * kb + acc_row(r, h) > row) sacc[kb][r] = -INFINITY;
+        if (k0 + 32 * kb + acc_row(r, h) > row) s[kb][r] = -INFINITY;
   }
-  float mx = -INFINITY;
+  float t0, t1;
+  auto form = [&]() {
+    const float mc = st.m_run * c;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-  mx = xhalf_max(mx);
-  if (__any((mx - st.m_run) * c > kRescaleTau)) {
+      for (int r = 0; r < 16; ++r)
+        pf[2 * kb + (r >> 3)][r & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+    t0 = t1 = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 pr = {pf[pc][2 * q], pf[pc][2 * q + 1]};
+        if (q & 1)
+          t1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, t1, false);
+        else
+          t0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, t0, false);
+      }
+  };
+  form();
+  if (__any(!(t0 + t1 <= kRescaleBound))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = xhalf_max(mx);
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f((st.m_run - m_new) * c);
     st.l0 *= alpha;
@@ -403,34 +433,10 @@ __device__ __forceinline__ void dma_max(f32x16* sacc, DmaLane<DK, DV>& st, float
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
     st.m_run = m_new;
+    form();
   }
-}
-
-// Probabilities exp2(c s - c m) of one tile as the bf16 B operand of
-// O^T += V^T P^T, and the row sums of the probabilities as rounded for that
-// product (pairwise, with v_dot2_f32_bf16 against (1, 1)).
-template <int DK, int DV, int BN>
-__device__ __forceinline__ void dma_probs(const f32x16* sacc, DmaLane<DK, DV>& st, float c,
-                                          bf16x8* pf) {
-  constexpr int NKB = BN / 32, NPC = BN / 16;
-  const float mc = st.m_run * c;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      pf[2 * kb + (r >> 3)][r & 7] =
-          (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c, -mc));
-  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
-#pragma unroll
-  for (int pc = 0; pc < NPC; ++pc)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bf16x2 pr = {pf[pc][2 * q], pf[pc][2 * q + 1]};
-      if (q & 1)
-        st.l1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l1, false);
-      else
-        st.l0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l0, false);
-    }
+  st.l0 += t0;
+  st.l1 += t1;
 }
 
 // O^T += V^T P^T for one key tile (V in LDS, read transposed).
@@ -467,7 +473,7 @@ __device__ __forceinline__ void dma_snapshot(const DmaTile<DK, NW, BN>& tile, co
 
 // Iteration j of the key loop on LDS buffer parity P = j % 2 (a constant, so
 // every LDS address is a lane offset plus an immediate). On entry K(j + 1) is
-// in Ks[P ^ 1] and V(j) in Vs[P]; sacc holds the exp2 arguments of tile j.
+// in Ks[P ^ 1] and V(j) in Vs[P]; pf holds the probabilities of tile j.
 // The iteration loads K(j + 2) over K(j) and V(j + 1) over V(j - 1), both
 // last read before the previous barrier, and waits for them at its end.
 // FULL: the caller knows that tile j + 1 is this wave's too and below its
@@ -481,7 +487,7 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
                                          const DmaTile<DK, NW, BN>& tile,
                                          const DmaTile<DV, NW, BN>& vtile, const bf16* K,
                                          const bf16* V, bf16* const* Ks, bf16* const* Vs, int n_s,
-                                         int w, int wfirst, DmaLane<DK, DV>& st, f32x16* sacc,
+                                         int w, int wfirst, DmaLane<DK, DV>& st, bf16x8* pf,
                                          float c, int row, int h, const bf16* Mts,
                                          const float* zs, float* Zs) {
   constexpr int NKB = BN / 32, NPC = BN / 16;
@@ -495,8 +501,6 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
   if (!FULL && j + 1 == n_kt)
     dma_snapshot<DK, DV, NW, BN>(tile, Mts, zs, Ks[P], Vs[P ^ 1], Zs, w);
   if (FULL || j + 1 < n_w) {
-    bf16x8 pf[NPC];
-    dma_probs<DK, DV, BN>(sacc, st, c, pf);
     f32x16 snext[NKB];
     dma_scores<DK, DV, BN>(Ks[P ^ 1], st, snext);
     dma_values<DK, DV, BN>(Vs[P], st, pf);
@@ -505,12 +509,8 @@ __device__ __forceinline__ void dma_iter(int j, int n_kt, int n_w,
     // the strategies for other instruction mixes were slower)
     if constexpr (FULL) __builtin_amdgcn_iglp_opt(0);
     const int k1 = (j + 1) * BN;
-    dma_max<DK, DV, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > wfirst);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = snext[kb];
+    dma_probs_lazy<DK, DV, BN>(snext, st, c, k1, row, h, !FULL && k1 + BN - 1 > wfirst, pf);
   } else if (!FULL && j < n_w) {  // this wave's last tile
-    bf16x8 pf[NPC];
-    dma_probs<DK, DV, BN>(sacc, st, c, pf);
     dma_values<DK, DV, BN>(Vs[P], st, pf);
   }
   if (FULL || j + 1 < n_kt) {
@@ -620,13 +620,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
 
   // key tiles this wave computes (its last is the one holding its last row)
   const int n_w = wave_on ? wave_last / BN + 1 : 0;
-  constexpr int NKB = BN / 32;
-  f32x16 sacc[NKB];
+  constexpr int NKB = BN / 32, NPC = BN / 16;
+  bf16x8 pf[NPC];  // the probabilities of the next tile to multiply into O
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (n_w > 0) {
-    dma_scores<DK, DV, BN>(Ks[0], st, sacc);
-    dma_max<DK, DV, BN>(sacc, st, c, 0, row, h, BN - 1 > wave_first);
+    f32x16 s0[NKB];
+    dma_scores<DK, DV, BN>(Ks[0], st, s0);
+    dma_probs_lazy<DK, DV, BN>(s0, st, c, 0, row, h, BN - 1 > wave_first, pf);
   }
   __syncthreads();  // K(0) read by every wave before iteration 0 loads K(2) over it
   // When every row of the block is in the segment, iterations j whose next
@@ -638,16 +639,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel_dma(AttnArgs a) {
   const bf16* Mts = static_cast<const bf16*>(a.snapM) + snap * DV * DK;
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
-    dma_iter<DK, DV, NW, BN, 0, true>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row, h,
+    dma_iter<DK, DV, NW, BN, 0, true>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, pf, c, row, h,
                                  Mts, zs, Zs);
-    dma_iter<DK, DV, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 1, true>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, pf, c, row,
                                  h, Mts, zs, Zs);
   }
   for (; j < n_kt; j += 2) {  // j is even here
-    dma_iter<DK, DV, NW, BN, 0, false>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c, row,
+    dma_iter<DK, DV, NW, BN, 0, false>(j, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, pf, c, row,
                                   h, Mts, zs, Zs);
     if (j + 1 < n_kt)
-      dma_iter<DK, DV, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, sacc, c,
+      dma_iter<DK, DV, NW, BN, 1, false>(j + 1, n_kt, n_w, tile, vtile, K, V, Ks, Vs, n_s, w, wave_first, st, pf, c,
                                     row, h, Mts, zs, Zs);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's part of M^T and z has landed
