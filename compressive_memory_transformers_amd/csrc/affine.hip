@@ -44,14 +44,17 @@ __global__ __launch_bounds__(256) void colsum_kernel(AffineArgs a) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  // four rows per step, loaded before any is used, so four loads are in flight
+  // eight rows per step, loaded before any is used, so eight loads are in
+  // flight (with one workgroup per segment and two per CU, four left the
+  // kernel at about 4.3 TB/s, bound by the bytes in flight)
+  constexpr int UR = 8;
   int t = tl;
-  for (; t + 3 * TL < n_s; t += 4 * TL) {
-    frag_t<T> kv[4];
+  for (; t + (UR - 1) * TL < n_s; t += UR * TL) {
+    frag_t<T> kv[UR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kv[u] = load8<T>(K + (int64_t)(t + u * TL) * D);
+    for (int u = 0; u < UR; ++u) kv[u] = load8<T>(K + (int64_t)(t + u * TL) * D);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < UR; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += feature_map(to_f32<T>(kv[u][e]));
   }
