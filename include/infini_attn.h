@@ -44,8 +44,9 @@
  *
  * Streams: a forward call with more than one segment, a workspace of the
  * full size (infini_attn_workspace_size) and a memory scan in the direct form
- * (seg_len < d, or d_key != d_value) on a large call (B*Hq*L*d >= 2^26)
- * starts the attention of segment 0 at once and runs the scan of the later
+ * (seg_len < d, or d_key != d_value), or the linear rule's affine form over
+ * at least 64 segments, on a large call (B*Hq*L*d >= 2^26) starts the
+ * attention of segment 0 at once and runs the scan of the later
  * segments on an auxiliary stream beside it, in two windows, each window's
  * attention on `stream` waiting for its own window's scan (events). Every
  * other call runs on `stream` alone: each window's scan, then its attention.

@@ -1,7 +1,8 @@
 """The overlapped forward plan against the serial one, on the GPU.
 
 With a workspace of the full size and a direct-form memory scan (seg_len < d,
-or d_key != d_value) on a large call (B*Hq*L*d >= 2^26), a forward call
+or d_key != d_value), or the linear rule's affine form over at least 64
+segments, on a large call (B*Hq*L*d >= 2^26), a forward call
 starts segment 0's attention at once (from a snapshot of the initial state)
 and runs the memory scan of the later segments on an auxiliary stream beside
 the attention on the caller's stream. The arithmetic is the same kernels on
@@ -56,6 +57,16 @@ def _run(lib, inp, seg_len, rule, ws_bytes, lse=None):
 @pytest.mark.parametrize("dk,dv,seg_len", [(128, 128, 64), (64, 128, 256)])
 @pytest.mark.parametrize("rule", ["linear", "delta"])
 def test_overlapped_equals_serial(lib, rule, dk, dv, seg_len):
+    _overlapped_equals_serial(lib, rule, dk, dv, seg_len)
+
+
+def test_overlapped_linear_affine_equals_serial(lib):
+    # the affine form's linear prefix over 128 segments (>= 64) of 256 tokens
+    # also runs overlapped
+    _overlapped_equals_serial(lib, "linear", 128, 128, 256)
+
+
+def _overlapped_equals_serial(lib, rule, dk, dv, seg_len):
     B, Hq, Hkv = 2, 8, 2
     L = MIN_ELEMS // (B * Hq * dk)
     _say(f"bf16 B{B} Hq{Hq} Hkv{Hkv} d_key {dk} d_value {dv}, L {L}, seg_len {seg_len}, {rule}")
