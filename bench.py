@@ -6,7 +6,11 @@
 One step is one infini_attn_forward call over the whole workload (every
 segment, every head): the memory scan and the fused local-attention /
 retrieval / gate kernel, on synthetic Gaussian inputs already resident in HBM.
-W untimed steps, then K timed steps between two device synchronisations.
+W untimed steps, then K timed steps between two device synchronisations: the
+step captured once into a HIP graph and replayed K times (the same kernels on
+the same buffers, without the host's per-launch work between them; the mean
+of K eager calls is reported beside it, and per-step and per-phase HIP events
+come from the eager calls).
 Prints one JSON line: tokens/s (B*L / step time), TFLOP/s and its fraction of
 the bf16 MFMA peak, the roofline record of the dominant kernel (timed with HIP
 events on the stream it runs on) and the fp64 CPU oracle's rate on a bounded
@@ -418,7 +422,7 @@ def bench_block(lib, w, rule, dev, args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--rule", default=None, choices=["linear", "delta"])
@@ -442,6 +446,11 @@ def main():
                     help="sample the shader clock N times while steps run (0: skip)")
     ap.add_argument("--cpu-procs", type=int, default=16,
                     help="worker processes of the CPU oracle (at most the host's CPUs)")
+    ap.add_argument("--graph", type=int, default=1, choices=[0, 1],
+                    help="1 (forward mode): ms_per_step and value from replays of a HIP graph "
+                         "captured from one step (the same kernels, without the host's "
+                         "per-launch work between them), the eager mean reported beside it; "
+                         "0: from eager launches")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the steps, copy MIB MiB device to device once (a kernel "
                          "of known traffic that calibrates the HBM byte counters)")
@@ -525,6 +534,37 @@ def main():
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in phase)
     median_ms = step_ms[len(step_ms) // 2]
 
+    # the same step captured once into a HIP graph and replayed: the same
+    # kernels on the same buffers, without the host's per-launch work
+    # between them
+    graph_ms, graph_error = None, None
+    if args.graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                lib.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["M0"], inp["z0"],
+                            w.seg_len, rule, out=out, M_final=M, z_final=z, workspace=ws,
+                            stream=torch.cuda.current_stream(dev))
+        except RuntimeError as e:  # capture refused: the eager timing stands
+            g, graph_error = None, str(e)[:200]
+            torch.cuda.synchronize()
+        if g is not None:
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            gs.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            ge.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = gs.elapsed_time(ge) / args.steps
+            del g
+    eager_ms = ms
+    if graph_ms is not None:
+        ms = graph_ms
+
     # cold: each step after a 512 MiB device copy (outside its events) that
     # evicts the inputs from L2 and the 256 MB MALL
     cold_ms = None
@@ -607,6 +647,10 @@ def main():
         "hbm_gbs_compulsory": synth.hbm_bytes(w) / (ms * 1e-3) / 1e9,
         "phase_ms": {"scan_exposed": scan_ms, "attn": attn_ms},
         "plan": args.plan,
+        "timing": ("replays of a HIP graph captured from one step" if graph_ms is not None
+                   else "eager launches"),
+        "eager_ms_per_step": eager_ms,
+        "graph_error": graph_error,
         "ms_per_step_median": median_ms,
         "cold_ms_per_step_median": cold_ms,
         "sclk_mhz": sclk_mhz,
