@@ -8,7 +8,10 @@ overwritten, another forward call on other inputs through another workspace)
 and checks every replay against the eager call bit for bit: the one-pass plan
 (short segments), the serial split plan (the affine form), the overlapped
 plan (a direct scan on an auxiliary stream, forked from and joined back into
-the captured stream by events) and the fp32 path.
+the captured stream by events) and the fp32 path. The streaming decode
+step is captured too: one step at a fixed position, and a whole segment of
+steps (each with its own position, the fold into the state at the last) as
+one graph, replayed from reset state buffers.
 """
 
 import sys
@@ -91,3 +94,79 @@ def test_graph_replays_equal_eager(lib, case):
         for got, want in zip((out, M, z), ref):
             assert torch.equal(got, want), f"replay {rep} differs from the eager call"
     del g
+
+
+def test_decode_graphs_replay_equal_eager(lib):
+    # a decode step at a fixed position, and a whole segment of steps (each
+    # with its own position, the fold into the state at the last) as one
+    # graph, both replayed from reset state buffers
+    B, Hq, Hkv, d, N, rule = 2, 8, 2, 128, 64, "delta"
+    _say(f"decode B{B} Hq{Hq} Hkv{Hkv} d{d} N{N} {rule}")
+    g = torch.Generator(device="cpu").manual_seed(41)
+    mk = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16).to(DEV)
+    q = [mk(B, Hq, d) for _ in range(N)]
+    k = [mk(B, Hkv, d) for _ in range(N)]
+    v = [mk(B, Hkv, d) for _ in range(N)]
+    beta = torch.randn(Hq, generator=g).to(DEV)
+    kc0 = torch.zeros(B, Hkv, N, d, dtype=torch.bfloat16, device=DEV)
+    M0 = (0.1 * torch.randn(B, Hkv, d, d, generator=g)).to(DEV)
+    z0 = (0.5 + torch.rand(B, Hkv, d, generator=g)).to(DEV)
+    ws = torch.empty(lib.decode_workspace_size(B, Hq, Hkv, d, N, rule, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    kc, vc = kc0.clone(), kc0.clone()
+    M, z = M0.clone(), z0.clone()
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=DEV)
+    outs = torch.empty(N, B, Hq, d, dtype=torch.bfloat16, device=DEV)
+
+    def segment(stream):
+        for pos in range(N):
+            lib.decode_step(q[pos], k[pos], v[pos], beta, kc, vc, M, z, pos, rule, out=out,
+                            workspace=ws, stream=stream)
+            outs[pos].copy_(out)
+
+    def reset():
+        kc.copy_(kc0)
+        vc.copy_(kc0)
+        M.copy_(M0)
+        z.copy_(z0)
+        outs.fill_(float("nan"))
+
+    cur = torch.cuda.current_stream(DEV)
+    segment(cur)
+    torch.cuda.synchronize()
+    ref = (outs.clone(), kc.clone(), vc.clone(), M.clone(), z.clone())
+    reset()
+    gseg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gseg):
+        segment(torch.cuda.current_stream(DEV))
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        gseg.replay()
+        torch.cuda.synchronize()
+        _say(f"segment replay {rep}")
+        for got, want in zip((outs, kc, vc, M, z), ref):
+            assert torch.equal(got, want), f"segment replay {rep} differs from the eager steps"
+
+    # one step at a full cache (no fold), against an eager call of it
+    pos = N - 2
+    lib.decode_step(q[pos], k[pos], v[pos], beta, kc, vc, M, z, pos, rule, out=out,
+                    workspace=ws, stream=cur)
+    torch.cuda.synchronize()
+    want = out.clone()
+    gstep = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gstep):
+        lib.decode_step(q[pos], k[pos], v[pos], beta, kc, vc, M, z, pos, rule, out=out,
+                        workspace=ws, stream=torch.cuda.current_stream(DEV))
+    kc2, vc2, M2, z2 = kc0.clone(), kc0.clone(), M0.clone(), z0.clone()
+    ws2, out2 = torch.empty_like(ws), torch.empty_like(out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        # eager work between: a step on other buffers
+        lib.decode_step(q[1], k[1], v[1], beta, kc2, vc2, M2, z2, 3, rule, out=out2,
+                        workspace=ws2, stream=cur)
+        torch.cuda.synchronize()
+        gstep.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"step replay {rep} differs from the eager step"
+    del gseg, gstep
