@@ -582,7 +582,6 @@ def main():
         if g is not None:
             for _ in range(args.warmup):
                 g.replay()
-            torch.cuda.synchronize()
             gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             gs.record(stream)
